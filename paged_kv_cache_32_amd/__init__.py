@@ -1,0 +1,216 @@
+"""paged_kv_cache_32_amd: paged-attention decode over a block-table KV cache
+for AMD Instinct MI355X (gfx950).
+
+The compute lives in ``lib/libpa.so`` (hand-written HIP kernels behind the C
+ABI in ``include/pa.h``).  This module is the thin Python binding: it checks
+torch tensors (device, dtype, contiguity, shapes), passes their device
+pointers and the current HIP stream to the C entry points of the same name,
+and raises on any non-OK status.  It computes nothing itself and has no
+fallback: without the built library every call raises.
+
+    pa_cache_write(k, v, slot_mapping, k_cache, v_cache, block_size=...)
+    pa_cache_write_fp8(k, v, slot_mapping, k_cache, v_cache, k_scale, v_scale, block_size=...)
+    pa_decode(q, k_cache, v_cache, block_tables, seq_lens, scale, out, block_size=...)
+    pa_decode_fp8(q, k_cache, v_cache, block_tables, seq_lens, scale, out, k_scale, v_scale, ...)
+    pa_decode_workspace_size(...)
+
+Cache tensors are flat (or any contiguous shape) with num_blocks *
+num_kv_heads * block_size * head_dim elements, bfloat16 for the bf16 cache
+and uint8 (e4m3fn codes) for the fp8 cache, in the tiled layout documented
+in ``include/pa.h``.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "libpa.so")
+
+PA_OK = 0
+_STATUS = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_UNSUPPORTED",
+           -4: "PA_ERR_WORKSPACE", -5: "PA_ERR_LAUNCH", -6: "PA_ERR_DEVICE"}
+
+
+class PagedAttentionError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn}: {msg} (status {status})")
+        self.status = status
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libpa.so is not built ({LIB_PATH}); run "
+                          "`python -m paged_kv_cache_32_amd.build` (gfx950 HIP library)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    dp = ctypes.POINTER(CacheDesc)
+    sigs = {
+        "pa_cache_write": ([dp, vp, vp, vp, i32, vp, vp, vp], i32),
+        "pa_cache_write_fp8": ([dp, vp, vp, vp, i32, vp, vp, f32, f32, vp], i32),
+        "pa_decode_workspace_size": ([dp, i32, i32, i32, i32], sz),
+        "pa_decode": ([dp, vp, i32, i32, vp, vp, vp, i32, vp, f32, vp, i32, vp, sz, vp], i32),
+        "pa_decode_fp8": ([dp, vp, i32, i32, vp, vp, vp, i32, vp, f32, f32, f32, vp, i32, vp, sz,
+                           vp], i32),
+        "pa_status_string": ([i32], ctypes.c_char_p),
+        "pa_abi_version": ([], i32),
+    }
+    for name, (args, res) in sigs.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def lib():
+    """The loaded ctypes library (raises ImportError if it is not built)."""
+    return _load()
+
+
+def _check(fn, status):
+    if status != PA_OK:
+        msg = _load().pa_status_string(status).decode()
+        raise PagedAttentionError(fn, status, msg)
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _need(t, name, dtype, device, ndim=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def make_desc(k_cache, num_kv_heads, head_dim, block_size):
+    per_block = num_kv_heads * block_size * head_dim
+    if per_block <= 0 or k_cache.numel() % per_block:
+        raise ValueError("cache size is not a whole number of blocks")
+    return CacheDesc(k_cache.numel() // per_block, block_size, num_kv_heads, head_dim)
+
+
+def _cache_write(fp8, k, v, slot_mapping, k_cache, v_cache, block_size, k_scale, v_scale):
+    dev = k.device
+    if dev.type != "cuda":
+        raise ValueError("pa_cache_write needs device tensors")
+    _need(k, "k", torch.bfloat16, dev, 3)
+    T, Hkv, D = k.shape
+    _need(v, "v", torch.bfloat16, dev, shape=k.shape)
+    _need(slot_mapping, "slot_mapping", torch.int64, dev, shape=(T,))
+    cdt = torch.uint8 if fp8 else torch.bfloat16
+    _need(k_cache, "k_cache", cdt, dev)
+    _need(v_cache, "v_cache", cdt, dev)
+    if v_cache.numel() != k_cache.numel():
+        raise ValueError("k_cache and v_cache differ in size")
+    desc = make_desc(k_cache, Hkv, D, block_size)
+    L = _load()
+    with torch.cuda.device(dev):
+        if fp8:
+            st = L.pa_cache_write_fp8(ctypes.byref(desc), _ptr(k), _ptr(v), _ptr(slot_mapping), T,
+                                      _ptr(k_cache), _ptr(v_cache), float(k_scale), float(v_scale),
+                                      _stream(k))
+        else:
+            st = L.pa_cache_write(ctypes.byref(desc), _ptr(k), _ptr(v), _ptr(slot_mapping), T,
+                                  _ptr(k_cache), _ptr(v_cache), _stream(k))
+    _check("pa_cache_write_fp8" if fp8 else "pa_cache_write", st)
+
+
+def pa_cache_write(k, v, slot_mapping, k_cache, v_cache, block_size):
+    """Scatter k, v [T, Hkv, D] bf16 into the bf16 caches at slot_mapping [T]
+    int64 (slot < 0: skip).  See pa_cache_write in include/pa.h."""
+    _cache_write(False, k, v, slot_mapping, k_cache, v_cache, block_size, 1.0, 1.0)
+
+
+def pa_cache_write_fp8(k, v, slot_mapping, k_cache, v_cache, k_scale, v_scale, block_size):
+    """As pa_cache_write into uint8 e4m3fn caches with per-tensor scales."""
+    _cache_write(True, k, v, slot_mapping, k_cache, v_cache, block_size, k_scale, v_scale)
+
+
+def pa_decode_workspace_size(num_blocks, block_size, num_kv_heads, head_dim, num_seqs,
+                             num_q_heads, max_blocks_per_seq, partition_tokens=0):
+    """Workspace bytes pa_decode needs on the current device."""
+    desc = CacheDesc(num_blocks, block_size, num_kv_heads, head_dim)
+    return int(_load().pa_decode_workspace_size(ctypes.byref(desc), num_seqs, num_q_heads,
+                                                max_blocks_per_seq, partition_tokens))
+
+
+def _decode(fp8, q, k_cache, v_cache, block_tables, seq_lens, scale, out, num_kv_heads,
+            block_size, k_scale, v_scale, partition_tokens, workspace):
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("pa_decode needs device tensors")
+    _need(q, "q", torch.bfloat16, dev, 3)
+    S, Hq, D = q.shape
+    cdt = torch.uint8 if fp8 else torch.bfloat16
+    _need(k_cache, "k_cache", cdt, dev)
+    _need(v_cache, "v_cache", cdt, dev)
+    if v_cache.numel() != k_cache.numel():
+        raise ValueError("k_cache and v_cache differ in size")
+    _need(block_tables, "block_tables", torch.int32, dev, 2)
+    if block_tables.shape[0] != S:
+        raise ValueError("block_tables must have one row per sequence")
+    _need(seq_lens, "seq_lens", torch.int32, dev, shape=(S,))
+    if out is None:
+        out = torch.empty((S, Hq, D), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, dev, shape=(S, Hq, D))
+    desc = make_desc(k_cache, num_kv_heads, D, block_size)
+    maxb = block_tables.shape[1]
+    L = _load()
+    with torch.cuda.device(dev):
+        if workspace is None:
+            need = L.pa_decode_workspace_size(ctypes.byref(desc), S, Hq, maxb, partition_tokens)
+            if need == 0 and S > 0:
+                raise PagedAttentionError("pa_decode_workspace_size", -6,
+                                          "no gfx950 device or invalid sizes")
+            workspace = torch.empty(max(int(need), 1), dtype=torch.uint8, device=dev)
+        _need(workspace, "workspace", torch.uint8, dev)
+        args = [ctypes.byref(desc), _ptr(q), S, Hq, _ptr(k_cache), _ptr(v_cache),
+                _ptr(block_tables), maxb, _ptr(seq_lens), float(scale)]
+        if fp8:
+            args += [float(k_scale), float(v_scale)]
+        args += [_ptr(out), int(partition_tokens), _ptr(workspace), workspace.numel(), _stream(q)]
+        st = (L.pa_decode_fp8 if fp8 else L.pa_decode)(*args)
+    _check("pa_decode_fp8" if fp8 else "pa_decode", st)
+    return out
+
+
+def pa_decode(q, k_cache, v_cache, block_tables, seq_lens, scale, out=None, *, num_kv_heads,
+              block_size, partition_tokens=0, workspace=None):
+    """Paged decode over a bf16 cache: q [S, Hq, D] bf16 -> out [S, Hq, D]
+    float32.  See pa_decode in include/pa.h."""
+    return _decode(False, q, k_cache, v_cache, block_tables, seq_lens, scale, out, num_kv_heads,
+                   block_size, 1.0, 1.0, partition_tokens, workspace)
+
+
+def pa_decode_fp8(q, k_cache, v_cache, block_tables, seq_lens, scale, k_scale, v_scale, out=None,
+                  *, num_kv_heads, block_size, partition_tokens=0, workspace=None):
+    """Paged decode over an e4m3fn cache with per-tensor scales."""
+    return _decode(True, q, k_cache, v_cache, block_tables, seq_lens, scale, out, num_kv_heads,
+                   block_size, k_scale, v_scale, partition_tokens, workspace)

@@ -1,0 +1,252 @@
+// extern "C" entry points of libpa.so: host-side validation, workspace
+// sizing and kernel launches.  See include/pa.h for the contract.
+#include <math.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "../../include/pa.h"
+#include "pa_internal.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+constexpr int kMaxGroup = 16;
+constexpr int kMaxBlockSize = 256;
+constexpr int kChunkMinAuto = 16;  // at least 256 tokens per wavefront when splitting automatically
+
+struct DeviceInfo {
+  bool queried = false;
+  bool gfx950 = false;
+  int resident[2][2] = {{0, 0}, {0, 0}};  // [head_dim == 128][fp8]
+};
+DeviceInfo g_dev[kMaxDevices];
+std::mutex g_mu;
+
+// Is the current device a gfx950, and how many decode wavefronts fit on it?
+bool device_info(int head_dim, bool fp8, int* resident) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return false;
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceInfo& d = g_dev[dev];
+  if (!d.queried) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return false;
+    d.gfx950 = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    d.queried = true;
+  }
+  if (!d.gfx950) return false;
+  int& r = d.resident[head_dim == 128][fp8];
+  if (r == 0) r = pa::decode_resident_waves(head_dim, fp8);
+  *resident = r;
+  return r > 0;
+}
+
+bool valid_desc(const pa_cache_desc* c) {
+  return c->num_blocks >= 1 && c->num_kv_heads >= 1 && c->block_size >= pa::kSub &&
+         c->block_size <= kMaxBlockSize && c->block_size % pa::kSub == 0 &&
+         (c->head_dim == 64 || c->head_dim == 128);
+}
+
+pa_status desc_status(const pa_cache_desc* c) {
+  if (c->num_blocks < 1 || c->num_kv_heads < 1 || c->block_size < 1 || c->head_dim < 1)
+    return PA_ERR_SHAPE;
+  if (!valid_desc(c)) return PA_ERR_UNSUPPORTED;
+  // Element offsets must fit in 63 bits with room to spare.
+  const double elems = (double)c->num_blocks * c->num_kv_heads * c->block_size * c->head_dim;
+  if (elems > 4.0e18) return PA_ERR_SHAPE;
+  return PA_OK;
+}
+
+bool good_scale(float s) { return isfinite(s) && s > 0.f; }
+
+pa_status cache_write(const pa_cache_desc* cache, const void* k, const void* v,
+                      const int64_t* slot_mapping, int32_t num_tokens, void* k_cache,
+                      void* v_cache, bool fp8, float k_scale, float v_scale, void* stream) {
+  if (!cache) return PA_ERR_NULL;
+  pa_status st = desc_status(cache);
+  if (st != PA_OK) return st;
+  if (num_tokens < 0) return PA_ERR_SHAPE;
+  if (fp8 && (!good_scale(k_scale) || !good_scale(v_scale))) return PA_ERR_SHAPE;
+  if (num_tokens == 0) return PA_OK;
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache) return PA_ERR_NULL;
+  int resident = 0;
+  if (!device_info(cache->head_dim, fp8, &resident)) return PA_ERR_DEVICE;
+  pa::CacheWriteParams p;
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.slots = slot_mapping;
+  p.k_cache = static_cast<uint8_t*>(k_cache);
+  p.v_cache = static_cast<uint8_t*>(v_cache);
+  p.num_tokens = num_tokens;
+  p.num_kv_heads = cache->num_kv_heads;
+  p.head_dim = cache->head_dim;
+  p.block_size = cache->block_size;
+  p.num_slots = (int64_t)cache->num_blocks * cache->block_size;
+  // Correctly rounded float32 reciprocals (IEEE division on the host).
+  volatile float one = 1.0f;
+  p.k_inv = fp8 ? one / k_scale : 1.0f;
+  p.v_inv = fp8 ? one / v_scale : 1.0f;
+  if (pa::launch_cache_write(p, fp8, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return PA_ERR_LAUNCH;
+  return PA_OK;
+}
+
+// Wavefronts to launch and the fixed chunk count per wavefront (0 = auto).
+pa_status plan(const pa_cache_desc* c, int32_t num_seqs, int32_t num_q_heads,
+               int32_t max_blocks_per_seq, int32_t partition_tokens, bool fp8,
+               int64_t* num_waves, int32_t* chunk_fixed) {
+  if (!c) return PA_ERR_NULL;
+  pa_status st = desc_status(c);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || num_q_heads < 1 || max_blocks_per_seq < 0) return PA_ERR_SHAPE;
+  if (num_q_heads % c->num_kv_heads != 0) return PA_ERR_SHAPE;
+  if (num_q_heads / c->num_kv_heads > kMaxGroup) return PA_ERR_UNSUPPORTED;
+  if (partition_tokens < 0 || partition_tokens % pa::kSub != 0) return PA_ERR_SHAPE;
+  if ((int64_t)max_blocks_per_seq * c->block_size > INT32_MAX) return PA_ERR_SHAPE;
+  int resident = 0;
+  if (!device_info(c->head_dim, fp8, &resident)) return PA_ERR_DEVICE;
+  if (partition_tokens == 0) {
+    *num_waves = resident;
+    *chunk_fixed = 0;
+  } else {
+    const int64_t per = partition_tokens / pa::kSub;
+    const int64_t chunks_per_seq = ((int64_t)max_blocks_per_seq * c->block_size + pa::kSub - 1) / pa::kSub;
+    const int64_t upper = (int64_t)num_seqs * c->num_kv_heads * chunks_per_seq;
+    int64_t w = (upper + per - 1) / per;
+    if (w < 1) w = 1;
+    if (w > (int64_t)INT32_MAX - pa::kWavesPerGroup) return PA_ERR_SHAPE;
+    *num_waves = w;
+    *chunk_fixed = (int32_t)per;
+  }
+  return PA_OK;
+}
+
+pa_status decode(const pa_cache_desc* cache, const void* q, int32_t num_seqs, int32_t num_q_heads,
+                 const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                 int32_t max_blocks_per_seq, const int32_t* seq_lens, float scale, float k_scale,
+                 float v_scale, bool fp8, float* out, int32_t partition_tokens, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  if (!cache) return PA_ERR_NULL;
+  if (!isfinite(scale)) return PA_ERR_SHAPE;
+  if (fp8 && (!good_scale(k_scale) || !good_scale(v_scale))) return PA_ERR_SHAPE;
+  int64_t num_waves = 0;
+  int32_t chunk_fixed = 0;
+  // Shape checks that need no device come first.
+  {
+    pa_status st = desc_status(cache);
+    if (st != PA_OK) return st;
+    if (num_seqs < 0 || num_q_heads < 1 || max_blocks_per_seq < 0) return PA_ERR_SHAPE;
+    if (num_q_heads % cache->num_kv_heads != 0) return PA_ERR_SHAPE;
+    if (num_q_heads / cache->num_kv_heads > kMaxGroup) return PA_ERR_UNSUPPORTED;
+    if (partition_tokens < 0 || partition_tokens % pa::kSub != 0) return PA_ERR_SHAPE;
+  }
+  if (num_seqs == 0) return PA_OK;
+  if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !out) return PA_ERR_NULL;
+  if (!workspace) return PA_ERR_WORKSPACE;
+  pa_status st = plan(cache, num_seqs, num_q_heads, max_blocks_per_seq, partition_tokens, fp8,
+                      &num_waves, &chunk_fixed);
+  if (st != PA_OK) return st;
+  const int group = num_q_heads / cache->num_kv_heads;
+  const pa::WorkspaceLayout lay = pa::workspace_layout(num_waves, group, cache->head_dim, num_seqs);
+  if (workspace_bytes < lay.total) return PA_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  pa::DecodeParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k_cache = static_cast<const uint8_t*>(k_cache);
+  p.v_cache = static_cast<const uint8_t*>(v_cache);
+  p.block_tables = block_tables;
+  p.seq_lens = seq_lens;
+  p.out = out;
+  p.partials = reinterpret_cast<float*>(ws + lay.partials_off);
+  p.cum = reinterpret_cast<int32_t*>(ws + lay.cum_off);
+  p.meta = reinterpret_cast<int64_t*>(ws + lay.meta_off);
+  p.num_seqs = num_seqs;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = cache->num_kv_heads;
+  p.group = group;
+  p.head_dim = cache->head_dim;
+  p.block_size = cache->block_size;
+  p.num_blocks = cache->num_blocks;
+  p.max_blocks = max_blocks_per_seq;
+  p.num_waves = (int32_t)num_waves;
+  p.chunk_min = kChunkMinAuto;
+  p.chunk_fixed = chunk_fixed;
+  p.qk_scale = scale * 1.4426950408889634f * (fp8 ? k_scale : 1.0f);
+  p.out_scale = fp8 ? v_scale : 1.0f;
+  if (pa::launch_decode(p, fp8, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return PA_ERR_LAUNCH;
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_cache_write(const pa_cache_desc* cache, const void* k, const void* v,
+                         const int64_t* slot_mapping, int32_t num_tokens, void* k_cache,
+                         void* v_cache, void* stream) {
+  return cache_write(cache, k, v, slot_mapping, num_tokens, k_cache, v_cache, false, 1.f, 1.f,
+                     stream);
+}
+
+pa_status pa_cache_write_fp8(const pa_cache_desc* cache, const void* k, const void* v,
+                             const int64_t* slot_mapping, int32_t num_tokens, void* k_cache,
+                             void* v_cache, float k_scale, float v_scale, void* stream) {
+  return cache_write(cache, k, v, slot_mapping, num_tokens, k_cache, v_cache, true, k_scale,
+                     v_scale, stream);
+}
+
+size_t pa_decode_workspace_size(const pa_cache_desc* cache, int32_t num_seqs, int32_t num_q_heads,
+                                int32_t max_blocks_per_seq, int32_t partition_tokens) {
+  int64_t w16 = 0, w8 = 0;
+  int32_t cf = 0;
+  if (plan(cache, num_seqs, num_q_heads, max_blocks_per_seq, partition_tokens, false, &w16, &cf) !=
+      PA_OK)
+    return 0;
+  if (plan(cache, num_seqs, num_q_heads, max_blocks_per_seq, partition_tokens, true, &w8, &cf) !=
+      PA_OK)
+    return 0;
+  const int group = num_q_heads / cache->num_kv_heads;
+  const pa::WorkspaceLayout lay =
+      pa::workspace_layout(w16 > w8 ? w16 : w8, group, cache->head_dim, num_seqs);
+  return lay.total;
+}
+
+pa_status pa_decode(const pa_cache_desc* cache, const void* q, int32_t num_seqs,
+                    int32_t num_q_heads, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* seq_lens, float scale, float* out, int32_t partition_tokens,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  return decode(cache, q, num_seqs, num_q_heads, k_cache, v_cache, block_tables,
+                max_blocks_per_seq, seq_lens, scale, 1.f, 1.f, false, out, partition_tokens,
+                workspace, workspace_bytes, stream);
+}
+
+pa_status pa_decode_fp8(const pa_cache_desc* cache, const void* q, int32_t num_seqs,
+                        int32_t num_q_heads, const void* k_cache, const void* v_cache,
+                        const int32_t* block_tables, int32_t max_blocks_per_seq,
+                        const int32_t* seq_lens, float scale, float k_scale, float v_scale,
+                        float* out, int32_t partition_tokens, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  return decode(cache, q, num_seqs, num_q_heads, k_cache, v_cache, block_tables,
+                max_blocks_per_seq, seq_lens, scale, k_scale, v_scale, true, out,
+                partition_tokens, workspace, workspace_bytes, stream);
+}
+
+const char* pa_status_string(pa_status s) {
+  switch (s) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_NULL: return "PA_ERR_NULL: a required pointer is NULL";
+    case PA_ERR_SHAPE: return "PA_ERR_SHAPE: sizes inconsistent or out of range";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: head_dim, block_size or group size not supported";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
+    case PA_ERR_LAUNCH: return "PA_ERR_LAUNCH: the HIP runtime reported an error";
+    case PA_ERR_DEVICE: return "PA_ERR_DEVICE: no gfx950 device is current";
+  }
+  return "unknown pa_status";
+}
+
+int32_t pa_abi_version(void) { return PA_ABI_VERSION; }
+
+}  // extern "C"

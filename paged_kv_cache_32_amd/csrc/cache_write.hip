@@ -1,0 +1,111 @@
+// Slot scatter of new tokens' K/V into the paged cache (bf16 and fp8).
+//
+// A slot is a physical token position, block * block_size + offset; the new
+// token of a sequence goes to the slot its block table gives for its
+// position ("Taming the token torrent", "The Block Table Logic";
+// rajatmohan.com serving design, "Paging, because contiguous allocation is
+// a disaster").  The fp8 variant stores e4m3fn codes of x / scale, rounded
+// to nearest even and saturated ("KV Cache Engineering for LLM Serving",
+// section 8, Quantization).
+//
+// The write is a few hundred bytes per token: it is latency bound, so the
+// kernel is one thread per 16-byte K chunk of a (token, kv head) row, with
+// the matching V elements, and no attempt at more.
+#include "pa_internal.h"
+
+namespace pa {
+
+namespace {
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// e4m3fn code of float32(x * inv): round to nearest even, saturate to
+// +-448, NaN -> 0x7F with x's sign.  Clamping first keeps the hardware
+// conversion inside the finite range, where it rounds to nearest even.
+__device__ __forceinline__ uint32_t e4m3_code(float x, float inv) {
+  if (__builtin_isnan(x)) return (__float_as_uint(x) >> 24 & 0x80u) | 0x7Fu;
+  float y = x * inv;
+  y = __builtin_fminf(__builtin_fmaxf(y, -448.0f), 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y, y, 0, false) & 0xFFu;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// One thread per (token, kv head, group of X elements), X = 16 bytes of
+// cache: 8 bf16 values or 16 fp8 codes.
+template <bool FP8>
+__global__ __launch_bounds__(256) void cache_write_kernel(const CacheWriteParams p) {
+  constexpr int X = FP8 ? 16 : 8;
+  const int groups = p.head_dim / X;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_token = (int64_t)p.num_kv_heads * groups;
+  if (gid >= (int64_t)p.num_tokens * per_token) return;
+  const int j = (int)(gid / per_token);
+  const int rem = (int)(gid - (int64_t)j * per_token);
+  const int h = rem / groups;
+  const int dg = rem - h * groups;
+
+  const int64_t slot = p.slots[j];
+  if (slot < 0 || slot >= p.num_slots) return;
+  const int64_t blk = slot / p.block_size;
+  const int off = (int)(slot - blk * p.block_size);
+  const int sub = off / kSub, r = off % kSub;
+  const int subs = p.block_size / kSub;
+  // Byte offset of this (block, head, sub-block) tile; K and V tiles have the
+  // same size: 16 tokens x head_dim elements.
+  const int eb = FP8 ? 1 : 2;
+  const int64_t tile = (((blk * p.num_kv_heads + h) * subs + sub) * (int64_t)(kSub * p.head_dim)) * eb;
+
+  const int64_t src = ((int64_t)j * p.num_kv_heads + h) * p.head_dim + (int64_t)dg * X;
+  uint8_t* kdst = p.k_cache + tile + ((int64_t)dg * kSub + r) * 16;    // [d/X][t%16][X]
+  uint8_t* vtile = p.v_cache + tile;                                   // [d][t%16]
+  if (!FP8) {
+    const u32x4 kv = *reinterpret_cast<const u32x4*>(p.k + src);
+    *reinterpret_cast<u32x4*>(kdst) = kv;
+    const u32x4 vv = *reinterpret_cast<const u32x4*>(p.v + src);
+    uint16_t* vdst = reinterpret_cast<uint16_t*>(vtile);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t w = vv[e >> 1];
+      vdst[(dg * 8 + e) * kSub + r] = (uint16_t)((e & 1) ? (w >> 16) : (w & 0xFFFFu));
+    }
+  } else {
+    u32x4 kin[2], vin[2];
+    kin[0] = *reinterpret_cast<const u32x4*>(p.k + src);
+    kin[1] = *reinterpret_cast<const u32x4*>(p.k + src + 8);
+    vin[0] = *reinterpret_cast<const u32x4*>(p.v + src);
+    vin[1] = *reinterpret_cast<const u32x4*>(p.v + src + 8);
+    u32x4 kout = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const uint32_t w = kin[e >> 3][(e >> 1) & 3];
+      const uint32_t code = e4m3_code(bf16_to_f32((e & 1) ? (w >> 16) : (w & 0xFFFFu)), p.k_inv);
+      kout[e >> 2] |= code << (8 * (e & 3));
+    }
+    *reinterpret_cast<u32x4*>(kdst) = kout;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const uint32_t w = vin[e >> 3][(e >> 1) & 3];
+      const uint32_t code = e4m3_code(bf16_to_f32((e & 1) ? (w >> 16) : (w & 0xFFFFu)), p.v_inv);
+      vtile[(dg * 16 + e) * kSub + r] = (uint8_t)code;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_cache_write(const CacheWriteParams& p, bool fp8, hipStream_t stream) {
+  const int X = fp8 ? 16 : 8;
+  const int64_t threads = (int64_t)p.num_tokens * p.num_kv_heads * (p.head_dim / X);
+  if (threads == 0) return hipSuccess;
+  const int64_t blocks = (threads + 255) / 256;
+  if (fp8)
+    hipLaunchKernelGGL(cache_write_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(cache_write_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,67 @@
+// Internal declarations shared by the HIP translation units of libpa.so.
+// Nothing here is part of the C ABI (see include/pa.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+// Tokens per cache sub-block: the unit one wavefront's MFMA tile covers.
+constexpr int kSub = 16;
+// Threads per workgroup of the decode kernel: four independent wavefronts.
+constexpr int kWavesPerGroup = 4;
+constexpr int kDecodeThreads = 64 * kWavesPerGroup;
+
+struct CacheWriteParams {
+  const uint16_t* k;          // [T][Hkv][D] bf16 bits
+  const uint16_t* v;
+  const int64_t* slots;       // [T]
+  uint8_t* k_cache;
+  uint8_t* v_cache;
+  int32_t num_tokens, num_kv_heads, head_dim, block_size;
+  int64_t num_slots;          // num_blocks * block_size
+  float k_inv, v_inv;         // 1 / scale (fp8 only)
+};
+
+struct DecodeParams {
+  const uint16_t* q;          // [S][Hq][D] bf16 bits
+  const uint8_t* k_cache;
+  const uint8_t* v_cache;
+  const int32_t* block_tables;  // [S][max_blocks]
+  const int32_t* seq_lens;      // [S]
+  float* out;                   // [S][Hq][D]
+  float* partials;              // [2 * num_waves][G * (D + 4)]
+  int32_t* cum;                 // [S + 1] chunk prefix per sequence (written by wave 0)
+  int64_t* meta;                // [0] chunks per wave, [1] total chunks
+  int32_t num_seqs, num_q_heads, num_kv_heads, group, head_dim, block_size, num_blocks, max_blocks;
+  int32_t num_waves;            // wavefronts launched
+  int32_t chunk_min;            // auto split: fewest chunks a wavefront takes
+  int32_t chunk_fixed;          // > 0: every wavefront takes this many chunks
+  float qk_scale;               // scale * log2(e) (* k_scale for fp8)
+  float out_scale;              // 1 (bf16) or v_scale (fp8)
+};
+
+// Host-side launchers (defined next to their kernels).
+hipError_t launch_cache_write(const CacheWriteParams& p, bool fp8, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, bool fp8, hipStream_t stream);
+// Resident wavefronts of the decode kernel on the current device (0 on error).
+int decode_resident_waves(int head_dim, bool fp8);
+
+// Workspace carve-up shared by the size query and the launcher.
+struct WorkspaceLayout {
+  size_t partials_off, cum_off, meta_off, total;
+};
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline WorkspaceLayout workspace_layout(int64_t num_waves, int group, int head_dim,
+                                        int num_seqs) {
+  WorkspaceLayout w;
+  w.partials_off = 0;
+  size_t part = (size_t)(2 * num_waves) * (size_t)group * (size_t)(head_dim + 4) * sizeof(float);
+  w.cum_off = align_up(part, 256);
+  w.meta_off = align_up(w.cum_off + (size_t)(num_seqs + 1) * sizeof(int32_t), 256);
+  w.total = w.meta_off + 256;
+  return w;
+}
+
+}  // namespace pa

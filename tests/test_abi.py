@@ -1,0 +1,119 @@
+"""The C ABI without a GPU: the library loads, exports every entry point the
+header declares, and rejects bad arguments on the host with the documented
+status codes before anything is launched."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_cache_32_amd as pa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+
+if not os.path.exists(pa.LIB_PATH):
+    pytest.skip("libpa.so not built", allow_module_level=True)
+
+OK, NULL, SHAPE, UNSUP, WS, LAUNCH, DEVICE = 0, -1, -2, -3, -4, -5, -6
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+
+
+def declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", src)))
+
+
+def desc(nb=10, bs=16, hkv=2, d=128):
+    return pa.CacheDesc(nb, bs, hkv, d)
+
+
+def test_exports_every_declared_symbol():
+    lib = pa.lib()
+    names = declared()
+    assert set(names) >= {"pa_cache_write", "pa_cache_write_fp8", "pa_decode", "pa_decode_fp8",
+                          "pa_decode_workspace_size", "pa_status_string", "pa_abi_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.pa_abi_version() == 1
+
+
+def test_status_strings():
+    lib = pa.lib()
+    for code in (OK, NULL, SHAPE, UNSUP, WS, LAUNCH, DEVICE):
+        s = lib.pa_status_string(code).decode()
+        assert s.startswith(pa._STATUS[code])
+    assert lib.pa_status_string(42).decode() == "unknown pa_status"
+
+
+def cw(d, T=4, k=FAKE, slots=FAKE, fp8=False, ks=1.0, vs=1.0):
+    lib = pa.lib()
+    if fp8:
+        return lib.pa_cache_write_fp8(ctypes.byref(d) if d else None, k, k, slots, T, FAKE, FAKE,
+                                      ks, vs, None)
+    return lib.pa_cache_write(ctypes.byref(d) if d else None, k, k, slots, T, FAKE, FAKE, None)
+
+
+def test_cache_write_validation():
+    assert cw(None) == NULL
+    assert cw(desc(d=96)) == UNSUP
+    assert cw(desc(bs=24)) == UNSUP
+    assert cw(desc(bs=512)) == UNSUP
+    assert cw(desc(nb=0)) == SHAPE
+    assert cw(desc(hkv=0)) == SHAPE
+    assert cw(desc(), T=-1) == SHAPE
+    assert cw(desc(), T=0) == OK                     # no-op, nothing launched
+    assert cw(desc(), k=None) == NULL
+    assert cw(desc(), slots=None) == NULL
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        assert cw(desc(), fp8=True, ks=bad) == SHAPE
+        assert cw(desc(), fp8=True, vs=bad) == SHAPE
+
+
+def dec(d, S=2, Hq=16, maxb=4, scale=0.1, part=0, q=FAKE, ws=FAKE, wsb=1 << 30, fp8=False,
+        ks=1.0, vs=1.0):
+    lib = pa.lib()
+    dp = ctypes.byref(d) if d else None
+    if fp8:
+        return lib.pa_decode_fp8(dp, q, S, Hq, FAKE, FAKE, FAKE, maxb, FAKE, scale, ks, vs, FAKE,
+                                 part, ws, wsb, None)
+    return lib.pa_decode(dp, q, S, Hq, FAKE, FAKE, FAKE, maxb, FAKE, scale, FAKE, part, ws, wsb,
+                         None)
+
+
+def test_decode_validation():
+    assert dec(None) == NULL
+    assert dec(desc(d=32)) == UNSUP
+    assert dec(desc(), Hq=3) == SHAPE                  # not a multiple of num_kv_heads
+    assert dec(desc(), Hq=34) == UNSUP                 # group of 17 > 16
+    assert dec(desc(), S=-1) == SHAPE
+    assert dec(desc(), Hq=0) == SHAPE
+    assert dec(desc(), maxb=-1) == SHAPE
+    assert dec(desc(), part=24) == SHAPE
+    assert dec(desc(), part=-16) == SHAPE
+    assert dec(desc(), scale=float("nan")) == SHAPE
+    assert dec(desc(), S=0) == OK                      # empty batch: nothing to do
+    assert dec(desc(), q=None) == NULL
+    assert dec(desc(), ws=None) == WS
+    assert dec(desc(), fp8=True, ks=0.0) == SHAPE
+    assert dec(desc(), fp8=True, vs=float("inf")) == SHAPE
+
+
+def test_device_errors_without_gpu():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    # Valid arguments reach the device query, which fails without a gfx950.
+    assert dec(desc()) == DEVICE
+    assert cw(desc()) == DEVICE
+    d = desc()
+    assert pa.lib().pa_decode_workspace_size(ctypes.byref(d), 2, 16, 4, 0) == 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(pa, "_lib", None)
+    monkeypatch.setattr(pa, "LIB_PATH", "/nonexistent/libpa.so")
+    with pytest.raises(ImportError):
+        pa.lib()
