@@ -125,6 +125,12 @@ size_t pa_decode_workspace_size(const pa_cache_desc* cache, int32_t num_seqs,
                                 int32_t num_q_heads, int32_t max_blocks_per_seq,
                                 int32_t partition_tokens);
 
+/* Zero-fill a decode workspace on `stream` (a small fill kernel, so it may
+ * be captured in a HIP graph).  Call once after allocating a workspace, or
+ * after a call that did not run to completion.  workspace_bytes == 0 is a
+ * no-op.                                                                    */
+pa_status pa_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
+
 /* Paged-attention decode, bf16 cache.
  * For every sequence s < num_seqs and query head i < num_q_heads, with
  * h = i / (num_q_heads / num_kv_heads) and L = seq_lens[s]:
@@ -143,9 +149,14 @@ size_t pa_decode_workspace_size(const pa_cache_desc* cache, int32_t num_seqs,
  * Long sequences are split across wavefronts into partitions of
  * partition_tokens tokens (a multiple of 16; 0 = choose from the device's
  * resident-wave count so every wavefront gets an equal share), and the
- * partial softmax states are merged with a log-sum-exp reduction.
+ * partial softmax states are merged with a log-sum-exp reduction inside the
+ * same kernel launch.
  *   workspace     device buffer of >= pa_decode_workspace_size(...) bytes,
- *                 no initial contents required; overwritten by each call.
+ *                 zero-filled before its first use (pa_decode_workspace_init
+ *                 or any zero fill).  Each call leaves it ready for the
+ *                 next one (its per-unit counters back at zero), for any
+ *                 sizes that fit; it must not be shared by calls that may
+ *                 run at the same time (different streams).
  * Results differ from exact arithmetic only by float32 rounding.            */
 pa_status pa_decode(const pa_cache_desc* cache, const void* q, int32_t num_seqs,
                     int32_t num_q_heads, const void* k_cache, const void* v_cache,

@@ -12,7 +12,7 @@ fallback: without the built library every call raises.
     pa_cache_write_fp8(k, v, slot_mapping, k_cache, v_cache, k_scale, v_scale, block_size=...)
     pa_decode(q, k_cache, v_cache, block_tables, seq_lens, scale, out, block_size=...)
     pa_decode_fp8(q, k_cache, v_cache, block_tables, seq_lens, scale, out, k_scale, v_scale, ...)
-    pa_decode_workspace_size(...)
+    pa_decode_workspace_size(...), pa_decode_workspace_init(workspace)
 
 Cache tensors are flat (or any contiguous shape) with num_blocks *
 num_kv_heads * block_size * head_dim elements, bfloat16 for the bf16 cache
@@ -61,6 +61,7 @@ def _load():
         "pa_cache_write": ([dp, vp, vp, vp, i32, vp, vp, vp], i32),
         "pa_cache_write_fp8": ([dp, vp, vp, vp, i32, vp, vp, f32, f32, vp], i32),
         "pa_decode_workspace_size": ([dp, i32, i32, i32, i32], sz),
+        "pa_decode_workspace_init": ([vp, sz, vp], i32),
         "pa_decode": ([dp, vp, i32, i32, vp, vp, vp, i32, vp, f32, vp, i32, vp, sz, vp], i32),
         "pa_decode_fp8": ([dp, vp, i32, i32, vp, vp, vp, i32, vp, f32, f32, f32, vp, i32, vp, sz,
                            vp], i32),
@@ -161,6 +162,26 @@ def pa_decode_workspace_size(num_blocks, block_size, num_kv_heads, head_dim, num
                                                 max_blocks_per_seq, partition_tokens))
 
 
+def pa_decode_workspace_init(workspace):
+    """Zero-fill a decode workspace (uint8 device tensor) on the current stream."""
+    _need(workspace, "workspace", torch.uint8, workspace.device)
+    with torch.cuda.device(workspace.device):
+        st = _load().pa_decode_workspace_init(_ptr(workspace), workspace.numel(), _stream(workspace))
+    _check("pa_decode_workspace_init", st)
+
+
+def alloc_workspace(num_blocks, block_size, num_kv_heads, head_dim, num_seqs, num_q_heads,
+                    max_blocks_per_seq, partition_tokens=0, device="cuda"):
+    """A zero-filled workspace of the size pa_decode needs for these sizes."""
+    dev = torch.device(device)
+    with torch.cuda.device(dev):
+        n = pa_decode_workspace_size(num_blocks, block_size, num_kv_heads, head_dim, num_seqs,
+                                     num_q_heads, max_blocks_per_seq, partition_tokens)
+    if n == 0:
+        raise PagedAttentionError("pa_decode_workspace_size", -6, "no gfx950 device or invalid sizes")
+    return torch.zeros(n, dtype=torch.uint8, device=dev)
+
+
 def _decode(fp8, q, k_cache, v_cache, block_tables, seq_lens, scale, out, num_kv_heads,
             block_size, k_scale, v_scale, partition_tokens, workspace):
     dev = q.device
@@ -189,7 +210,7 @@ def _decode(fp8, q, k_cache, v_cache, block_tables, seq_lens, scale, out, num_kv
             if need == 0 and S > 0:
                 raise PagedAttentionError("pa_decode_workspace_size", -6,
                                           "no gfx950 device or invalid sizes")
-            workspace = torch.empty(max(int(need), 1), dtype=torch.uint8, device=dev)
+            workspace = torch.zeros(max(int(need), 1), dtype=torch.uint8, device=dev)
         _need(workspace, "workspace", torch.uint8, dev)
         args = [ctypes.byref(desc), _ptr(q), S, Hq, _ptr(k_cache), _ptr(v_cache),
                 _ptr(block_tables), maxb, _ptr(seq_lens), float(scale)]

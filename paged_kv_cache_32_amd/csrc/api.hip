@@ -148,7 +148,8 @@ pa_status decode(const pa_cache_desc* cache, const void* q, int32_t num_seqs, in
                       &num_waves, &chunk_fixed);
   if (st != PA_OK) return st;
   const int group = num_q_heads / cache->num_kv_heads;
-  const pa::WorkspaceLayout lay = pa::workspace_layout(num_waves, group, cache->head_dim, num_seqs);
+  const pa::WorkspaceLayout lay =
+      pa::workspace_layout(num_waves, group, cache->head_dim, num_seqs, cache->num_kv_heads);
   if (workspace_bytes < lay.total) return PA_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
   pa::DecodeParams p;
@@ -159,8 +160,7 @@ pa_status decode(const pa_cache_desc* cache, const void* q, int32_t num_seqs, in
   p.seq_lens = seq_lens;
   p.out = out;
   p.partials = reinterpret_cast<float*>(ws + lay.partials_off);
-  p.cum = reinterpret_cast<int32_t*>(ws + lay.cum_off);
-  p.meta = reinterpret_cast<int64_t*>(ws + lay.meta_off);
+  p.counters = reinterpret_cast<int32_t*>(ws + lay.counters_off);
   p.num_seqs = num_seqs;
   p.num_q_heads = num_q_heads;
   p.num_kv_heads = cache->num_kv_heads;
@@ -208,9 +208,19 @@ size_t pa_decode_workspace_size(const pa_cache_desc* cache, int32_t num_seqs, in
       PA_OK)
     return 0;
   const int group = num_q_heads / cache->num_kv_heads;
-  const pa::WorkspaceLayout lay =
-      pa::workspace_layout(w16 > w8 ? w16 : w8, group, cache->head_dim, num_seqs);
+  const pa::WorkspaceLayout lay = pa::workspace_layout(w16 > w8 ? w16 : w8, group, cache->head_dim,
+                                                       num_seqs, cache->num_kv_heads);
   return lay.total;
+}
+
+pa_status pa_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+  if (workspace_bytes == 0) return PA_OK;
+  if (!workspace) return PA_ERR_NULL;
+  int resident = 0;
+  if (!device_info(128, false, &resident)) return PA_ERR_DEVICE;
+  if (pa::launch_zero(workspace, workspace_bytes, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return PA_ERR_LAUNCH;
+  return PA_OK;
 }
 
 pa_status pa_decode(const pa_cache_desc* cache, const void* q, int32_t num_seqs,

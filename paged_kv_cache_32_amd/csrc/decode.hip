@@ -34,12 +34,27 @@
 //    list of 16-token chunks, and wavefront w takes chunks
 //    [w*C, (w+1)*C).  A unit that a wavefront covers completely is written
 //    to `out` directly; a piece of a unit is written as a partial softmax
-//    state and merged by merge_kernel (out = sum e^(m_p - M) acc_p /
-//    sum e^(m_p - M) l_p); a partial record is acc[G][D], m[G], l[G]
-//    padded to G * (D + 4) floats so every record is 16-byte aligned.
-//    Every wavefront scans seq_lens itself, so there is no planning kernel
-//    and no host synchronisation.
+//    state (acc[G][D], m[G], l[G], padded to G * (D + 4) floats so records
+//    stay 16-byte aligned).  Each piece is counted in with an agent-scope
+//    atomic once its (coherent, write-through) stores have completed; the
+//    wavefront that stores the last piece of a unit merges them (out = sum e^(m_p - M) acc_p / sum e^(m_p - M)
+//    l_p) and re-arms the counter to zero, so one kernel launch does the
+//    whole decode.  Every wavefront scans seq_lens itself, so there is no
+//    planning kernel and no host synchronisation.
 #include "pa_internal.h"
+
+// Sub-blocks loaded per online-softmax step, and the fewest wavefronts per
+// SIMD the register allocation must leave room for.
+#ifndef PA_DECODE_STAGE
+#define PA_DECODE_STAGE 4
+#endif
+#ifndef PA_DECODE_MIN_WAVES
+#define PA_DECODE_MIN_WAVES 1
+#endif
+// 1: K/V tiles are read with the non-temporal hint (read once, no reuse).
+#ifndef PA_DECODE_NT
+#define PA_DECODE_NT 1
+#endif
 
 namespace pa {
 
@@ -64,6 +79,12 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 }
 
 __device__ __forceinline__ int readlane(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+
+__device__ __forceinline__ int wave_reduce_sum(int v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+  return v;
+}
 
 // Chunks (16-token pieces) of a sequence; -1 marks an invalid length.
 __device__ __forceinline__ int chunks_of(int L, int max_len) {
@@ -99,6 +120,15 @@ __device__ __forceinline__ void split_p(const float p[4], i16x4& hi, i16x4& lo) 
   lo = as_i16x4(Lo);
 }
 
+template <typename V>
+__device__ __forceinline__ V load_kv(const V* p) {
+#if PA_DECODE_NT
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
+}
+
 template <int D, bool FP8>
 struct Tile {
   static constexpr int EB = FP8 ? 1 : 2;           // bytes per cache element
@@ -131,13 +161,13 @@ __device__ __forceinline__ void run_stage(const DecodeParams& p, int cnt, const 
     if (k < cnt) {
 #pragma unroll
       for (int c = 0; c < T::KLD; ++c)
-        kr[k][c] = *reinterpret_cast<const u32x4*>(kt[k] + c * 1024 + lane * 16);
+        kr[k][c] = load_kv(reinterpret_cast<const u32x4*>(kt[k] + c * 1024 + lane * 16));
 #pragma unroll
       for (int dc = 0; dc < T::DC; ++dc) {
         if constexpr (FP8)
-          vr[k][dc] = *reinterpret_cast<const uint32_t*>(vt[k] + dc * 256 + col * 16 + qd * 4);
+          vr[k][dc] = load_kv(reinterpret_cast<const uint32_t*>(vt[k] + dc * 256 + col * 16 + qd * 4));
         else
-          vr[k][dc] = *reinterpret_cast<const u32x2*>(vt[k] + dc * 512 + col * 32 + qd * 8);
+          vr[k][dc] = load_kv(reinterpret_cast<const u32x2*>(vt[k] + dc * 512 + col * 32 + qd * 8));
       }
     }
   }
@@ -230,8 +260,54 @@ __device__ __forceinline__ void run_stage(const DecodeParams& p, int cnt, const 
   }
 }
 
+// Partial records are shared between wavefronts that may sit on different
+// XCDs, whose L2 caches are not coherent with each other.  They are written
+// and read with agent-scope atomic accesses, which the gfx950 memory system
+// keeps coherent per instruction (write-through stores, L2-bypassing loads),
+// so no cache-wide write-back or invalidate is needed: a writer waits for its
+// stores to complete (s_waitcnt) before counting its piece in, and the merger
+// only loads after it has read the counter.
+__device__ __forceinline__ void store_shared(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_shared(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Merge the partial softmax states of unit (s, h), pieces from wavefronts
+// w0..w1, into out (run by the wavefront that stored the last piece):
+// out = sum_p e^(m_p - M) acc_p / sum_p e^(m_p - M) l_p, M = max_p m_p.
+template <int D>
+__device__ __forceinline__ void merge_unit(const DecodeParams& p, int s, int h, int64_t u0,
+                                           int64_t w0, int64_t w1, int64_t C, int lane) {
+  const int G = p.group;
+  const int64_t rec_len = (int64_t)G * (D + 4);
+  float* o = p.out + ((int64_t)s * p.num_q_heads + (int64_t)h * G) * D;
+  const int vec = G * D / 4;
+  for (int e = lane; e < vec; e += 64) {
+    const int g = e / (D / 4), d4 = e - g * (D / 4);
+    float M = kNegInf;
+    for (int64_t w = w0; w <= w1; ++w) {
+      const int64_t slot = (w == w0 && u0 != w0 * C) ? 2 * w + 1 : 2 * w;
+      M = __builtin_fmaxf(M, load_shared(p.partials + slot * rec_len + (int64_t)G * D + g));
+    }
+    f32x4 num = {0.f, 0.f, 0.f, 0.f};
+    float den = 0.f;
+    for (int64_t w = w0; w <= w1; ++w) {
+      const int64_t slot = (w == w0 && u0 != w0 * C) ? 2 * w + 1 : 2 * w;
+      const float* rec = p.partials + slot * rec_len;
+      const float m = load_shared(rec + (int64_t)G * D + g);
+      const float f = (m == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m - M);
+      const float* a = rec + (int64_t)g * D + d4 * 4;
+      num += f * f32x4{load_shared(a), load_shared(a + 1), load_shared(a + 2), load_shared(a + 3)};
+      den += f * load_shared(rec + (int64_t)G * D + G + g);
+    }
+    reinterpret_cast<f32x4*>(o)[e] = num * (p.out_scale / den);
+  }
+}
+
 template <int D, bool FP8, int NSUB>
-__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(kDecodeThreads, PA_DECODE_MIN_WAVES) void decode_kernel(const DecodeParams p) {
   using T = Tile<D, FP8>;
   const int lane = threadIdx.x & 63;
   const int wave = blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
@@ -240,28 +316,32 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodePara
   const int max_len = p.max_blocks * p.block_size;
   const int subs = p.block_size / kSub;
 
-  // Pass 1: total chunks.  Wavefront 0 also records the per-sequence chunk
-  // prefix for the merge kernel.
+  // Pass 1: total chunks.  Wavefront 0 also writes the rows no other
+  // wavefront will touch: zeros for empty sequences, NaN for invalid ones.
   int64_t total = 0;
   for (int base = 0; base < S; base += 64) {
-    const int s = base + lane;
+    const int si = base + lane;
     int n = 0;
-    if (s < S) n = chunks_of(p.seq_lens[s], max_len);
+    if (si < S) n = chunks_of(p.seq_lens[si], max_len);
+    if (wave == 0) {
+      uint64_t todo = __ballot(si < S && n <= 0);
+      while (todo) {
+        const int l0 = __builtin_ctzll(todo);
+        todo &= todo - 1;
+        const float v = (readlane(n, l0) < 0) ? __builtin_nanf("") : 0.f;
+        float* o = p.out + (int64_t)(base + l0) * p.num_q_heads * D;
+        for (int e = lane; e < p.num_q_heads * D / 4; e += 64)
+          reinterpret_cast<f32x4*>(o)[e] = f32x4{v, v, v, v};
+      }
+    }
     n = n < 0 ? 0 : n;
-    const int incl = wave_incl_scan(n, lane);
-    if (wave == 0 && s < S) p.cum[s] = (int32_t)(total + incl - n);
-    total += readlane(incl, 63);
+    total += wave_reduce_sum(n);
   }
   const int64_t W = total * Hkv;
   int64_t C = p.chunk_fixed;
   if (C <= 0) {
     C = (W + p.num_waves - 1) / p.num_waves;
     if (C < p.chunk_min) C = p.chunk_min;
-  }
-  if (wave == 0 && lane == 0) {
-    p.cum[S] = (int32_t)total;
-    p.meta[0] = C;
-    p.meta[1] = W;
   }
   const int64_t a = (int64_t)wave * C;
   if (a >= W) return;
@@ -296,11 +376,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodePara
     const int L = p.seq_lens[s];
     const int n = chunks_of(L, max_len);
     if (n <= 0) { ++s; continue; }
-    const int64_t u0 = (int64_t)Hkv * before;
-    const int64_t off = x - u0;
+    const int64_t u0s = (int64_t)Hkv * before;
+    const int64_t off = x - u0s;
     const int h = (int)(off / n);
     const int j0 = (int)(off - (int64_t)h * n);
-    const int64_t uend = u0 + (int64_t)(h + 1) * n;
+    const int64_t u0 = u0s + (int64_t)h * n;
+    const int64_t uend = u0 + n;
     const int64_t seg_end = (b < uend) ? b : uend;
     const int j1 = j0 + (int)(seg_end - x);
 
@@ -374,16 +455,30 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodePara
         for (int dc = 0; dc < T::DC; ++dc) *reinterpret_cast<f32x4*>(o + dc * 16) = st.acc[dc] * inv;
       }
     } else {
+      // Store this piece, then count it in; the wavefront that stores the
+      // unit's last piece merges all of them and re-arms the counter.
       const int64_t slot = (x == a) ? 2 * (int64_t)wave : 2 * (int64_t)wave + 1;
       float* rec = p.partials + slot * (int64_t)G * (D + 4);
       if (col < G) {
         float* o = rec + (int64_t)col * D + qd * 4;
 #pragma unroll
-        for (int dc = 0; dc < T::DC; ++dc) *reinterpret_cast<f32x4*>(o + dc * 16) = st.acc[dc];
+        for (int dc = 0; dc < T::DC; ++dc)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) store_shared(o + dc * 16 + i, st.acc[dc][i]);
         if (qd == 0) {
-          rec[(int64_t)G * D + col] = st.m;
-          rec[(int64_t)G * D + G + col] = ltot;
+          store_shared(rec + (int64_t)G * D + col, st.m);
+          store_shared(rec + (int64_t)G * D + G + col, ltot);
         }
+      }
+      const int64_t w0 = u0 / C, w1 = (uend - 1) / C;
+      int32_t* counter = p.counters + (int64_t)s * Hkv + h;
+      __builtin_amdgcn_s_waitcnt(0);  // this wavefront's record stores have completed
+      int prior = 0;
+      if (lane == 0) prior = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      prior = readlane(prior, 0);
+      if (prior == (int)(w1 - w0)) {
+        merge_unit<D>(p, s, h, u0, w0, w1, C, lane);
+        if (lane == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
 
@@ -395,63 +490,16 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodePara
   }
 }
 
-// One workgroup per (sequence, KV head): merge the partial states of a unit
-// that several wavefronts shared; write zeros for empty sequences and NaN
-// for invalid ones.
-template <int D>
-__global__ __launch_bounds__(256) void merge_kernel(const DecodeParams p) {
-  const int unit = blockIdx.x;
-  const int Hkv = p.num_kv_heads, G = p.group;
-  const int s = unit / Hkv, h = unit - s * Hkv;
-  const int max_len = p.max_blocks * p.block_size;
-  const int L = p.seq_lens[s];
-  const int n = chunks_of(L, max_len);
-  float* o = p.out + ((int64_t)s * p.num_q_heads + (int64_t)h * G) * D;
-  const int vec = G * D / 4;
-  if (n <= 0) {
-    const float v = (n < 0) ? __builtin_nanf("") : 0.f;
-    for (int e = threadIdx.x; e < vec; e += blockDim.x)
-      reinterpret_cast<f32x4*>(o)[e] = f32x4{v, v, v, v};
-    return;
-  }
-  const int64_t C = p.meta[0];
-  const int64_t u0 = (int64_t)Hkv * p.cum[s] + (int64_t)h * n;
-  const int64_t u1 = u0 + n;
-  const int64_t w0 = u0 / C, w1 = (u1 - 1) / C;
-  if (w0 == w1) return;  // one wavefront covered the unit and wrote it
-  const int64_t rec_len = (int64_t)G * (D + 4);
-  for (int e = threadIdx.x; e < vec; e += blockDim.x) {
-    const int g = e / (D / 4), d4 = e - g * (D / 4);
-    float M = kNegInf;
-    for (int64_t w = w0; w <= w1; ++w) {
-      const int64_t slot = (w == w0 && u0 != w0 * C) ? 2 * w + 1 : 2 * w;
-      M = __builtin_fmaxf(M, p.partials[slot * rec_len + (int64_t)G * D + g]);
-    }
-    f32x4 num = {0.f, 0.f, 0.f, 0.f};
-    float den = 0.f;
-    for (int64_t w = w0; w <= w1; ++w) {
-      const int64_t slot = (w == w0 && u0 != w0 * C) ? 2 * w + 1 : 2 * w;
-      const float* rec = p.partials + slot * rec_len;
-      const float m = rec[(int64_t)G * D + g];
-      const float f = (m == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m - M);
-      num += f * *reinterpret_cast<const f32x4*>(rec + (int64_t)g * D + d4 * 4);
-      den += f * rec[(int64_t)G * D + G + g];
-    }
-    reinterpret_cast<f32x4*>(o)[e] = num * (p.out_scale / den);
-  }
-}
+constexpr int kStage = PA_DECODE_STAGE;
 
-constexpr int kStage = 4;  // sub-blocks loaded per online-softmax step
+__global__ __launch_bounds__(256) void zero_kernel(uint32_t* p, size_t words) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < words; i += (size_t)gridDim.x * 256) p[i] = 0u;
+}
 
 template <int D, bool FP8>
 hipError_t launch_typed(const DecodeParams& p, hipStream_t stream) {
   const unsigned groups = (unsigned)((p.num_waves + kWavesPerGroup - 1) / kWavesPerGroup);
   hipLaunchKernelGGL((decode_kernel<D, FP8, kStage>), dim3(groups), dim3(kDecodeThreads), 0, stream, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const unsigned units = (unsigned)(p.num_seqs * p.num_kv_heads);
-  if (units == 0) return hipSuccess;
-  hipLaunchKernelGGL(merge_kernel<D>, dim3(units), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -467,6 +515,16 @@ int resident_waves_typed() {
 }
 
 }  // namespace
+
+hipError_t launch_zero(void* ptr, size_t bytes, hipStream_t stream) {
+  const size_t words = bytes / 4;
+  if (words == 0) return hipSuccess;
+  size_t blocks = (words + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     static_cast<uint32_t*>(ptr), words);
+  return hipGetLastError();
+}
 
 hipError_t launch_decode(const DecodeParams& p, bool fp8, hipStream_t stream) {
   if (p.head_dim == 128) return fp8 ? launch_typed<128, true>(p, stream) : launch_typed<128, false>(p, stream);

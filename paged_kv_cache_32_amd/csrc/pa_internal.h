@@ -32,8 +32,7 @@ struct DecodeParams {
   const int32_t* seq_lens;      // [S]
   float* out;                   // [S][Hq][D]
   float* partials;              // [2 * num_waves][G * (D + 4)]
-  int32_t* cum;                 // [S + 1] chunk prefix per sequence (written by wave 0)
-  int64_t* meta;                // [0] chunks per wave, [1] total chunks
+  int32_t* counters;            // [S * Hkv] pieces stored per unit; zero between calls
   int32_t num_seqs, num_q_heads, num_kv_heads, group, head_dim, block_size, num_blocks, max_blocks;
   int32_t num_waves;            // wavefronts launched
   int32_t chunk_min;            // auto split: fewest chunks a wavefront takes
@@ -45,22 +44,22 @@ struct DecodeParams {
 // Host-side launchers (defined next to their kernels).
 hipError_t launch_cache_write(const CacheWriteParams& p, bool fp8, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, bool fp8, hipStream_t stream);
+hipError_t launch_zero(void* ptr, size_t bytes, hipStream_t stream);
 // Resident wavefronts of the decode kernel on the current device (0 on error).
 int decode_resident_waves(int head_dim, bool fp8);
 
 // Workspace carve-up shared by the size query and the launcher.
 struct WorkspaceLayout {
-  size_t partials_off, cum_off, meta_off, total;
+  size_t partials_off, counters_off, total;
 };
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline WorkspaceLayout workspace_layout(int64_t num_waves, int group, int head_dim,
-                                        int num_seqs) {
+                                        int num_seqs, int num_kv_heads) {
   WorkspaceLayout w;
   w.partials_off = 0;
   size_t part = (size_t)(2 * num_waves) * (size_t)group * (size_t)(head_dim + 4) * sizeof(float);
-  w.cum_off = align_up(part, 256);
-  w.meta_off = align_up(w.cum_off + (size_t)(num_seqs + 1) * sizeof(int32_t), 256);
-  w.total = w.meta_off + 256;
+  w.counters_off = align_up(part, 256);
+  w.total = align_up(w.counters_off + (size_t)num_seqs * (size_t)num_kv_heads * sizeof(int32_t), 256);
   return w;
 }
 

@@ -101,6 +101,12 @@ def test_decode_validation():
     assert dec(desc(), fp8=True, vs=float("inf")) == SHAPE
 
 
+def test_workspace_init_validation():
+    lib = pa.lib()
+    assert lib.pa_decode_workspace_init(None, 0, None) == OK
+    assert lib.pa_decode_workspace_init(None, 64, None) == NULL
+
+
 def test_device_errors_without_gpu():
     import torch
     if torch.cuda.is_available():
@@ -110,6 +116,7 @@ def test_device_errors_without_gpu():
     assert cw(desc()) == DEVICE
     d = desc()
     assert pa.lib().pa_decode_workspace_size(ctypes.byref(d), 2, 16, 4, 0) == 0
+    assert pa.lib().pa_decode_workspace_init(FAKE, 64, None) == DEVICE
 
 
 def test_binding_fails_loudly_without_library(monkeypatch):

@@ -134,6 +134,7 @@ def test_workspace_reuse_and_too_small():
     need = pa.pa_decode_workspace_size(w.num_blocks, 16, 2, 64, 4, 8, w.max_blocks_per_seq, 16)
     assert need > 0
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    pa.pa_decode_workspace_init(ws)
     H.gpu_write(w, t)
     a = H.gpu_decode(w, t, partition_tokens=16, workspace=ws).clone()
     b = H.gpu_decode(w, t, partition_tokens=16, workspace=ws).clone()
