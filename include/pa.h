@@ -44,13 +44,15 @@
  * Cache layout (both caches have num_blocks * num_kv_heads * block_size *
  * head_dim elements; block_size is a multiple of 16).  A block is split
  * into sub-blocks of 16 tokens; with X = 16 bytes / element size (X = 8 for
- * bf16, 16 for fp8):
+ * bf16, 16 for fp8) and R = X / 4 (2 for bf16, 4 for fp8):
  *     K element (block b, kv head h, token t, dim d) is at
  *         [b][h][t / 16][d / X][t % 16][d % X]
  *     V element (b, h, t, d) is at
- *         [b][h][t / 16][d][t % 16]
+ *         [b][h][t / 16][d / 16R][d % 16][(t % 16) / 4][(d / 16) % R][t % 4]
  * so each 16-token sub-block of one head is one contiguous tile of
- * 16 * head_dim elements for K and for V.
+ * 16 * head_dim elements for K and for V, ordered so that the decode
+ * kernel reads every tile with whole 16-byte loads straight into its
+ * matrix-core operands.
  */
 #ifndef PA_H_
 #define PA_H_

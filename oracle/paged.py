@@ -32,7 +32,8 @@ into sub-blocks of 16 tokens.  With X = 16 bytes / element size (8 for bf16,
     K element (blk, h, t, d) at
         [blk][h][t // 16][d // X][t % 16][d % X]
     V element (blk, h, t, d) at
-        [blk][h][t // 16][d][t % 16]
+        [blk][h][t // 16][d // (16 R)][d % 16][(t % 16) // 4][(d // 16) % R][t % 4]
+    with R = 16 bytes / (4 elements) / element size (R = 2 for bf16, 4 for fp8)
 
 Both caches are flat element arrays of num_blocks * kv_heads * block_size *
 head_dim elements.  ``k_offset``/``v_offset`` state the layout as index
@@ -66,6 +67,10 @@ class Geom:
         return 16 // self.elem_bytes
 
     @property
+    def r(self):
+        return 4 // self.elem_bytes
+
+    @property
     def cache_elems(self):
         return self.num_blocks * self.num_kv_heads * self.block_size * self.head_dim
 
@@ -90,8 +95,11 @@ def k_offset(g, blk, h, t, d):
 def v_offset(g, blk, h, t, d):
     """Flat element offset of V element (block, kv head, token-in-block, dim)."""
     sb = g.block_size // SUB
-    return ((((blk * g.num_kv_heads + h) * sb + t // SUB) * g.head_dim + d) * SUB
-            + t % SUB)
+    r = g.r
+    tile = (blk * g.num_kv_heads + h) * sb + t // SUB
+    tt = t % SUB
+    return (((((tile * (g.head_dim // (16 * r)) + d // (16 * r)) * 16 + d % 16) * 4 + tt // 4)
+             * r + (d // 16) % r) * 4 + tt % 4)
 
 
 def slot_to_block(slot, block_size):
@@ -150,12 +158,14 @@ def gather(g, k_cache, v_cache, block_row, seq_len, h, k_scale=1.0, v_scale=1.0)
         return np.zeros((0, g.head_dim)), np.zeros((0, g.head_dim))
     sb = g.block_size // SUB
     blocks = np.asarray(block_row[:nblk], dtype=np.int64)
+    r = g.r
     kc = k_cache.reshape(g.num_blocks, g.num_kv_heads, sb, g.head_dim // g.x, SUB, g.x)
-    vc = v_cache.reshape(g.num_blocks, g.num_kv_heads, sb, g.head_dim, SUB)
+    vc = v_cache.reshape(g.num_blocks, g.num_kv_heads, sb, g.head_dim // (16 * r), 16, 4, r, 4)
     kt = kc[blocks, h]                                   # [nblk, sb, D/X, 16, X]
-    vt = vc[blocks, h]                                   # [nblk, sb, D, 16]
+    vt = vc[blocks, h]                                   # [nblk, sb, D/16R, d%16, t/4, (d/16)%R, t%4]
     k_tok = kt.transpose(0, 1, 3, 2, 4).reshape(nblk * g.block_size, g.head_dim)
-    v_tok = vt.transpose(0, 1, 3, 2).reshape(nblk * g.block_size, g.head_dim)
+    # -> [nblk, sb, t/4, t%4, D/16R, (d/16)%R, d%16]
+    v_tok = vt.transpose(0, 1, 4, 6, 2, 5, 3).reshape(nblk * g.block_size, g.head_dim)
     return (_values(g, k_tok[:seq_len], k_scale),
             _values(g, v_tok[:seq_len], v_scale))
 

@@ -14,6 +14,11 @@ constexpr int kMaxDevices = 64;
 constexpr int kMaxGroup = 16;
 constexpr int kMaxBlockSize = 256;
 constexpr int kChunkMinAuto = 16;  // at least 256 tokens per wavefront when splitting automatically
+// Wavefronts launched per resident slot in the automatic split: ranges left
+// over are picked up by whichever slots free up first.
+#ifndef PA_DECODE_OVERSUB
+#define PA_DECODE_OVERSUB 1
+#endif
 
 struct DeviceInfo {
   bool queried = false;
@@ -107,7 +112,7 @@ pa_status plan(const pa_cache_desc* c, int32_t num_seqs, int32_t num_q_heads,
   int resident = 0;
   if (!device_info(c->head_dim, fp8, &resident)) return PA_ERR_DEVICE;
   if (partition_tokens == 0) {
-    *num_waves = resident;
+    *num_waves = (int64_t)resident * PA_DECODE_OVERSUB;
     *chunk_fixed = 0;
   } else {
     const int64_t per = partition_tokens / pa::kSub;

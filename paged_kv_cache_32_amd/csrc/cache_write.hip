@@ -29,6 +29,13 @@ __device__ __forceinline__ uint32_t e4m3_code(float x, float inv) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y, y, 0, false) & 0xFFu;
 }
 
+// Element index of V (token r of a 16-token tile, dim d) inside its tile:
+// [d / 16R][d % 16][r / 4][(d / 16) % R][r % 4].
+template <int R>
+__device__ __forceinline__ int v_elem(int d, int r) {
+  return ((((d / (16 * R)) * 16 + d % 16) * 4 + r / 4) * R + (d / 16) % R) * 4 + r % 4;
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
@@ -60,7 +67,7 @@ __global__ __launch_bounds__(256) void cache_write_kernel(const CacheWriteParams
 
   const int64_t src = ((int64_t)j * p.num_kv_heads + h) * p.head_dim + (int64_t)dg * X;
   uint8_t* kdst = p.k_cache + tile + ((int64_t)dg * kSub + r) * 16;    // [d/X][t%16][X]
-  uint8_t* vtile = p.v_cache + tile;                                   // [d][t%16]
+  uint8_t* vtile = p.v_cache + tile;  // [d/16R][d%16][(t%16)/4][(d/16)%R][t%4], R = 4 / eb
   if (!FP8) {
     const u32x4 kv = *reinterpret_cast<const u32x4*>(p.k + src);
     *reinterpret_cast<u32x4*>(kdst) = kv;
@@ -69,7 +76,7 @@ __global__ __launch_bounds__(256) void cache_write_kernel(const CacheWriteParams
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const uint32_t w = vv[e >> 1];
-      vdst[(dg * 8 + e) * kSub + r] = (uint16_t)((e & 1) ? (w >> 16) : (w & 0xFFFFu));
+      vdst[v_elem<2>(dg * 8 + e, r)] = (uint16_t)((e & 1) ? (w >> 16) : (w & 0xFFFFu));
     }
   } else {
     u32x4 kin[2], vin[2];
@@ -89,7 +96,7 @@ __global__ __launch_bounds__(256) void cache_write_kernel(const CacheWriteParams
     for (int e = 0; e < 16; ++e) {
       const uint32_t w = vin[e >> 3][(e >> 1) & 3];
       const uint32_t code = e4m3_code(bf16_to_f32((e & 1) ? (w >> 16) : (w & 0xFFFFu)), p.v_inv);
-      vtile[(dg * 16 + e) * kSub + r] = (uint8_t)code;
+      vtile[v_elem<4>(dg * 16 + e, r)] = (uint8_t)code;
     }
   }
 }

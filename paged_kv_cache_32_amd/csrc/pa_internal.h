@@ -9,8 +9,11 @@ namespace pa {
 
 // Tokens per cache sub-block: the unit one wavefront's MFMA tile covers.
 constexpr int kSub = 16;
-// Threads per workgroup of the decode kernel: four independent wavefronts.
-constexpr int kWavesPerGroup = 4;
+// Wavefronts per workgroup of the decode kernel (independent of each other).
+#ifndef PA_DECODE_WAVES_PER_GROUP
+#define PA_DECODE_WAVES_PER_GROUP 4
+#endif
+constexpr int kWavesPerGroup = PA_DECODE_WAVES_PER_GROUP;
 constexpr int kDecodeThreads = 64 * kWavesPerGroup;
 
 struct CacheWriteParams {

@@ -241,23 +241,27 @@ class Workload:
         used[self.used_blocks()] = True
         return np.nonzero(~used)[0].tolist()
 
-    # Element indices of token rows, from the cache layout:
-    #   K (blk, h, t, d) at [blk][h][t//16][d//X][t%16][d%X], X = 16 / elem bytes
-    #   V (blk, h, t, d) at [blk][h][t//16][d][t%16]
+    # Element indices of token rows, from the cache layout (X = 16 / element
+    # bytes, R = 4 / element bytes):
+    #   K (blk, h, t, d) at [blk][h][t//16][d//X][t%16][d%X]
+    #   V (blk, h, t, d) at [blk][h][t//16][d//16R][d%16][(t%16)//4][(d//16)%R][t%4]
     def _row_elems(self, blk, tok, dev):
         """Flat K and V element indices of all (kv head, dim) of the given
         (block, token) rows; blk, tok: int64 tensors of equal length R.
         Returns two [R * Hkv * D] index tensors."""
         Hkv, D, BS = self.num_kv_heads, self.head_dim, self.block_size
         X = 16 // self.elem_bytes
+        R = 4 // self.elem_bytes
         sb = BS // SUB
         h = torch.arange(Hkv, device=dev, dtype=torch.int64).view(1, Hkv, 1)
         d = torch.arange(D, device=dev, dtype=torch.int64).view(1, 1, D)
         b = blk.view(-1, 1, 1)
         t = tok.view(-1, 1, 1)
         tile = (b * Hkv + h) * sb + t // SUB
-        k_idx = ((tile * (D // X) + d // X) * SUB + t % SUB) * X + d % X
-        v_idx = (tile * D + d) * SUB + t % SUB
+        tt = t % SUB
+        k_idx = ((tile * (D // X) + d // X) * SUB + tt) * X + d % X
+        v_idx = ((((tile * (D // (16 * R)) + d // (16 * R)) * 16 + d % 16) * 4 + tt // 4) * R
+                 + (d // 16) % R) * 4 + tt % 4
         return k_idx.reshape(-1), v_idx.reshape(-1)
 
     def _poison_positions(self, dev):

@@ -52,7 +52,7 @@ def make_paged(rng, lens, Hq, Hkv, D, BS, kv_dtype="bf16", extra_blocks=2, scale
     return g, kc, vc, bt, np.array(lens, dtype=np.int32), q, dense
 
 
-@pytest.mark.parametrize("Hq,Hkv,D,BS", [(4, 1, 64, 16), (8, 2, 32, 32), (16, 8, 128, 16), (6, 6, 16, 48)])
+@pytest.mark.parametrize("Hq,Hkv,D,BS", [(4, 1, 64, 16), (8, 2, 32, 32), (16, 8, 128, 16), (6, 6, 64, 48)])
 def test_matches_dense_contiguous_attention(Hq, Hkv, D, BS):
     rng = np.random.default_rng(Hq * 100 + BS)
     lens = [1, 17, 40, 5, 33]
@@ -78,24 +78,26 @@ def test_fp8_matches_dense_on_dequantized_values():
 
 def test_offsets_and_reshape_describe_the_same_layout():
     for kv_dtype in ("bf16", "fp8"):
-        g = paged.Geom(3, 32, 2, 32, kv_dtype)
+        g = paged.Geom(3, 32, 2, 64, kv_dtype)
         k = np.zeros(g.cache_elems, dtype=np.int64)
         v = np.zeros(g.cache_elems, dtype=np.int64)
         for blk in range(3):
             for h in range(2):
                 for t in range(32):
-                    for d in range(32):
-                        tag = ((blk * 2 + h) * 32 + t) * 32 + d
+                    for d in range(64):
+                        tag = ((blk * 2 + h) * 32 + t) * 64 + d
                         k[paged.k_offset(g, blk, h, t, d)] = tag
                         v[paged.v_offset(g, blk, h, t, d)] = tag
         assert sorted(k.tolist()) == list(range(g.cache_elems))
-        kt = k.reshape(3, 2, 2, 32 // g.x, 16, g.x)
-        vt = v.reshape(3, 2, 2, 32, 16)
+        assert sorted(v.tolist()) == list(range(g.cache_elems))
+        r = g.r
+        kt = k.reshape(3, 2, 2, 64 // g.x, 16, g.x)
+        vt = v.reshape(3, 2, 2, 64 // (16 * r), 16, 4, r, 4)
         for blk in range(3):
             for h in range(2):
-                K = kt[blk, h].transpose(0, 2, 1, 3).reshape(32, 32)
-                V = vt[blk, h].transpose(0, 2, 1).reshape(32, 32)
-                want = ((blk * 2 + h) * 32 + np.arange(32)[:, None]) * 32 + np.arange(32)[None, :]
+                K = kt[blk, h].transpose(0, 2, 1, 3).reshape(32, 64)
+                V = vt[blk, h].transpose(0, 3, 5, 1, 4, 2).reshape(32, 64)
+                want = ((blk * 2 + h) * 32 + np.arange(32)[:, None]) * 64 + np.arange(64)[None, :]
                 assert np.array_equal(K, want) and np.array_equal(V, want)
 
 
