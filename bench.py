@@ -20,8 +20,10 @@ Prints exactly one JSON line on stdout; everything else goes to stderr.
 """
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -53,6 +55,34 @@ def algorithmic_bytes(w):
     tables = int(sum(-(-int(L) // w.block_size) for L in w.seq_lens)) * 4
     other = S * Hq * D * 2 + S * Hq * D * 4 + tables + 4 * S
     return kv, kv + other
+
+
+KERNEL_SOURCES = ("paged_kv_cache_32_amd/csrc/decode.hip", "paged_kv_cache_32_amd/csrc/pa_internal.h",
+                  "paged_kv_cache_32_amd/csrc/api.hip")
+TRAFFIC_PROFILE = "profiles/decode_kernel_llama70b_bs64_traffic.md"
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the committed rocprofv3 counter
+    summary, or None when the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, TRAFFIC_PROFILE)
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("traffic_bytes_per_launch")
 
 
 def cpu_baseline(w, t, out_gpu, min_seconds=10.0, max_seconds=30.0):
@@ -127,8 +157,10 @@ def main():
                                            w.num_seqs, w.num_q_heads, w.max_blocks_per_seq,
                                            args.partition_tokens)
     ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)  # zero-filled once, as required
-    scrub = torch.ones(SCRUB_BYTES // 4, dtype=torch.int32, device=dev)
-    sink = torch.zeros((), dtype=torch.int64, device=dev)
+    # float32 so the reduction reads the buffer directly (an int32 sum would
+    # first widen it to int64, writing 1 GiB).
+    scrub = torch.ones(SCRUB_BYTES // 4, dtype=torch.float32, device=dev)
+    sink = torch.zeros((), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def step():
@@ -204,7 +236,8 @@ def main():
         "decode_tok_s_80layer_equiv": round(w.num_seqs / (MODEL_LAYERS * step_ms / 1e3), 1),
         "wall_s_timed_region": round(wall, 4),
         "roofline": {"bound": "hbm", "achieved": round(alg_gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(alg_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(alg_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(),
                      "kernel": "decode_kernel (pa_decode is one launch)",
                      "bytes_per_launch": alg_bytes},
     }
