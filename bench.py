@@ -1,12 +1,14 @@
 """Benchmark: paged-attention decode on a Llama-70B-shaped layer, batch 64.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-scrub] [--skip-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-scrub] [--skip-cpu] [--partition-tokens P]
 
-One step = the whole hot path over one batch: pa_cache_write of the 64 new
-tokens (one per sequence) into their slots, then pa_decode of the 64
-sequences (64 query heads, 8 KV heads, head_dim 128, bf16 KV cache, block
-size 16, lognormal lengths with median 2,400 and p95 about 18,000 clipped to
-[16, 32768]).  Inputs are synthetic and already resident in HBM.
+Default workload (llama70b_layer_bs64).  One step = the whole hot path over
+one batch: pa_cache_write of the 64 new tokens (one per sequence) into their
+slots, then pa_decode of the 64 sequences (64 query heads, 8 KV heads,
+head_dim 128, bf16 KV cache, block size 16, lognormal lengths with median
+2,400 and p95 about 18,000 clipped to [16, 32768]).  Inputs are synthetic and
+already resident in HBM.
 
 Before every timed step a 512 MiB buffer is read (a reduction) so the KV
 blocks of the previous step are not served from the 256 MiB Infinity Cache
@@ -15,6 +17,16 @@ the write and the decode are each bracketed by HIP events recorded on the
 stream they run on, so the scrub is not timed.  `value` is KV bytes read per
 decode call (sum of sequence lengths x 2 x 8 heads x 128 x 2 B) divided by
 the mean event-timed duration of pa_decode, in GB/s (1e9 B/s).
+
+Other workloads (--workload), each on the same 70B layer shape:
+  prefix_shared_bs256  256 sequences, block 32, a shared 900-token system
+                       prompt and 12 shared prefix pools; `value` counts the
+                       distinct (physical) KV bytes, logical bytes reported too
+  long_context_128k    4 sequences of 131,072 tokens, 1% of K rows x8
+  fp8_80layer_bs128    a full 80-layer step with an e4m3fn cache: per layer
+                       pa_cache_write_fp8 then pa_decode_fp8, 160 launches
+                       replayed as one HIP graph; `value` is KV GB/s over the
+                       whole step, decode tok/s = 128 / step time
 
 Prints exactly one JSON line on stdout; everything else goes to stderr.
 """
@@ -36,22 +48,26 @@ if ROOT not in sys.path:
 
 import paged_kv_cache_32_amd as pa  # noqa: E402
 from paged_kv_cache_32_amd import workloads as W  # noqa: E402
+from paged_kv_cache_32_amd.step import DecodeStep  # noqa: E402
 
 METRIC = "paged-decode KV GB/s (% of HBM peak) + decode tok/s, 70B-shaped layer, bs=64"
 HBM_PEAK_GBS = 8000.0
 MODEL_LAYERS = 80
 SCRUB_BYTES = 512 << 20
+WORKLOADS = {"llama70b_layer_bs64": 2, "prefix_shared_bs256": 3, "long_context_128k": 4,
+             "fp8_80layer_bs128": 5}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(w):
+def algorithmic_bytes(w, physical=False):
     """Bytes one decode call must move at minimum: K and V of every cached
-    token, the queries, the outputs, the block-table entries and lengths."""
+    token (each distinct token once when ``physical``), the queries, the
+    outputs, the block-table entries and lengths."""
     S, Hq, D = w.num_seqs, w.num_q_heads, w.head_dim
-    kv = w.logical_kv_bytes()
+    kv = w.physical_kv_bytes() if physical else w.logical_kv_bytes()
     tables = int(sum(-(-int(L) // w.block_size) for L in w.seq_lens)) * 4
     other = S * Hq * D * 2 + S * Hq * D * 4 + tables + 4 * S
     return kv, kv + other
@@ -59,7 +75,10 @@ def algorithmic_bytes(w):
 
 KERNEL_SOURCES = ("paged_kv_cache_32_amd/csrc/decode.hip", "paged_kv_cache_32_amd/csrc/pa_internal.h",
                   "paged_kv_cache_32_amd/csrc/api.hip")
-TRAFFIC_PROFILE = "profiles/decode_kernel_llama70b_bs64_traffic.md"
+TRAFFIC_PROFILES = {"llama70b_layer_bs64": "profiles/decode_kernel_llama70b_bs64_traffic.md",
+                    "prefix_shared_bs256": "profiles/decode_kernel_prefix_shared_bs256_traffic.md",
+                    "long_context_128k": "profiles/decode_kernel_long_context_128k_traffic.md",
+                    "fp8_80layer_bs128": "profiles/decode_kernel_fp8_80layer_bs128_traffic.md"}
 
 
 def kernel_source_hash():
@@ -70,10 +89,11 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def measured_traffic():
+def measured_traffic(workload="llama70b_layer_bs64"):
     """HBM bytes per decode launch from the committed rocprofv3 counter
-    summary, or None when the kernel sources changed since it was taken."""
-    path = os.path.join(ROOT, TRAFFIC_PROFILE)
+    summary of this workload, or None when there is none or the kernel
+    sources changed since it was taken."""
+    path = os.path.join(ROOT, TRAFFIC_PROFILES[workload])
     if not os.path.exists(path):
         return None
     m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
@@ -85,67 +105,82 @@ def measured_traffic():
     return rec.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(w, t, out_gpu, min_seconds=10.0, max_seconds=30.0):
-    """Time the CPU oracle (float64 numpy) on the same batch: whole-batch
-    passes repeated until about 10 s have elapsed; also report its agreement
-    with the GPU output on that batch."""
+def cpu_baseline(w, t, out_gpu, layer=0, min_seconds=10.0, max_seconds=30.0):
+    """Time the CPU oracle (float64 numpy) on a bounded sample of the same
+    workload: one sequence at a time, in order and wrapping around, until
+    about 10 s have elapsed (a whole pass when the batch fits in that time).
+    Reports logical KV GB/s of the oracle and its agreement with the GPU on
+    the sequences it computed."""
     from threadpoolctl import threadpool_info
 
     from oracle import paged
     g = paged.Geom(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.kv_dtype)
 
     def bits(x):
-        return x.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+        x = x.detach().cpu()
+        return x.view(torch.int16).numpy().view(np.uint16) if x.dtype == torch.bfloat16 else x.numpy()
 
-    kc, vc, q = bits(t["k_cache"][0]), bits(t["v_cache"][0]), bits(t["q"][0])
+    kc, vc, q = bits(t["k_cache"][layer]), bits(t["v_cache"][layer]), bits(t["q"][layer])
+    kn, vn = bits(t["k_new"][layer]), bits(t["v_new"][layer])
     # The oracle's own write of this step's tokens: every slot the kernels
     # wrote is overwritten with the oracle's encoding; all other slots still
     # hold the generator's values.
-    paged.cache_write_bf16(g, bits(t["k_new"][0]), bits(t["v_new"][0]), w.slot_mapping, kc, vc)
+    if w.kv_dtype == "bf16":
+        ks = vs = 1.0
+        paged.cache_write_bf16(g, kn, vn, w.slot_mapping, kc, vc)
+    else:
+        ks, vs = float(t["k_scale"][layer]), float(t["v_scale"][layer])
+        paged.cache_write_fp8(g, kn, vn, w.slot_mapping, kc, vc, np.float32(ks), np.float32(vs))
     threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    passes, elapsed, ref = 0, 0.0, None
-    seqs = list(range(w.num_seqs))
+    per_token = 2 * w.num_kv_heads * w.head_dim * w.elem_bytes
+    ref = np.full((w.num_seqs, w.num_q_heads, w.head_dim), np.nan)
+    done = set()
+    calls, elapsed, nbytes, s = 0, 0.0, 0, 0
     while elapsed < min_seconds and elapsed < max_seconds:
         t0 = time.perf_counter()
-        ref = paged.decode(g, q, kc, vc, w.block_tables, w.seq_lens, w.scale, seqs=seqs)
+        r = paged.decode(g, q, kc, vc, w.block_tables, w.seq_lens, w.scale, k_scale=ks,
+                         v_scale=vs, seqs=[s])
         elapsed += time.perf_counter() - t0
-        passes += 1
-        if passes * (elapsed / passes) > max_seconds:
-            break
-    per_pass = elapsed / passes
-    err = np.abs(out_gpu.detach().cpu().double().numpy() - ref)
-    kv = w.logical_kv_bytes()
+        nbytes += int(w.seq_lens[s]) * per_token
+        calls += 1
+        if s not in done:
+            ref[s] = r[s]
+            done.add(s)
+        s = (s + 1) % w.num_seqs
+    got = out_gpu.detach().cpu().double().numpy()
+    idx = sorted(done)
+    err = np.abs(got[idx] - ref[idx])
+    whole = len(done) == w.num_seqs
+    what = (f"{calls // w.num_seqs} whole pass(es) over the {w.num_seqs}-sequence batch"
+            if whole and calls % w.num_seqs == 0 else
+            f"{calls} single-sequence decodes covering {len(done)} of the {w.num_seqs} sequences")
     return {
-        "value": kv / per_pass / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-        "sample": (f"whole {w.num_seqs}-sequence batch of the same workload, float64 numpy oracle, "
-                   f"{passes} pass(es) in {elapsed:.1f} s ({per_pass:.2f} s/pass)"),
-        "seconds_per_call": per_pass,
+        "value": nbytes / elapsed / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+        "sample": (f"{what} of the same workload (layer {layer}), float64 numpy oracle, "
+                   f"{elapsed:.1f} s, {nbytes / 1e9:.2f} GB of logical KV"),
+        "seconds": elapsed,
         "gpu_vs_oracle_max_abs": float(err.max()), "gpu_vs_oracle_mean_abs": float(err.mean()),
     }
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--no-scrub", action="store_true", help="do not overwrite 512 MiB between steps")
-    ap.add_argument("--skip-cpu", action="store_true", help="do not time the CPU oracle")
-    ap.add_argument("--partition-tokens", type=int, default=0)
-    args = ap.parse_args()
+def base_record(args, w, K):
+    return {
+        "metric": METRIC, "value": None, "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8" if w.kv_dtype == "fp8" else "bf16",
+        "data": "synthetic (seeded lognormal lengths, N(0,1) bf16 q/k/v, shuffled block pool)",
+        "config": {"workload": args.workload, "num_seqs": w.num_seqs,
+                   "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+                   "head_dim": w.head_dim, "block_size": w.block_size, "kv_dtype": w.kv_dtype,
+                   "num_layers": w.num_layers, "tokens": int(w.seq_lens.sum()),
+                   "partition_tokens": args.partition_tokens},
+    }
 
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(run with --gpus 1)", file=sys.stderr)
-        sys.exit(2)
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(2)
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    pa.lib()
 
-    w = W.config(2)
+def bench_layer(args, dev):
+    """One-layer workloads: the cache write and the decode of one batch."""
+    w = W.config(WORKLOADS[args.workload])
+    shared = args.workload == "prefix_shared_bs256"
     log("workload:", json.dumps(w.summary()))
     t = w.make_tensors(dev)
     bt = torch.from_numpy(w.block_tables).to(dev)
@@ -163,15 +198,18 @@ def main():
     sink = torch.zeros((), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step():
+    def write():
         pa.pa_cache_write(kn, vn, sm, kc, vc, block_size=w.block_size)
+
+    def decode():
         pa.pa_decode(q, kc, vc, bt, sl, w.scale, out, num_kv_heads=w.num_kv_heads,
                      block_size=w.block_size, partition_tokens=args.partition_tokens, workspace=ws)
 
     for i in range(args.warmup):
         if not args.no_scrub:
             torch.sum(scrub, dim=0, out=sink)
-        step()
+        write()
+        decode()
     torch.cuda.synchronize()
 
     K = args.steps
@@ -182,10 +220,9 @@ def main():
         if not args.no_scrub:
             torch.sum(scrub, dim=0, out=sink)
         ev[i][0].record(stream)
-        pa.pa_cache_write(kn, vn, sm, kc, vc, block_size=w.block_size)
+        write()
         ev[i][1].record(stream)
-        pa.pa_decode(q, kc, vc, bt, sl, w.scale, out, num_kv_heads=w.num_kv_heads,
-                     block_size=w.block_size, partition_tokens=args.partition_tokens, workspace=ws)
+        decode()
         ev[i][2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -196,36 +233,25 @@ def main():
     hot = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     hot[0].record(stream)
     for _ in range(K):
-        pa.pa_decode(q, kc, vc, bt, sl, w.scale, out, num_kv_heads=w.num_kv_heads,
-                     block_size=w.block_size, partition_tokens=args.partition_tokens, workspace=ws)
+        decode()
     hot[1].record(stream)
     torch.cuda.synchronize()
     hot_ms = hot[0].elapsed_time(hot[1]) / K
 
-    kv_bytes, alg_bytes = algorithmic_bytes(w)
+    kv_bytes, alg_bytes = algorithmic_bytes(w, physical=shared)
+    logical_kv = w.logical_kv_bytes()
     dec_s = float(dec_ms.mean()) / 1e3
     step_ms = float((write_ms + dec_ms).mean())
     kv_gbs = kv_bytes / dec_s / 1e9
     alg_gbs = alg_bytes / dec_s / 1e9
-    res = {
-        "metric": METRIC,
-        "value": round(kv_gbs, 1),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": args.warmup,
-        "ms_per_step": round(step_ms, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded lognormal lengths, N(0,1) bf16 q/k/v, shuffled block pool)",
-        "config": {"workload": "llama70b_layer_bs64", "num_seqs": w.num_seqs,
-                   "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
-                   "head_dim": w.head_dim, "block_size": w.block_size, "kv_dtype": "bf16",
-                   "tokens": int(w.seq_lens.sum()), "kv_bytes_per_call": kv_bytes,
-                   "partition_tokens": args.partition_tokens, "scrub_mib_between_steps":
-                       0 if args.no_scrub else SCRUB_BYTES >> 20},
+    res = base_record(args, w, K)
+    if args.workload != "llama70b_layer_bs64":
+        res["metric"] = f"paged-decode KV GB/s (% of HBM peak) + decode tok/s, {args.workload}"
+    res.update({"value": round(kv_gbs, 1), "ms_per_step": round(step_ms, 4)})
+    res["config"].update({"kv_bytes_per_call": kv_bytes, "kv_bytes_basis":
+                          "distinct (physical) tokens" if shared else "every cached token",
+                          "scrub_mib_between_steps": 0 if args.no_scrub else SCRUB_BYTES >> 20})
+    res.update({
         "hbm_peak_frac": round(kv_gbs / HBM_PEAK_GBS, 4),
         "decode_us": {"mean": round(dec_s * 1e6, 2), "p10": round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
                       "p50": round(float(np.median(dec_ms)) * 1e3, 2),
@@ -237,12 +263,142 @@ def main():
         "wall_s_timed_region": round(wall, 4),
         "roofline": {"bound": "hbm", "achieved": round(alg_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(alg_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(),
+                     "traffic": measured_traffic(args.workload),
                      "kernel": "decode_kernel (pa_decode is one launch)",
                      "bytes_per_launch": alg_bytes},
-    }
+    })
+    if shared:
+        res["logical_kv_gbs"] = round(logical_kv / dec_s / 1e9, 1)
+        res["logical_kv_bytes_per_call"] = logical_kv
     if not args.skip_cpu:
         res["cpu_baseline"] = cpu_baseline(w, t, out)
+    return res
+
+
+def bench_model_step(args, dev):
+    """The 80-layer fp8 step: per layer the fp8 write and the fp8 decode, all
+    160 launches captured once in a HIP graph and replayed per step."""
+    w = W.config(WORKLOADS[args.workload])
+    log("workload:", json.dumps(w.summary()))
+    t0 = time.perf_counter()
+    t = w.make_tensors(dev)
+    log(f"tensors for {w.num_layers} layers drawn in {time.perf_counter() - t0:.1f} s")
+    n = w.num_layers
+    bt = torch.from_numpy(w.block_tables).to(dev)
+    sl = torch.from_numpy(w.seq_lens).to(dev)
+    sm = torch.from_numpy(w.slot_mapping).to(dev)
+    out = torch.empty((n, w.num_seqs, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    step = DecodeStep(q=t["q"], k_new=t["k_new"], v_new=t["v_new"], k_cache=t["k_cache"],
+                      v_cache=t["v_cache"], out=out, block_tables=bt, seq_lens=sl, slot_mapping=sm,
+                      scale=w.scale, num_kv_heads=w.num_kv_heads, block_size=w.block_size,
+                      k_scale=t["k_scale"].tolist(), v_scale=t["v_scale"].tolist(),
+                      partition_tokens=args.partition_tokens)
+    stream = torch.cuda.current_stream(dev)
+
+    # Eager, with an event after every layer: per-layer times.
+    K = args.steps
+    for _ in range(max(args.warmup, 1)):
+        step.run()
+    torch.cuda.synchronize()
+    lay_ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    eager_ms = []
+    per_layer = np.zeros(n)
+    eager_steps = min(K, 5)
+    for _ in range(eager_steps):
+        step.run(events=lay_ev)
+        torch.cuda.synchronize()
+        eager_ms.append(lay_ev[0].elapsed_time(lay_ev[n]))
+        per_layer += np.array([lay_ev[i].elapsed_time(lay_ev[i + 1]) for i in range(n)])
+    per_layer /= eager_steps
+
+    # One write + one decode of a middle layer, each between events, for the
+    # decode kernel's own time (the roofline's unit).
+    mid = n // 2
+    kd = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    for i in range(K):
+        kd[i][0].record(stream)
+        step.write(mid)
+        kd[i][1].record(stream)
+        step.decode(mid)
+        kd[i][2].record(stream)
+    torch.cuda.synchronize()
+    write_ms = np.array([e[0].elapsed_time(e[1]) for e in kd])
+    dec_ms = np.array([e[1].elapsed_time(e[2]) for e in kd])
+
+    # Graph: the whole step as one replay.
+    step.capture()
+    for _ in range(args.warmup):
+        step.replay()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    tw = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        step.replay()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - tw
+    graph_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+
+    kv_layer, alg_layer = algorithmic_bytes(w)
+    step_s = float(graph_ms.mean()) / 1e3
+    dec_s = float(dec_ms.mean()) / 1e3
+    kv_gbs = n * kv_layer / step_s / 1e9
+    res = base_record(args, w, K)
+    res["metric"] = f"paged-decode KV GB/s (% of HBM peak) + decode tok/s, {args.workload}"
+    res.update({"value": round(kv_gbs, 1), "ms_per_step": round(float(graph_ms.mean()), 4)})
+    res["config"].update({"kv_bytes_per_step": n * kv_layer, "kv_bytes_per_layer": kv_layer,
+                          "step": "per layer pa_cache_write_fp8 + pa_decode_fp8, one HIP graph"})
+    res.update({
+        "hbm_peak_frac": round(kv_gbs / HBM_PEAK_GBS, 4),
+        "decode_tok_s": round(w.num_seqs / step_s, 1),
+        "step_ms": {"graph_mean": round(float(graph_ms.mean()), 4),
+                    "graph_p10": round(float(np.percentile(graph_ms, 10)), 4),
+                    "graph_p90": round(float(np.percentile(graph_ms, 90)), 4),
+                    "eager_mean": round(float(np.mean(eager_ms)), 4)},
+        "layer_ms_eager": {"mean": round(float(per_layer.mean()), 4),
+                           "min": round(float(per_layer.min()), 4),
+                           "max": round(float(per_layer.max()), 4)},
+        "decode_us_one_layer": round(dec_s * 1e6, 2),
+        "cache_write_us_one_layer": round(float(write_ms.mean()) * 1e3, 2),
+        "wall_s_timed_region": round(wall, 4),
+        "roofline": {"bound": "hbm", "achieved": round(alg_layer / dec_s / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(alg_layer / dec_s / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(args.workload),
+                     "kernel": "decode_kernel fp8 (one layer's pa_decode_fp8)",
+                     "bytes_per_launch": alg_layer},
+    })
+    if not args.skip_cpu:
+        res["cpu_baseline"] = cpu_baseline(w, t, out[0], layer=0)
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama70b_layer_bs64", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-scrub", action="store_true", help="do not read 512 MiB between steps")
+    ap.add_argument("--skip-cpu", action="store_true", help="do not time the CPU oracle")
+    ap.add_argument("--partition-tokens", type=int, default=0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pa.lib()
+    if args.workload == "fp8_80layer_bs128":
+        res = bench_model_step(args, dev)
+    else:
+        res = bench_layer(args, dev)
     print(json.dumps(res), flush=True)
 
 
