@@ -109,6 +109,11 @@ pa_status plan(const pa_cache_desc* c, int32_t num_seqs, int32_t num_q_heads,
   if (num_q_heads / c->num_kv_heads > kMaxGroup) return PA_ERR_UNSUPPORTED;
   if (partition_tokens < 0 || partition_tokens % pa::kSub != 0) return PA_ERR_SHAPE;
   if ((int64_t)max_blocks_per_seq * c->block_size > INT32_MAX) return PA_ERR_SHAPE;
+  // Every index of the kernel's chunk list must fit an int (with headroom).
+  {
+    const int64_t chunks_per_seq = ((int64_t)max_blocks_per_seq * c->block_size + pa::kSub - 1) / pa::kSub;
+    if ((int64_t)num_seqs * c->num_kv_heads * chunks_per_seq >= ((int64_t)1 << 30)) return PA_ERR_SHAPE;
+  }
   int resident = 0;
   if (!device_info(c->head_dim, fp8, &resident)) return PA_ERR_DEVICE;
   if (partition_tokens == 0) {
@@ -177,6 +182,9 @@ pa_status decode(const pa_cache_desc* cache, const void* q, int32_t num_seqs, in
   p.num_waves = (int32_t)num_waves;
   p.chunk_min = kChunkMinAuto;
   p.chunk_fixed = chunk_fixed;
+  p.subs = cache->block_size / pa::kSub;
+  p.subs_magic = p.subs > 1 ? (uint32_t)((((uint64_t)1 << 32) + p.subs - 1) / p.subs) : 0u;
+  p.blk_stride = (int64_t)cache->num_kv_heads * p.subs * pa::kSub * cache->head_dim * (fp8 ? 1 : 2);
   p.qk_scale = scale * 1.4426950408889634f * (fp8 ? k_scale : 1.0f);
   p.out_scale = fp8 ? v_scale : 1.0f;
   if (pa::launch_decode(p, fp8, static_cast<hipStream_t>(stream)) != hipSuccess)

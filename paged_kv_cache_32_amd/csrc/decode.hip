@@ -21,16 +21,15 @@
 //    per-lane load (1 KiB per instruction) that lands directly in the MFMA
 //    operand registers: K tile [d/X][16][X] gives lane (t, k-group) the 8
 //    consecutive d of token t; V tile [d/16R][d%16][t/4][(d/16)%R][t%4]
-//    gives lane (d%16, t-group) 4 consecutive tokens of R dims 16 apart,
-//    the V^T operand of R MFMAs.
+//    gives lane (d%16, t-group) 4 consecutive tokens of R dims 16 apart.
 //  * S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (rows = tokens, cols = query
 //    heads, fp32 accumulate; bf16 products are exact).  O^T = V^T P^T with
 //    v_mfma_f32_16x16x16_bf16; P is split into a bf16 high part and a bf16
 //    remainder so the probabilities keep ~16 significant bits.  fp8 codes
 //    are widened to bf16 exactly on load.
-//  * Online softmax in base 2 (scale * log2 e folded into the logit scale),
-//    one max/rescale per stage of NSUB sub-blocks; cross-lane reductions
-//    use 2 xor shuffles.
+//  * Online softmax in base 2 (scale * log2 e folded into the logit scale);
+//    the accumulator is rescaled only when a head's maximum grows by more
+//    than kRescaleSlack.
 //  * Load balance: all (sequence, KV head) units are laid end to end as a
 //    list of 16-token chunks, and wavefront w takes chunks
 //    [w*C, (w+1)*C).  A unit that a wavefront covers completely is written
@@ -47,7 +46,10 @@
 // Sub-blocks loaded per online-softmax step, and the fewest wavefronts per
 // SIMD the register allocation must leave room for.
 #ifndef PA_DECODE_STAGE
-#define PA_DECODE_STAGE 4
+#define PA_DECODE_STAGE 2
+#endif
+#ifndef PA_DECODE_STAGE_FP8
+#define PA_DECODE_STAGE_FP8 4
 #endif
 #ifndef PA_DECODE_MIN_WAVES
 #define PA_DECODE_MIN_WAVES 1
@@ -62,13 +64,20 @@ namespace pa {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kNegInf = -__builtin_huge_valf();
+
+// Largest growth of a query head's running maximum (base-2 logits) that is
+// absorbed without rescaling: probabilities are then taken against the old
+// maximum and may reach 2^kRescaleSlack, which the bf16 hi/lo operands and
+// the fp32 sums carry as well as any other value.  The accumulator is
+// rescaled only when some head's maximum grows by more, which after the
+// first stage of a piece is rare.
+constexpr float kRescaleSlack = 8.0f;
 
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 #pragma unroll
@@ -104,21 +113,17 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
 
 // Pack four probabilities into two bf16 operands: hi = p truncated to bf16,
 // lo = (p - hi) truncated to bf16, so hi + lo = p to about 2^-16 relative.
-__device__ __forceinline__ void split_p(const float p[4], i16x4& hi, i16x4& lo) {
-  uint32_t h[4], l[4];
+__device__ __forceinline__ void split_p(const float p[4], u32x2& hi, u32x2& lo) {
+  uint32_t l[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint32_t b = __float_as_uint(p[i]);
-    h[i] = b;
     l[i] = __float_as_uint(p[i] - __uint_as_float(b & 0xFFFF0000u));
   }
-  u32x2 H, Lo;
-  H[0] = (h[0] >> 16) | (h[1] & 0xFFFF0000u);
-  H[1] = (h[2] >> 16) | (h[3] & 0xFFFF0000u);
-  Lo[0] = (l[0] >> 16) | (l[1] & 0xFFFF0000u);
-  Lo[1] = (l[2] >> 16) | (l[3] & 0xFFFF0000u);
-  hi = as_i16x4(H);
-  lo = as_i16x4(Lo);
+  hi[0] = (__float_as_uint(p[0]) >> 16) | (__float_as_uint(p[1]) & 0xFFFF0000u);
+  hi[1] = (__float_as_uint(p[2]) >> 16) | (__float_as_uint(p[3]) & 0xFFFF0000u);
+  lo[0] = (l[0] >> 16) | (l[1] & 0xFFFF0000u);
+  lo[1] = (l[2] >> 16) | (l[3] & 0xFFFF0000u);
 }
 
 template <typename V>
@@ -130,15 +135,9 @@ __device__ __forceinline__ V load_kv(const V* p) {
 #endif
 }
 
-
 // Values the whole wavefront agrees on, marked so for the compiler (so that
 // control flow and the addresses of scalar loads stay in scalar registers).
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
-__device__ __forceinline__ int64_t uni64(int64_t v) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)v >> 32));
-  return (int64_t)(((uint64_t)hi << 32) | lo);
-}
 
 // Scalar (SMEM) loads of uniform indices: block ids and sequence lengths are
 // read through the constant address space so they come back on the scalar
@@ -162,8 +161,8 @@ struct Tile {
   static constexpr int TILE_BYTES = kSub * D * EB;  // one (block, head, sub-block) tile
   static constexpr int KLD = FP8 ? D / 64 : D / 32; // 16-byte K loads per lane per tile
   static constexpr int QK = D / 32;                 // 16x16x32 MFMAs per tile (QK^T)
-  static constexpr int DC = D / 16;                 // 16x16x16 MFMAs per tile (PV), per P half
-  static constexpr int R = FP8 ? 4 : 2;             // PV MFMAs fed by one 16-byte V load
+  static constexpr int DC = D / 16;                 // 16-row blocks of O^T
+  static constexpr int R = FP8 ? 4 : 2;             // dim blocks fed by one 16-byte V load
   static constexpr int VLD = DC / R;                // 16-byte V loads per lane per tile
 };
 
@@ -181,283 +180,203 @@ struct StageBuf {
 // Softmax state of the unit piece a wavefront is working on.
 template <int D>
 struct Softmax {
-  float m;        // running max of base-2 logits of query head (lane & 15)
+  float m;        // reference maximum of base-2 logits of query head (lane & 15)
   float l;        // this lane's share of the running sum
   f32x4 acc[D / 16];
 };
 
-// One stage of a wavefront's work, uniform across the wavefront: up to NSUB
-// consecutive 16-token chunks of unit (s, h).
+// Stage flags.
+enum : int {
+  kValid = 1,    // the stage holds chunks
+  kFirst = 2,    // first stage of a piece: load Q, reset the softmax state
+  kLast = 4,     // last stage of a piece: write it out or store the partial
+  kTail = 8,     // ends in the unit's last chunk, which is partial
+  kAtA = 16,     // the piece starts at the wavefront's first chunk
+  kWhole = 32,   // the piece is its whole unit
+};
+
+// A piece: chunks [j0, j1) of unit (s, h), whose first chunk sits at u0 in
+// the linear chunk list; the unit has n chunks and the sequence L tokens.
+struct Piece {
+  int s, h, n, L, u0, j0, j1;
+};
+
+// One stage, uniform across the wavefront: chunks [j, j + cnt) of a piece.
 struct Stage {
-  int s, h, j, cnt, L, n;
-  int j_first;     // chunk (within the unit) where this wavefront's piece starts
-  int64_t u0;      // linear index of the unit's first chunk
-  bool valid;      // false past the end of the wavefront's range
-  bool first;      // first stage of the piece: load Q, reset the softmax state
-  bool last;       // last stage of the piece: write it out or store the partial
-  bool piece_at_a; // the piece starts at the wavefront's first chunk
-  bool bad;        // a block id of this stage is outside the pool
+  int s, h, n, L, u0, j, cnt, flags;
 };
 
-// Where a wavefront stands: chunk x of the linear list, chunk j of unit
-// (s, h); the sub-range being walked ends at `end`.
-struct Pos {
-  int64_t x, end;
-  int64_t before;  // chunks (per KV head) of the sequences before s
-  int s, n, L, h, j;
-};
-
-// Uniform cursor over the wavefront's range [a, b), walked as up to three
-// sub-ranges: the piece holding chunk a, the piece holding chunk b - 1, and
-// the whole units between them.  The two boundary pieces (the ones another
-// wavefront shares) go first, so that split units are merged early rather
-// than at the end of the kernel.
+// Where a wavefront stands in its range [a, b) of the chunk list.  The
+// range is walked as the piece holding chunk a (A), then the piece holding
+// chunk b - 1 (Z) when that is another unit, then the whole units between
+// them: the boundary pieces, which other wavefronts share, go first so that
+// split units are merged early rather than at the end of the kernel.
 struct Cursor {
-  Pos cur;
-  Pos queue[2];
-  int nq;
-  int64_t a;
-  int j_first;
-  int64_t piece_x;
-  bool new_piece;
+  Piece cur;       // piece being walked
+  Piece z;         // piece Z (j1 = 0 when there is none; z.u0 ends the middle walk)
+  int j;           // next chunk of cur
+  int phase;       // 0: A, 1: Z, 2: middle units, 3: done
+  int a_end;       // chunk-list index just past unit A
+  int a_s, a_h;    // unit A, where the middle walk starts from
 };
 
 // A partial piece on its way to being counted in: stored (its stores must
 // complete first), then counted (the counter's old value is in flight).
 struct Pending {
-  int state;       // 0 empty, 1 stored, 2 counted
-  int s, h;
-  int64_t u0, w0, w1;
+  int state;       // 0 empty/done, 1 stored, 2 counted, 3 to be merged here
+  int s, h, u0, n;
   int prior;       // lane 0: counter value before this piece was counted
 };
 
-// Pieces of wavefront w are stored in slot 2w (the piece that starts at the
-// wavefront's first chunk) or 2w + 1 (the piece that ends at its last).
-__device__ __forceinline__ int64_t piece_slot(int64_t w, int64_t w0, int64_t u0, int64_t C) {
-  return (w == w0 && u0 != w0 * C) ? 2 * w + 1 : 2 * w;
-}
-
-// Partial records are shared between wavefronts that may sit on different
-// XCDs, whose L2 caches are not coherent with each other.  They are written
-// and read with buffer accesses carrying the device-coherence cache bit
-// (write-through stores, loads that miss the L2), so no cache-wide
-// write-back or invalidate is needed: a writer counts its piece in only after
-// its stores have completed (s_waitcnt), and the merger only loads after it
-// has read the counter.  A record holds acc as [D/4][G][4] floats (16-byte
-// pieces, lane-contiguous per store) and then {m, l, 0, 0} per query head.
-constexpr int kDeviceCoherent = 16;           // sc1
-constexpr int kBufferWord3 = 0x00020000;      // raw 32-bit buffer access
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t record_rsrc(const float* rec, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(rec), 0, bytes, kBufferWord3);
-}
-__device__ __forceinline__ void store_record(__amdgpu_buffer_rsrc_t r, int byte_off, f32x4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, byte_off, 0, kDeviceCoherent);
-}
-__device__ __forceinline__ f32x4 load_record(__amdgpu_buffer_rsrc_t r, int byte_off) {
-  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kDeviceCoherent));
-}
-
-// Merge the partial softmax states of unit (s, h), pieces from wavefronts
-// w0..w1, into out (run by the wavefront that counted in the last piece):
-// out = sum_p e^(m_p - M) acc_p / sum_p e^(m_p - M) l_p, M = max_p m_p, taken
-// one piece at a time with a running maximum.  Lane l handles the 4-float
-// groups e = l + 64 i of the G x D output, kIt of them per pass; all loads of
-// one piece for a pass are issued together.
-template <int D>
-__device__ __forceinline__ void merge_unit(const DecodeParams& p, const Pending& pd, int64_t C,
-                                           int lane) {
-  constexpr int kIt = 4;
-  const int G = p.group;
-  const int groups = G * D / 4;
-  const int rec_bytes = G * (D + 4) * 4;
-  f32x4* o = reinterpret_cast<f32x4*>(p.out + ((int64_t)pd.s * p.num_q_heads + (int64_t)pd.h * G) * D);
-  for (int e0 = 0; e0 < groups; e0 += 64 * kIt) {
-    float M[kIt], den[kIt];
-    f32x4 num[kIt];
-#pragma unroll
-    for (int it = 0; it < kIt; ++it) {
-      M[it] = kNegInf;
-      den[it] = 0.f;
-      num[it] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    for (int64_t w = pd.w0; w <= pd.w1; ++w) {
-      const auto r = record_rsrc(p.partials + piece_slot(w, pd.w0, pd.u0, C) * (rec_bytes / 4), rec_bytes);
-      f32x4 ml[kIt], acc[kIt];
-#pragma unroll
-      for (int it = 0; it < kIt; ++it) {
-        const int e = e0 + lane + 64 * it;
-        const int g = e / (D / 4), d4 = e - g * (D / 4);
-        if (e < groups) {
-          ml[it] = load_record(r, (G * D + g * 4) * 4);
-          acc[it] = load_record(r, (d4 * G + g) * 16);
-        }
-      }
-#pragma unroll
-      for (int it = 0; it < kIt; ++it) {
-        if (e0 + lane + 64 * it < groups) {
-          const float m_new = __builtin_fmaxf(M[it], ml[it][0]);
-          const float a = (M[it] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(M[it] - m_new);
-          const float f = (ml[it][0] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(ml[it][0] - m_new);
-          num[it] = num[it] * a + acc[it] * f;
-          den[it] = den[it] * a + ml[it][1] * f;
-          M[it] = m_new;
-        }
-      }
-    }
-#pragma unroll
-    for (int it = 0; it < kIt; ++it) {
-      const int e = e0 + lane + 64 * it;
-      if (e < groups) o[e] = num[it] * (p.out_scale / den[it]);
-    }
-  }
-}
-
-// Count a stored piece in (its stores have completed).
-__device__ __forceinline__ void count_piece(const DecodeParams& p, Pending& pd, int lane) {
-  int32_t* counter = p.counters + (int64_t)pd.s * p.num_kv_heads + pd.h;
-  pd.prior = 0;
-  if (lane == 0) pd.prior = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  pd.state = 2;
-}
-
-// Read the counter's old value: the wavefront that counted in the unit's
-// last piece merges all of them and re-arms the counter for the next call.
-template <int D>
-__device__ __forceinline__ void resolve_piece(const DecodeParams& p, Pending& pd, int64_t C, int lane) {
-  const int prior = readlane(pd.prior, 0);
-  if (prior == (int)(pd.w1 - pd.w0)) {
-    merge_unit<D>(p, pd, C, lane);
-    if (lane == 0)
-      __hip_atomic_store(p.counters + (int64_t)pd.s * p.num_kv_heads + pd.h, 0, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-  }
-  pd.state = 0;
-}
-
-// The unit after the one p stands in (p.j reset to 0); seq_lens is read for
-// the following sequences when p's was its sequence's last unit.
-__device__ __forceinline__ void next_unit(Pos& c, const DecodeParams& p, int max_len) {
-  c.j = 0;
-  if (c.h + 1 < p.num_kv_heads) {
-    ++c.h;
+// The unit after (s, h): (s, h + 1), or head 0 of the next sequence with
+// chunks (n and L are updated then).  Only called while chunks remain, so
+// such a sequence exists.
+__device__ __forceinline__ void next_unit(const DecodeParams& p, int max_len, int& s, int& h,
+                                          int& n, int& L) {
+  if (h + 1 < p.num_kv_heads) {
+    ++h;
     return;
   }
-  c.h = 0;
-  c.before += c.n;
-  // Only called while chunks remain, so a later sequence with chunks exists.
+  h = 0;
   for (;;) {
-    ++c.s;
-    c.L = sload(p.seq_lens, c.s);
-    c.n = chunks_of(c.L, max_len);
-    if (c.n > 0) break;
+    ++s;
+    L = sload(p.seq_lens, s);
+    n = chunks_of(L, max_len);
+    if (n > 0) break;
   }
 }
 
 // Next stage of the cursor's range; moves the cursor past it.
 template <int NSUB>
-__device__ __forceinline__ Stage next_stage(Cursor& cc, const DecodeParams& p, int max_len) {
-  if (cc.cur.x >= cc.cur.end && cc.nq > 0) {
-    cc.cur = cc.queue[0];
-    cc.queue[0] = cc.queue[1];
-    --cc.nq;
-    cc.new_piece = true;
+__device__ __forceinline__ Stage next_stage(Cursor& c, const DecodeParams& p, int max_len) {
+  if (c.phase < 3 && c.j == c.cur.j1) {
+    if (c.phase == 0 && c.z.j1 > 0) {
+      c.cur = c.z;
+      c.phase = 1;
+    } else if (c.phase <= 1 && c.a_end < c.z.u0) {
+      // First middle unit: the one after unit A.
+      int s = c.a_s, h = c.a_h;
+      int L = sload(p.seq_lens, s);
+      int n = chunks_of(L, max_len);
+      next_unit(p, max_len, s, h, n, L);
+      c.cur = Piece{s, h, n, L, c.a_end, 0, n};
+      c.phase = 2;
+    } else if (c.phase == 2 && c.cur.u0 + c.cur.n < c.z.u0) {
+      int s = c.cur.s, h = c.cur.h, n = c.cur.n, L = c.cur.L;
+      const int u0 = c.cur.u0 + n;
+      next_unit(p, max_len, s, h, n, L);
+      c.cur = Piece{s, h, n, L, u0, 0, n};
+    } else {
+      c.phase = 3;
+    }
+    c.j = c.cur.j0;
   }
-  Pos& c = cc.cur;
   Stage st;
-  st.valid = c.x < c.end;
-  st.s = uni(c.s); st.h = uni(c.h); st.j = uni(c.j); st.L = uni(c.L); st.n = uni(c.n);
-  st.u0 = uni64((int64_t)p.num_kv_heads * c.before + (int64_t)c.h * c.n);
-  st.bad = false;
-  st.first = cc.new_piece;
-  if (cc.new_piece) {
-    cc.j_first = c.j;
-    cc.piece_x = c.x;
-  }
-  st.j_first = cc.j_first;
-  st.piece_at_a = (cc.piece_x == cc.a);
-  if (!st.valid) {
-    st.cnt = 0;
-    st.first = st.last = false;
+  if (c.phase == 3) {
+    st = Stage{0, 0, 0, 0, 0, 0, 0, 0};
     return st;
   }
-  int64_t cnt = c.n - c.j;
-  if (c.end - c.x < cnt) cnt = c.end - c.x;
-  if (NSUB < cnt) cnt = NSUB;
-  st.cnt = uni((int)cnt);
-  c.x += cnt;
-  c.j += (int)cnt;
-  cc.new_piece = false;
-  st.last = (c.j == c.n) || (c.x == c.end);
-  if (c.j == c.n && c.x < c.end) {
-    cc.new_piece = true;
-    next_unit(c, p, max_len);
-  }
+  const Piece& pc = c.cur;
+  int cnt = pc.j1 - c.j;
+  if (cnt > NSUB) cnt = NSUB;
+  int f = kValid;
+  if (c.j == pc.j0) f |= kFirst;
+  if (c.j + cnt == pc.j1) f |= kLast;
+  if (c.j + cnt == pc.n && pc.n * kSub > pc.L) f |= kTail;
+  if (c.phase == 0) f |= kAtA;
+  if (pc.j0 == 0 && pc.j1 == pc.n) f |= kWhole;
+  st = Stage{uni(pc.s), uni(pc.h), uni(pc.n), uni(pc.L), uni(pc.u0), uni(c.j), uni(cnt), uni(f)};
+  c.j += cnt;
   return st;
 }
 
 // Issue every load of a stage: exactly StageBuf::kLoads vector loads, always,
 // so the wait counts the compiler derives do not depend on the branch taken.
-// Chunk slots past the stage (or a stage past the range) read one fixed line.
+// Chunk slots past the stage, tiles of out-of-pool blocks and the query of a
+// stage that does not start a piece read tile 0 / query row 0 instead, with
+// the same lane offsets, so every address stays inside its buffer.  Returns
+// whether a block id of the stage lies outside the pool.
 template <int D, bool FP8, int NSUB>
-__device__ __forceinline__ void issue_stage(const DecodeParams& p, Stage& st,
-                                            StageBuf<D, FP8, NSUB>& buf, int lane) {
+__device__ __forceinline__ bool issue_stage(const DecodeParams& p, const Stage& st,
+                                            StageBuf<D, FP8, NSUB>& buf, int q_off, int k_off,
+                                            int v_off) {
   using T = Tile<D, FP8>;
-  const int qd = lane >> 4, col = lane & 15;
   const int G = p.group;
-  const int subs = p.block_size / kSub;
-  // Query operand: lane (col = head in group, qd = k-group) holds 8 dims.
+  // Query operand: lane (col = head in group, qd = k-group) holds 8 dims;
+  // bf16 K tiles put dims 32c + 8qd .. +7 in MFMA c; fp8 K tiles put dims
+  // 64(c/2) + 16qd + 8(c%2) .. +7 there.
   {
-    const bool want = st.first && col < G;
-    const uint16_t* qrow = p.q + ((int64_t)st.s * p.num_q_heads + (int64_t)st.h * G + col) * D;
+    const int64_t row = (st.flags & kFirst) ? ((int64_t)st.s * p.num_q_heads + (int64_t)st.h * G) * D : 0;
+    const uint8_t* qb = reinterpret_cast<const uint8_t*>(p.q + row) + q_off;
 #pragma unroll
     for (int c = 0; c < T::QK; ++c) {
-      // bf16 K tiles put dims 32c + 8qd .. +7 in MFMA c; fp8 K tiles put
-      // dims 64(c/2) + 16qd + 8(c%2) .. +7 there.
-      const int d0 = FP8 ? 64 * (c >> 1) + 16 * qd + 8 * (c & 1) : 32 * c + 8 * qd;
-      buf.q[c] = *reinterpret_cast<const u32x4*>(want ? qrow + d0 : p.q);
+      const int imm = FP8 ? 128 * (c >> 1) + 16 * (c & 1) : 64 * c;
+      buf.q[c] = *reinterpret_cast<const u32x4*>(qb + imm);
     }
   }
+  // Block ids of the stage's chunks: chunk j lies in block j / subs at
+  // sub-block j % subs.  All ids are loaded first (scalar loads); ids past
+  // the stage repeat its last one, so no table entry past the sequence's
+  // blocks is read.
+  const int subs = p.subs;
+  const int jlast = st.j + (st.cnt > 0 ? st.cnt - 1 : 0);
+  const int bi0 = (subs == 1) ? st.j : (int)__umulhi((unsigned)st.j, p.subs_magic);
+  const int bil = (subs == 1) ? jlast : (int)__umulhi((unsigned)jlast, p.subs_magic);
   const int32_t* bt = p.block_tables + (int64_t)st.s * p.max_blocks;
-  const int64_t head_tiles = (int64_t)st.h * subs;
-  // All block ids of the stage first (scalar loads, one wait), then the
-  // tiles.  Chunk slots past the stage re-read the last valid id.
-  int blk[NSUB];
-  const int jlast = st.valid ? st.j + st.cnt - 1 : 0;
+  int blk[NSUB], sub[NSUB];
+  {
+    int bi = bi0, sb = st.j - bi0 * subs;
 #pragma unroll
-  for (int k = 0; k < NSUB; ++k) {
-    const int jj = (st.j + k < jlast) ? st.j + k : jlast;
-    blk[k] = sload(bt, jj / subs);
-  }
-#pragma unroll
-  for (int k = 0; k < NSUB; ++k) {
-    int64_t tile = 0;
-    bool ok = false;
-    if (k < st.cnt) {
-      const int jj = st.j + k;
-      const int bi = jj / subs;
-      ok = (unsigned)blk[k] < (unsigned)p.num_blocks;
-      if (ok)
-        tile = ((int64_t)blk[k] * p.num_kv_heads * subs + head_tiles + (jj - bi * subs)) * T::TILE_BYTES;
-      else
-        st.bad = true;
+    for (int k = 0; k < NSUB; ++k) {
+      blk[k] = sload(bt, bi < bil ? bi : bil);
+      sub[k] = sb;
+      if (++sb == subs) {
+        sb = 0;
+        ++bi;
+      }
     }
-    const uint8_t* kt = p.k_cache + tile;
-    const uint8_t* vt = p.v_cache + tile;
-    const int kl = ok ? lane * 16 : 0;
-    const int vl = ok ? (col * 4 + qd) * 16 : 0;
-#pragma unroll
-    for (int c = 0; c < T::KLD; ++c)
-      buf.k[k][c] = load_kv(reinterpret_cast<const u32x4*>(kt + c * 1024 + kl));
-    // V tile [d/16R][d%16][t/4][(d/16)%R][t%4]: lane (col, qd) reads the 16
-    // bytes holding tokens 4qd..4qd+3 of dims 16(R e + r) + col.
-#pragma unroll
-    for (int e = 0; e < T::VLD; ++e)
-      buf.v[k][e] = load_kv(reinterpret_cast<const u32x4*>(vt + e * 1024 + vl));
   }
+  bool bad = false;
+#pragma unroll
+  for (int k = 0; k < NSUB; ++k) {
+    const bool in = k < st.cnt;
+    const bool ok = (unsigned)blk[k] < (unsigned)p.num_blocks;
+    bad |= in && !ok;
+    const int64_t tile = (in && ok) ? (int64_t)blk[k] * p.blk_stride +
+                                          (int64_t)(st.h * subs + sub[k]) * T::TILE_BYTES
+                                    : 0;
+    const uint8_t* kt = p.k_cache + tile + k_off;
+    const uint8_t* vt = p.v_cache + tile + v_off;
+#pragma unroll
+    for (int c = 0; c < T::KLD; ++c) buf.k[k][c] = load_kv(reinterpret_cast<const u32x4*>(kt + c * 1024));
+#pragma unroll
+    for (int e = 0; e < T::VLD; ++e) buf.v[k][e] = load_kv(reinterpret_cast<const u32x4*>(vt + e * 1024));
+  }
+  return bad;
+}
+
+// bf16 pair {tokens 4qd, 4qd+1}, {4qd+2, 4qd+3} of sub-block k for the V^T
+// operand rows 16 dc + col.
+template <int D, bool FP8, int NSUB>
+__device__ __forceinline__ u32x2 v_operand(const StageBuf<D, FP8, NSUB>& buf, int k, int dc) {
+  using T = Tile<D, FP8>;
+  u32x2 a;
+  if constexpr (FP8) {
+    const uint32_t w = buf.v[k][dc / T::R][dc % T::R];
+    a[0] = fp8x2_to_bf16x2<false>(w);
+    a[1] = fp8x2_to_bf16x2<true>(w);
+  } else {
+    a[0] = buf.v[k][dc / T::R][2 * (dc % T::R)];
+    a[1] = buf.v[k][dc / T::R][2 * (dc % T::R) + 1];
+  }
+  return a;
 }
 
 // The math of one stage: logits, online-softmax update, P V accumulation.
-template <int D, bool FP8, int NSUB>
+// MASK: the stage holds the unit's last chunk and it is partial, so logits
+// of tokens at or past L are set to -inf and their V elements to zero (they
+// hold arbitrary bits, possibly NaN, and 0 * NaN is NaN).
+template <int D, bool FP8, int NSUB, bool MASK>
 __device__ __forceinline__ void compute_stage(const DecodeParams& p, const Stage& st,
                                               const StageBuf<D, FP8, NSUB>& buf,
                                               const bf16x8* qop, Softmax<D>& sm, int lane) {
@@ -494,91 +413,187 @@ __device__ __forceinline__ void compute_stage(const DecodeParams& p, const Stage
       const int tok0 = first_tok + k * kSub + qd * 4;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float v = s[i] * p.qk_scale;
-        z[k][i] = (tok0 + i < L) ? v : kNegInf;
+        z[k][i] = s[i] * p.qk_scale;
+        if (MASK && tok0 + i >= L) z[k][i] = kNegInf;
         mx = __builtin_fmaxf(mx, z[k][i]);
       }
     }
   }
   mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16, 64));
   mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32, 64));
-  const float m_new = __builtin_fmaxf(sm.m, mx);
-  const float alpha = (sm.m == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(sm.m - m_new);
-  sm.m = m_new;
-
-  float psum = 0.f;
-  float pz[NSUB][4];
+  if (__builtin_amdgcn_ballot_w64(mx > sm.m + kRescaleSlack) != 0) {
+    const float m_new = __builtin_fmaxf(sm.m, mx);
+    const float alpha = (sm.m == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(sm.m - m_new);
+    sm.m = m_new;
+    sm.l *= alpha;
 #pragma unroll
-  for (int k = 0; k < NSUB; ++k) {
-    if (k < st.cnt) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pz[k][i] = __builtin_amdgcn_exp2f(z[k][i] - m_new);
-        psum += pz[k][i];
-      }
-    }
+    for (int dc = 0; dc < T::DC; ++dc) sm.acc[dc] *= alpha;
   }
-  sm.l = sm.l * alpha + psum;
-#pragma unroll
-  for (int dc = 0; dc < T::DC; ++dc) sm.acc[dc] *= alpha;
 
+  // O^T += V^T P^T, one 16-deep product per sub-block and P half; the V^T
+  // operand of dim block dc is a register pair of the loaded tile, so the
+  // loads feed the matrix cores without any register copies.
 #pragma unroll
   for (int k = 0; k < NSUB; ++k) {
     if (k < st.cnt) {
-      i16x4 phi, plo;
-      split_p(pz[k], phi, plo);
-      // Tokens past the sequence end hold arbitrary bits (possibly NaN):
-      // their probability is 0, but 0 * NaN is NaN, so zero their V.
-      const int tok0 = first_tok + k * kSub + qd * 4;
-      const bool tail = (first_tok + k * kSub + kSub > L);
-      const uint32_t m0 = (tok0 + 0 < L ? 0x0000FFFFu : 0u) | (tok0 + 1 < L ? 0xFFFF0000u : 0u);
-      const uint32_t m1 = (tok0 + 2 < L ? 0x0000FFFFu : 0u) | (tok0 + 3 < L ? 0xFFFF0000u : 0u);
+      float pz[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pz[i] = __builtin_amdgcn_exp2f(z[k][i] - sm.m);
+      sm.l += (pz[0] + pz[1]) + (pz[2] + pz[3]);
+      u32x2 hi, lo;
+      split_p(pz, hi, lo);
+      uint32_t m0 = 0xFFFFFFFFu, m1 = 0xFFFFFFFFu;
+      if (MASK) {
+        const int tok0 = first_tok + k * kSub + qd * 4;
+        m0 = (tok0 + 0 < L ? 0x0000FFFFu : 0u) | (tok0 + 1 < L ? 0xFFFF0000u : 0u);
+        m1 = (tok0 + 2 < L ? 0x0000FFFFu : 0u) | (tok0 + 3 < L ? 0xFFFF0000u : 0u);
+      }
 #pragma unroll
       for (int dc = 0; dc < T::DC; ++dc) {
-        u32x2 a;
-        if constexpr (FP8) {
-          const uint32_t w = buf.v[k][dc / T::R][dc % T::R];
-          a[0] = fp8x2_to_bf16x2<false>(w);
-          a[1] = fp8x2_to_bf16x2<true>(w);
-        } else {
-          a[0] = buf.v[k][dc / T::R][2 * (dc % T::R)];
-          a[1] = buf.v[k][dc / T::R][2 * (dc % T::R) + 1];
-        }
-        if (tail) {
+        u32x2 a = v_operand<D, FP8, NSUB>(buf, k, dc);
+        if (MASK) {
           a[0] &= m0;
           a[1] &= m1;
         }
         const i16x4 av = as_i16x4(a);
-        sm.acc[dc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, phi, sm.acc[dc], 0, 0, 0);
-        sm.acc[dc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, plo, sm.acc[dc], 0, 0, 0);
+        sm.acc[dc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, as_i16x4(hi), sm.acc[dc], 0, 0, 0);
+        sm.acc[dc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, as_i16x4(lo), sm.acc[dc], 0, 0, 0);
       }
     }
   }
 }
 
-// Per-wavefront state carried across stages.
+// Partial records are shared between wavefronts that may sit on different
+// XCDs, whose L2 caches are not coherent with each other.  They are written
+// and read with buffer accesses carrying the device-coherence cache bit
+// (write-through stores, loads that miss the L2), so no cache-wide
+// write-back or invalidate is needed: a writer counts its piece in only after
+// its stores have completed (s_waitcnt), and the merger only loads after it
+// has read the counter.  A record holds acc as [D/4][G][4] floats (16-byte
+// pieces, lane-contiguous per store) and then {m, l, 0, 0} per query head.
+constexpr int kDeviceCoherent = 16;           // sc1
+constexpr int kBufferWord3 = 0x00020000;      // raw 32-bit buffer access
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t record_rsrc(const float* rec, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(rec), 0, bytes, kBufferWord3);
+}
+__device__ __forceinline__ void store_record(__amdgpu_buffer_rsrc_t r, int byte_off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, byte_off, 0, kDeviceCoherent);
+}
+__device__ __forceinline__ f32x4 load_record(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kDeviceCoherent));
+}
+
+// Pieces of wavefront w are stored in slot 2w (the piece that starts at the
+// wavefront's first chunk) or 2w + 1 (the piece that ends at its last).
+__device__ __forceinline__ int piece_slot(int w, int w0, int u0, int C) {
+  return (w == w0 && u0 != w0 * C) ? 2 * w + 1 : 2 * w;
+}
+
+// Merge the partial softmax states of unit (s, h), pieces from wavefronts
+// w0..w1, into out (run by the wavefront that counted in the last piece):
+// out = sum_p e^(m_p - M) acc_p / sum_p e^(m_p - M) l_p, M = max_p m_p, taken
+// one piece at a time with a running maximum.  Lane l handles the 4-float
+// groups e = l + 64 i of the G x D output, kIt of them per pass; the loads of
+// kBatch pieces are issued together.
+template <int D, int kIt, int kBatch>
+__device__ __forceinline__ void merge_unit(const DecodeParams& p, const Pending& pd, int C, int lane) {
+  const int G = p.group;
+  const int groups = G * D / 4;
+  const int rec_bytes = G * (D + 4) * 4;
+  const int w0 = pd.u0 / C, w1 = (pd.u0 + pd.n - 1) / C;
+  f32x4* o = reinterpret_cast<f32x4*>(p.out + ((int64_t)pd.s * p.num_q_heads + (int64_t)pd.h * G) * D);
+  for (int e0 = 0; e0 < groups; e0 += 64 * kIt) {
+    float M[kIt], den[kIt];
+    f32x4 num[kIt];
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      M[it] = kNegInf;
+      den[it] = 0.f;
+      num[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int wb = w0; wb <= w1; wb += kBatch) {
+      f32x4 ml[kBatch][kIt], acc[kBatch][kIt];
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        const int w = (wb + b <= w1) ? wb + b : w1;
+        const auto r = record_rsrc(p.partials + (int64_t)piece_slot(w, w0, pd.u0, C) * (rec_bytes / 4), rec_bytes);
+#pragma unroll
+        for (int it = 0; it < kIt; ++it) {
+          const int e = e0 + lane + 64 * it;
+          const int g = e / (D / 4), d4 = e - g * (D / 4);
+          const bool in = e < groups;
+          ml[b][it] = load_record(r, in ? (G * D + g * 4) * 4 : 0);
+          acc[b][it] = load_record(r, in ? (d4 * G + g) * 16 : 0);
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        if (wb + b <= w1) {
+#pragma unroll
+          for (int it = 0; it < kIt; ++it) {
+            const float m_new = __builtin_fmaxf(M[it], ml[b][it][0]);
+            const float a = (M[it] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(M[it] - m_new);
+            const float f = (ml[b][it][0] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(ml[b][it][0] - m_new);
+            num[it] = num[it] * a + acc[b][it] * f;
+            den[it] = den[it] * a + ml[b][it][1] * f;
+            M[it] = m_new;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const int e = e0 + lane + 64 * it;
+      if (e < groups) o[e] = num[it] * (p.out_scale / den[it]);
+    }
+  }
+}
+
+// Count a stored piece in (its stores have completed).
+__device__ __forceinline__ void count_piece(const DecodeParams& p, Pending& pd, int lane) {
+  int32_t* counter = p.counters + (int64_t)pd.s * p.num_kv_heads + pd.h;
+  pd.prior = 0;
+  if (lane == 0) pd.prior = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  pd.state = 2;
+}
+
+// Read the counter's old value: the wavefront that counted in the unit's
+// last piece merges all of them (state 3) and then re-arms the counter for
+// the next call; the others are done with the piece.
+__device__ __forceinline__ void resolve_piece(Pending& pd, int C) {
+  const int prior = readlane(pd.prior, 0);
+  const int pieces = (pd.u0 + pd.n - 1) / C - pd.u0 / C + 1;
+  pd.state = (prior == pieces - 1) ? 3 : 0;
+}
+
 template <int D>
-struct WaveState_ {
+__device__ __forceinline__ void merge_and_rearm(const DecodeParams& p, Pending& pd, int C, int lane) {
+  merge_unit<D, D / 32, 4>(p, pd, C, lane);
+  if (lane == 0)
+    __hip_atomic_store(p.counters + (int64_t)pd.s * p.num_kv_heads + pd.h, 0, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  pd.state = 0;
+}
+
+// Per-wavefront state carried across stages.
+template <int D, bool FP8>
+struct WaveState {
   Softmax<D> sm;
   bool bad;
   Pending pend[2];
-};
-template <int D, bool FP8>
-struct WaveState : WaveState_<D> {
   bf16x8 q[Tile<D, FP8>::QK];
 };
 
 // Math of a stage plus, at a piece boundary, the piece's output.
 template <int D, bool FP8, int NSUB>
-__device__ __forceinline__ void finish_stage(const DecodeParams& p, const Stage& st,
+__device__ __forceinline__ void finish_stage(const DecodeParams& p, const Stage& st, bool st_bad,
                                              const StageBuf<D, FP8, NSUB>& buf,
-                                             WaveState<D, FP8>& ws, int64_t wave, int64_t C,
-                                             int lane) {
+                                             WaveState<D, FP8>& ws, int wave, int lane) {
   using T = Tile<D, FP8>;
-  if (!st.valid) return;
+  if (!(st.flags & kValid)) return;
   const int qd = lane >> 4, col = lane & 15;
   const int G = p.group;
-  if (st.first) {
+  if (st.flags & kFirst) {
 #pragma unroll
     for (int c = 0; c < T::QK; ++c) ws.q[c] = as_bf16x8(col < G ? buf.q[c] : u32x4{0u, 0u, 0u, 0u});
     ws.sm.m = kNegInf;
@@ -587,14 +602,17 @@ __device__ __forceinline__ void finish_stage(const DecodeParams& p, const Stage&
     for (int dc = 0; dc < T::DC; ++dc) ws.sm.acc[dc] = f32x4{0.f, 0.f, 0.f, 0.f};
     ws.bad = false;
   }
-  ws.bad |= st.bad;
-  compute_stage<D, FP8, NSUB>(p, st, buf, ws.q, ws.sm, lane);
-  if (!st.last) return;
+  ws.bad |= st_bad;
+  if (st.flags & kTail)
+    compute_stage<D, FP8, NSUB, true>(p, st, buf, ws.q, ws.sm, lane);
+  else
+    compute_stage<D, FP8, NSUB, false>(p, st, buf, ws.q, ws.sm, lane);
+  if (!(st.flags & kLast)) return;
 
   float ltot = ws.sm.l + __shfl_xor(ws.sm.l, 16, 64);
   ltot += __shfl_xor(ltot, 32, 64);
   if (ws.bad) ltot = __builtin_nanf("");
-  if (st.j_first == 0 && st.j + st.cnt == st.n) {
+  if (st.flags & kWhole) {
     // The whole unit is this wavefront's: write the output directly.
     if (col < G) {
       const float inv = p.out_scale / ltot;
@@ -604,32 +622,35 @@ __device__ __forceinline__ void finish_stage(const DecodeParams& p, const Stage&
     }
     return;
   }
-  const int64_t slot = st.piece_at_a ? 2 * wave : 2 * wave + 1;
+  const int slot = (st.flags & kAtA) ? 2 * wave : 2 * wave + 1;
   const int rec_bytes = G * (D + 4) * 4;
-  const auto r = record_rsrc(p.partials + slot * (rec_bytes / 4), rec_bytes);
+  const auto r = record_rsrc(p.partials + (int64_t)slot * (rec_bytes / 4), rec_bytes);
   if (col < G) {
 #pragma unroll
     for (int dc = 0; dc < T::DC; ++dc) store_record(r, ((dc * 4 + qd) * G + col) * 16, ws.sm.acc[dc]);
     if (qd == 0) store_record(r, (G * D + col * 4) * 4, f32x4{ws.sm.m, ltot, 0.f, 0.f});
   }
+  // A wavefront stores at most two pieces (its boundary pieces A and Z), so
+  // a free slot always exists.
   Pending& pd = (ws.pend[0].state == 0) ? ws.pend[0] : ws.pend[1];
   pd.state = 1;
   pd.s = st.s;
   pd.h = st.h;
   pd.u0 = st.u0;
-  pd.w0 = st.u0 / C;
-  pd.w1 = (st.u0 + st.n - 1) / C;
+  pd.n = st.n;
 }
 
 // Advance the pieces waiting to be counted in.  Called right after a
 // stage's loads were issued: every piece stored before that issue has its
 // stores complete once all but those loads are done, and every counter
-// value read before it has arrived by then too.
-template <int D, int LOADS>
-__device__ __forceinline__ void settle(const DecodeParams& p, WaveState_<D>& ws, int64_t C, int lane) {
+// value read before it has arrived by then too.  A merge this wavefront
+// owes is left for the end of its range, where the registers that hold the
+// pipeline's loads are free for the merge's own.
+template <int D, bool FP8, int LOADS>
+__device__ __forceinline__ void settle(const DecodeParams& p, WaveState<D, FP8>& ws, int C, int lane) {
 #pragma unroll
   for (int i = 0; i < 2; ++i)
-    if (ws.pend[i].state == 2) resolve_piece<D>(p, ws.pend[i], C, lane);
+    if (ws.pend[i].state == 2) resolve_piece(ws.pend[i], C);
   if (ws.pend[0].state == 1 || ws.pend[1].state == 1) {
     wait_vmcnt<LOADS>();
 #pragma unroll
@@ -641,6 +662,7 @@ __device__ __forceinline__ void settle(const DecodeParams& p, WaveState_<D>& ws,
 template <int D, bool FP8, int NSUB>
 __global__ __launch_bounds__(kDecodeThreads, PA_DECODE_MIN_WAVES) void decode_kernel(const DecodeParams p) {
   using Buf = StageBuf<D, FP8, NSUB>;
+  using T = Tile<D, FP8>;
   static_assert(Buf::kLoads <= 63, "a stage must fit the vector-memory counter");
   const int lane = threadIdx.x & 63;
   // Workgroups are dispatched round-robin over the 8 XCDs; the ones that
@@ -651,14 +673,14 @@ __global__ __launch_bounds__(kDecodeThreads, PA_DECODE_MIN_WAVES) void decode_ke
   const int full = ngroups / 64 * 64;
   int g = blockIdx.x;
   if (g < full) g = (g / 64) * 64 + (g % 8) * 8 + (g % 64) / 8;
-  const int wave = __builtin_amdgcn_readfirstlane(g * kWavesPerGroup + (threadIdx.x >> 6));
+  const int wave = uni(g * kWavesPerGroup + (threadIdx.x >> 6));
   if (wave >= p.num_waves) return;
   const int S = p.num_seqs, Hkv = p.num_kv_heads;
   const int max_len = p.max_blocks * p.block_size;
 
   // Pass 1: total chunks.  Wavefront 0 also writes the rows no other
   // wavefront will touch: zeros for empty sequences, NaN for invalid ones.
-  int64_t total = 0;
+  int total = 0;
   for (int base = 0; base < S; base += 64) {
     const int si = base + lane;
     int n = 0;
@@ -677,24 +699,24 @@ __global__ __launch_bounds__(kDecodeThreads, PA_DECODE_MIN_WAVES) void decode_ke
     n = n < 0 ? 0 : n;
     total += uni(wave_reduce_sum(n));
   }
-  const int64_t W = uni64(total * Hkv);
-  int64_t C = p.chunk_fixed;
+  // The host guarantees num_seqs * Hkv * (chunks per sequence) < 2^30, so
+  // every chunk-list index below fits an int.
+  const int W = uni(total * Hkv);
+  int C = p.chunk_fixed;
   if (C <= 0) {
     C = (W + p.num_waves - 1) / p.num_waves;
     if (C < p.chunk_min) C = p.chunk_min;
   }
-  C = uni64(C);
-  const int64_t a = uni64((int64_t)wave * C);
-  if (a >= W) return;
+  C = uni(C);
+  if ((int64_t)wave * C >= W) return;
+  const int a = uni(wave * C);
+  const int b = (W - a > C) ? a + C : W;
 
-  const int64_t b = (a + C < W) ? a + C : W;
-
-  // Pass 2: the sequences holding chunks a and b - 1.
-  Pos pa_, pz;
-  pa_.s = pz.s = 0;
-  pa_.before = pz.before = 0;
+  // Pass 2: the sequences holding chunks a and b - 1, and the chunks of
+  // the sequences before them.
+  int sa = 0, sz = 0, before_a = 0, before_z = 0;
   {
-    int64_t carry = 0;
+    int carry = 0;
     bool found_a = false, found_z = false;
     for (int base = 0; base < S && !(found_a && found_z); base += 64) {
       const int si = base + lane;
@@ -702,64 +724,52 @@ __global__ __launch_bounds__(kDecodeThreads, PA_DECODE_MIN_WAVES) void decode_ke
       if (si < S) n = chunks_of(p.seq_lens[si], max_len);
       n = n < 0 ? 0 : n;
       const int incl = wave_incl_scan(n, lane);
-      const int64_t lo = (int64_t)Hkv * (carry + incl - n), hi = (int64_t)Hkv * (carry + incl);
+      const int lo = Hkv * (carry + incl - n), hi = Hkv * (carry + incl);
       const uint64_t hit_a = __ballot(n > 0 && lo <= a && a < hi);
       const uint64_t hit_z = __ballot(n > 0 && lo <= b - 1 && b - 1 < hi);
       if (hit_a && !found_a) {
         const int l0 = uni(__builtin_ctzll(hit_a));
-        pa_.s = uni(base + l0);
-        pa_.before = uni64(carry + readlane(incl - n, l0));
+        sa = uni(base + l0);
+        before_a = uni(carry + readlane(incl - n, l0));
         found_a = true;
       }
       if (hit_z && !found_z) {
         const int l0 = uni(__builtin_ctzll(hit_z));
-        pz.s = uni(base + l0);
-        pz.before = uni64(carry + readlane(incl - n, l0));
+        sz = uni(base + l0);
+        before_z = uni(carry + readlane(incl - n, l0));
         found_z = true;
       }
       carry += readlane(incl, 63);
     }
   }
   Cursor cur;
-  cur.a = a;
-  cur.nq = 0;
-  cur.new_piece = true;
-  pa_.L = sload(p.seq_lens, pa_.s);
-  pa_.n = chunks_of(pa_.L, max_len);
-  pz.L = sload(p.seq_lens, pz.s);
-  pz.n = chunks_of(pz.L, max_len);
   {
-    const int64_t off = a - (int64_t)Hkv * pa_.before;
-    pa_.h = uni((int)(off / pa_.n));
-    pa_.j = uni((int)(off - (int64_t)pa_.h * pa_.n));
-    pa_.x = a;
-  }
-  {
-    const int64_t off = (b - 1) - (int64_t)Hkv * pz.before;
-    pz.h = uni((int)(off / pz.n));
-    pz.j = 0;  // walk the last piece from its unit's start (or from a)
-    pz.x = (int64_t)Hkv * pz.before + (int64_t)pz.h * pz.n;
-  }
-  const int64_t a_unit_end = (int64_t)Hkv * pa_.before + (int64_t)(pa_.h + 1) * pa_.n;
-  if (b <= a_unit_end) {
-    // The whole range lies in one unit.
-    pa_.end = b;
-    cur.cur = pa_;
-  } else {
-    Pos mid = pa_;
-    pa_.end = a_unit_end;
-    pz.end = b;
-    cur.cur = pa_;
-    cur.queue[0] = pz;
-    cur.nq = 1;
-    if (a_unit_end < pz.x) {
-      next_unit(mid, p, max_len);
-      mid.x = a_unit_end;
-      mid.end = pz.x;
-      cur.queue[1] = mid;
-      cur.nq = 2;
+    const int La = sload(p.seq_lens, sa), na = chunks_of(La, max_len);
+    const int ha = uni((a - Hkv * before_a) / na);
+    const int u0a = Hkv * before_a + ha * na;
+    const int a_end = u0a + na;
+    cur.cur = Piece{sa, ha, na, La, u0a, a - u0a, (b < a_end ? b : a_end) - u0a};
+    cur.j = cur.cur.j0;
+    cur.phase = 0;
+    cur.a_end = a_end;
+    cur.a_s = sa;
+    cur.a_h = ha;
+    cur.z = Piece{0, 0, 0, 0, a_end, 0, 0};  // no piece Z: j1 = 0, middle walk ends at a_end
+    if (b > a_end) {
+      const int Lz = sload(p.seq_lens, sz), nz = chunks_of(Lz, max_len);
+      const int hz = uni((b - 1 - Hkv * before_z) / nz);
+      const int u0z = Hkv * before_z + hz * nz;
+      cur.z = Piece{sz, hz, nz, Lz, u0z, 0, b - u0z};
     }
   }
+
+  // Lane offsets of the stage loads (constant per lane): query row of head
+  // col (clamped into the group) at k-group qd; K lane = 16 bytes; V lane
+  // (col, qd) reads tokens 4qd..4qd+3 of dims 16(R e + r) + col.
+  const int qd = lane >> 4, col = lane & 15;
+  const int q_off = ((col < p.group ? col : p.group - 1) * D) * 2 + (FP8 ? 32 : 16) * qd;
+  const int k_off = lane * 16;
+  const int v_off = (col * 4 + qd) * 16;
 
   // Two-stage software pipeline: the loads of the next stage are in flight
   // while the current stage's math runs.
@@ -767,34 +777,35 @@ __global__ __launch_bounds__(kDecodeThreads, PA_DECODE_MIN_WAVES) void decode_ke
   ws.pend[0].state = ws.pend[1].state = 0;
   ws.bad = false;
   Buf A, B;
-  Stage sa = next_stage<NSUB>(cur, p, max_len);
-  issue_stage<D, FP8, NSUB>(p, sa, A, lane);
+  Stage sta = next_stage<NSUB>(cur, p, max_len);
+  bool bad_a = issue_stage<D, FP8, NSUB>(p, sta, A, q_off, k_off, v_off);
   for (;;) {
-    Stage sb = next_stage<NSUB>(cur, p, max_len);
-    issue_stage<D, FP8, NSUB>(p, sb, B, lane);
-    settle<D, Buf::kLoads>(p, ws, C, lane);
-    finish_stage<D, FP8, NSUB>(p, sa, A, ws, wave, C, lane);
-    if (!sb.valid) break;
-    sa = next_stage<NSUB>(cur, p, max_len);
-    issue_stage<D, FP8, NSUB>(p, sa, A, lane);
-    settle<D, Buf::kLoads>(p, ws, C, lane);
-    finish_stage<D, FP8, NSUB>(p, sb, B, ws, wave, C, lane);
-    if (!sa.valid) break;
+    const Stage stb = next_stage<NSUB>(cur, p, max_len);
+    const bool bad_b = issue_stage<D, FP8, NSUB>(p, stb, B, q_off, k_off, v_off);
+    settle<D, FP8, Buf::kLoads>(p, ws, C, lane);
+    finish_stage<D, FP8, NSUB>(p, sta, bad_a, A, ws, wave, lane);
+    if (!(stb.flags & kValid)) break;
+    sta = next_stage<NSUB>(cur, p, max_len);
+    bad_a = issue_stage<D, FP8, NSUB>(p, sta, A, q_off, k_off, v_off);
+    settle<D, FP8, Buf::kLoads>(p, ws, C, lane);
+    finish_stage<D, FP8, NSUB>(p, stb, bad_b, B, ws, wave, lane);
+    if (!(sta.flags & kValid)) break;
   }
   // Drain: everything issued has completed after this wait.
   wait_vmcnt<0>();
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-    if (ws.pend[i].state == 2) resolve_piece<D>(p, ws.pend[i], C, lane);
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-    if (ws.pend[i].state == 1) {
-      count_piece(p, ws.pend[i], lane);
-      resolve_piece<D>(p, ws.pend[i], C, lane);
-    }
+  for (int i = 0; i < 2; ++i) {
+    if (ws.pend[i].state == 1) count_piece(p, ws.pend[i], lane);
+    if (ws.pend[i].state == 2) resolve_piece(ws.pend[i], C);
+    if (ws.pend[i].state == 3) merge_and_rearm<D>(p, ws.pend[i], C, lane);
+  }
 }
 
-constexpr int kStage = PA_DECODE_STAGE;
+// fp8 tiles are half the bytes of bf16 ones: twice the sub-blocks per stage
+// keep the same bytes in flight per wavefront (16 KiB per stage, two stages
+// in flight).
+template <bool FP8>
+constexpr int kStage = FP8 ? PA_DECODE_STAGE_FP8 : PA_DECODE_STAGE;
 
 __global__ __launch_bounds__(256) void zero_kernel(uint32_t* p, size_t words) {
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < words; i += (size_t)gridDim.x * 256) p[i] = 0u;
@@ -803,7 +814,7 @@ __global__ __launch_bounds__(256) void zero_kernel(uint32_t* p, size_t words) {
 template <int D, bool FP8>
 hipError_t launch_typed(const DecodeParams& p, hipStream_t stream) {
   const unsigned groups = (unsigned)((p.num_waves + kWavesPerGroup - 1) / kWavesPerGroup);
-  hipLaunchKernelGGL((decode_kernel<D, FP8, kStage>), dim3(groups), dim3(kDecodeThreads), 0, stream, p);
+  hipLaunchKernelGGL((decode_kernel<D, FP8, kStage<FP8>>), dim3(groups), dim3(kDecodeThreads), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -812,7 +823,7 @@ int resident_waves_typed() {
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<D, FP8, kStage>, kDecodeThreads, 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<D, FP8, kStage<FP8>>, kDecodeThreads, 0) !=
       hipSuccess)
     return 0;
   return cus * per_cu * kWavesPerGroup;
