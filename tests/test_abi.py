@@ -95,6 +95,9 @@ def test_decode_validation():
     assert dec(desc(), part=-16) == SHAPE
     assert dec(desc(), scale=float("nan")) == SHAPE
     assert dec(desc(), S=0) == OK                      # empty batch: nothing to do
+    # chunk-list indices must fit 32 bits: S * Hkv * chunks per sequence < 2^30
+    assert dec(desc(), S=1 << 20, maxb=1 << 12) == SHAPE
+    assert dec(desc(), maxb=1 << 27) == SHAPE          # max_blocks * block_size > INT32_MAX
     assert dec(desc(), q=None) == NULL
     assert dec(desc(), ws=None) == WS
     assert dec(desc(), fp8=True, ks=0.0) == SHAPE
