@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 1
+#define PA_ABI_VERSION 2
 
 typedef enum pa_status {
   PA_OK = 0,
@@ -73,7 +73,9 @@ typedef enum pa_status {
   PA_ERR_UNSUPPORTED = -3, /* head_dim, block_size or group size not built     */
   PA_ERR_WORKSPACE = -4,   /* workspace NULL or smaller than required          */
   PA_ERR_LAUNCH = -5,      /* the HIP runtime reported an error                */
-  PA_ERR_DEVICE = -6       /* no gfx950 device current, or a query failed      */
+  PA_ERR_DEVICE = -6,      /* no gfx950 device current, or a query failed      */
+  PA_ERR_NO_BLOCKS = -7,   /* block manager: the free list is too short         */
+  PA_ERR_NOT_FOUND = -8    /* block manager: unknown (or already used) seq id   */
 } pa_status;
 
 /* Geometry of one layer's KV cache.

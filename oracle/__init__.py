@@ -17,10 +17,13 @@ eye:
   softmax attention per query head, plus a textbook contiguous attention used
   only to cross-check the gather, and a log-sum-exp merge used only in a
   self-test.
+* ``oracle.blocks`` - the block manager's rules (FIFO free list, reference
+  counts, full-prefix keys with a model key, fork, copy-on-write) and the
+  whole-block copy.
 
 Every function is pinned by a ``-m "not gpu"`` test in ``tests/`` against a
 value the pages print, a closed form, an invariant or brute force; none is
 "parity unpinned".
 """
 
-from . import e4m3, pages, paged  # noqa: F401
+from . import blocks, e4m3, pages, paged  # noqa: F401

@@ -1,0 +1,162 @@
+"""Block manager model: free list, reference counts, prefix reuse, fork and
+copy-on-write (oracle side).
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__``).
+
+What a block manager does, from the pages:
+
+* The pool is a list of free block ids.  A request takes blocks from the
+  front of the list; a finished request hands its blocks back to the end, in
+  the order its block table lists them, and the next request may take them
+  at once ("KV Cache Engineering for LLM Serving", section 10, Paging, with
+  its six-block example).
+* A completed block is stored under a key made of the entire token prefix
+  up to the end of that block, so a block is reused only when all preceding
+  context is identical (same page, section 11, Prefix reuse; rajatmohan.com
+  serving design, "Prefix sharing is where the real win lives").  The key
+  also carries the model / adapter identity, since identical tokens give
+  different K and V under different weights (rajatmohan.com, same section).
+* A reused block gets its reference count incremented instead of new memory;
+  when one user writes tokens of its own into a block others still hold, it
+  first gets a private copy: copy-on-write ("Taming the token torrent",
+  "Implementing Radix Tree Prefix Caching").
+
+This model follows those rules with plain Python containers: the key is the
+tuple (model key, all tokens up to the block's end), exactly the page's
+readable stand-in for chained hashes, so there are no collisions to reason
+about.  Only full blocks are ever stored under a key; a sequence's partly
+filled last block is private unless the sequence was forked.
+"""
+
+
+class OutOfBlocks(Exception):
+    pass
+
+
+class BlockManager:
+    def __init__(self, num_blocks, block_size):
+        self.block_size = block_size
+        self.free = list(range(num_blocks))   # front = next to hand out
+        self.ref = [0] * num_blocks
+        self.key_block = {}                   # prefix key -> block
+        self.block_key = {}                   # block -> prefix key it is stored under
+        self.seqs = {}                        # seq id -> {"tokens", "table", "model"}
+        self.hits = 0
+        self.misses = 0
+
+    # -- allocation -------------------------------------------------------
+    def _take(self):
+        if not self.free:
+            raise OutOfBlocks("no free block")
+        b = self.free.pop(0)
+        self.ref[b] = 1
+        return b
+
+    def _release(self, b):
+        self.ref[b] -= 1
+        if self.ref[b] == 0:
+            k = self.block_key.pop(b, None)
+            if k is not None and self.key_block.get(k) == b:
+                del self.key_block[k]
+            self.free.append(b)
+
+    def _key(self, model, tokens, end):
+        return (model, tuple(tokens[:end]))
+
+    def _store(self, b, key):
+        """Record a just-completed block under its prefix key, unless an
+        equal block is already stored."""
+        if key not in self.key_block:
+            self.key_block[key] = b
+            self.block_key[b] = key
+
+    # -- operations ---------------------------------------------------------
+    def add_sequence(self, seq, tokens, model=0):
+        """A new request with prompt ``tokens``: every full block whose key
+        is stored is reused, every other block is taken from the free list.
+        Returns the number of reused blocks.  When the pool cannot supply
+        the new blocks nothing changes and OutOfBlocks is raised."""
+        if seq in self.seqs:
+            raise KeyError(seq)
+        bs = self.block_size
+        full = len(tokens) // bs
+        keys = [self._key(model, tokens, (i + 1) * bs) for i in range(full)]
+        need = sum(k not in self.key_block for k in keys) + (1 if len(tokens) % bs else 0)
+        if need > len(self.free):
+            raise OutOfBlocks(f"need {need} blocks, {len(self.free)} free")
+        table, reused = [], 0
+        for key in keys:
+            b = self.key_block.get(key)
+            if b is not None:
+                self.ref[b] += 1
+                reused += 1
+            else:
+                b = self._take()
+                self._store(b, key)
+            table.append(b)
+        if len(tokens) % bs:
+            table.append(self._take())
+        self.hits += reused
+        self.misses += len(table) - reused
+        self.seqs[seq] = {"tokens": list(tokens), "table": table, "model": model}
+        return reused
+
+    def fork(self, parent, child):
+        """``child`` shares every block of ``parent``, partial last block
+        included."""
+        if child in self.seqs:
+            raise KeyError(child)
+        p = self.seqs[parent]
+        for b in p["table"]:
+            self.ref[b] += 1
+        self.seqs[child] = {"tokens": list(p["tokens"]), "table": list(p["table"]),
+                            "model": p["model"]}
+
+    def append_token(self, seq, token):
+        """One generated token.  Returns (slot, copy_src, copy_dst): the slot
+        the token's K/V go to, and the block copy that must happen first
+        (-1, -1 when none)."""
+        s = self.seqs[seq]
+        bs = self.block_size
+        pos = len(s["tokens"])
+        src = dst = -1
+        if (pos % bs == 0 or self.ref[s["table"][-1]] > 1) and not self.free:
+            raise OutOfBlocks("no free block")
+        if pos % bs == 0:
+            s["table"].append(self._take())
+        else:
+            last = s["table"][-1]
+            if self.ref[last] > 1:
+                dst = self._take()
+                src = last
+                self.ref[last] -= 1
+                s["table"][-1] = dst
+        s["tokens"].append(token)
+        blk = s["table"][pos // bs]
+        if (pos + 1) % bs == 0:
+            self._store(blk, self._key(s["model"], s["tokens"], pos + 1))
+        return blk * bs + pos % bs, src, dst
+
+    def free_sequence(self, seq):
+        s = self.seqs.pop(seq)
+        for b in s["table"]:
+            self._release(b)
+
+    # -- queries ----------------------------------------------------------
+    def table(self, seq):
+        return list(self.seqs[seq]["table"])
+
+    def length(self, seq):
+        return len(self.seqs[seq]["tokens"])
+
+    def num_free(self):
+        return len(self.free)
+
+
+def copy_blocks(k_cache, v_cache, pairs, block_elems):
+    """Copy whole blocks (every KV head, K and V) from src to dst for each
+    (src, dst) pair, in order, on flat caches whose blocks are contiguous
+    runs of ``block_elems`` elements."""
+    for src, dst in pairs:
+        for c in (k_cache, v_cache):
+            c[dst * block_elems:(dst + 1) * block_elems] = c[src * block_elems:(src + 1) * block_elems]

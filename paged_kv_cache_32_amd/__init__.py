@@ -13,6 +13,8 @@ fallback: without the built library every call raises.
     pa_decode(q, k_cache, v_cache, block_tables, seq_lens, scale, out, block_size=...)
     pa_decode_fp8(q, k_cache, v_cache, block_tables, seq_lens, scale, out, k_scale, v_scale, ...)
     pa_decode_workspace_size(...), pa_decode_workspace_init(workspace)
+    pa_copy_blocks(k_cache, v_cache, pairs, ...)
+    BlockManager(num_blocks, block_size)   (host block manager, include/pa_blocks.h)
 
 Cache tensors are flat (or any contiguous shape) with num_blocks *
 num_kv_heads * block_size * head_dim elements, bfloat16 for the bf16 cache
@@ -30,7 +32,8 @@ LIB_PATH = os.path.join(_HERE, "lib", "libpa.so")
 
 PA_OK = 0
 _STATUS = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_UNSUPPORTED",
-           -4: "PA_ERR_WORKSPACE", -5: "PA_ERR_LAUNCH", -6: "PA_ERR_DEVICE"}
+           -4: "PA_ERR_WORKSPACE", -5: "PA_ERR_LAUNCH", -6: "PA_ERR_DEVICE",
+           -7: "PA_ERR_NO_BLOCKS", -8: "PA_ERR_NOT_FOUND"}
 
 
 class PagedAttentionError(RuntimeError):
@@ -55,7 +58,7 @@ def _load():
         raise ImportError(f"libpa.so is not built ({LIB_PATH}); run "
                           "`python -m paged_kv_cache_32_amd.build` (gfx950 HIP library)")
     lib = ctypes.CDLL(LIB_PATH)
-    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     dp = ctypes.POINTER(CacheDesc)
     sigs = {
         "pa_cache_write": ([dp, vp, vp, vp, i32, vp, vp, vp], i32),
@@ -67,6 +70,22 @@ def _load():
                            vp], i32),
         "pa_status_string": ([i32], ctypes.c_char_p),
         "pa_abi_version": ([], i32),
+        "pa_copy_blocks": ([dp, i32, vp, vp, vp, i32, vp], i32),
+        "pa_bm_create": ([i32, i32, ctypes.POINTER(vp)], i32),
+        "pa_bm_destroy": ([vp], None),
+        "pa_bm_add_sequence": ([vp, i64, ctypes.POINTER(i32), i32, ctypes.c_uint64,
+                                ctypes.POINTER(i32)], i32),
+        "pa_bm_fork": ([vp, i64, i64], i32),
+        "pa_bm_append_token": ([vp, i64, i32, ctypes.POINTER(i64), ctypes.POINTER(i32),
+                                ctypes.POINTER(i32)], i32),
+        "pa_bm_free_sequence": ([vp, i64], i32),
+        "pa_bm_num_free": ([vp], i32),
+        "pa_bm_sequence_info": ([vp, i64, ctypes.POINTER(i32), ctypes.POINTER(i32)], i32),
+        "pa_bm_block_table": ([vp, i64, ctypes.POINTER(i32), i32], i32),
+        "pa_bm_refcount": ([vp, i32, ctypes.POINTER(i32)], i32),
+        "pa_bm_stats": ([vp, ctypes.POINTER(i64), ctypes.POINTER(i64)], i32),
+        "pa_bm_batch": ([vp, ctypes.POINTER(i64), i32, i32, ctypes.POINTER(i32),
+                         ctypes.POINTER(i32)], i32),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(lib, name)
@@ -235,3 +254,111 @@ def pa_decode_fp8(q, k_cache, v_cache, block_tables, seq_lens, scale, k_scale, v
     """Paged decode over an e4m3fn cache with per-tensor scales."""
     return _decode(True, q, k_cache, v_cache, block_tables, seq_lens, scale, out, num_kv_heads,
                    block_size, k_scale, v_scale, partition_tokens, workspace)
+
+
+def pa_copy_blocks(k_cache, v_cache, pairs, *, num_kv_heads, head_dim, block_size):
+    """Copy whole blocks of both caches on the GPU: pairs is an int32 device
+    tensor [n, 2] of {src, dst} block ids.  See pa_copy_blocks in
+    include/pa_blocks.h."""
+    dev = k_cache.device
+    if dev.type != "cuda":
+        raise ValueError("pa_copy_blocks needs device tensors")
+    if k_cache.dtype not in (torch.bfloat16, torch.uint8):
+        raise TypeError("caches must be bfloat16 or uint8 (e4m3fn codes)")
+    _need(k_cache, "k_cache", k_cache.dtype, dev)
+    _need(v_cache, "v_cache", k_cache.dtype, dev, shape=tuple(k_cache.shape))
+    _need(pairs, "pairs", torch.int32, dev, 2)
+    if pairs.shape[1] != 2:
+        raise ValueError("pairs must be [n, 2]")
+    desc = make_desc(k_cache, num_kv_heads, head_dim, block_size)
+    eb = 2 if k_cache.dtype == torch.bfloat16 else 1
+    with torch.cuda.device(dev):
+        st = _load().pa_copy_blocks(ctypes.byref(desc), eb, _ptr(k_cache), _ptr(v_cache), _ptr(pairs),
+                                    pairs.shape[0], _stream(k_cache))
+    _check("pa_copy_blocks", st)
+
+
+class BlockManager:
+    """Host block manager of include/pa_blocks.h (FIFO free list, reference
+    counts, exact prefix keys with a model key, fork, copy-on-write).  Thin
+    wrapper: every method is one C call."""
+
+    def __init__(self, num_blocks, block_size):
+        L = _load()
+        h = ctypes.c_void_p()
+        _check("pa_bm_create", L.pa_bm_create(num_blocks, block_size, ctypes.byref(h)))
+        self._h = h
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+
+    def close(self):
+        if self._h:
+            _load().pa_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def add_sequence(self, seq, tokens, model_key=0):
+        """Returns the number of reused (prefix-shared) blocks."""
+        arr = (ctypes.c_int32 * len(tokens))(*[int(t) for t in tokens])
+        reused = ctypes.c_int32()
+        _check("pa_bm_add_sequence", _load().pa_bm_add_sequence(
+            self._h, seq, arr, len(tokens), model_key, ctypes.byref(reused)))
+        return reused.value
+
+    def fork(self, parent, child):
+        _check("pa_bm_fork", _load().pa_bm_fork(self._h, parent, child))
+
+    def append_token(self, seq, token):
+        """Returns (slot, copy_src, copy_dst); copy ids are -1 when no
+        copy-on-write is needed."""
+        slot, src, dst = ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int32()
+        _check("pa_bm_append_token", _load().pa_bm_append_token(
+            self._h, seq, int(token), ctypes.byref(slot), ctypes.byref(src), ctypes.byref(dst)))
+        return slot.value, src.value, dst.value
+
+    def free_sequence(self, seq):
+        _check("pa_bm_free_sequence", _load().pa_bm_free_sequence(self._h, seq))
+
+    def num_free(self):
+        return _load().pa_bm_num_free(self._h)
+
+    def length(self, seq):
+        n, b = ctypes.c_int32(), ctypes.c_int32()
+        _check("pa_bm_sequence_info", _load().pa_bm_sequence_info(self._h, seq, ctypes.byref(n), ctypes.byref(b)))
+        return n.value
+
+    def table(self, seq):
+        n, b = ctypes.c_int32(), ctypes.c_int32()
+        L = _load()
+        _check("pa_bm_sequence_info", L.pa_bm_sequence_info(self._h, seq, ctypes.byref(n), ctypes.byref(b)))
+        out = (ctypes.c_int32 * max(b.value, 1))()
+        _check("pa_bm_block_table", L.pa_bm_block_table(self._h, seq, out, b.value))
+        return list(out[:b.value])
+
+    def refcount(self, block):
+        r = ctypes.c_int32()
+        _check("pa_bm_refcount", _load().pa_bm_refcount(self._h, block, ctypes.byref(r)))
+        return r.value
+
+    def stats(self):
+        h, m = ctypes.c_int64(), ctypes.c_int64()
+        _check("pa_bm_stats", _load().pa_bm_stats(self._h, ctypes.byref(h), ctypes.byref(m)))
+        return h.value, m.value
+
+    def batch(self, seqs, max_blocks):
+        """Host numpy arrays (block_tables [n, max_blocks] int32, padded with
+        -1; seq_lens [n] int32) for a decode batch of these sequences."""
+        import numpy as np
+        n = len(seqs)
+        ids = (ctypes.c_int64 * max(n, 1))(*seqs)
+        bt = np.empty((n, max_blocks), dtype=np.int32)
+        sl = np.empty(n, dtype=np.int32)
+        _check("pa_bm_batch", _load().pa_bm_batch(
+            self._h, ids, n, max_blocks, bt.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+            sl.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))))
+        return bt, sl

@@ -2,9 +2,10 @@
 
     python -m paged_kv_cache_32_amd.build [--verbose]
 
-Compiles every ``csrc/*.hip`` with hipcc for gfx950 only and links them into
-``paged_kv_cache_32_amd/lib/libpa.so``.  Packed-fp32 VALU forms are switched
-off for the device code (plain fp32 VALU and MFMA only).
+Compiles every ``csrc/*.hip`` with hipcc for gfx950 only, and the host-only
+``csrc/*.cpp`` (the block manager) with the host C++ compiler, and links them
+into ``paged_kv_cache_32_amd/lib/libpa.so``.  Packed-fp32 VALU forms are
+switched off for the device code (plain fp32 VALU and MFMA only).
 """
 
 import glob
@@ -36,14 +37,28 @@ def flags(extra=()):
     ]
 
 
+def host_cxx():
+    for cand in (os.environ.get("CXX"), shutil.which("g++"), shutil.which("c++")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("no host C++ compiler found")
+
+
+def host_flags():
+    return ["-O2", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}"]
+
+
 def build(verbose=False, extra=()):
     os.makedirs(LIBDIR, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + sorted(glob.glob(os.path.join(CSRC, "*.cpp")))
     objs = []
     cc = hipcc()
     for src in srcs:
         obj = os.path.join(LIBDIR, os.path.basename(src) + ".o")
-        cmd = [cc, *flags(extra), "-c", src, "-o", obj]
+        if src.endswith(".cpp"):
+            cmd = [host_cxx(), *host_flags(), "-c", src, "-o", obj]
+        else:
+            cmd = [cc, *flags(extra), "-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)

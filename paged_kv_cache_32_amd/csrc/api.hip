@@ -6,6 +6,7 @@
 #include <mutex>
 
 #include "../../include/pa.h"
+#include "../../include/pa_blocks.h"
 #include "pa_internal.h"
 
 namespace {
@@ -257,6 +258,31 @@ pa_status pa_decode_fp8(const pa_cache_desc* cache, const void* q, int32_t num_s
                 partition_tokens, workspace, workspace_bytes, stream);
 }
 
+pa_status pa_copy_blocks(const pa_cache_desc* cache, int32_t elem_bytes, void* k_cache,
+                         void* v_cache, const int32_t* pairs, int32_t num_pairs, void* stream) {
+  if (!cache) return PA_ERR_NULL;
+  pa_status st = desc_status(cache);
+  if (st != PA_OK) return st;
+  if (elem_bytes != 1 && elem_bytes != 2) return PA_ERR_UNSUPPORTED;
+  if (num_pairs < 0) return PA_ERR_SHAPE;
+  // Grid size: num_pairs * 2 * segments workgroups must fit a launch.
+  const int64_t block_bytes = (int64_t)cache->num_kv_heads * cache->block_size * cache->head_dim * elem_bytes;
+  if ((int64_t)num_pairs * 2 * ((block_bytes + 16383) / 16384) > INT32_MAX) return PA_ERR_SHAPE;
+  if (num_pairs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !pairs) return PA_ERR_NULL;
+  int resident = 0;
+  if (!device_info(128, false, &resident)) return PA_ERR_DEVICE;
+  pa::CopyBlocksParams p;
+  p.k_cache = static_cast<uint8_t*>(k_cache);
+  p.v_cache = static_cast<uint8_t*>(v_cache);
+  p.pairs = pairs;
+  p.block_bytes = block_bytes;
+  p.num_pairs = num_pairs;
+  p.num_blocks = cache->num_blocks;
+  if (pa::launch_copy_blocks(p, static_cast<hipStream_t>(stream)) != hipSuccess) return PA_ERR_LAUNCH;
+  return PA_OK;
+}
+
 const char* pa_status_string(pa_status s) {
   switch (s) {
     case PA_OK: return "PA_OK";
@@ -266,6 +292,8 @@ const char* pa_status_string(pa_status s) {
     case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
     case PA_ERR_LAUNCH: return "PA_ERR_LAUNCH: the HIP runtime reported an error";
     case PA_ERR_DEVICE: return "PA_ERR_DEVICE: no gfx950 device is current";
+    case PA_ERR_NO_BLOCKS: return "PA_ERR_NO_BLOCKS: not enough free blocks";
+    case PA_ERR_NOT_FOUND: return "PA_ERR_NOT_FOUND: unknown or already used sequence id";
   }
   return "unknown pa_status";
 }

@@ -1,0 +1,47 @@
+// Whole-block copies inside the K and V caches (the copy-on-write step of
+// the block manager: "Taming the token torrent", "Implementing Radix Tree
+// Prefix Caching").  A block of the cache layout is one contiguous run of
+// Hkv * block_size * head_dim elements, so a copy is a plain streaming copy
+// of block_bytes per cache; the kernel is bound by HBM bandwidth (each pair
+// reads and writes 2 * block_bytes).
+#include "pa_internal.h"
+
+namespace pa {
+
+namespace {
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// Workgroup (pair, cache, segment): 256 lanes move one kSegment-byte piece of
+// one block of one cache, 16 bytes per lane per step.
+constexpr int kSegment = 16384;
+
+__global__ __launch_bounds__(256) void copy_blocks_kernel(const CopyBlocksParams p) {
+  const int64_t segs = (p.block_bytes + kSegment - 1) / kSegment;
+  const int64_t w = blockIdx.x;
+  const int64_t pair = w / (2 * segs);
+  const int64_t rest = w - pair * 2 * segs;
+  const int cache = (int)(rest / segs);
+  const int64_t seg = rest - (int64_t)cache * segs;
+  const int src = p.pairs[2 * pair], dst = p.pairs[2 * pair + 1];
+  if ((unsigned)src >= (unsigned)p.num_blocks || (unsigned)dst >= (unsigned)p.num_blocks) return;
+  uint8_t* base = cache ? p.v_cache : p.k_cache;
+  const u32x4* from = reinterpret_cast<const u32x4*>(base + (int64_t)src * p.block_bytes + seg * kSegment);
+  u32x4* to = reinterpret_cast<u32x4*>(base + (int64_t)dst * p.block_bytes + seg * kSegment);
+  int64_t n = p.block_bytes - seg * kSegment;
+  if (n > kSegment) n = kSegment;
+  for (int64_t i = threadIdx.x; i < n / 16; i += 256)
+    __builtin_nontemporal_store(__builtin_nontemporal_load(from + i), to + i);
+}
+
+}  // namespace
+
+hipError_t launch_copy_blocks(const CopyBlocksParams& p, hipStream_t stream) {
+  if (p.num_pairs == 0) return hipSuccess;
+  const int64_t segs = (p.block_bytes + kSegment - 1) / kSegment;
+  const int64_t groups = (int64_t)p.num_pairs * 2 * segs;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)groups), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -662,7 +662,6 @@ __device__ __forceinline__ void settle(const DecodeParams& p, WaveState<D, FP8>&
 template <int D, bool FP8, int NSUB>
 __global__ __launch_bounds__(kDecodeThreads, PA_DECODE_MIN_WAVES) void decode_kernel(const DecodeParams p) {
   using Buf = StageBuf<D, FP8, NSUB>;
-  using T = Tile<D, FP8>;
   static_assert(Buf::kLoads <= 63, "a stage must fit the vector-memory counter");
   const int lane = threadIdx.x & 63;
   // Workgroups are dispatched round-robin over the 8 XCDs; the ones that

@@ -47,10 +47,19 @@ struct DecodeParams {
   float out_scale;              // 1 (bf16) or v_scale (fp8)
 };
 
+struct CopyBlocksParams {
+  uint8_t* k_cache;
+  uint8_t* v_cache;
+  const int32_t* pairs;         // [num_pairs][2] {src, dst}
+  int64_t block_bytes;          // Hkv * block_size * head_dim * element bytes
+  int32_t num_pairs, num_blocks;
+};
+
 // Host-side launchers (defined next to their kernels).
 hipError_t launch_cache_write(const CacheWriteParams& p, bool fp8, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, bool fp8, hipStream_t stream);
 hipError_t launch_zero(void* ptr, size_t bytes, hipStream_t stream);
+hipError_t launch_copy_blocks(const CopyBlocksParams& p, hipStream_t stream);
 // Resident wavefronts of the decode kernel on the current device (0 on error).
 int decode_resident_waves(int head_dim, bool fp8);
 

@@ -1,0 +1,181 @@
+"""The block-manager model in the oracle, pinned to the pages' printed traces
+and to the invariants the rules imply."""
+
+import random
+
+import numpy as np
+import pytest
+
+from oracle import blocks as B
+from oracle import paged
+
+
+def unique_tokens(start, n):
+    return list(range(start, start + n))
+
+
+def test_free_list_trace_of_the_paging_section(pages):
+    """Six free blocks; A takes three, B two; A finishes; C takes two
+    ("KV Cache Engineering for LLM Serving", section 10, printed output)."""
+    c = pages["free_list_trace"]
+    bm = B.BlockManager(len(c["free"]), 4)
+    bm.add_sequence("A", unique_tokens(100, 12))
+    bm.add_sequence("B", unique_tokens(200, 8))
+    assert bm.table("A") == c["request_a"] and bm.table("B") == c["request_b"]
+    bm.free_sequence("A")
+    assert bm.free == c["free_after_a"]
+    bm.add_sequence("C", unique_tokens(300, 8))
+    assert bm.table("C") == c["request_c"]
+
+
+def test_prefix_reuse_of_the_prefix_section(pages):
+    """Four-token blocks: the first request reuses 0 of 3 blocks, the second
+    (same first 8 tokens) 2 of 3 and computes 1 new block (same page,
+    section 11, printed output)."""
+    c = pages["prefix_reuse"]
+    bm = B.BlockManager(16, c["block_size"])
+    assert bm.add_sequence(1, c["first"]) == c["first_reused"]
+    assert len(bm.table(1)) == c["blocks"]
+    assert bm.add_sequence(2, c["second"]) == c["second_reused"]
+    assert bm.misses - c["blocks"] == c["second_new"]
+    t1, t2 = bm.table(1), bm.table(2)
+    assert t2[:2] == t1[:2] and t2[2] != t1[2]
+    assert [bm.ref[b] for b in t1] == [2, 2, 1]
+
+
+def test_whole_prefix_and_model_key_must_match():
+    """Matching tokens in the middle reuse nothing; identical tokens under
+    another model / adapter key reuse nothing (rajatmohan.com, "Prefix
+    sharing is where the real win lives")."""
+    bm = B.BlockManager(32, 4)
+    first = [10, 11, 12, 13, 20, 21, 22, 23, 30, 31, 32, 33]
+    bm.add_sequence(1, first)
+    assert bm.add_sequence(2, [99, 98, 97, 96] + first[4:]) == 0
+    assert set(bm.table(2)).isdisjoint(bm.table(1))
+    assert bm.add_sequence(3, first, model=7) == 0
+    assert bm.add_sequence(4, first, model=0) == 3
+
+
+def test_partial_blocks_are_never_shared_by_key():
+    bm = B.BlockManager(8, 4)
+    bm.add_sequence(1, [1, 2, 3, 4, 5, 6])
+    assert bm.add_sequence(2, [1, 2, 3, 4, 5, 6]) == 1
+    assert bm.table(1)[0] == bm.table(2)[0] and bm.table(1)[1] != bm.table(2)[1]
+
+
+def test_block_address_rule_for_appends():
+    """The slot of position i is table[i // bs] * bs + i % bs ("Taming the
+    token torrent", "The Block Table Logic")."""
+    bm = B.BlockManager(8, 4)
+    bm.add_sequence(1, [5, 6, 7])
+    slots = [bm.append_token(1, t)[0] for t in range(10)]
+    t = bm.table(1)
+    assert slots == [t[i // 4] * 4 + i % 4 for i in range(3, 13)]
+
+
+def test_fork_and_copy_on_write():
+    bm = B.BlockManager(8, 4)
+    bm.add_sequence("p", [1, 2, 3, 4, 5, 6])          # one full block, one partial
+    bm.fork("p", "c")
+    full, part = bm.table("p")
+    assert bm.ref[full] == 2 and bm.ref[part] == 2
+    slot, src, dst = bm.append_token("c", 9)          # c writes into the shared partial block
+    assert src == part and dst not in (full, part) and bm.table("c") == [full, dst]
+    assert slot == dst * 4 + 2 and bm.ref[part] == 1 and bm.ref[dst] == 1
+    slot, src, dst = bm.append_token("p", 8)          # p now holds its block alone: no copy
+    assert (src, dst) == (-1, -1) and slot == part * 4 + 2
+    # completing the block stores it under its key: an equal prompt reuses it
+    bm.append_token("p", 7)
+    assert bm.add_sequence("q", [1, 2, 3, 4, 5, 6, 8, 7]) == 2
+
+
+def test_out_of_blocks_changes_nothing():
+    bm = B.BlockManager(3, 4)
+    bm.add_sequence(1, unique_tokens(0, 8))
+    before = (list(bm.free), list(bm.ref), dict(bm.key_block))
+    with pytest.raises(B.OutOfBlocks):
+        bm.add_sequence(2, unique_tokens(50, 9))
+    assert (list(bm.free), list(bm.ref), dict(bm.key_block)) == before and 2 not in bm.seqs
+    bm.add_sequence(3, unique_tokens(90, 4))
+    with pytest.raises(B.OutOfBlocks):
+        bm.append_token(3, 1)
+    assert bm.length(3) == 4
+
+
+def random_ops(bm, rng, steps, vocab=3, max_prompt=14):
+    """Random mix of adds (small vocabulary, so prefixes repeat), forks,
+    appends and frees; yields the result of each operation."""
+    live, next_id = [], 0
+    for _ in range(steps):
+        op = rng.random()
+        try:
+            if op < 0.3 or not live:
+                n = rng.randrange(0, max_prompt)
+                toks = [rng.randrange(vocab) for _ in range(n)]
+                model = rng.randrange(2)
+                r = bm.add_sequence(next_id, toks, model)
+                live.append(next_id)
+                yield ("add", next_id, r)
+                next_id += 1
+            elif op < 0.4:
+                p = rng.choice(live)
+                bm.fork(p, next_id)
+                live.append(next_id)
+                yield ("fork", p, next_id)
+                next_id += 1
+            elif op < 0.85:
+                s = rng.choice(live)
+                yield ("append", s, bm.append_token(s, rng.randrange(vocab)))
+            else:
+                s = live.pop(rng.randrange(len(live)))
+                bm.free_sequence(s)
+                yield ("free", s)
+        except B.OutOfBlocks:
+            yield ("oob",)
+
+
+def check_invariants(bm, num_blocks):
+    counts = [0] * num_blocks
+    for s in bm.seqs.values():
+        for b in s["table"]:
+            counts[b] += 1
+        assert len(s["table"]) == -(-len(s["tokens"]) // bm.block_size)
+    assert counts == bm.ref                       # reference count = tables naming the block
+    assert sorted(bm.free) == [b for b in range(num_blocks) if counts[b] == 0]
+    for key, b in bm.key_block.items():           # a stored block holds exactly its key's tokens
+        model, prefix = key
+        assert bm.ref[b] > 0 and len(prefix) % bm.block_size == 0
+        holders = [s for s in bm.seqs.values() if b in s["table"]]
+        for s in holders:
+            i = s["table"].index(b)
+            assert tuple(s["tokens"][:(i + 1) * bm.block_size]) == prefix and s["model"] == model
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_random_operations_keep_the_invariants(seed):
+    rng = random.Random(seed)
+    bm = B.BlockManager(40, 4)
+    for i, _ in enumerate(random_ops(bm, rng, 600)):
+        if i % 25 == 0:
+            check_invariants(bm, 40)
+    check_invariants(bm, 40)
+
+
+def test_copy_blocks_moves_exactly_the_blocks_elements():
+    """A block of the cache layout is one contiguous run of
+    Hkv * block_size * D elements: the oracle's layout offsets of every
+    (head, token, dim) of block b fill exactly that run."""
+    g = paged.Geom(num_blocks=5, block_size=32, num_kv_heads=2, head_dim=64)
+    E = g.num_kv_heads * g.block_size * g.head_dim
+    h, t, d = np.meshgrid(np.arange(g.num_kv_heads), np.arange(g.block_size), np.arange(g.head_dim),
+                          indexing="ij")
+    for b in range(g.num_blocks):
+        for off in (paged.k_offset, paged.v_offset):
+            o = np.sort(off(g, b, h, t, d).ravel())
+            assert np.array_equal(o, np.arange(b * E, (b + 1) * E))
+    k = np.arange(g.cache_elems, dtype=np.int64)
+    v = -k
+    B.copy_blocks(k, v, [(1, 3), (4, 0)], E)
+    assert np.array_equal(k[3 * E:4 * E], np.arange(E, 2 * E)) and np.array_equal(k[0:E], np.arange(4 * E, 5 * E))
+    assert np.array_equal(v[3 * E:4 * E], -np.arange(E, 2 * E))
+    assert np.array_equal(k[E:3 * E], np.arange(E, 3 * E))   # sources untouched
