@@ -27,6 +27,10 @@ Other workloads (--workload), each on the same 70B layer shape:
                        pa_cache_write_fp8 then pa_decode_fp8, 160 launches
                        replayed as one HIP graph; `value` is KV GB/s over the
                        whole step, decode tok/s = 128 / step time
+  copy_blocks_llama70b pa_copy_blocks of 4,096 independent block pairs on the
+                       70B layer's bf16 pool (block 16): `value` is bytes read
+                       plus written per call / time; also the host block
+                       manager's add_sequence / append_token rates
 
 Prints exactly one JSON line on stdout; everything else goes to stderr.
 """
@@ -55,7 +59,7 @@ HBM_PEAK_GBS = 8000.0
 MODEL_LAYERS = 80
 SCRUB_BYTES = 512 << 20
 WORKLOADS = {"llama70b_layer_bs64": 2, "prefix_shared_bs256": 3, "long_context_128k": 4,
-             "fp8_80layer_bs128": 5}
+             "fp8_80layer_bs128": 5, "copy_blocks_llama70b": 2}
 
 
 def log(*a):
@@ -374,6 +378,77 @@ def bench_model_step(args, dev):
     return res
 
 
+def bench_copy_blocks(args, dev):
+    """pa_copy_blocks on the 70B layer's pool, and the host block manager."""
+    w = W.config(2)
+    Hkv, D, BS = w.num_kv_heads, w.head_dim, w.block_size
+    n_pairs = 4096
+    elems = w.num_blocks * Hkv * BS * D
+    kc = torch.empty(elems, dtype=torch.bfloat16, device=dev).normal_()
+    vc = torch.empty(elems, dtype=torch.bfloat16, device=dev).normal_()
+    rng = np.random.default_rng(2)
+    perm = rng.permutation(w.num_blocks)
+    pairs = torch.from_numpy(np.stack([perm[:n_pairs], perm[n_pairs:2 * n_pairs]], 1).astype(np.int32)).to(dev)
+    scrub = torch.ones(SCRUB_BYTES // 4, dtype=torch.float32, device=dev)
+    sink = torch.zeros((), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def copy():
+        pa.pa_copy_blocks(kc, vc, pairs, num_kv_heads=Hkv, head_dim=D, block_size=BS)
+
+    for _ in range(args.warmup):
+        copy()
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        if not args.no_scrub:
+            torch.sum(scrub, dim=0, out=sink)
+        ev[i][0].record(stream)
+        copy()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    block_bytes = Hkv * BS * D * 2
+    moved = n_pairs * 2 * block_bytes * 2             # K and V, read and write
+    gbs = moved / (ms.mean() / 1e3) / 1e9
+
+    # Host block manager: the batch's prompts (a shared 900-token system
+    # prompt, then private tokens) added, then one append per sequence per
+    # step for 256 steps.
+    bm = pa.BlockManager(w.num_blocks, BS)
+    system = list(range(900))
+    t0 = time.perf_counter()
+    for s, L in enumerate(w.seq_lens):
+        L = int(L)
+        bm.add_sequence(s, (system + list(range(10_000 + s * 40_000, 10_000 + s * 40_000 + L)))[:L])
+    t_add = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    n_app = 0
+    for step in range(256):
+        for s in range(w.num_seqs):
+            bm.append_token(s, step)
+            n_app += 1
+    t_app = time.perf_counter() - t0
+    hits, misses = bm.stats()
+    res = base_record(args, w, K)
+    res["metric"] = "pa_copy_blocks GB/s (read + write) on the 70B layer pool, and block manager op rates"
+    res.update({"value": round(gbs, 1), "ms_per_step": round(float(ms.mean()), 4)})
+    res["config"].update({"workload": args.workload, "pairs": n_pairs, "block_bytes_per_cache": block_bytes,
+                          "bytes_moved_per_call": moved})
+    res.update({
+        "copy_us": {"mean": round(float(ms.mean()) * 1e3, 2), "p10": round(float(np.percentile(ms, 10)) * 1e3, 2),
+                    "p90": round(float(np.percentile(ms, 90)) * 1e3, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "copy_blocks_kernel (pa_copy_blocks is one launch)", "bytes_per_launch": moved},
+        "block_manager": {"add_sequence_tokens_per_s": round(float(w.seq_lens.sum()) / t_add, 1),
+                          "append_token_per_s": round(n_app / t_app, 1),
+                          "prefix_hits": hits, "blocks_taken": misses},
+    })
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -397,6 +472,8 @@ def main():
     pa.lib()
     if args.workload == "fp8_80layer_bs128":
         res = bench_model_step(args, dev)
+    elif args.workload == "copy_blocks_llama70b":
+        res = bench_copy_blocks(args, dev)
     else:
         res = bench_layer(args, dev)
     print(json.dumps(res), flush=True)

@@ -11,19 +11,21 @@ import pytest
 import paged_kv_cache_32_amd as pa
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "pa.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("pa.h", "pa_blocks.h")]
 
 if not os.path.exists(pa.LIB_PATH):
     pytest.skip("libpa.so not built", allow_module_level=True)
 
-OK, NULL, SHAPE, UNSUP, WS, LAUNCH, DEVICE = 0, -1, -2, -3, -4, -5, -6
+OK, NULL, SHAPE, UNSUP, WS, LAUNCH, DEVICE, NO_BLOCKS, NOT_FOUND = 0, -1, -2, -3, -4, -5, -6, -7, -8
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
 
 
 def declared():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", src)))
+    names = set()
+    for h in HEADERS:
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", src))
+    return sorted(names)
 
 
 def desc(nb=10, bs=16, hkv=2, d=128):
@@ -34,15 +36,16 @@ def test_exports_every_declared_symbol():
     lib = pa.lib()
     names = declared()
     assert set(names) >= {"pa_cache_write", "pa_cache_write_fp8", "pa_decode", "pa_decode_fp8",
-                          "pa_decode_workspace_size", "pa_status_string", "pa_abi_version"}
+                          "pa_decode_workspace_size", "pa_status_string", "pa_abi_version",
+                          "pa_copy_blocks", "pa_bm_create", "pa_bm_append_token", "pa_bm_batch"}
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.pa_abi_version() == 1
+    assert lib.pa_abi_version() == 2
 
 
 def test_status_strings():
     lib = pa.lib()
-    for code in (OK, NULL, SHAPE, UNSUP, WS, LAUNCH, DEVICE):
+    for code in (OK, NULL, SHAPE, UNSUP, WS, LAUNCH, DEVICE, NO_BLOCKS, NOT_FOUND):
         s = lib.pa_status_string(code).decode()
         assert s.startswith(pa._STATUS[code])
     assert lib.pa_status_string(42).decode() == "unknown pa_status"
@@ -110,6 +113,18 @@ def test_workspace_init_validation():
     assert lib.pa_decode_workspace_init(None, 64, None) == NULL
 
 
+def test_copy_blocks_validation():
+    lib = pa.lib()
+    d = desc()
+    assert lib.pa_copy_blocks(None, 2, FAKE, FAKE, FAKE, 1, None) == NULL
+    assert lib.pa_copy_blocks(ctypes.byref(d), 4, FAKE, FAKE, FAKE, 1, None) == UNSUP
+    assert lib.pa_copy_blocks(ctypes.byref(d), 2, FAKE, FAKE, FAKE, -1, None) == SHAPE
+    assert lib.pa_copy_blocks(ctypes.byref(d), 2, FAKE, FAKE, FAKE, 0, None) == OK
+    assert lib.pa_copy_blocks(ctypes.byref(d), 2, None, FAKE, FAKE, 1, None) == NULL
+    bad = desc(d=96)
+    assert lib.pa_copy_blocks(ctypes.byref(bad), 2, FAKE, FAKE, FAKE, 1, None) == UNSUP
+
+
 def test_device_errors_without_gpu():
     import torch
     if torch.cuda.is_available():
@@ -120,6 +135,7 @@ def test_device_errors_without_gpu():
     d = desc()
     assert pa.lib().pa_decode_workspace_size(ctypes.byref(d), 2, 16, 4, 0) == 0
     assert pa.lib().pa_decode_workspace_init(FAKE, 64, None) == DEVICE
+    assert pa.lib().pa_copy_blocks(ctypes.byref(d), 2, FAKE, FAKE, FAKE, 1, None) == DEVICE
 
 
 def test_binding_fails_loudly_without_library(monkeypatch):

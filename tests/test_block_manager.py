@@ -60,19 +60,24 @@ def test_errors():
 
 
 def run_both(seed, num_blocks, block_size, steps, vocab, max_prompt):
+    """Random adds (prompts = a shared stem cut anywhere + a random tail, so
+    prefixes repeat), forks, appends and frees, applied to both managers."""
     rng = random.Random(seed)
     ref = B.BlockManager(num_blocks, block_size)
     got = pa.BlockManager(num_blocks, block_size)
+    stems = [[rng.randrange(vocab) for _ in range(max_prompt)] for _ in range(3)]
     live, next_id = [], 0
+    cow = oob = 0
     for step in range(steps):
         op = rng.random()
-        if op < 0.3 or not live:
-            n = rng.randrange(0, max_prompt)
-            toks = [rng.randrange(vocab) for _ in range(n)]
-            model = rng.randrange(2)
+        if op < 0.25 or not live:
+            cut = rng.randrange(0, max_prompt)
+            toks = rng.choice(stems)[:cut] + [rng.randrange(vocab) for _ in range(rng.randrange(0, 2 * block_size))]
+            model = int(rng.random() < 0.2)
             try:
                 r = ref.add_sequence(next_id, toks, model)
             except B.OutOfBlocks:
+                oob += 1
                 with pytest.raises(pa.PagedAttentionError) as e:
                     got.add_sequence(next_id, toks, model)
                 assert e.value.status == NO_BLOCKS
@@ -80,22 +85,24 @@ def run_both(seed, num_blocks, block_size, steps, vocab, max_prompt):
                 assert got.add_sequence(next_id, toks, model) == r, step
                 live.append(next_id)
                 next_id += 1
-        elif op < 0.4:
+        elif op < 0.35:
             p = rng.choice(live)
             ref.fork(p, next_id)
             got.fork(p, next_id)
             live.append(next_id)
             next_id += 1
-        elif op < 0.85:
+        elif op < 0.8:
             s = rng.choice(live)
             t = rng.randrange(vocab)
             try:
                 r = ref.append_token(s, t)
             except B.OutOfBlocks:
+                oob += 1
                 with pytest.raises(pa.PagedAttentionError) as e:
                     got.append_token(s, t)
                 assert e.value.status == NO_BLOCKS
             else:
+                cow += r[1] >= 0
                 assert got.append_token(s, t) == r, step
         else:
             s = live.pop(rng.randrange(len(live)))
@@ -108,6 +115,8 @@ def run_both(seed, num_blocks, block_size, steps, vocab, max_prompt):
                 assert got.length(s) == ref.length(s)
             assert [got.refcount(b) for b in range(num_blocks)] == ref.ref
     assert got.stats() == (ref.hits, ref.misses)
+    counts = {"hits": ref.hits, "cow": cow, "no_blocks": oob}
+    assert min(counts.values()) > 0, counts           # every path was taken
     bt, sl = got.batch(live, 64)
     for i, s in enumerate(live):
         t = ref.table(s)
