@@ -277,6 +277,8 @@ pa_status pa_copy_blocks(const pa_cache_desc* cache, int32_t elem_bytes, void* k
   p.v_cache = static_cast<uint8_t*>(v_cache);
   p.pairs = pairs;
   p.block_bytes = block_bytes;
+  p.segs = (int32_t)((block_bytes + 16383) / 16384);
+  p.last_words = (int32_t)((block_bytes - (int64_t)(p.segs - 1) * 16384) / 16);
   p.num_pairs = num_pairs;
   p.num_blocks = cache->num_blocks;
   if (pa::launch_copy_blocks(p, static_cast<hipStream_t>(stream)) != hipSuccess) return PA_ERR_LAUNCH;

@@ -15,36 +15,36 @@ namespace {
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-// Workgroup (pair, cache, segment): 256 lanes move one kSegment-byte piece of
-// one block of one cache, 16 bytes per lane per step.
+// Workgroup (pair, cache, segment): 256 lanes move one segment of one block
+// of one cache, 16 bytes per lane per step.  Every segment is kSegment bytes
+// except a block's last, whose 16-byte word count the host computes.
 constexpr int kSegment = 16384;
+constexpr int kSegWords = kSegment / 16;
 
 __global__ __launch_bounds__(256) void copy_blocks_kernel(const CopyBlocksParams p) {
-  const int64_t segs = (p.block_bytes + kSegment - 1) / kSegment;
-  const int64_t w = blockIdx.x;
-  const int64_t pair = w / (2 * segs);
-  const int64_t rest = w - pair * 2 * segs;
-  const int cache = (int)(rest / segs);
-  const int64_t seg = rest - (int64_t)cache * segs;
+  const int segs = p.segs;
+  const int w = blockIdx.x;
+  const int pair = w / (2 * segs);
+  const int rest = w - pair * 2 * segs;
+  const int cache = rest / segs;
+  const int seg = rest - cache * segs;
   const int src = p.pairs[2 * pair], dst = p.pairs[2 * pair + 1];
   if ((unsigned)src >= (unsigned)p.num_blocks || (unsigned)dst >= (unsigned)p.num_blocks) return;
   uint8_t* base = cache ? p.v_cache : p.k_cache;
-  const u32x4* from = reinterpret_cast<const u32x4*>(base + (int64_t)src * p.block_bytes + seg * kSegment);
-  u32x4* to = reinterpret_cast<u32x4*>(base + (int64_t)dst * p.block_bytes + seg * kSegment);
-  int64_t n = p.block_bytes - seg * kSegment;
-  if (n > kSegment) n = kSegment;
-  const int64_t words = n / 16;
-  if (words == kSegment / 16) {
+  const int64_t off = (int64_t)seg * kSegment;
+  const u32x4* from = reinterpret_cast<const u32x4*>(base + (int64_t)src * p.block_bytes + off);
+  u32x4* to = reinterpret_cast<u32x4*>(base + (int64_t)dst * p.block_bytes + off);
+  const int lane = threadIdx.x;
+  if (seg + 1 < segs || p.last_words == kSegWords) {
     // Whole segment: all of this lane's loads in flight before any store.
-    constexpr int kPer = kSegment / 16 / 256;
+    constexpr int kPer = kSegWords / 256;
     u32x4 r[kPer];
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) r[i] = __builtin_nontemporal_load(from + threadIdx.x + 256 * i);
+    for (int i = 0; i < kPer; ++i) r[i] = __builtin_nontemporal_load(from + lane + 256 * i);
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) to[threadIdx.x + 256 * i] = r[i];
+    for (int i = 0; i < kPer; ++i) to[lane + 256 * i] = r[i];
   } else {
-    for (int64_t i = threadIdx.x; i < words; i += 256)
-      to[i] = __builtin_nontemporal_load(from + i);
+    for (int i = lane; i < p.last_words; i += 256) to[i] = __builtin_nontemporal_load(from + i);
   }
 }
 
@@ -52,8 +52,7 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(const CopyBlocksParams
 
 hipError_t launch_copy_blocks(const CopyBlocksParams& p, hipStream_t stream) {
   if (p.num_pairs == 0) return hipSuccess;
-  const int64_t segs = (p.block_bytes + kSegment - 1) / kSegment;
-  const int64_t groups = (int64_t)p.num_pairs * 2 * segs;
+  const int64_t groups = (int64_t)p.num_pairs * 2 * p.segs;
   hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)groups), dim3(256), 0, stream, p);
   return hipGetLastError();
 }

@@ -52,6 +52,8 @@ struct CopyBlocksParams {
   uint8_t* v_cache;
   const int32_t* pairs;         // [num_pairs][2] {src, dst}
   int64_t block_bytes;          // Hkv * block_size * head_dim * element bytes
+  int32_t segs;                 // 16 KiB segments per block (the last may be shorter)
+  int32_t last_words;           // 16-byte words in a block's last segment
   int32_t num_pairs, num_blocks;
 };
 
