@@ -180,6 +180,28 @@ pa_status pa_decode_fp8(const pa_cache_desc* cache, const void* q, int32_t num_s
                         float* out, int32_t partition_tokens, void* workspace,
                         size_t workspace_bytes, void* stream);
 
+/* Sliding-window decode: as pa_decode / pa_decode_fp8, except that each
+ * sequence attends only to its last `window` tokens, positions
+ * [max(0, L - window), L); window == 0 attends to all of them (the same
+ * result as pa_decode).  A local layer keeps only the most recent `window`
+ * positions: each new token drops the oldest once the window is full
+ * ("KV Cache Engineering for LLM Serving", section 3, sliding windows).
+ * Block-table entries of blocks that hold no position of the window are
+ * never read (they may be -1, e.g. after pa_bm_trim released the blocks).
+ * window < 0 gives PA_ERR_SHAPE.                                            */
+pa_status pa_decode_window(const pa_cache_desc* cache, const void* q, int32_t num_seqs,
+                           int32_t num_q_heads, const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* seq_lens, int32_t window, float scale, float* out,
+                           int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                           void* stream);
+pa_status pa_decode_window_fp8(const pa_cache_desc* cache, const void* q, int32_t num_seqs,
+                               int32_t num_q_heads, const void* k_cache, const void* v_cache,
+                               const int32_t* block_tables, int32_t max_blocks_per_seq,
+                               const int32_t* seq_lens, int32_t window, float scale,
+                               float k_scale, float v_scale, float* out, int32_t partition_tokens,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
 /* Human-readable name of a status code (static string, never NULL).        */
 const char* pa_status_string(pa_status status);
 

@@ -77,10 +77,19 @@ pa_status pa_bm_append_token(pa_block_manager* bm, int64_t seq, int32_t token, i
  * block left with none drops its key and goes to the back of the free list. */
 pa_status pa_bm_free_sequence(pa_block_manager* bm, int64_t seq);
 
+/* Sliding window ("KV Cache Engineering for LLM Serving", section 3): the
+ * blocks of `seq` that hold only positions before its last keep_tokens
+ * tokens (keep_tokens >= 1) each lose one reference, and their table entries
+ * become -1; the table keeps its length, so later positions keep their
+ * logical blocks.  pa_decode_window with window <= keep_tokens never reads
+ * the released entries.  *released (may be NULL) receives the count.        */
+pa_status pa_bm_trim(pa_block_manager* bm, int64_t seq, int32_t keep_tokens, int32_t* released);
+
 /* Free blocks (or -1 for a NULL manager).                                    */
 int32_t pa_bm_num_free(const pa_block_manager* bm);
 
-/* Token count and block count of `seq`.                                      */
+/* Token count and block count (table length, released entries included) of
+ * `seq`.                                                                     */
 pa_status pa_bm_sequence_info(const pa_block_manager* bm, int64_t seq, int32_t* num_tokens,
                               int32_t* num_blocks);
 

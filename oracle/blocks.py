@@ -16,6 +16,9 @@ What a block manager does, from the pages:
   serving design, "Prefix sharing is where the real win lives").  The key
   also carries the model / adapter identity, since identical tokens give
   different K and V under different weights (rajatmohan.com, same section).
+* A local (sliding-window) layer keeps only its most recent positions, so the
+  blocks that hold nothing newer can go back to the pool ("KV Cache
+  Engineering for LLM Serving", section 3): ``trim``.
 * A reused block gets its reference count incremented instead of new memory;
   when one user writes tokens of its own into a block others still hold, it
   first gets a private copy: copy-on-write ("Taming the token torrent",
@@ -108,7 +111,8 @@ class BlockManager:
             raise KeyError(child)
         p = self.seqs[parent]
         for b in p["table"]:
-            self.ref[b] += 1
+            if b >= 0:
+                self.ref[b] += 1
         self.seqs[child] = {"tokens": list(p["tokens"]), "table": list(p["table"]),
                             "model": p["model"]}
 
@@ -137,10 +141,29 @@ class BlockManager:
             self._store(blk, self._key(s["model"], s["tokens"], pos + 1))
         return blk * bs + pos % bs, src, dst
 
+    def trim(self, seq, keep):
+        """Sliding window: release the blocks of ``seq`` that hold only
+        positions before its last ``keep`` tokens (keep >= 1); their table
+        entries become -1 and later positions keep their logical blocks.
+        Returns the number of entries released."""
+        if keep < 1:
+            raise ValueError("keep must be >= 1")
+        s = self.seqs[seq]
+        bs = self.block_size
+        first = max(len(s["tokens"]) - keep, 0) // bs   # first block with a kept position
+        n = 0
+        for i in range(first):
+            if s["table"][i] >= 0:
+                self._release(s["table"][i])
+                s["table"][i] = -1
+                n += 1
+        return n
+
     def free_sequence(self, seq):
         s = self.seqs.pop(seq)
         for b in s["table"]:
-            self._release(b)
+            if b >= 0:
+                self._release(b)
 
     # -- queries ----------------------------------------------------------
     def table(self, seq):

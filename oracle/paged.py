@@ -183,14 +183,26 @@ def softmax_attention(q, K, V, scale):
     return w @ V
 
 
+def window_positions(L, window):
+    """Positions a local layer with a window of ``window`` tokens keeps (and
+    attends to) once L tokens exist: the most recent ``window`` of them, all
+    of them when window is 0 ("KV Cache Engineering for LLM Serving",
+    section 3: each new entry removes the oldest once the window is full)."""
+    if window <= 0 or L <= window:
+        return list(range(L))
+    return list(range(L - window, L))
+
+
 def decode(g, q_bits, k_cache, v_cache, block_tables, seq_lens, scale,
-           k_scale=1.0, v_scale=1.0, seqs=None, heads=None):
+           k_scale=1.0, v_scale=1.0, seqs=None, heads=None, window=0):
     """Paged decode: out[s, i, :] = softmax(scale * q[s, i] K_s^T) V_s with
-    K_s, V_s gathered for KV head i // (Hq / Hkv).
+    K_s, V_s gathered for KV head i // (Hq / Hkv); with a window, K_s and V_s
+    are the rows of ``window_positions(L, window)`` only.
 
     q_bits: [S, Hq, D] bf16 bit patterns.  Returns float64 [S, Hq, D]; when
     ``seqs`` (and optionally ``heads``, a list of KV heads) restrict the work,
-    rows that were not computed are NaN."""
+    rows that were not computed are NaN.  With a window, block-table entries
+    of blocks holding no kept position are not read."""
     q = bf16_bits_to_f64(q_bits)
     S, Hq, D = q.shape
     G = Hq // g.num_kv_heads
@@ -199,9 +211,14 @@ def decode(g, q_bits, k_cache, v_cache, block_tables, seq_lens, scale,
     heads = range(g.num_kv_heads) if heads is None else heads
     for s in seqs:
         L = max(int(seq_lens[s]), 0)
+        keep = window_positions(L, window)
+        first_block = keep[0] // g.block_size if keep else 0
+        row = np.asarray(block_tables[s]).copy()
+        row[:first_block] = row[first_block] if keep else 0   # entries never read
         for h in heads:
-            K, V = gather(g, k_cache, v_cache, block_tables[s], L, h, k_scale, v_scale)
-            out[s, h * G:(h + 1) * G] = softmax_attention(q[s, h * G:(h + 1) * G], K, V, scale)
+            K, V = gather(g, k_cache, v_cache, row, L, h, k_scale, v_scale)
+            out[s, h * G:(h + 1) * G] = softmax_attention(q[s, h * G:(h + 1) * G], K[keep], V[keep],
+                                                          scale)
     return out
 
 

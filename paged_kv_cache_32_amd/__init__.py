@@ -79,6 +79,10 @@ def _load():
         "pa_bm_append_token": ([vp, i64, i32, ctypes.POINTER(i64), ctypes.POINTER(i32),
                                 ctypes.POINTER(i32)], i32),
         "pa_bm_free_sequence": ([vp, i64], i32),
+        "pa_bm_trim": ([vp, i64, i32, ctypes.POINTER(i32)], i32),
+        "pa_decode_window": ([dp, vp, i32, i32, vp, vp, vp, i32, vp, i32, f32, vp, i32, vp, sz, vp], i32),
+        "pa_decode_window_fp8": ([dp, vp, i32, i32, vp, vp, vp, i32, vp, i32, f32, f32, f32, vp, i32, vp,
+                                  sz, vp], i32),
         "pa_bm_num_free": ([vp], i32),
         "pa_bm_sequence_info": ([vp, i64, ctypes.POINTER(i32), ctypes.POINTER(i32)], i32),
         "pa_bm_block_table": ([vp, i64, ctypes.POINTER(i32), i32], i32),
@@ -202,7 +206,7 @@ def alloc_workspace(num_blocks, block_size, num_kv_heads, head_dim, num_seqs, nu
 
 
 def _decode(fp8, q, k_cache, v_cache, block_tables, seq_lens, scale, out, num_kv_heads,
-            block_size, k_scale, v_scale, partition_tokens, workspace):
+            block_size, k_scale, v_scale, partition_tokens, workspace, window=None):
     dev = q.device
     if dev.type != "cuda":
         raise ValueError("pa_decode needs device tensors")
@@ -232,12 +236,16 @@ def _decode(fp8, q, k_cache, v_cache, block_tables, seq_lens, scale, out, num_kv
             workspace = torch.zeros(max(int(need), 1), dtype=torch.uint8, device=dev)
         _need(workspace, "workspace", torch.uint8, dev)
         args = [ctypes.byref(desc), _ptr(q), S, Hq, _ptr(k_cache), _ptr(v_cache),
-                _ptr(block_tables), maxb, _ptr(seq_lens), float(scale)]
+                _ptr(block_tables), maxb, _ptr(seq_lens)]
+        if window is not None:
+            args += [int(window)]
+        args += [float(scale)]
         if fp8:
             args += [float(k_scale), float(v_scale)]
         args += [_ptr(out), int(partition_tokens), _ptr(workspace), workspace.numel(), _stream(q)]
-        st = (L.pa_decode_fp8 if fp8 else L.pa_decode)(*args)
-    _check("pa_decode_fp8" if fp8 else "pa_decode", st)
+        name = "pa_decode" + ("_window" if window is not None else "") + ("_fp8" if fp8 else "")
+        st = getattr(L, name)(*args)
+    _check(name, st)
     return out
 
 
@@ -324,6 +332,13 @@ class BlockManager:
     def free_sequence(self, seq):
         _check("pa_bm_free_sequence", _load().pa_bm_free_sequence(self._h, seq))
 
+    def trim(self, seq, keep_tokens):
+        """Release the blocks holding only positions before the last
+        keep_tokens tokens; returns how many table entries were released."""
+        n = ctypes.c_int32()
+        _check("pa_bm_trim", _load().pa_bm_trim(self._h, seq, keep_tokens, ctypes.byref(n)))
+        return n.value
+
     def num_free(self):
         return _load().pa_bm_num_free(self._h)
 
@@ -362,3 +377,19 @@ class BlockManager:
             self._h, ids, n, max_blocks, bt.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
             sl.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))))
         return bt, sl
+
+
+def pa_decode_window(q, k_cache, v_cache, block_tables, seq_lens, window, scale, out=None, *,
+                     num_kv_heads, block_size, partition_tokens=0, workspace=None):
+    """Sliding-window decode over a bf16 cache: each sequence attends to its
+    last `window` tokens (0 = all).  See pa_decode_window in include/pa.h."""
+    return _decode(False, q, k_cache, v_cache, block_tables, seq_lens, scale, out, num_kv_heads,
+                   block_size, 1.0, 1.0, partition_tokens, workspace, window)
+
+
+def pa_decode_window_fp8(q, k_cache, v_cache, block_tables, seq_lens, window, scale, k_scale,
+                         v_scale, out=None, *, num_kv_heads, block_size, partition_tokens=0,
+                         workspace=None):
+    """Sliding-window decode over an e4m3fn cache."""
+    return _decode(True, q, k_cache, v_cache, block_tables, seq_lens, scale, out, num_kv_heads,
+                   block_size, k_scale, v_scale, partition_tokens, workspace, window)

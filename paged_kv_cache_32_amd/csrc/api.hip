@@ -135,11 +135,11 @@ pa_status plan(const pa_cache_desc* c, int32_t num_seqs, int32_t num_q_heads,
 
 pa_status decode(const pa_cache_desc* cache, const void* q, int32_t num_seqs, int32_t num_q_heads,
                  const void* k_cache, const void* v_cache, const int32_t* block_tables,
-                 int32_t max_blocks_per_seq, const int32_t* seq_lens, float scale, float k_scale,
-                 float v_scale, bool fp8, float* out, int32_t partition_tokens, void* workspace,
-                 size_t workspace_bytes, void* stream) {
+                 int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t window, float scale,
+                 float k_scale, float v_scale, bool fp8, float* out, int32_t partition_tokens,
+                 void* workspace, size_t workspace_bytes, void* stream) {
   if (!cache) return PA_ERR_NULL;
-  if (!isfinite(scale)) return PA_ERR_SHAPE;
+  if (!isfinite(scale) || window < 0) return PA_ERR_SHAPE;
   if (fp8 && (!good_scale(k_scale) || !good_scale(v_scale))) return PA_ERR_SHAPE;
   int64_t num_waves = 0;
   int32_t chunk_fixed = 0;
@@ -183,6 +183,7 @@ pa_status decode(const pa_cache_desc* cache, const void* q, int32_t num_seqs, in
   p.num_waves = (int32_t)num_waves;
   p.chunk_min = kChunkMinAuto;
   p.chunk_fixed = chunk_fixed;
+  p.window = window;
   p.subs = cache->block_size / pa::kSub;
   p.subs_magic = p.subs > 1 ? (uint32_t)((((uint64_t)1 << 32) + p.subs - 1) / p.subs) : 0u;
   p.blk_stride = (int64_t)cache->num_kv_heads * p.subs * pa::kSub * cache->head_dim * (fp8 ? 1 : 2);
@@ -243,8 +244,19 @@ pa_status pa_decode(const pa_cache_desc* cache, const void* q, int32_t num_seqs,
                     const int32_t* seq_lens, float scale, float* out, int32_t partition_tokens,
                     void* workspace, size_t workspace_bytes, void* stream) {
   return decode(cache, q, num_seqs, num_q_heads, k_cache, v_cache, block_tables,
-                max_blocks_per_seq, seq_lens, scale, 1.f, 1.f, false, out, partition_tokens,
+                max_blocks_per_seq, seq_lens, 0, scale, 1.f, 1.f, false, out, partition_tokens,
                 workspace, workspace_bytes, stream);
+}
+
+pa_status pa_decode_window(const pa_cache_desc* cache, const void* q, int32_t num_seqs,
+                           int32_t num_q_heads, const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* seq_lens, int32_t window, float scale, float* out,
+                           int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  return decode(cache, q, num_seqs, num_q_heads, k_cache, v_cache, block_tables,
+                max_blocks_per_seq, seq_lens, window, scale, 1.f, 1.f, false, out,
+                partition_tokens, workspace, workspace_bytes, stream);
 }
 
 pa_status pa_decode_fp8(const pa_cache_desc* cache, const void* q, int32_t num_seqs,
@@ -254,7 +266,18 @@ pa_status pa_decode_fp8(const pa_cache_desc* cache, const void* q, int32_t num_s
                         float* out, int32_t partition_tokens, void* workspace,
                         size_t workspace_bytes, void* stream) {
   return decode(cache, q, num_seqs, num_q_heads, k_cache, v_cache, block_tables,
-                max_blocks_per_seq, seq_lens, scale, k_scale, v_scale, true, out,
+                max_blocks_per_seq, seq_lens, 0, scale, k_scale, v_scale, true, out,
+                partition_tokens, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_decode_window_fp8(const pa_cache_desc* cache, const void* q, int32_t num_seqs,
+                               int32_t num_q_heads, const void* k_cache, const void* v_cache,
+                               const int32_t* block_tables, int32_t max_blocks_per_seq,
+                               const int32_t* seq_lens, int32_t window, float scale,
+                               float k_scale, float v_scale, float* out, int32_t partition_tokens,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  return decode(cache, q, num_seqs, num_q_heads, k_cache, v_cache, block_tables,
+                max_blocks_per_seq, seq_lens, window, scale, k_scale, v_scale, true, out,
                 partition_tokens, workspace, workspace_bytes, stream);
 }
 

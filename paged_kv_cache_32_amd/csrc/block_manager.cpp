@@ -226,7 +226,8 @@ pa_status pa_bm_fork(pa_block_manager* bm, int64_t parent, int64_t child) {
   auto it = bm->seqs.find(parent);
   if (it == bm->seqs.end() || bm->seqs.count(child)) return PA_ERR_NOT_FOUND;
   Sequence c = it->second;
-  for (int32_t b : c.table) bm->ref[b]++;
+  for (int32_t b : c.table)
+    if (b >= 0) bm->ref[b]++;
   for (uint64_t id : c.prefixes) bm->prefixes.at(id).holders++;
   bm->seqs.emplace(child, std::move(c));
   return PA_OK;
@@ -269,9 +270,30 @@ pa_status pa_bm_free_sequence(pa_block_manager* bm, int64_t seq) {
   if (!bm) return PA_ERR_NULL;
   auto it = bm->seqs.find(seq);
   if (it == bm->seqs.end()) return PA_ERR_NOT_FOUND;
-  for (int32_t b : it->second.table) bm->release(b);
+  for (int32_t b : it->second.table)
+    if (b >= 0) bm->release(b);
   for (uint64_t id : it->second.prefixes) bm->drop(id);
   bm->seqs.erase(it);
+  return PA_OK;
+}
+
+pa_status pa_bm_trim(pa_block_manager* bm, int64_t seq, int32_t keep_tokens, int32_t* released) {
+  if (!bm) return PA_ERR_NULL;
+  if (keep_tokens < 1) return PA_ERR_SHAPE;
+  auto it = bm->seqs.find(seq);
+  if (it == bm->seqs.end()) return PA_ERR_NOT_FOUND;
+  Sequence& s = it->second;
+  const int64_t n = (int64_t)s.tokens.size();
+  const int64_t first = (n > keep_tokens ? n - keep_tokens : 0) / bm->block_size;
+  int32_t count = 0;
+  for (int64_t i = 0; i < first; ++i) {
+    if (s.table[i] >= 0) {
+      bm->release(s.table[i]);
+      s.table[i] = -1;
+      ++count;
+    }
+  }
+  if (released) *released = count;
   return PA_OK;
 }
 

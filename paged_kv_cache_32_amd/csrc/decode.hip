@@ -96,10 +96,16 @@ __device__ __forceinline__ int wave_reduce_sum(int v) {
   return v;
 }
 
-// Chunks (16-token pieces) of a sequence; -1 marks an invalid length.
-__device__ __forceinline__ int chunks_of(int L, int max_len) {
+// First token a sequence of L tokens attends to: L - W with a window of W
+// tokens ("KV Cache Engineering for LLM Serving", section 3, sliding
+// windows), 0 without one (W = 0) or while L <= W.
+__device__ __forceinline__ int window_lo(int L, int W) { return (W > 0 && L > W) ? L - W : 0; }
+
+// Chunks (16-token pieces) of a sequence's unit: the chunks holding tokens
+// [window_lo, L); -1 marks an invalid length.
+__device__ __forceinline__ int chunks_of(int L, int max_len, int W) {
   if (L < 0 || L > max_len) return -1;
-  return (L + kSub - 1) / kSub;
+  return (L + kSub - 1) / kSub - window_lo(L, W) / kSub;
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -193,15 +199,18 @@ enum : int {
   kTail = 8,     // ends in the unit's last chunk, which is partial
   kAtA = 16,     // the piece starts at the wavefront's first chunk
   kWhole = 32,   // the piece is its whole unit
+  kHead = 64,    // starts at the unit's first chunk, which begins before the window
 };
 
 // A piece: chunks [j0, j1) of unit (s, h), whose first chunk sits at u0 in
 // the linear chunk list; the unit has n chunks and the sequence L tokens.
+// Unit chunk j is the sequence's chunk window_lo(L, W) / 16 + j.
 struct Piece {
   int s, h, n, L, u0, j0, j1;
 };
 
-// One stage, uniform across the wavefront: chunks [j, j + cnt) of a piece.
+// One stage, uniform across the wavefront: chunks [j, j + cnt) of a piece,
+// j counted in the sequence (not in the unit).
 struct Stage {
   int s, h, n, L, u0, j, cnt, flags;
 };
@@ -241,7 +250,7 @@ __device__ __forceinline__ void next_unit(const DecodeParams& p, int max_len, in
   for (;;) {
     ++s;
     L = sload(p.seq_lens, s);
-    n = chunks_of(L, max_len);
+    n = chunks_of(L, max_len, p.window);
     if (n > 0) break;
   }
 }
@@ -257,7 +266,7 @@ __device__ __forceinline__ Stage next_stage(Cursor& c, const DecodeParams& p, in
       // First middle unit: the one after unit A.
       int s = c.a_s, h = c.a_h;
       int L = sload(p.seq_lens, s);
-      int n = chunks_of(L, max_len);
+      int n = chunks_of(L, max_len, p.window);
       next_unit(p, max_len, s, h, n, L);
       c.cur = Piece{s, h, n, L, c.a_end, 0, n};
       c.phase = 2;
@@ -277,15 +286,18 @@ __device__ __forceinline__ Stage next_stage(Cursor& c, const DecodeParams& p, in
     return st;
   }
   const Piece& pc = c.cur;
+  const int lo = window_lo(pc.L, p.window);
+  const int c0 = lo / kSub;
   int cnt = pc.j1 - c.j;
   if (cnt > NSUB) cnt = NSUB;
   int f = kValid;
   if (c.j == pc.j0) f |= kFirst;
   if (c.j + cnt == pc.j1) f |= kLast;
-  if (c.j + cnt == pc.n && pc.n * kSub > pc.L) f |= kTail;
+  if (c.j + cnt == pc.n && (c0 + pc.n) * kSub > pc.L) f |= kTail;
+  if (c.j == 0 && lo > c0 * kSub) f |= kHead;
   if (c.phase == 0) f |= kAtA;
   if (pc.j0 == 0 && pc.j1 == pc.n) f |= kWhole;
-  st = Stage{uni(pc.s), uni(pc.h), uni(pc.n), uni(pc.L), uni(pc.u0), uni(c.j), uni(cnt), uni(f)};
+  st = Stage{uni(pc.s), uni(pc.h), uni(pc.n), uni(pc.L), uni(pc.u0), uni(c0 + c.j), uni(cnt), uni(f)};
   c.j += cnt;
   return st;
 }
@@ -373,9 +385,10 @@ __device__ __forceinline__ u32x2 v_operand(const StageBuf<D, FP8, NSUB>& buf, in
 }
 
 // The math of one stage: logits, online-softmax update, P V accumulation.
-// MASK: the stage holds the unit's last chunk and it is partial, so logits
-// of tokens at or past L are set to -inf and their V elements to zero (they
-// hold arbitrary bits, possibly NaN, and 0 * NaN is NaN).
+// MASK: the stage holds a partial chunk (the unit's last, or its first when
+// the window starts inside it), so logits of tokens outside [lo, L) are set
+// to -inf and their V elements to zero (they hold arbitrary bits, possibly
+// NaN, and 0 * NaN is NaN).
 template <int D, bool FP8, int NSUB, bool MASK>
 __device__ __forceinline__ void compute_stage(const DecodeParams& p, const Stage& st,
                                               const StageBuf<D, FP8, NSUB>& buf,
@@ -384,6 +397,7 @@ __device__ __forceinline__ void compute_stage(const DecodeParams& p, const Stage
   const int qd = lane >> 4;
   const int first_tok = st.j * kSub;
   const int L = st.L;
+  const int lo = MASK ? window_lo(L, p.window) : 0;
 
   // Logits, base 2: lane holds tokens 4*qd + i of each sub-block, head col.
   float z[NSUB][4];
@@ -414,7 +428,7 @@ __device__ __forceinline__ void compute_stage(const DecodeParams& p, const Stage
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         z[k][i] = s[i] * p.qk_scale;
-        if (MASK && tok0 + i >= L) z[k][i] = kNegInf;
+        if (MASK && (tok0 + i >= L || tok0 + i < lo)) z[k][i] = kNegInf;
         mx = __builtin_fmaxf(mx, z[k][i]);
       }
     }
@@ -440,13 +454,15 @@ __device__ __forceinline__ void compute_stage(const DecodeParams& p, const Stage
 #pragma unroll
       for (int i = 0; i < 4; ++i) pz[i] = __builtin_amdgcn_exp2f(z[k][i] - sm.m);
       sm.l += (pz[0] + pz[1]) + (pz[2] + pz[3]);
-      u32x2 hi, lo;
-      split_p(pz, hi, lo);
+      u32x2 p_hi, p_lo;
+      split_p(pz, p_hi, p_lo);
       uint32_t m0 = 0xFFFFFFFFu, m1 = 0xFFFFFFFFu;
       if (MASK) {
         const int tok0 = first_tok + k * kSub + qd * 4;
-        m0 = (tok0 + 0 < L ? 0x0000FFFFu : 0u) | (tok0 + 1 < L ? 0xFFFF0000u : 0u);
-        m1 = (tok0 + 2 < L ? 0x0000FFFFu : 0u) | (tok0 + 3 < L ? 0xFFFF0000u : 0u);
+        const bool t0 = tok0 + 0 < L && tok0 + 0 >= lo, t1 = tok0 + 1 < L && tok0 + 1 >= lo;
+        const bool t2 = tok0 + 2 < L && tok0 + 2 >= lo, t3 = tok0 + 3 < L && tok0 + 3 >= lo;
+        m0 = (t0 ? 0x0000FFFFu : 0u) | (t1 ? 0xFFFF0000u : 0u);
+        m1 = (t2 ? 0x0000FFFFu : 0u) | (t3 ? 0xFFFF0000u : 0u);
       }
 #pragma unroll
       for (int dc = 0; dc < T::DC; ++dc) {
@@ -456,8 +472,8 @@ __device__ __forceinline__ void compute_stage(const DecodeParams& p, const Stage
           a[1] &= m1;
         }
         const i16x4 av = as_i16x4(a);
-        sm.acc[dc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, as_i16x4(hi), sm.acc[dc], 0, 0, 0);
-        sm.acc[dc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, as_i16x4(lo), sm.acc[dc], 0, 0, 0);
+        sm.acc[dc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, as_i16x4(p_hi), sm.acc[dc], 0, 0, 0);
+        sm.acc[dc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, as_i16x4(p_lo), sm.acc[dc], 0, 0, 0);
       }
     }
   }
@@ -603,7 +619,7 @@ __device__ __forceinline__ void finish_stage(const DecodeParams& p, const Stage&
     ws.bad = false;
   }
   ws.bad |= st_bad;
-  if (st.flags & kTail)
+  if (st.flags & (kTail | kHead))
     compute_stage<D, FP8, NSUB, true>(p, st, buf, ws.q, ws.sm, lane);
   else
     compute_stage<D, FP8, NSUB, false>(p, st, buf, ws.q, ws.sm, lane);
@@ -683,7 +699,7 @@ __global__ __launch_bounds__(kDecodeThreads, PA_DECODE_MIN_WAVES) void decode_ke
   for (int base = 0; base < S; base += 64) {
     const int si = base + lane;
     int n = 0;
-    if (si < S) n = chunks_of(p.seq_lens[si], max_len);
+    if (si < S) n = chunks_of(p.seq_lens[si], max_len, p.window);
     if (wave == 0) {
       uint64_t todo = __ballot(si < S && n <= 0);
       while (todo) {
@@ -720,7 +736,7 @@ __global__ __launch_bounds__(kDecodeThreads, PA_DECODE_MIN_WAVES) void decode_ke
     for (int base = 0; base < S && !(found_a && found_z); base += 64) {
       const int si = base + lane;
       int n = 0;
-      if (si < S) n = chunks_of(p.seq_lens[si], max_len);
+      if (si < S) n = chunks_of(p.seq_lens[si], max_len, p.window);
       n = n < 0 ? 0 : n;
       const int incl = wave_incl_scan(n, lane);
       const int lo = Hkv * (carry + incl - n), hi = Hkv * (carry + incl);
@@ -743,7 +759,7 @@ __global__ __launch_bounds__(kDecodeThreads, PA_DECODE_MIN_WAVES) void decode_ke
   }
   Cursor cur;
   {
-    const int La = sload(p.seq_lens, sa), na = chunks_of(La, max_len);
+    const int La = sload(p.seq_lens, sa), na = chunks_of(La, max_len, p.window);
     const int ha = uni((a - Hkv * before_a) / na);
     const int u0a = Hkv * before_a + ha * na;
     const int a_end = u0a + na;
@@ -755,7 +771,7 @@ __global__ __launch_bounds__(kDecodeThreads, PA_DECODE_MIN_WAVES) void decode_ke
     cur.a_h = ha;
     cur.z = Piece{0, 0, 0, 0, a_end, 0, 0};  // no piece Z: j1 = 0, middle walk ends at a_end
     if (b > a_end) {
-      const int Lz = sload(p.seq_lens, sz), nz = chunks_of(Lz, max_len);
+      const int Lz = sload(p.seq_lens, sz), nz = chunks_of(Lz, max_len, p.window);
       const int hz = uni((b - 1 - Hkv * before_z) / nz);
       const int u0z = Hkv * before_z + hz * nz;
       cur.z = Piece{sz, hz, nz, Lz, u0z, 0, b - u0z};

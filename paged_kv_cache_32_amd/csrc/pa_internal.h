@@ -40,6 +40,7 @@ struct DecodeParams {
   int32_t num_waves;            // wavefronts launched
   int32_t chunk_min;            // auto split: fewest chunks a wavefront takes
   int32_t chunk_fixed;          // > 0: every wavefront takes this many chunks
+  int32_t window;               // > 0: attend to the last `window` tokens only
   int32_t subs;                 // 16-token sub-blocks per block (block_size / 16)
   uint32_t subs_magic;          // ceil(2^32 / subs) for subs > 1: j / subs = umulhi(j, magic)
   int64_t blk_stride;           // bytes from one block's tiles to the next: Hkv * subs * tile

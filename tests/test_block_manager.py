@@ -61,7 +61,8 @@ def test_errors():
 
 def run_both(seed, num_blocks, block_size, steps, vocab, max_prompt):
     """Random adds (prompts = a shared stem cut anywhere + a random tail, so
-    prefixes repeat), forks, appends and frees, applied to both managers."""
+    prefixes repeat), forks, appends, sliding-window trims and frees, applied
+    to both managers."""
     rng = random.Random(seed)
     ref = B.BlockManager(num_blocks, block_size)
     got = pa.BlockManager(num_blocks, block_size)
@@ -104,6 +105,10 @@ def run_both(seed, num_blocks, block_size, steps, vocab, max_prompt):
             else:
                 cow += r[1] >= 0
                 assert got.append_token(s, t) == r, step
+        elif op < 0.88:
+            s = rng.choice(live)
+            keep = rng.randrange(1, 3 * block_size)
+            assert got.trim(s, keep) == ref.trim(s, keep), step
         else:
             s = live.pop(rng.randrange(len(live)))
             ref.free_sequence(s)

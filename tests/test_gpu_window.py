@@ -1,0 +1,120 @@
+"""Sliding-window decode (pa_decode_window / pa_decode_window_fp8) against the
+oracle: windows shorter than a chunk, not a multiple of 16, longer than every
+sequence, with table entries before the window released (-1), several
+partition sizes, and decode steps whose tables come from the block manager
+with trims."""
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_32_amd as pa
+from oracle import blocks as B
+from oracle import paged
+from paged_kv_cache_32_amd import workloads as W
+from tests.gpu_helpers import (BF16_TOL, compare, device_inputs, gpu_write, host_bits, oracle_caches)
+
+pytestmark = pytest.mark.gpu
+
+
+def window_decode(w, t, window, part=0, bt=None):
+    kc, vc = t["k_cache"][0], t["v_cache"][0]
+    bt = t["block_tables"] if bt is None else bt
+    if w.kv_dtype == "bf16":
+        return pa.pa_decode_window(t["q"][0], kc, vc, bt, t["seq_lens"], window, w.scale,
+                                   num_kv_heads=w.num_kv_heads, block_size=w.block_size,
+                                   partition_tokens=part)
+    return pa.pa_decode_window_fp8(t["q"][0], kc, vc, bt, t["seq_lens"], window, w.scale,
+                                   float(t["k_scale"][0]), float(t["v_scale"][0]),
+                                   num_kv_heads=w.num_kv_heads, block_size=w.block_size,
+                                   partition_tokens=part)
+
+
+CASES = [  # seed, S, Hq, Hkv, D, BS, max_len, kv, windows
+    (1, 12, 16, 2, 128, 16, 700, "bf16", (1, 7, 16, 33, 256, 5000)),
+    (2, 9, 8, 1, 64, 32, 900, "bf16", (17, 100, 1024)),
+    (3, 10, 64, 8, 128, 16, 1500, "fp8", (1, 50, 512)),
+    (4, 7, 12, 4, 64, 48, 600, "fp8", (31, 200)),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"{c[7]}_d{c[4]}_bs{c[5]}" for c in CASES])
+def test_window_decode_matches_the_oracle(case):
+    seed, S, Hq, Hkv, D, BS, max_len, kv, windows = case
+    w = W.random_workload(seed, S, Hq, Hkv, D, BS, max_len, kv_dtype=kv, min_len=1)
+    print(f"[window] {w.name} {kv} lens={list(w.seq_lens)}", flush=True)
+    t = device_inputs(w)
+    kc0, vc0 = host_bits(t["k_cache"][0]), host_bits(t["v_cache"][0])
+    ks = float(t["k_scale"][0]) if kv == "fp8" else 1.0
+    vs = float(t["v_scale"][0]) if kv == "fp8" else 1.0
+    gpu_write(w, t)
+    kc_ref, vc_ref = oracle_caches(w, kc0, vc0, host_bits(t["k_new"][0]), host_bits(t["v_new"][0]), ks, vs)
+    g = paged.Geom(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.kv_dtype)
+    q = host_bits(t["q"][0])
+    for win in windows:
+        ref = paged.decode(g, q, kc_ref, vc_ref, w.block_tables, w.seq_lens, w.scale,
+                           k_scale=ks, v_scale=vs, window=win)
+        for part in (0, 32):
+            out = window_decode(w, t, win, part)
+            torch.cuda.synchronize()
+            compare(out, ref, kv, label=f"window={win} part={part}")
+        # entries of blocks before the window released: never read
+        bt = w.block_tables.copy()
+        for s, L in enumerate(w.seq_lens):
+            bt[s, :max(0, int(L) - win) // BS] = -1
+        out = window_decode(w, t, win, 0, torch.from_numpy(bt).cuda())
+        torch.cuda.synchronize()
+        compare(out, ref, kv, label=f"window={win} released")
+    # window 0 is full attention, the same as pa_decode
+    ref = paged.decode(g, q, kc_ref, vc_ref, w.block_tables, w.seq_lens, w.scale, k_scale=ks, v_scale=vs)
+    compare(window_decode(w, t, 0), ref, kv, label="window=0")
+
+
+def test_window_decode_with_manager_trims():
+    """A local layer's step loop: append, trim to the window, decode; the
+    released blocks go back to the pool, so each sequence holds a bounded
+    number of blocks however long it grows."""
+    Hq, Hkv, D, BS, NB, WIN = 8, 2, 64, 16, 40, 40
+    g = paged.Geom(NB, BS, Hkv, D, "bf16")
+    rng = np.random.default_rng(21)
+    native, model = pa.BlockManager(NB, BS), B.BlockManager(NB, BS)
+    seqs = [0, 1, 2]
+    for s in seqs:
+        prompt = list(rng.integers(0, 9, int(rng.integers(20, 60))))
+        native.add_sequence(s, prompt)
+        model.add_sequence(s, prompt)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(3)
+    kc = torch.randn(g.cache_elems, generator=gen, device="cuda").to(torch.bfloat16)
+    vc = torch.randn(g.cache_elems, generator=gen, device="cuda").to(torch.bfloat16)
+    k_ref, v_ref = host_bits(kc).copy(), host_bits(vc).copy()
+    for step in range(40):
+        slots = []
+        for s in seqs:
+            tok = int(rng.integers(0, 9))
+            got = native.append_token(s, tok)
+            assert got == model.append_token(s, tok) and got[1] < 0
+            slots.append(got[0])
+            assert native.trim(s, WIN) == model.trim(s, WIN)
+        S = len(seqs)
+        k_new = torch.randn((S, Hkv, D), generator=gen, device="cuda").to(torch.bfloat16)
+        v_new = torch.randn((S, Hkv, D), generator=gen, device="cuda").to(torch.bfloat16)
+        q = torch.randn((S, Hq, D), generator=gen, device="cuda").to(torch.bfloat16)
+        bt, sl = native.batch(seqs, 16)
+        pa.pa_cache_write(k_new, v_new, torch.tensor(slots, dtype=torch.int64, device="cuda"), kc, vc,
+                          block_size=BS)
+        out = pa.pa_decode_window(q, kc, vc, torch.from_numpy(bt).cuda(), torch.from_numpy(sl).cuda(),
+                                  WIN, 0.125, num_kv_heads=Hkv, block_size=BS)
+        torch.cuda.synchronize()
+        paged.cache_write_bf16(g, host_bits(k_new), host_bits(v_new), np.array(slots), k_ref, v_ref)
+        bt_o = np.full((S, 16), -1, dtype=np.int32)
+        for i, s in enumerate(seqs):
+            tt = model.table(s)
+            bt_o[i, :len(tt)] = tt
+        assert np.array_equal(bt, bt_o)
+        ref = paged.decode(g, host_bits(q), k_ref, v_ref, bt_o, sl, 0.125, window=WIN)
+        err = np.abs(out.cpu().double().numpy() - ref)
+        assert err.max() <= BF16_TOL[0] and err.mean() <= BF16_TOL[1], (step, err.max())
+    # the pool stays bounded: each sequence holds at most ceil(WIN / BS) + 1 blocks
+    assert all(sum(b >= 0 for b in model.table(s)) <= -(-WIN // BS) + 1 for s in seqs)
+    assert model.num_free() >= NB - len(seqs) * (-(-WIN // BS) + 1)

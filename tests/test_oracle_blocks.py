@@ -179,3 +179,50 @@ def test_copy_blocks_moves_exactly_the_blocks_elements():
     assert np.array_equal(k[3 * E:4 * E], np.arange(E, 2 * E)) and np.array_equal(k[0:E], np.arange(4 * E, 5 * E))
     assert np.array_equal(v[3 * E:4 * E], -np.arange(E, 2 * E))
     assert np.array_equal(k[E:3 * E], np.arange(E, 3 * E))   # sources untouched
+
+
+def test_trim_releases_blocks_outside_the_window():
+    bm = B.BlockManager(12, 4)
+    sysp = unique_tokens(0, 8)                       # two full shared blocks
+    bm.add_sequence("a", sysp + unique_tokens(100, 9))
+    bm.add_sequence("b", sysp + unique_tokens(200, 3))
+    ta, tb = bm.table("a"), bm.table("b")
+    assert ta[:2] == tb[:2]
+    free0 = bm.num_free()
+    # a has 17 tokens; keeping the last 6 keeps positions 11..16 (blocks 2..4)
+    assert bm.trim("a", 6) == 2
+    assert bm.table("a")[:2] == [-1, -1] and bm.table("a")[2:] == ta[2:]
+    assert bm.num_free() == free0                    # the shared blocks are still held by b
+    assert [bm.ref[b] for b in tb[:2]] == [1, 1]
+    assert bm.trim("a", 6) == 0                      # idempotent
+    slot, _, _ = bm.append_token("a", 5)             # positions keep their logical blocks
+    assert slot == ta[4] * 4 + 1
+    bm.free_sequence("b")
+    assert bm.free[-3:] == tb                        # b's blocks, now unreferenced, in table order
+    bm.free_sequence("a")
+    check_invariants_with_trims(bm, 12)
+    with pytest.raises(ValueError):
+        bm.trim("x", 0)
+
+
+def check_invariants_with_trims(bm, num_blocks):
+    counts = [0] * num_blocks
+    for s in bm.seqs.values():
+        for b in s["table"]:
+            if b >= 0:
+                counts[b] += 1
+    assert counts == bm.ref
+    assert sorted(bm.free) == [b for b in range(num_blocks) if counts[b] == 0]
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_random_operations_with_trims_keep_the_invariants(seed):
+    rng = random.Random(100 + seed)
+    bm = B.BlockManager(30, 4)
+    for i, _ in enumerate(random_ops(bm, rng, 500)):
+        if bm.seqs and rng.random() < 0.2:
+            s = rng.choice(list(bm.seqs))
+            bm.trim(s, rng.randrange(1, 12))
+        if i % 20 == 0:
+            check_invariants_with_trims(bm, 30)
+    check_invariants_with_trims(bm, 30)

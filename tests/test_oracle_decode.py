@@ -292,3 +292,45 @@ def test_planted_off_by_one_block_index_is_caught(monkeypatch):
     monkeypatch.setattr(paged, "slot_to_block", lambda slot, bs: orig(slot + 1, bs))
     with pytest.raises(AssertionError):
         test_cache_write_touches_only_its_slots()
+
+
+# ---------------------------------------------------------------- sliding window
+def test_window_positions_follow_the_pages_trace(pages):
+    """A four-token window over ten tokens keeps the printed positions after
+    every token ("KV Cache Engineering for LLM Serving", section 3)."""
+    c = pages["sliding_window_trace"]
+    for p in range(c["tokens"]):
+        assert paged.window_positions(p + 1, c["window"]) == c["retained_after_token"][p]
+    assert max(len(paged.window_positions(L, c["window"])) for L in range(50)) == c["max_retained"]
+    assert paged.window_positions(7, 0) == list(range(7))
+
+
+@pytest.mark.parametrize("W", [1, 5, 16, 17, 33, 64, 1000])
+def test_window_decode_is_dense_attention_over_the_window(W):
+    rng = np.random.default_rng(40 + W)
+    lens = [1, 9, 40, 77, 130]
+    g, kc, vc, bt, sl, q, dense = make_paged(rng, lens, 8, 2, 32, 16)
+    out = paged.decode(g, q, kc, vc, bt, sl, 0.3, window=W)
+    qf = paged.bf16_bits_to_f64(q)
+    for s, (K, V) in enumerate(dense):
+        lo = max(0, lens[s] - W)
+        ref = paged.dense_attention(qf[s], K[lo:], V[lo:], 0.3)
+        assert np.max(np.abs(out[s] - ref)) < 1e-12, (W, s)
+    if W >= max(lens):        # a window at least as long as every sequence is full attention
+        assert np.array_equal(out, paged.decode(g, q, kc, vc, bt, sl, 0.3))
+
+
+def test_window_of_one_returns_the_last_value_and_ignores_released_blocks():
+    rng = np.random.default_rng(77)
+    lens = [20, 47, 64]
+    g, kc, vc, bt, sl, q, dense = make_paged(rng, lens, 4, 1, 32, 16)
+    out = paged.decode(g, q, kc, vc, bt, sl, 0.3, window=1)
+    for s, (K, V) in enumerate(dense):
+        assert np.array_equal(out[s], np.repeat(V[-1:, 0], 4, 0))
+    # Table entries of blocks before the window are never read.
+    W = 20
+    ref = paged.decode(g, q, kc, vc, bt, sl, 0.3, window=W)
+    bt2 = bt.copy()
+    for s, L in enumerate(lens):
+        bt2[s, :max(0, L - W) // 16] = -1
+    assert np.array_equal(paged.decode(g, q, kc, vc, bt2, sl, 0.3, window=W), ref)
