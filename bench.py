@@ -27,6 +27,9 @@ Other workloads (--workload), each on the same 70B layer shape:
                        pa_cache_write_fp8 then pa_decode_fp8, 160 launches
                        replayed as one HIP graph; `value` is KV GB/s over the
                        whole step, decode tok/s = 128 / step time
+  sliding_window_llama70b  the default batch decoded by a local layer with a
+                       1,024-token window (pa_decode_window): `value` counts the
+                       K/V of the last min(L, 1024) tokens of each sequence
   copy_blocks_llama70b pa_copy_blocks of 4,096 independent block pairs on the
                        70B layer's bf16 pool (block 16): `value` is bytes read
                        plus written per call / time; also the host block
@@ -59,18 +62,26 @@ HBM_PEAK_GBS = 8000.0
 MODEL_LAYERS = 80
 SCRUB_BYTES = 512 << 20
 WORKLOADS = {"llama70b_layer_bs64": 2, "prefix_shared_bs256": 3, "long_context_128k": 4,
-             "fp8_80layer_bs128": 5, "copy_blocks_llama70b": 2}
+             "fp8_80layer_bs128": 5, "copy_blocks_llama70b": 2, "sliding_window_llama70b": 2}
+LOCAL_WINDOW = 1024   # a local layer's window ("KV Cache Engineering for LLM Serving", section 3)
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(w, physical=False):
+def algorithmic_bytes(w, physical=False, window=0):
     """Bytes one decode call must move at minimum: K and V of every cached
-    token (each distinct token once when ``physical``), the queries, the
+    token (each distinct token once when ``physical``; only the last
+    ``window`` tokens of each sequence with a window), the queries, the
     outputs, the block-table entries and lengths."""
     S, Hq, D = w.num_seqs, w.num_q_heads, w.head_dim
+    if window:
+        toks = [min(int(L), window) for L in w.seq_lens]
+        kv = sum(toks) * 2 * w.num_kv_heads * w.head_dim * w.elem_bytes
+        blocks = sum(-(-int(L) // w.block_size) - max(int(L) - window, 0) // w.block_size for L in w.seq_lens)
+        tables = blocks * 4
+        return kv, kv + S * Hq * D * 2 + S * Hq * D * 4 + tables + 4 * S
     kv = w.physical_kv_bytes() if physical else w.logical_kv_bytes()
     tables = int(sum(-(-int(L) // w.block_size) for L in w.seq_lens)) * 4
     other = S * Hq * D * 2 + S * Hq * D * 4 + tables + 4 * S
@@ -109,7 +120,7 @@ def measured_traffic(workload="llama70b_layer_bs64"):
     return rec.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(w, t, out_gpu, layer=0, min_seconds=10.0, max_seconds=30.0):
+def cpu_baseline(w, t, out_gpu, layer=0, min_seconds=10.0, max_seconds=30.0, window=0):
     """Time the CPU oracle (float64 numpy) on a bounded sample of the same
     workload: one sequence at a time, in order and wrapping around, until
     about 10 s have elapsed (a whole pass when the batch fits in that time).
@@ -137,15 +148,16 @@ def cpu_baseline(w, t, out_gpu, layer=0, min_seconds=10.0, max_seconds=30.0):
         paged.cache_write_fp8(g, kn, vn, w.slot_mapping, kc, vc, np.float32(ks), np.float32(vs))
     threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     per_token = 2 * w.num_kv_heads * w.head_dim * w.elem_bytes
+    read = (lambda L: min(L, window)) if window else (lambda L: L)
     ref = np.full((w.num_seqs, w.num_q_heads, w.head_dim), np.nan)
     done = set()
     calls, elapsed, nbytes, s = 0, 0.0, 0, 0
     while elapsed < min_seconds and elapsed < max_seconds:
         t0 = time.perf_counter()
         r = paged.decode(g, q, kc, vc, w.block_tables, w.seq_lens, w.scale, k_scale=ks,
-                         v_scale=vs, seqs=[s])
+                         v_scale=vs, seqs=[s], window=window)
         elapsed += time.perf_counter() - t0
-        nbytes += int(w.seq_lens[s]) * per_token
+        nbytes += read(int(w.seq_lens[s])) * per_token
         calls += 1
         if s not in done:
             ref[s] = r[s]
@@ -185,6 +197,7 @@ def bench_layer(args, dev):
     """One-layer workloads: the cache write and the decode of one batch."""
     w = W.config(WORKLOADS[args.workload])
     shared = args.workload == "prefix_shared_bs256"
+    window = LOCAL_WINDOW if args.workload == "sliding_window_llama70b" else 0
     log("workload:", json.dumps(w.summary()))
     t = w.make_tensors(dev)
     bt = torch.from_numpy(w.block_tables).to(dev)
@@ -206,8 +219,13 @@ def bench_layer(args, dev):
         pa.pa_cache_write(kn, vn, sm, kc, vc, block_size=w.block_size)
 
     def decode():
-        pa.pa_decode(q, kc, vc, bt, sl, w.scale, out, num_kv_heads=w.num_kv_heads,
-                     block_size=w.block_size, partition_tokens=args.partition_tokens, workspace=ws)
+        if window:
+            pa.pa_decode_window(q, kc, vc, bt, sl, window, w.scale, out, num_kv_heads=w.num_kv_heads,
+                                block_size=w.block_size, partition_tokens=args.partition_tokens,
+                                workspace=ws)
+        else:
+            pa.pa_decode(q, kc, vc, bt, sl, w.scale, out, num_kv_heads=w.num_kv_heads,
+                         block_size=w.block_size, partition_tokens=args.partition_tokens, workspace=ws)
 
     for i in range(args.warmup):
         if not args.no_scrub:
@@ -242,7 +260,7 @@ def bench_layer(args, dev):
     torch.cuda.synchronize()
     hot_ms = hot[0].elapsed_time(hot[1]) / K
 
-    kv_bytes, alg_bytes = algorithmic_bytes(w, physical=shared)
+    kv_bytes, alg_bytes = algorithmic_bytes(w, physical=shared, window=window)
     logical_kv = w.logical_kv_bytes()
     dec_s = float(dec_ms.mean()) / 1e3
     step_ms = float((write_ms + dec_ms).mean())
@@ -253,7 +271,9 @@ def bench_layer(args, dev):
         res["metric"] = f"paged-decode KV GB/s (% of HBM peak) + decode tok/s, {args.workload}"
     res.update({"value": round(kv_gbs, 1), "ms_per_step": round(step_ms, 4)})
     res["config"].update({"kv_bytes_per_call": kv_bytes, "kv_bytes_basis":
-                          "distinct (physical) tokens" if shared else "every cached token",
+                          "distinct (physical) tokens" if shared else
+                          (f"last {window} tokens of each sequence" if window else "every cached token"),
+                          "window": window,
                           "scrub_mib_between_steps": 0 if args.no_scrub else SCRUB_BYTES >> 20})
     res.update({
         "hbm_peak_frac": round(kv_gbs / HBM_PEAK_GBS, 4),
@@ -275,7 +295,7 @@ def bench_layer(args, dev):
         res["logical_kv_gbs"] = round(logical_kv / dec_s / 1e9, 1)
         res["logical_kv_bytes_per_call"] = logical_kv
     if not args.skip_cpu:
-        res["cpu_baseline"] = cpu_baseline(w, t, out)
+        res["cpu_baseline"] = cpu_baseline(w, t, out, window=window)
     return res
 
 
