@@ -108,6 +108,8 @@ def measured_traffic(workload="llama70b_layer_bs64"):
     """HBM bytes per decode launch from the committed rocprofv3 counter
     summary of this workload, or None when there is none or the kernel
     sources changed since it was taken."""
+    if workload not in TRAFFIC_PROFILES:
+        return None
     path = os.path.join(ROOT, TRAFFIC_PROFILES[workload])
     if not os.path.exists(path):
         return None
