@@ -34,6 +34,12 @@ Other workloads (--workload), each on the same 70B layer shape:
                        70B layer's bf16 pool (block 16): `value` is bytes read
                        plus written per call / time; also the host block
                        manager's add_sequence / append_token rates
+  swap_blocks_llama70b pa_swap_out then pa_swap_in of 1,024 blocks (64 MiB of
+                       K+V) through pinned host memory: `value` is bytes moved
+                       per direction / time (bound by the host link, PCIe 5.0
+                       x16, 64 GB/s per direction); also the default batch's
+                       decode timed alone and with a swap in flight on a
+                       second stream
 
 Prints exactly one JSON line on stdout; everything else goes to stderr.
 """
@@ -62,7 +68,9 @@ HBM_PEAK_GBS = 8000.0
 MODEL_LAYERS = 80
 SCRUB_BYTES = 512 << 20
 WORKLOADS = {"llama70b_layer_bs64": 2, "prefix_shared_bs256": 3, "long_context_128k": 4,
-             "fp8_80layer_bs128": 5, "copy_blocks_llama70b": 2, "sliding_window_llama70b": 2}
+             "fp8_80layer_bs128": 5, "copy_blocks_llama70b": 2, "sliding_window_llama70b": 2,
+             "swap_blocks_llama70b": 2}
+HOST_LINK_GBS = 64.0  # PCIe 5.0 x16, per direction: 32 GT/s x 16 lanes / 8 bits
 LOCAL_WINDOW = 1024   # a local layer's window ("KV Cache Engineering for LLM Serving", section 3)
 
 
@@ -471,6 +479,112 @@ def bench_copy_blocks(args, dev):
     return res
 
 
+def bench_swap(args, dev):
+    """pa_swap_out / pa_swap_in of 1,024 blocks of the 70B layer's pool, and
+    the default batch's decode with a swap running beside it on a second
+    stream (the overlap the swapping design relies on)."""
+    w = W.config(2)
+    Hkv, D, BS = w.num_kv_heads, w.head_dim, w.block_size
+    n = 1024
+    block_bytes = Hkv * BS * D * 2
+    # The pool has n spare blocks past the ones the batch's tables use: the
+    # swap-in lands there, so the concurrent decode never reads a block that
+    # is being written.
+    t = w.make_tensors(dev, poison=False)
+    extra = n * Hkv * BS * D
+    kc = torch.cat([t["k_cache"][0].reshape(-1), torch.zeros(extra, dtype=torch.bfloat16, device=dev)])
+    vc = torch.cat([t["v_cache"][0].reshape(-1), torch.zeros(extra, dtype=torch.bfloat16, device=dev)])
+    del t["k_cache"], t["v_cache"]
+    rng = np.random.default_rng(3)
+    out_ids = torch.from_numpy(rng.permutation(w.num_blocks)[:n].astype(np.int32)).to(dev)
+    in_ids = torch.from_numpy((w.num_blocks + rng.permutation(n)).astype(np.int32)).to(dev)
+    nbytes = 2 * n * block_bytes
+    host = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    kw = dict(num_kv_heads=Hkv, head_dim=D, block_size=BS)
+    bt = torch.from_numpy(w.block_tables).to(dev)
+    sl = torch.from_numpy(w.seq_lens).to(dev)
+    q = t["q"][0]
+    out = torch.empty((w.num_seqs, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    ws = torch.zeros(pa.pa_decode_workspace_size(w.num_blocks + n, BS, Hkv, D, w.num_seqs, w.num_q_heads,
+                                                 w.max_blocks_per_seq, 0), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    side = torch.cuda.Stream(dev)
+    scrub = torch.ones(SCRUB_BYTES // 4, dtype=torch.float32, device=dev)
+    sink = torch.zeros((), dtype=torch.float32, device=dev)
+
+    def swap_out():
+        pa.pa_swap_out(kc, vc, out_ids, host, **kw)
+
+    def swap_in():
+        pa.pa_swap_in(kc, vc, in_ids, host, **kw)
+
+    def decode():
+        pa.pa_decode(q, kc, vc, bt, sl, w.scale, out, num_kv_heads=Hkv, block_size=BS, workspace=ws)
+
+    for _ in range(args.warmup):
+        swap_out()
+        swap_in()
+        decode()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    for i in range(K):
+        ev[i][0].record(stream)
+        swap_out()
+        ev[i][1].record(stream)
+        swap_in()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    out_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    in_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
+
+    # Decode alone, then decode with a swap-out + swap-in on the side stream.
+    def timed_decodes(with_swap):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+        side_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+        for i in range(K):
+            if not args.no_scrub:
+                torch.sum(scrub, dim=0, out=sink)
+            side.wait_stream(stream)
+            evs[i][0].record(stream)
+            if with_swap:
+                with torch.cuda.stream(side):
+                    side_ev[i][0].record(side)
+                    swap_out()
+                    swap_in()
+                    side_ev[i][1].record(side)
+            decode()
+            evs[i][1].record(stream)
+            stream.wait_stream(side)
+        torch.cuda.synchronize()
+        dec = np.array([e[0].elapsed_time(e[1]) for e in evs])
+        sw = np.array([e[0].elapsed_time(e[1]) for e in side_ev]) if with_swap else None
+        return dec, sw
+
+    dec_alone, _ = timed_decodes(False)
+    dec_busy, swap_busy = timed_decodes(True)
+    out_gbs = nbytes / (out_ms.mean() / 1e3) / 1e9
+    in_gbs = nbytes / (in_ms.mean() / 1e3) / 1e9
+    gbs = 2 * nbytes / ((out_ms + in_ms).mean() / 1e3) / 1e9
+    res = base_record(args, w, K)
+    res["metric"] = "pa_swap_out + pa_swap_in GB/s per direction (pinned host), 70B layer pool"
+    res.update({"value": round(gbs, 2), "ms_per_step": round(float((out_ms + in_ms).mean()), 4)})
+    res["config"].update({"workload": args.workload, "blocks": n, "block_bytes_per_cache": block_bytes,
+                          "bytes_per_direction": nbytes, "partition_tokens": 0})
+    res.update({
+        "swap_out": {"ms": round(float(out_ms.mean()), 4), "gbs": round(out_gbs, 2)},
+        "swap_in": {"ms": round(float(in_ms.mean()), 4), "gbs": round(in_gbs, 2)},
+        "overlap": {"decode_alone_us": round(float(dec_alone.mean()) * 1e3, 2),
+                    "decode_with_swap_us": round(float(dec_busy.mean()) * 1e3, 2),
+                    "swap_beside_decode_ms": round(float(swap_busy.mean()), 4)},
+        "roofline": {"bound": "host_link", "achieved": round(gbs, 2), "peak": HOST_LINK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HOST_LINK_GBS, 4), "traffic": None,
+                     "kernel": "move_blocks_kernel on a capped grid (pa_swap_out / pa_swap_in are one launch each)",
+                     "bytes_per_launch": nbytes},
+    })
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -496,6 +610,8 @@ def main():
         res = bench_model_step(args, dev)
     elif args.workload == "copy_blocks_llama70b":
         res = bench_copy_blocks(args, dev)
+    elif args.workload == "swap_blocks_llama70b":
+        res = bench_swap(args, dev)
     else:
         res = bench_layer(args, dev)
     print(json.dumps(res), flush=True)

@@ -75,7 +75,9 @@ typedef enum pa_status {
   PA_ERR_LAUNCH = -5,      /* the HIP runtime reported an error                */
   PA_ERR_DEVICE = -6,      /* no gfx950 device current, or a query failed      */
   PA_ERR_NO_BLOCKS = -7,   /* block manager: the free list is too short         */
-  PA_ERR_NOT_FOUND = -8    /* block manager: unknown (or already used) seq id   */
+  PA_ERR_NOT_FOUND = -8,   /* block manager: unknown (or already used) seq id   */
+  PA_ERR_SWAPPED = -9,     /* block manager: the sequence is (not) swapped out  */
+  PA_ERR_HOST_MEMORY = -10 /* a host buffer is not pinned (hipHostMalloc) memory */
 } pa_status;
 
 /* Geometry of one layer's KV cache.

@@ -85,6 +85,29 @@ pa_status pa_bm_free_sequence(pa_block_manager* bm, int64_t seq);
  * the released entries.  *released (may be NULL) receives the count.        */
 pa_status pa_bm_trim(pa_block_manager* bm, int64_t seq, int32_t keep_tokens, int32_t* released);
 
+/* Swap-out bookkeeping: the blocks of `seq` that no other sequence holds
+ * (reference count 1) are listed, in table order, in blocks[0..*n) and
+ * released to the free list (their keys dropped); their table entries become
+ * -2 (swapped).  Shared blocks stay with the sequence, since a prefix other
+ * sequences use is the last thing to move out ("Taming the token torrent",
+ * "The Swapping Mechanism").  The caller copies the listed blocks out with
+ * pa_swap_out on its stream before anything it enqueues later can write
+ * them.  A swapped sequence cannot be appended to, forked, trimmed or
+ * batched until pa_bm_swap_in (PA_ERR_SWAPPED).  PA_ERR_SHAPE, with nothing
+ * changed, if more than `capacity` blocks would be listed.                   */
+pa_status pa_bm_swap_out(pa_block_manager* bm, int64_t seq, int32_t* blocks, int32_t capacity,
+                         int32_t* n);
+
+/* Swap-in bookkeeping: each swapped entry of `seq`, in table order, gets a
+ * block from the free list, listed in blocks[0..*n) in the same order as
+ * pa_bm_swap_out listed the blocks it replaced, so the host copy's i-th
+ * block goes to blocks[i] (pa_swap_in).  A full block is stored under its
+ * prefix key again unless an equal block is stored.  PA_ERR_NO_BLOCKS or
+ * PA_ERR_SHAPE (capacity), with nothing changed; PA_ERR_SWAPPED if `seq` is
+ * not swapped out.                                                          */
+pa_status pa_bm_swap_in(pa_block_manager* bm, int64_t seq, int32_t* blocks, int32_t capacity,
+                        int32_t* n);
+
 /* Free blocks (or -1 for a NULL manager).                                    */
 int32_t pa_bm_num_free(const pa_block_manager* bm);
 
@@ -123,6 +146,30 @@ pa_status pa_bm_batch(const pa_block_manager* bm, const int64_t* seqs, int32_t n
  * pairs of pa_bm_append_token always satisfy this.                          */
 pa_status pa_copy_blocks(const pa_cache_desc* cache, int32_t elem_bytes, void* k_cache,
                          void* v_cache, const int32_t* pairs, int32_t num_pairs, void* stream);
+
+/* Swap blocks out to host memory: blocks[i] of k_cache and v_cache (for
+ * i < num_blocks; DEVICE int32 array) are copied into `host`, which holds the
+ * K blocks in list order, then the V blocks: 2 * num_blocks * block_bytes
+ * bytes, block_bytes = num_kv_heads * block_size * head_dim * elem_bytes.
+ * `host` must be pinned memory from hipHostMalloc (any offset into such an
+ * allocation), else PA_ERR_HOST_MEMORY: a kernel on `stream` writes it
+ * directly through its device mapping, so there is no staging buffer and no
+ * separate DMA step.  The call returns without waiting; the host copy is
+ * complete when the stream's work is.  Ids outside [0, num_blocks of the
+ * cache) are skipped (their slots of `host` are left as they were).  The
+ * kernel occupies a small fixed grid, so it can run on a second stream
+ * beside decode work on another ("Taming the token torrent", "The Swapping
+ * Mechanism": the copy back is hidden under the first layers' work).        */
+pa_status pa_swap_out(const pa_cache_desc* cache, int32_t elem_bytes, const void* k_cache,
+                      const void* v_cache, const int32_t* blocks, int32_t num_blocks, void* host,
+                      void* stream);
+
+/* Swap blocks back in: the reverse of pa_swap_out.  The i-th K and V blocks
+ * of `host` (pinned, laid out as pa_swap_out writes it) become blocks[i] of
+ * k_cache and v_cache; ids outside [0, num_blocks of the cache) are skipped.
+ * The host buffer must not change until the stream's work is complete.     */
+pa_status pa_swap_in(const pa_cache_desc* cache, int32_t elem_bytes, void* k_cache, void* v_cache,
+                     const int32_t* blocks, int32_t num_blocks, const void* host, void* stream);
 
 #ifdef __cplusplus
 }

@@ -19,6 +19,10 @@ What a block manager does, from the pages:
 * A local (sliding-window) layer keeps only its most recent positions, so the
   blocks that hold nothing newer can go back to the pool ("KV Cache
   Engineering for LLM Serving", section 3): ``trim``.
+* Blocks a paused sequence does not need can move to host memory and come
+  back when it resumes ("KV Cache Engineering for LLM Serving", section 12,
+  Cache Offloading); the blocks of a shared prefix stay on the GPU ("Taming
+  the token torrent", "The Swapping Mechanism"): ``swap_out`` / ``swap_in``.
 * A reused block gets its reference count incremented instead of new memory;
   when one user writes tokens of its own into a block others still hold, it
   first gets a private copy: copy-on-write ("Taming the token torrent",
@@ -31,9 +35,18 @@ about.  Only full blocks are ever stored under a key; a sequence's partly
 filled last block is private unless the sequence was forked.
 """
 
+import numpy as np
+
 
 class OutOfBlocks(Exception):
     pass
+
+
+class Swapped(Exception):
+    """The operation needs a resident sequence (or a swapped one)."""
+
+
+SWAPPED = -2   # table entry of a block moved to host memory
 
 
 class BlockManager:
@@ -101,7 +114,7 @@ class BlockManager:
             table.append(self._take())
         self.hits += reused
         self.misses += len(table) - reused
-        self.seqs[seq] = {"tokens": list(tokens), "table": table, "model": model}
+        self.seqs[seq] = {"tokens": list(tokens), "table": table, "model": model, "swapped": False}
         return reused
 
     def fork(self, parent, child):
@@ -110,17 +123,21 @@ class BlockManager:
         if child in self.seqs:
             raise KeyError(child)
         p = self.seqs[parent]
+        if p["swapped"]:
+            raise Swapped(parent)
         for b in p["table"]:
             if b >= 0:
                 self.ref[b] += 1
         self.seqs[child] = {"tokens": list(p["tokens"]), "table": list(p["table"]),
-                            "model": p["model"]}
+                            "model": p["model"], "swapped": False}
 
     def append_token(self, seq, token):
         """One generated token.  Returns (slot, copy_src, copy_dst): the slot
         the token's K/V go to, and the block copy that must happen first
         (-1, -1 when none)."""
         s = self.seqs[seq]
+        if s["swapped"]:
+            raise Swapped(seq)
         bs = self.block_size
         pos = len(s["tokens"])
         src = dst = -1
@@ -149,6 +166,8 @@ class BlockManager:
         if keep < 1:
             raise ValueError("keep must be >= 1")
         s = self.seqs[seq]
+        if s["swapped"]:
+            raise Swapped(seq)
         bs = self.block_size
         first = max(len(s["tokens"]) - keep, 0) // bs   # first block with a kept position
         n = 0
@@ -158,6 +177,42 @@ class BlockManager:
                 s["table"][i] = -1
                 n += 1
         return n
+
+    def swap_out(self, seq):
+        """Release the blocks only ``seq`` holds, in table order, marking
+        their entries SWAPPED; returns those blocks (the ones to copy out)."""
+        s = self.seqs[seq]
+        if s["swapped"]:
+            raise Swapped(seq)
+        out = []
+        for i, b in enumerate(s["table"]):
+            if b >= 0 and self.ref[b] == 1:
+                out.append(b)
+                self._release(b)
+                s["table"][i] = SWAPPED
+        s["swapped"] = True
+        return out
+
+    def swap_in(self, seq):
+        """Give every SWAPPED entry a block from the free list, in table
+        order; a full block goes back under its prefix key unless an equal
+        block is stored.  Returns the new blocks in that order."""
+        s = self.seqs[seq]
+        if not s["swapped"]:
+            raise Swapped(seq)
+        idx = [i for i, b in enumerate(s["table"]) if b == SWAPPED]
+        if len(idx) > len(self.free):
+            raise OutOfBlocks(f"need {len(idx)} blocks, {len(self.free)} free")
+        bs = self.block_size
+        out = []
+        for i in idx:
+            b = self._take()
+            s["table"][i] = b
+            out.append(b)
+            if (i + 1) * bs <= len(s["tokens"]):
+                self._store(b, self._key(s["model"], s["tokens"], (i + 1) * bs))
+        s["swapped"] = False
+        return out
 
     def free_sequence(self, seq):
         s = self.seqs.pop(seq)
@@ -183,3 +238,19 @@ def copy_blocks(k_cache, v_cache, pairs, block_elems):
     for src, dst in pairs:
         for c in (k_cache, v_cache):
             c[dst * block_elems:(dst + 1) * block_elems] = c[src * block_elems:(src + 1) * block_elems]
+
+
+def swap_image(k_cache, v_cache, blocks, block_elems):
+    """The host copy of a swap-out: the K blocks named by ``blocks``, in list
+    order, followed by the V blocks in the same order."""
+    return np.concatenate([c[b * block_elems:(b + 1) * block_elems] for c in (k_cache, v_cache)
+                           for b in blocks] or [k_cache[:0]])
+
+
+def swap_restore(k_cache, v_cache, blocks, image, block_elems):
+    """The swap-in of a host copy: its i-th K and V blocks become block
+    blocks[i] of each cache."""
+    n = len(blocks)
+    for i, b in enumerate(blocks):
+        k_cache[b * block_elems:(b + 1) * block_elems] = image[i * block_elems:(i + 1) * block_elems]
+        v_cache[b * block_elems:(b + 1) * block_elems] = image[(n + i) * block_elems:(n + i + 1) * block_elems]

@@ -33,7 +33,8 @@ LIB_PATH = os.path.join(_HERE, "lib", "libpa.so")
 PA_OK = 0
 _STATUS = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_UNSUPPORTED",
            -4: "PA_ERR_WORKSPACE", -5: "PA_ERR_LAUNCH", -6: "PA_ERR_DEVICE",
-           -7: "PA_ERR_NO_BLOCKS", -8: "PA_ERR_NOT_FOUND"}
+           -7: "PA_ERR_NO_BLOCKS", -8: "PA_ERR_NOT_FOUND", -9: "PA_ERR_SWAPPED",
+           -10: "PA_ERR_HOST_MEMORY"}
 
 
 class PagedAttentionError(RuntimeError):
@@ -80,6 +81,10 @@ def _load():
                                 ctypes.POINTER(i32)], i32),
         "pa_bm_free_sequence": ([vp, i64], i32),
         "pa_bm_trim": ([vp, i64, i32, ctypes.POINTER(i32)], i32),
+        "pa_bm_swap_out": ([vp, i64, ctypes.POINTER(i32), i32, ctypes.POINTER(i32)], i32),
+        "pa_bm_swap_in": ([vp, i64, ctypes.POINTER(i32), i32, ctypes.POINTER(i32)], i32),
+        "pa_swap_out": ([dp, i32, vp, vp, vp, i32, vp, vp], i32),
+        "pa_swap_in": ([dp, i32, vp, vp, vp, i32, vp, vp], i32),
         "pa_decode_window": ([dp, vp, i32, i32, vp, vp, vp, i32, vp, i32, f32, vp, i32, vp, sz, vp], i32),
         "pa_decode_window_fp8": ([dp, vp, i32, i32, vp, vp, vp, i32, vp, i32, f32, f32, f32, vp, i32, vp,
                                   sz, vp], i32),
@@ -286,6 +291,41 @@ def pa_copy_blocks(k_cache, v_cache, pairs, *, num_kv_heads, head_dim, block_siz
     _check("pa_copy_blocks", st)
 
 
+def _swap(out, k_cache, v_cache, blocks, host, num_kv_heads, head_dim, block_size):
+    dev = k_cache.device
+    _need(k_cache, "k_cache", k_cache.dtype, dev)
+    _need(v_cache, "v_cache", k_cache.dtype, dev, shape=tuple(k_cache.shape))
+    _need(blocks, "blocks", torch.int32, dev, 1)
+    if not isinstance(host, torch.Tensor) or host.device.type != "cpu" or not host.is_contiguous() \
+            or host.dtype != torch.uint8:
+        raise ValueError("host must be a contiguous uint8 CPU tensor in pinned memory")
+    desc = make_desc(k_cache, num_kv_heads, head_dim, block_size)
+    eb = 2 if k_cache.dtype == torch.bfloat16 else 1
+    need = 2 * blocks.numel() * num_kv_heads * block_size * head_dim * eb
+    if host.numel() < need:
+        raise ValueError(f"host buffer holds {host.numel()} bytes, {need} needed")
+    L = _load()
+    fn = L.pa_swap_out if out else L.pa_swap_in
+    with torch.cuda.device(dev):
+        st = fn(ctypes.byref(desc), eb, _ptr(k_cache), _ptr(v_cache), _ptr(blocks), blocks.numel(),
+                ctypes.c_void_p(host.data_ptr()), _stream(k_cache))
+    _check("pa_swap_out" if out else "pa_swap_in", st)
+
+
+def pa_swap_out(k_cache, v_cache, blocks, host, *, num_kv_heads, head_dim, block_size):
+    """Copy blocks (int32 device tensor) of both caches into `host` (uint8
+    CPU tensor in pinned memory, e.g. torch.empty(..., pin_memory=True)): the
+    K blocks in list order, then the V blocks.  Asynchronous on the current
+    stream.  See include/pa_blocks.h."""
+    _swap(True, k_cache, v_cache, blocks, host, num_kv_heads, head_dim, block_size)
+
+
+def pa_swap_in(k_cache, v_cache, blocks, host, *, num_kv_heads, head_dim, block_size):
+    """Copy the i-th K and V blocks of `host` (as pa_swap_out wrote it) into
+    blocks[i] of the caches.  Asynchronous on the current stream."""
+    _swap(False, k_cache, v_cache, blocks, host, num_kv_heads, head_dim, block_size)
+
+
 class BlockManager:
     """Host block manager of include/pa_blocks.h (FIFO free list, reference
     counts, exact prefix keys with a model key, fork, copy-on-write).  Thin
@@ -338,6 +378,24 @@ class BlockManager:
         n = ctypes.c_int32()
         _check("pa_bm_trim", _load().pa_bm_trim(self._h, seq, keep_tokens, ctypes.byref(n)))
         return n.value
+
+    def swap_out(self, seq):
+        """Release the blocks only `seq` holds; returns them (to copy out
+        with pa_swap_out), in table order."""
+        n = ctypes.c_int32()
+        cap = len(self.table(seq))
+        out = (ctypes.c_int32 * max(cap, 1))()
+        _check("pa_bm_swap_out", _load().pa_bm_swap_out(self._h, seq, out, cap, ctypes.byref(n)))
+        return list(out[:n.value])
+
+    def swap_in(self, seq):
+        """New blocks for the swapped entries of `seq` (for pa_swap_in), in
+        the order swap_out listed the blocks they replace."""
+        n = ctypes.c_int32()
+        cap = len(self.table(seq))
+        out = (ctypes.c_int32 * max(cap, 1))()
+        _check("pa_bm_swap_in", _load().pa_bm_swap_in(self._h, seq, out, cap, ctypes.byref(n)))
+        return list(out[:n.value])
 
     def num_free(self):
         return _load().pa_bm_num_free(self._h)

@@ -20,6 +20,15 @@ constexpr int kChunkMinAuto = 16;  // at least 256 tokens per wavefront when spl
 #ifndef PA_DECODE_OVERSUB
 #define PA_DECODE_OVERSUB 1
 #endif
+// Workgroups of a swap to or from host memory.  Each keeps 16 KiB of
+// requests in flight; 8 of them (128 KiB) keep the host link at 51-57 GB/s
+// on MI355X.  More add no throughput: the extra requests only queue in the
+// memory system, where they hold up the HBM reads of a decode running beside
+// the swap (measured: a 64 MiB swap-out next to the 70B-layer decode slows
+// it 1.6x at 8 workgroups, 5x at 16 or more).
+#ifndef PA_SWAP_GROUPS
+#define PA_SWAP_GROUPS 8
+#endif
 
 struct DeviceInfo {
   bool queried = false;
@@ -194,6 +203,43 @@ pa_status decode(const pa_cache_desc* cache, const void* q, int32_t num_seqs, in
   return PA_OK;
 }
 
+// Shared checks of the block copy / swap entry points: block bytes of the
+// cache layout, and a launch grid (items * 2 caches * 16 KiB segments) that
+// fits.
+pa_status block_move_check(const pa_cache_desc* cache, int32_t elem_bytes, int32_t n,
+                           int64_t* block_bytes) {
+  if (!cache) return PA_ERR_NULL;
+  pa_status st = desc_status(cache);
+  if (st != PA_OK) return st;
+  if (elem_bytes != 1 && elem_bytes != 2) return PA_ERR_UNSUPPORTED;
+  if (n < 0) return PA_ERR_SHAPE;
+  *block_bytes = (int64_t)cache->num_kv_heads * cache->block_size * cache->head_dim * elem_bytes;
+  if ((int64_t)n * 2 * ((*block_bytes + 16383) / 16384) > INT32_MAX) return PA_ERR_SHAPE;
+  return PA_OK;
+}
+
+// The device address of pinned host memory (hipHostMalloc); false for any
+// other pointer.  The failed query's error is cleared so that it is not
+// reported by a later launch check.
+bool host_mapping(const void* host, uint8_t** mapped) {
+  void* d = nullptr;
+  if (hipHostGetDevicePointer(&d, const_cast<void*>(host), 0) != hipSuccess || !d) {
+    (void)hipGetLastError();
+    return false;
+  }
+  *mapped = static_cast<uint8_t*>(d);
+  return true;
+}
+
+pa::BlockMoveParams block_move_params(int64_t block_bytes, int32_t n) {
+  pa::BlockMoveParams p{};
+  p.block_bytes = block_bytes;
+  p.segs = (int32_t)((block_bytes + 16383) / 16384);
+  p.last_words = (int32_t)((block_bytes - (int64_t)(p.segs - 1) * 16384) / 16);
+  p.num_items = n;
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -283,28 +329,69 @@ pa_status pa_decode_window_fp8(const pa_cache_desc* cache, const void* q, int32_
 
 pa_status pa_copy_blocks(const pa_cache_desc* cache, int32_t elem_bytes, void* k_cache,
                          void* v_cache, const int32_t* pairs, int32_t num_pairs, void* stream) {
-  if (!cache) return PA_ERR_NULL;
-  pa_status st = desc_status(cache);
-  if (st != PA_OK) return st;
-  if (elem_bytes != 1 && elem_bytes != 2) return PA_ERR_UNSUPPORTED;
-  if (num_pairs < 0) return PA_ERR_SHAPE;
-  // Grid size: num_pairs * 2 * segments workgroups must fit a launch.
-  const int64_t block_bytes = (int64_t)cache->num_kv_heads * cache->block_size * cache->head_dim * elem_bytes;
-  if ((int64_t)num_pairs * 2 * ((block_bytes + 16383) / 16384) > INT32_MAX) return PA_ERR_SHAPE;
-  if (num_pairs == 0) return PA_OK;
+  int64_t block_bytes = 0;
+  pa_status st = block_move_check(cache, elem_bytes, num_pairs, &block_bytes);
+  if (st != PA_OK || num_pairs == 0) return st;
   if (!k_cache || !v_cache || !pairs) return PA_ERR_NULL;
   int resident = 0;
   if (!device_info(128, false, &resident)) return PA_ERR_DEVICE;
-  pa::CopyBlocksParams p;
-  p.k_cache = static_cast<uint8_t*>(k_cache);
-  p.v_cache = static_cast<uint8_t*>(v_cache);
-  p.pairs = pairs;
-  p.block_bytes = block_bytes;
-  p.segs = (int32_t)((block_bytes + 16383) / 16384);
-  p.last_words = (int32_t)((block_bytes - (int64_t)(p.segs - 1) * 16384) / 16);
-  p.num_pairs = num_pairs;
-  p.num_blocks = cache->num_blocks;
-  if (pa::launch_copy_blocks(p, static_cast<hipStream_t>(stream)) != hipSuccess) return PA_ERR_LAUNCH;
+  pa::BlockMoveParams p = block_move_params(block_bytes, num_pairs);
+  p.src_k = p.dst_k = static_cast<uint8_t*>(k_cache);
+  p.src_v = p.dst_v = static_cast<uint8_t*>(v_cache);
+  p.src_ids = pairs;
+  p.dst_ids = pairs + 1;
+  p.id_stride = 2;
+  p.src_blocks = p.dst_blocks = cache->num_blocks;
+  if (pa::launch_move_blocks(p, 0, static_cast<hipStream_t>(stream)) != hipSuccess) return PA_ERR_LAUNCH;
+  return PA_OK;
+}
+
+pa_status pa_swap_out(const pa_cache_desc* cache, int32_t elem_bytes, const void* k_cache,
+                      const void* v_cache, const int32_t* blocks, int32_t num_blocks, void* host,
+                      void* stream) {
+  int64_t block_bytes = 0;
+  pa_status st = block_move_check(cache, elem_bytes, num_blocks, &block_bytes);
+  if (st != PA_OK || num_blocks == 0) return st;
+  if (!k_cache || !v_cache || !blocks || !host) return PA_ERR_NULL;
+  int resident = 0;
+  if (!device_info(128, false, &resident)) return PA_ERR_DEVICE;
+  uint8_t* mapped = nullptr;
+  if (!host_mapping(host, &mapped)) return PA_ERR_HOST_MEMORY;
+  pa::BlockMoveParams p = block_move_params(block_bytes, num_blocks);
+  p.src_k = static_cast<const uint8_t*>(k_cache);
+  p.src_v = static_cast<const uint8_t*>(v_cache);
+  p.dst_k = mapped;
+  p.dst_v = mapped + (size_t)num_blocks * block_bytes;
+  p.src_ids = blocks;
+  p.id_stride = 1;
+  p.src_blocks = cache->num_blocks;
+  p.dst_blocks = num_blocks;
+  if (pa::launch_move_blocks(p, PA_SWAP_GROUPS, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return PA_ERR_LAUNCH;
+  return PA_OK;
+}
+
+pa_status pa_swap_in(const pa_cache_desc* cache, int32_t elem_bytes, void* k_cache, void* v_cache,
+                     const int32_t* blocks, int32_t num_blocks, const void* host, void* stream) {
+  int64_t block_bytes = 0;
+  pa_status st = block_move_check(cache, elem_bytes, num_blocks, &block_bytes);
+  if (st != PA_OK || num_blocks == 0) return st;
+  if (!k_cache || !v_cache || !blocks || !host) return PA_ERR_NULL;
+  int resident = 0;
+  if (!device_info(128, false, &resident)) return PA_ERR_DEVICE;
+  uint8_t* mapped = nullptr;
+  if (!host_mapping(host, &mapped)) return PA_ERR_HOST_MEMORY;
+  pa::BlockMoveParams p = block_move_params(block_bytes, num_blocks);
+  p.src_k = mapped;
+  p.src_v = mapped + (size_t)num_blocks * block_bytes;
+  p.dst_k = static_cast<uint8_t*>(k_cache);
+  p.dst_v = static_cast<uint8_t*>(v_cache);
+  p.dst_ids = blocks;
+  p.id_stride = 1;
+  p.src_blocks = num_blocks;
+  p.dst_blocks = cache->num_blocks;
+  if (pa::launch_move_blocks(p, PA_SWAP_GROUPS, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return PA_ERR_LAUNCH;
   return PA_OK;
 }
 
@@ -319,6 +406,8 @@ const char* pa_status_string(pa_status s) {
     case PA_ERR_DEVICE: return "PA_ERR_DEVICE: no gfx950 device is current";
     case PA_ERR_NO_BLOCKS: return "PA_ERR_NO_BLOCKS: not enough free blocks";
     case PA_ERR_NOT_FOUND: return "PA_ERR_NOT_FOUND: unknown or already used sequence id";
+    case PA_ERR_SWAPPED: return "PA_ERR_SWAPPED: the sequence is swapped out (or not swapped out)";
+    case PA_ERR_HOST_MEMORY: return "PA_ERR_HOST_MEMORY: the host buffer is not pinned (hipHostMalloc) memory";
   }
   return "unknown pa_status";
 }

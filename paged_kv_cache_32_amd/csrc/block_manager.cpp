@@ -61,11 +61,15 @@ struct Prefix {
   PrefixKey key;     // kept to find the entry again by id
 };
 
+constexpr int32_t kReleased = -1;  // table entry released by a sliding-window trim
+constexpr int32_t kSwapped = -2;   // table entry whose block was swapped out
+
 struct Sequence {
   std::vector<int32_t> tokens;
-  std::vector<int32_t> table;       // physical block of each logical block
+  std::vector<int32_t> table;       // physical block of each logical block (or kReleased / kSwapped)
   std::vector<uint64_t> prefixes;   // prefix id of each full block
   uint64_t model;
+  bool swapped = false;
 };
 
 }  // namespace
@@ -225,6 +229,7 @@ pa_status pa_bm_fork(pa_block_manager* bm, int64_t parent, int64_t child) {
   if (!bm) return PA_ERR_NULL;
   auto it = bm->seqs.find(parent);
   if (it == bm->seqs.end() || bm->seqs.count(child)) return PA_ERR_NOT_FOUND;
+  if (it->second.swapped) return PA_ERR_SWAPPED;
   Sequence c = it->second;
   for (int32_t b : c.table)
     if (b >= 0) bm->ref[b]++;
@@ -239,6 +244,7 @@ pa_status pa_bm_append_token(pa_block_manager* bm, int64_t seq, int32_t token, i
   auto it = bm->seqs.find(seq);
   if (it == bm->seqs.end()) return PA_ERR_NOT_FOUND;
   Sequence& s = it->second;
+  if (s.swapped) return PA_ERR_SWAPPED;
   const int32_t bs = bm->block_size;
   const int64_t pos = (int64_t)s.tokens.size();
   const bool new_block = pos % bs == 0;
@@ -283,17 +289,67 @@ pa_status pa_bm_trim(pa_block_manager* bm, int64_t seq, int32_t keep_tokens, int
   auto it = bm->seqs.find(seq);
   if (it == bm->seqs.end()) return PA_ERR_NOT_FOUND;
   Sequence& s = it->second;
+  if (s.swapped) return PA_ERR_SWAPPED;
   const int64_t n = (int64_t)s.tokens.size();
   const int64_t first = (n > keep_tokens ? n - keep_tokens : 0) / bm->block_size;
   int32_t count = 0;
   for (int64_t i = 0; i < first; ++i) {
     if (s.table[i] >= 0) {
       bm->release(s.table[i]);
-      s.table[i] = -1;
+      s.table[i] = kReleased;
       ++count;
     }
   }
   if (released) *released = count;
+  return PA_OK;
+}
+
+pa_status pa_bm_swap_out(pa_block_manager* bm, int64_t seq, int32_t* blocks, int32_t capacity,
+                         int32_t* n) {
+  if (!bm || !n || (!blocks && capacity > 0)) return PA_ERR_NULL;
+  auto it = bm->seqs.find(seq);
+  if (it == bm->seqs.end()) return PA_ERR_NOT_FOUND;
+  Sequence& s = it->second;
+  if (s.swapped) return PA_ERR_SWAPPED;
+  int32_t count = 0;
+  for (int32_t b : s.table)
+    if (b >= 0 && bm->ref[b] == 1) ++count;
+  if (count > capacity) return PA_ERR_SHAPE;
+  int32_t k = 0;
+  for (int32_t& b : s.table) {
+    if (b >= 0 && bm->ref[b] == 1) {
+      blocks[k++] = b;
+      bm->release(b);
+      b = kSwapped;
+    }
+  }
+  s.swapped = true;
+  *n = count;
+  return PA_OK;
+}
+
+pa_status pa_bm_swap_in(pa_block_manager* bm, int64_t seq, int32_t* blocks, int32_t capacity,
+                        int32_t* n) {
+  if (!bm || !n || (!blocks && capacity > 0)) return PA_ERR_NULL;
+  auto it = bm->seqs.find(seq);
+  if (it == bm->seqs.end()) return PA_ERR_NOT_FOUND;
+  Sequence& s = it->second;
+  if (!s.swapped) return PA_ERR_SWAPPED;
+  int32_t count = 0;
+  for (int32_t b : s.table)
+    if (b == kSwapped) ++count;
+  if (count > capacity) return PA_ERR_SHAPE;
+  if (count > (int32_t)bm->free_list.size()) return PA_ERR_NO_BLOCKS;
+  int32_t k = 0;
+  for (size_t i = 0; i < s.table.size(); ++i) {
+    if (s.table[i] != kSwapped) continue;
+    const int32_t b = bm->take();
+    s.table[i] = b;
+    blocks[k++] = b;
+    if (i < s.prefixes.size()) bm->store(b, s.prefixes[i]);
+  }
+  s.swapped = false;
+  *n = count;
   return PA_OK;
 }
 
@@ -345,6 +401,7 @@ pa_status pa_bm_batch(const pa_block_manager* bm, const int64_t* seqs, int32_t n
   for (int32_t i = 0; i < n; ++i) {
     auto it = bm->seqs.find(seqs[i]);
     if (it == bm->seqs.end()) return PA_ERR_NOT_FOUND;
+    if (it->second.swapped) return PA_ERR_SWAPPED;
     if ((int64_t)it->second.table.size() > max_blocks) return PA_ERR_SHAPE;
   }
   for (int32_t i = 0; i < n; ++i) {

@@ -48,21 +48,27 @@ struct DecodeParams {
   float out_scale;              // 1 (bf16) or v_scale (fp8)
 };
 
-struct CopyBlocksParams {
-  uint8_t* k_cache;
-  uint8_t* v_cache;
-  const int32_t* pairs;         // [num_pairs][2] {src, dst}
+struct BlockMoveParams {
+  const uint8_t* src_k;         // source buffers (caches, or pinned host memory)
+  const uint8_t* src_v;
+  uint8_t* dst_k;               // destination buffers
+  uint8_t* dst_v;
+  const int32_t* src_ids;       // item i reads block src_ids[i * id_stride] (null: block i)
+  const int32_t* dst_ids;       // item i writes block dst_ids[i * id_stride] (null: block i)
   int64_t block_bytes;          // Hkv * block_size * head_dim * element bytes
+  int32_t id_stride;
   int32_t segs;                 // 16 KiB segments per block (the last may be shorter)
   int32_t last_words;           // 16-byte words in a block's last segment
-  int32_t num_pairs, num_blocks;
+  int32_t num_items, src_blocks, dst_blocks;
 };
 
 // Host-side launchers (defined next to their kernels).
 hipError_t launch_cache_write(const CacheWriteParams& p, bool fp8, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, bool fp8, hipStream_t stream);
 hipError_t launch_zero(void* ptr, size_t bytes, hipStream_t stream);
-hipError_t launch_copy_blocks(const CopyBlocksParams& p, hipStream_t stream);
+// max_groups > 0 caps the grid (the workgroups then stride over the
+// segments); 0 launches one workgroup per segment.
+hipError_t launch_move_blocks(const BlockMoveParams& p, int max_groups, hipStream_t stream);
 // Resident wavefronts of the decode kernel on the current device (0 on error).
 int decode_resident_waves(int head_dim, bool fp8);
 

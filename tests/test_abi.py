@@ -16,7 +16,7 @@ HEADERS = [os.path.join(ROOT, "include", h) for h in ("pa.h", "pa_blocks.h")]
 if not os.path.exists(pa.LIB_PATH):
     pytest.skip("libpa.so not built", allow_module_level=True)
 
-OK, NULL, SHAPE, UNSUP, WS, LAUNCH, DEVICE, NO_BLOCKS, NOT_FOUND = 0, -1, -2, -3, -4, -5, -6, -7, -8
+OK, NULL, SHAPE, UNSUP, WS, LAUNCH, DEVICE, NO_BLOCKS, NOT_FOUND, SWAPPED, HOST_MEMORY = range(0, -11, -1)
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
 
 
@@ -37,7 +37,8 @@ def test_exports_every_declared_symbol():
     names = declared()
     assert set(names) >= {"pa_cache_write", "pa_cache_write_fp8", "pa_decode", "pa_decode_fp8",
                           "pa_decode_workspace_size", "pa_status_string", "pa_abi_version",
-                          "pa_copy_blocks", "pa_bm_create", "pa_bm_append_token", "pa_bm_batch"}
+                          "pa_copy_blocks", "pa_swap_out", "pa_swap_in", "pa_bm_create",
+                          "pa_bm_append_token", "pa_bm_batch", "pa_bm_swap_out", "pa_bm_swap_in"}
     for n in names:
         assert hasattr(lib, n), n
     assert lib.pa_abi_version() == 2
@@ -45,7 +46,7 @@ def test_exports_every_declared_symbol():
 
 def test_status_strings():
     lib = pa.lib()
-    for code in (OK, NULL, SHAPE, UNSUP, WS, LAUNCH, DEVICE, NO_BLOCKS, NOT_FOUND):
+    for code in (OK, NULL, SHAPE, UNSUP, WS, LAUNCH, DEVICE, NO_BLOCKS, NOT_FOUND, SWAPPED, HOST_MEMORY):
         s = lib.pa_status_string(code).decode()
         assert s.startswith(pa._STATUS[code])
     assert lib.pa_status_string(42).decode() == "unknown pa_status"
@@ -125,6 +126,21 @@ def test_copy_blocks_validation():
     assert lib.pa_copy_blocks(ctypes.byref(bad), 2, FAKE, FAKE, FAKE, 1, None) == UNSUP
 
 
+@pytest.mark.parametrize("name", ["pa_swap_out", "pa_swap_in"])
+def test_swap_validation(name):
+    fn = getattr(pa.lib(), name)
+    d = desc()
+    ok = (ctypes.byref(d), 2, FAKE, FAKE, FAKE, 3, FAKE, None)
+    assert fn(None, *ok[1:]) == NULL
+    assert fn(ctypes.byref(d), 4, *ok[2:]) == UNSUP
+    assert fn(*ok[:5], -1, *ok[6:]) == SHAPE
+    assert fn(*ok[:5], 0, None, None) == OK           # nothing to move
+    assert fn(*ok[:6], None, None) == NULL            # no host buffer
+    assert fn(*ok[:4], None, *ok[5:]) == NULL
+    bad = desc(bs=0)
+    assert fn(ctypes.byref(bad), *ok[1:]) == SHAPE
+
+
 def test_device_errors_without_gpu():
     import torch
     if torch.cuda.is_available():
@@ -136,6 +152,8 @@ def test_device_errors_without_gpu():
     assert pa.lib().pa_decode_workspace_size(ctypes.byref(d), 2, 16, 4, 0) == 0
     assert pa.lib().pa_decode_workspace_init(FAKE, 64, None) == DEVICE
     assert pa.lib().pa_copy_blocks(ctypes.byref(d), 2, FAKE, FAKE, FAKE, 1, None) == DEVICE
+    for fn in (pa.lib().pa_swap_out, pa.lib().pa_swap_in):
+        assert fn(ctypes.byref(d), 2, FAKE, FAKE, FAKE, 1, FAKE, None) == DEVICE
 
 
 def test_binding_fails_loudly_without_library(monkeypatch):

@@ -1,7 +1,8 @@
 """The native block manager (host C++ behind include/pa_blocks.h) against the
 oracle's model: the pages' traces, error paths, and long random operation
-sequences compared step by step (tables, slots, copies, reference counts,
-free list length).  Host logic only: no GPU is used."""
+sequences (with trims and swaps) compared step by step (tables, slots,
+copies, swapped block lists, reference counts, free list length).  Host
+logic only: no GPU is used."""
 
 import os
 import random
@@ -14,7 +15,7 @@ from oracle import blocks as B
 if not os.path.exists(pa.LIB_PATH):
     pytest.skip("libpa.so not built", allow_module_level=True)
 
-NO_BLOCKS, NOT_FOUND = -7, -8
+NO_BLOCKS, NOT_FOUND, SWAPPED = -7, -8, -9
 
 
 def test_page_traces(pages):
@@ -59,19 +60,70 @@ def test_errors():
         pa.BlockManager(0, 16)
 
 
+def test_offload_trace_and_swap_errors(pages):
+    """The offloading example (two sessions' room; C moves A out, A's return
+    moves B out) and the swapped-state errors, native against the oracle."""
+    c = pages["offload_trace"]
+    ref, got = B.BlockManager(6, 4), pa.BlockManager(6, 4)
+    toks = {s: list(range(100 * s, 100 * s + 12)) for s in range(3)}
+    for m in (ref, got):
+        m.add_sequence(0, toks[0])
+        m.add_sequence(1, toks[1])
+    t0 = got.table(0)
+    assert got.swap_out(0) == ref.swap_out(0) == t0
+    assert got.table(0) == ref.table(0) == [B.SWAPPED] * 3
+    for m in (ref, got):
+        m.add_sequence(2, toks[2])
+    with pytest.raises(pa.PagedAttentionError) as e:
+        got.swap_in(0)
+    assert e.value.status == NO_BLOCKS and got.table(0) == [B.SWAPPED] * 3
+    for op in (lambda: got.append_token(0, 1), lambda: got.fork(0, 9), lambda: got.trim(0, 2),
+               lambda: got.swap_out(0), lambda: got.swap_in(1), lambda: got.batch([0], 4)):
+        with pytest.raises(pa.PagedAttentionError) as e:
+            op()
+        assert e.value.status == SWAPPED
+    assert got.swap_out(1) == ref.swap_out(1)
+    assert got.swap_in(0) == ref.swap_in(0) == got.table(0)
+    assert [got.refcount(b) for b in range(6)] == ref.ref and got.num_free() == ref.num_free() == 0
+    assert got.table(1) == [B.SWAPPED] * 3            # GPU: sessions 2 and 0; host: session 1
+    assert len(c["gpu_after_a_returns"]) == 2 and c["cpu_after_a_returns"] == ["cache-b"]
+
+
 def run_both(seed, num_blocks, block_size, steps, vocab, max_prompt):
     """Random adds (prompts = a shared stem cut anywhere + a random tail, so
-    prefixes repeat), forks, appends, sliding-window trims and frees, applied
-    to both managers."""
+    prefixes repeat), forks, appends, sliding-window trims, swaps out and in
+    and frees, applied to both managers."""
     rng = random.Random(seed)
     ref = B.BlockManager(num_blocks, block_size)
     got = pa.BlockManager(num_blocks, block_size)
     stems = [[rng.randrange(vocab) for _ in range(max_prompt)] for _ in range(3)]
-    live, next_id = [], 0
-    cow = oob = 0
+    live, next_id, swapped = [], 0, set()
+    cow = oob = swaps = 0
     for step in range(steps):
         op = rng.random()
-        if op < 0.25 or not live:
+        resident = [s for s in live if s not in swapped]
+        if swapped and op < 0.04:
+            s = rng.choice(sorted(swapped))
+            try:
+                r = ref.swap_in(s)
+            except B.OutOfBlocks:
+                with pytest.raises(pa.PagedAttentionError) as e:
+                    got.swap_in(s)
+                assert e.value.status == NO_BLOCKS
+            else:
+                assert got.swap_in(s) == r, step
+                swapped.discard(s)
+                swaps += 1
+        elif resident and op < 0.07:
+            s = rng.choice(resident)
+            assert got.swap_out(s) == ref.swap_out(s), step
+            swapped.add(s)
+        elif swapped and op < 0.08:
+            s = rng.choice(sorted(swapped))
+            with pytest.raises(pa.PagedAttentionError) as e:
+                got.append_token(s, 0)
+            assert e.value.status == SWAPPED
+        elif op < 0.25 or not resident:
             cut = rng.randrange(0, max_prompt)
             toks = rng.choice(stems)[:cut] + [rng.randrange(vocab) for _ in range(rng.randrange(0, 2 * block_size))]
             model = int(rng.random() < 0.2)
@@ -87,13 +139,13 @@ def run_both(seed, num_blocks, block_size, steps, vocab, max_prompt):
                 live.append(next_id)
                 next_id += 1
         elif op < 0.35:
-            p = rng.choice(live)
+            p = rng.choice(resident)
             ref.fork(p, next_id)
             got.fork(p, next_id)
             live.append(next_id)
             next_id += 1
         elif op < 0.8:
-            s = rng.choice(live)
+            s = rng.choice(resident)
             t = rng.randrange(vocab)
             try:
                 r = ref.append_token(s, t)
@@ -106,11 +158,12 @@ def run_both(seed, num_blocks, block_size, steps, vocab, max_prompt):
                 cow += r[1] >= 0
                 assert got.append_token(s, t) == r, step
         elif op < 0.88:
-            s = rng.choice(live)
+            s = rng.choice(resident)
             keep = rng.randrange(1, 3 * block_size)
             assert got.trim(s, keep) == ref.trim(s, keep), step
         else:
             s = live.pop(rng.randrange(len(live)))
+            swapped.discard(s)
             ref.free_sequence(s)
             got.free_sequence(s)
         assert got.num_free() == ref.num_free(), step
@@ -120,10 +173,11 @@ def run_both(seed, num_blocks, block_size, steps, vocab, max_prompt):
                 assert got.length(s) == ref.length(s)
             assert [got.refcount(b) for b in range(num_blocks)] == ref.ref
     assert got.stats() == (ref.hits, ref.misses)
-    counts = {"hits": ref.hits, "cow": cow, "no_blocks": oob}
+    counts = {"hits": ref.hits, "cow": cow, "no_blocks": oob, "swap_in": swaps}
     assert min(counts.values()) > 0, counts           # every path was taken
-    bt, sl = got.batch(live, 64)
-    for i, s in enumerate(live):
+    resident = [s for s in live if s not in swapped]
+    bt, sl = got.batch(resident, 64)
+    for i, s in enumerate(resident):
         t = ref.table(s)
         assert list(bt[i, :len(t)]) == t and (bt[i, len(t):] == -1).all() and sl[i] == ref.length(s)
 

@@ -130,8 +130,8 @@ def random_ops(bm, rng, steps, vocab=3, max_prompt=14):
                 s = live.pop(rng.randrange(len(live)))
                 bm.free_sequence(s)
                 yield ("free", s)
-        except B.OutOfBlocks:
-            yield ("oob",)
+        except (B.OutOfBlocks, B.Swapped) as e:
+            yield (type(e).__name__,)
 
 
 def check_invariants(bm, num_blocks):
@@ -226,3 +226,125 @@ def test_random_operations_with_trims_keep_the_invariants(seed):
         if i % 20 == 0:
             check_invariants_with_trims(bm, 30)
     check_invariants_with_trims(bm, 30)
+
+
+def test_offload_trace_of_the_offloading_section(pages):
+    """A pool with room for two sessions: C's arrival moves A out, A's return
+    moves B out ("KV Cache Engineering for LLM Serving", section 12, printed
+    output).  On each side of the trace, the sessions whose blocks are on the
+    GPU and those swapped to the host are the ones the page prints."""
+    c = pages["offload_trace"]
+    per = 3                                            # blocks per session
+    bm = B.BlockManager(c["gpu_sessions"] * per, 4)
+    name = {"a": "cache-a", "b": "cache-b", "c": "cache-c"}
+    toks = {s: unique_tokens(100 * i, 4 * per) for i, s in enumerate("abc")}
+    host = {}
+
+    def state():
+        gpu = [name[s] for s in bm.seqs if not bm.seqs[s]["swapped"]]
+        cpu = [name[s] for s in bm.seqs if bm.seqs[s]["swapped"]]
+        return gpu, cpu
+
+    bm.add_sequence("a", toks["a"])
+    bm.add_sequence("b", toks["b"])
+    with pytest.raises(B.OutOfBlocks):
+        bm.add_sequence("c", toks["c"])
+    table_a = bm.table("a")
+    host["a"] = bm.swap_out("a")
+    assert host["a"] == table_a and bm.table("a") == [B.SWAPPED] * per
+    bm.add_sequence("c", toks["c"])
+    gpu, cpu = state()
+    assert sorted(gpu) == sorted(c["gpu_after_c_arrives"]) and cpu == c["cpu_after_c_arrives"]
+    with pytest.raises(B.OutOfBlocks):
+        bm.swap_in("a")
+    assert bm.table("a") == [B.SWAPPED] * per        # nothing changed
+    host["b"] = bm.swap_out("b")
+    back = bm.swap_in("a")
+    assert bm.table("a") == back and len(back) == per
+    gpu, cpu = state()
+    assert sorted(gpu) == sorted(c["gpu_after_a_returns"]) and cpu == c["cpu_after_a_returns"]
+    # A's full blocks are stored under their keys again: an equal prompt reuses them
+    assert bm.num_free() == 0 and bm.add_sequence("a2", toks["a"][:8]) == 2
+    check_invariants_with_swaps(bm, c["gpu_sessions"] * per)
+
+
+def test_swap_keeps_shared_blocks_and_refuses_updates():
+    """Only blocks no other sequence holds move out; the shared prefix stays
+    ("Taming the token torrent", "The Swapping Mechanism").  A swapped
+    sequence takes no appends, forks or trims until it is swapped in."""
+    bm = B.BlockManager(16, 4)
+    sysp = unique_tokens(0, 8)
+    bm.add_sequence("a", sysp + unique_tokens(100, 6))
+    bm.add_sequence("b", sysp + unique_tokens(200, 2))
+    ta = bm.table("a")
+    free0 = bm.num_free()
+    out = bm.swap_out("a")
+    assert out == ta[2:] and bm.table("a") == ta[:2] + [B.SWAPPED, B.SWAPPED]
+    assert bm.num_free() == free0 + 2 and [bm.ref[b] for b in ta[:2]] == [2, 2]
+    for op in (lambda: bm.append_token("a", 1), lambda: bm.fork("a", "z"), lambda: bm.trim("a", 2),
+               lambda: bm.swap_out("a")):
+        with pytest.raises(B.Swapped):
+            op()
+    with pytest.raises(B.Swapped):
+        bm.swap_in("b")
+    back = bm.swap_in("a")
+    assert bm.table("a") == ta[:2] + back
+    slot, src, dst = bm.append_token("a", 7)          # the partial block is private again
+    assert (src, dst) == (-1, -1) and slot == back[1] * 4 + 2
+    # a swapped sequence's table entries are not references: freeing it
+    # releases only what it still holds
+    bm.swap_out("b")
+    bm.free_sequence("b")
+    check_invariants_with_swaps(bm, 16)
+
+
+def check_invariants_with_swaps(bm, num_blocks):
+    check_invariants_with_trims(bm, num_blocks)
+    for s in bm.seqs.values():
+        assert (B.SWAPPED in s["table"]) <= s["swapped"]
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_random_operations_with_swaps_keep_the_invariants(seed):
+    rng = random.Random(200 + seed)
+    bm = B.BlockManager(30, 4)
+    ops = random_ops(bm, rng, 500)
+    for i in range(500):
+        swapped = [s for s in bm.seqs if bm.seqs[s]["swapped"]]
+        try:
+            if swapped and rng.random() < 0.3:
+                bm.swap_in(rng.choice(swapped))
+            elif bm.seqs and rng.random() < 0.1:
+                bm.swap_out(rng.choice([s for s in bm.seqs if s not in swapped] or [None]))
+            else:
+                next(ops)
+        except (B.OutOfBlocks, B.Swapped, KeyError):
+            pass
+        if i % 20 == 0:
+            check_invariants_with_swaps(bm, 30)
+    check_invariants_with_swaps(bm, 30)
+
+
+def test_swap_image_round_trip():
+    """A host copy holds each listed block's K elements, then its V elements,
+    every (head, token, dim) of the block (located through the oracle's
+    layout offsets); restoring it into other blocks moves exactly those."""
+    g = paged.Geom(num_blocks=7, block_size=16, num_kv_heads=2, head_dim=64)
+    E = g.num_kv_heads * g.block_size * g.head_dim
+    k = np.arange(g.cache_elems, dtype=np.int64)
+    v = 10 ** 6 + k
+    blocks = [5, 1, 4]
+    img = B.swap_image(k, v, blocks, E)
+    assert img.shape == (2 * len(blocks) * E,)
+    h, t, d = 1, 9, 33
+    for i, b in enumerate(blocks):
+        assert img[i * E + paged.k_offset(g, b, h, t, d) - b * E] == k[paged.k_offset(g, b, h, t, d)]
+        j = len(blocks) + i
+        assert img[j * E + paged.v_offset(g, b, h, t, d) - b * E] == v[paged.v_offset(g, b, h, t, d)]
+    k2, v2 = np.zeros_like(k), np.zeros_like(v)
+    B.swap_restore(k2, v2, [0, 6, 2], img, E)
+    for src, dst in zip(blocks, [0, 6, 2]):
+        assert np.array_equal(k2[dst * E:(dst + 1) * E], k[src * E:(src + 1) * E])
+        assert np.array_equal(v2[dst * E:(dst + 1) * E], v[src * E:(src + 1) * E])
+    assert not k2[E:2 * E].any() and not v2[3 * E:6 * E].any()
+    assert B.swap_image(k, v, [], E).size == 0
