@@ -19,11 +19,14 @@ eye:
   self-test.
 * ``oracle.blocks`` - the block manager's rules (FIFO free list, reference
   counts, full-prefix keys with a model key, fork, copy-on-write) and the
-  whole-block copy.
+  whole-block copy, and swaps to host memory and back.
+* ``oracle.quest``  - query-aware page selection: per-block min/max key
+  summaries (recomputed, or kept by the cache writes), page scores, the
+  top-budget choice, and attention over the chosen pages.
 
 Every function is pinned by a ``-m "not gpu"`` test in ``tests/`` against a
 value the pages print, a closed form, an invariant or brute force; none is
 "parity unpinned".
 """
 
-from . import blocks, e4m3, pages, paged  # noqa: F401
+from . import blocks, e4m3, pages, paged, quest  # noqa: F401
