@@ -34,6 +34,16 @@ Other workloads (--workload), each on the same 70B layer shape:
                        70B layer's bf16 pool (block 16): `value` is bytes read
                        plus written per call / time; also the host block
                        manager's add_sequence / append_token rates
+  quest_long_context_128k  the long-context batch (4 x 131,072 tokens) decoded
+                       with query-aware page selection, 256 pages (4,096
+                       tokens) per (sequence, KV head): a step is the cache
+                       write, pa_quest_update, pa_quest_select and
+                       pa_decode_quest; `value` counts the bytes the step
+                       must read (page summaries, chosen K/V, q, out,
+                       tables); the plain decode of the same batch is timed
+                       beside it
+  quest_llama70b_bs64  the same on the 70B layer bs=64 batch, 64 pages
+                       (1,024 tokens) per (sequence, KV head)
   swap_blocks_llama70b pa_swap_out then pa_swap_in of 1,024 blocks (64 MiB of
                        K+V) through pinned host memory: `value` is bytes moved
                        per direction / time (bound by the host link, PCIe 5.0
@@ -45,6 +55,7 @@ Prints exactly one JSON line on stdout; everything else goes to stderr.
 """
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -69,7 +80,8 @@ MODEL_LAYERS = 80
 SCRUB_BYTES = 512 << 20
 WORKLOADS = {"llama70b_layer_bs64": 2, "prefix_shared_bs256": 3, "long_context_128k": 4,
              "fp8_80layer_bs128": 5, "copy_blocks_llama70b": 2, "sliding_window_llama70b": 2,
-             "swap_blocks_llama70b": 2}
+             "swap_blocks_llama70b": 2, "quest_long_context_128k": 4, "quest_llama70b_bs64": 2}
+QUEST_BUDGET = {"quest_long_context_128k": 256, "quest_llama70b_bs64": 64}   # pages per (seq, KV head)
 HOST_LINK_GBS = 64.0  # PCIe 5.0 x16, per direction: 32 GT/s x 16 lanes / 8 bits
 LOCAL_WINDOW = 1024   # a local layer's window ("KV Cache Engineering for LLM Serving", section 3)
 
@@ -479,6 +491,184 @@ def bench_copy_blocks(args, dev):
     return res
 
 
+def quest_bytes(w, budget):
+    """Algorithmic bytes of one query-aware step, per call: the update reads
+    the new keys and rewrites their blocks' summary words; the selection
+    reads every page's summary words, the queries and the table entries and
+    writes the chosen tables; the decode reads the chosen pages' K and V
+    (the tokens each (sequence, KV head) keeps), the queries and the chosen
+    tables, and writes the outputs."""
+    S, Hq, Hkv, D, BS, eb = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size, w.elem_bytes
+    pages = [-(-int(L) // BS) for L in w.seq_lens]
+    update = S * Hkv * D * eb + 2 * S * Hkv * D * 4
+    select = sum(pages) * Hkv * D * 4 + S * Hq * D * 2 + sum(pages) * 4 + 4 * S + S * Hkv * (budget + 1) * 4
+    kept = 0
+    for L, n in zip(w.seq_lens, pages):
+        L = int(L)
+        kept += Hkv * (L if n <= budget else budget * BS)      # the last page may be short: upper bound
+    decode = kept * 2 * D * eb + S * Hq * D * 2 + S * Hq * D * 4 + S * Hkv * (min(budget, max(pages)) + 1) * 4
+    return {"update": update, "select": select, "decode": decode, "kept_tokens_upper": kept}
+
+
+def quest_cpu_baseline(w, t, out_gpu, budget, min_seconds=10.0):
+    """The Quest oracle on a bounded sample of the same batch: (sequence, KV
+    head) units in order until about 10 s have elapsed; bytes as the GPU's
+    algorithmic bytes for those units (summaries of every page, K/V of the
+    kept tokens)."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import paged, quest
+    g = paged.Geom(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.kv_dtype)
+
+    def bits(x):
+        x = x.detach().cpu()
+        return x.view(torch.int16).numpy().view(np.uint16) if x.dtype == torch.bfloat16 else x.numpy()
+
+    kc, vc = bits(t["k_cache"][0]), bits(t["v_cache"][0])
+    paged.cache_write_bf16(g, bits(t["k_new"][0]), bits(t["v_new"][0]), w.slot_mapping, kc, vc)
+    qf = paged.bf16_bits_to_f64(bits(t["q"][0]))
+    G, BS, D = w.num_q_heads // w.num_kv_heads, w.block_size, w.head_dim
+    got = out_gpu.detach().cpu().double().numpy()
+    threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    elapsed, nbytes, units, errs = 0.0, 0, 0, []
+    u = 0
+    while elapsed < min_seconds and units < w.num_seqs * w.num_kv_heads:
+        s, h = divmod(u, w.num_kv_heads)
+        L = int(w.seq_lens[s])
+        t0 = time.perf_counter()
+        mn, mx = quest.sequence_page_summaries(g, kc, w.block_tables[s], L, h)
+        chosen = quest.select_pages(quest.page_scores(qf[s, h * G:(h + 1) * G].astype(np.float32), mn, mx),
+                                    budget)
+        K, V = paged.gather(g, kc, vc, w.block_tables[s], L, h)
+        pos = [p * BS + i for p in chosen for i in range(BS) if p * BS + i < L]
+        ref = paged.softmax_attention(qf[s, h * G:(h + 1) * G], K[pos], V[pos], w.scale)
+        elapsed += time.perf_counter() - t0
+        nbytes += len(mn) * D * 4 + len(pos) * 2 * D * w.elem_bytes
+        errs.append(float(np.abs(got[s, h * G:(h + 1) * G] - ref).max()))
+        units += 1
+        u += 1
+    return {"value": nbytes / elapsed / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"{units} of the {w.num_seqs * w.num_kv_heads} (sequence, KV head) units of the same "
+                       f"batch, float64 numpy Quest oracle (summaries from the gathered sequence, float32 "
+                       f"scores, choice, attention over the kept tokens), {elapsed:.1f} s"),
+            "seconds": elapsed, "gpu_vs_oracle_max_abs": max(errs)}
+
+
+def bench_quest(args, dev):
+    """Query-aware step (write, summary update, page choice, decode over the
+    chosen pages) against the plain decode of the same batch."""
+    w = W.config(WORKLOADS[args.workload])
+    budget = QUEST_BUDGET[args.workload]
+    Hkv, D, BS = w.num_kv_heads, w.head_dim, w.block_size
+    kw = dict(num_kv_heads=Hkv, block_size=BS)
+    log("workload:", json.dumps(w.summary()), "budget pages:", budget)
+    t = w.make_tensors(dev, poison=False)
+    bt = torch.from_numpy(w.block_tables).to(dev)
+    sl = torch.from_numpy(w.seq_lens).to(dev)
+    sm = torch.from_numpy(w.slot_mapping).to(dev)
+    q, kn, vn, kc, vc = t["q"][0], t["k_new"][0], t["v_new"][0], t["k_cache"][0], t["v_cache"][0]
+    S = w.num_seqs
+    out = torch.empty((S, w.num_q_heads, D), dtype=torch.float32, device=dev)
+    full_out = torch.empty_like(out)
+    # The step's write once, then summaries of every block the batch holds
+    # (set-up, not timed): the summaries then cover the written tokens.
+    pa.pa_cache_write(kn, vn, sm, kc, vc, block_size=BS)
+    items = {}
+    for s, L in enumerate(w.seq_lens):
+        L = int(L)
+        for p in range(-(-L // BS)):
+            items[int(w.block_tables[s, p])] = min(BS, L - p * BS)
+    summ = pa.quest_summaries(kc, num_kv_heads=Hkv, head_dim=D, block_size=BS)
+    pa.pa_quest_summarize(kc, torch.tensor(list(items), dtype=torch.int32, device=dev),
+                          torch.tensor(list(items.values()), dtype=torch.int32, device=dev), summ,
+                          num_kv_heads=Hkv, head_dim=D, block_size=BS)
+    sel_t = torch.empty((S * Hkv, budget), dtype=torch.int32, device=dev)
+    sel_l = torch.empty((S * Hkv,), dtype=torch.int32, device=dev)
+    sel_ws = torch.empty(max(pa.lib().pa_quest_select_workspace_size(S, Hkv, w.max_blocks_per_seq), 1),
+                         dtype=torch.uint8, device=dev)
+    desc = pa.make_desc(kc, Hkv, D, BS)
+    dws = torch.zeros(pa.lib().pa_decode_quest_workspace_size(ctypes.byref(desc), S, w.num_q_heads, budget, 0),
+                      dtype=torch.uint8, device=dev)
+    fws = torch.zeros(pa.pa_decode_workspace_size(w.num_blocks, BS, Hkv, D, S, w.num_q_heads,
+                                                  w.max_blocks_per_seq, 0), dtype=torch.uint8, device=dev)
+    scrub = torch.ones(SCRUB_BYTES // 4, dtype=torch.float32, device=dev)
+    sink = torch.zeros((), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def phases():
+        pa.pa_cache_write(kn, vn, sm, kc, vc, block_size=BS)
+        yield
+        pa.pa_quest_update(kc, sm, summ, num_kv_heads=Hkv, head_dim=D, block_size=BS)
+        yield
+        pa.pa_quest_select(q, summ, bt, sl, budget, sel_tables=sel_t, sel_lens=sel_l, workspace=sel_ws, **kw)
+        yield
+        pa.pa_decode_quest(q, kc, vc, sel_t, sel_l, w.scale, out, workspace=dws, **kw)
+        yield
+
+    def full():
+        pa.pa_decode(q, kc, vc, bt, sl, w.scale, full_out, workspace=fws, **kw)
+
+    for _ in range(args.warmup):
+        for _ in phases():
+            pass
+        full()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    fev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    t0 = time.perf_counter()
+    for i in range(K):
+        if not args.no_scrub:
+            torch.sum(scrub, dim=0, out=sink)
+        ev[i][0].record(stream)
+        for j, _ in enumerate(phases()):
+            ev[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for i in range(K):
+        if not args.no_scrub:
+            torch.sum(scrub, dim=0, out=sink)
+        fev[i][0].record(stream)
+        full()
+        fev[i][1].record(stream)
+    torch.cuda.synchronize()
+    ph = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in ev])   # ms
+    full_ms = np.array([e[0].elapsed_time(e[1]) for e in fev])
+    step_ms = float(ph.sum(axis=1).mean())
+    qb = quest_bytes(w, budget)
+    kept = int(sel_l.clamp(min=0).sum().item())
+    qb["decode"] -= (qb["kept_tokens_upper"] - kept) * 2 * D * w.elem_bytes     # the exact kept tokens
+    total = qb["update"] + qb["select"] + qb["decode"] + S * Hkv * D * 2 * w.elem_bytes
+    names = ["cache_write", "quest_update", "quest_select", "decode_quest"]
+    means = {n: float(ph[:, j].mean()) for j, n in enumerate(names)}
+    dom = max(("quest_select", "decode_quest"), key=lambda n: means[n])
+    dom_bytes = qb["select"] if dom == "quest_select" else qb["decode"]
+    dom_gbs = dom_bytes / (means[dom] / 1e3) / 1e9
+    full_kv, _ = algorithmic_bytes(w)
+    res = base_record(args, w, K)
+    res["metric"] = f"query-aware (Quest) decode step: algorithmic GB/s and speed-up over plain decode, {args.workload}"
+    res.update({"value": round(total / (step_ms / 1e3) / 1e9, 1), "ms_per_step": round(step_ms, 4)})
+    res["config"].update({"workload": args.workload, "budget_pages": budget, "budget_tokens": budget * BS,
+                          "kept_tokens": kept, "bytes_per_step": total,
+                          "scrub_mib_between_steps": 0 if args.no_scrub else SCRUB_BYTES >> 20})
+    res.update({
+        "phase_us": {n: round(v * 1e3, 2) for n, v in means.items()},
+        "full_decode_us": round(float(full_ms.mean()) * 1e3, 2),
+        "speedup_vs_full_decode": round(float(full_ms.mean()) / step_ms, 3),
+        "full_kv_bytes": full_kv, "kept_kv_bytes": kept * 2 * D * w.elem_bytes,
+        "layer_tok_s": round(S / (step_ms / 1e3), 1),
+        "wall_s_timed_region": round(wall, 4),
+        "roofline": {"bound": "hbm", "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": {"quest_select": "page_score_kernel + page_select_kernel (pa_quest_select)",
+                                "decode_quest": "decode_kernel (pa_decode_quest is one launch)"}[dom],
+                     "bytes_per_launch": dom_bytes},
+    })
+    if not args.skip_cpu:
+        res["cpu_baseline"] = quest_cpu_baseline(w, t, out, budget)
+    return res
+
+
 def bench_swap(args, dev):
     """pa_swap_out / pa_swap_in of 1,024 blocks of the 70B layer's pool, and
     the default batch's decode with a swap running beside it on a second
@@ -612,6 +802,8 @@ def main():
         res = bench_copy_blocks(args, dev)
     elif args.workload == "swap_blocks_llama70b":
         res = bench_swap(args, dev)
+    elif args.workload.startswith("quest_"):
+        res = bench_quest(args, dev)
     else:
         res = bench_layer(args, dev)
     print(json.dumps(res), flush=True)

@@ -23,10 +23,13 @@ Readings where the page is silent (each is listed in the design notes):
       score for the group is the largest of its query heads' scores: it is
       read if any head of the group ranks it high.
 * Q3  The choice of pages is an integer decision taken from a floating-point
-      score, so both sides compute the score the same way: float32 products
-      (exact for bf16 operands), float32 sums in dimension order d = 0, 1,
-      ..., D - 1, then the maximum over the group.  No scale is applied:
-      a positive softmax scale does not change the ranking.
+      score, so both sides compute the score the same way: float32 products,
+      float32 sums in dimension order d = 0, 1, ..., D - 1, then the maximum
+      over the group.  A product of two bf16 values is exact in float32
+      whenever its magnitude is at least 2^-134, so any float32 evaluation
+      that rounds once per added term (a fused multiply-add included) gives
+      the same sums.  No scale is applied: a positive softmax scale does not
+      change the ranking.
 * Q4  The ``budget`` pages with the highest scores are chosen; equal scores
       go to the lower page index.  A budget at least the page count chooses
       every page, which is plain decode.  The selected pages are read in
@@ -104,6 +107,20 @@ def update_summaries(g, k_cache, slot_mapping, mn, mx):
         k = _token_keys(g, k_cache, blk, off)
         mn[blk] = np.fmin(mn[blk], k)
         mx[blk] = np.fmax(mx[blk], k)
+
+
+def sequence_page_summaries(g, k_cache, block_row, L, h):
+    """(min, max), [pages, D] each, of KV head h over the pages of one
+    sequence of length L: page p covers positions p * block_size up to
+    min(L, (p + 1) * block_size).  The same values as ``block_summary`` of
+    each block with its count of tokens, taken here from the gathered
+    sequence (for long sequences)."""
+    K, _ = paged.gather(g, k_cache, k_cache, block_row, L, h, 1.0, 1.0)   # stored values (Q5)
+    pages = -(-L // g.block_size)
+    pad = pages * g.block_size - L
+    lo = np.concatenate([K, np.full((pad, g.head_dim), np.inf)]).reshape(pages, g.block_size, g.head_dim)
+    hi = np.concatenate([K, np.full((pad, g.head_dim), -np.inf)]).reshape(pages, g.block_size, g.head_dim)
+    return np.fmin.reduce(lo, axis=1), np.fmax.reduce(hi, axis=1)
 
 
 def page_scores(q_group, mn, mx):

@@ -88,6 +88,15 @@ def _load():
         "pa_decode_window": ([dp, vp, i32, i32, vp, vp, vp, i32, vp, i32, f32, vp, i32, vp, sz, vp], i32),
         "pa_decode_window_fp8": ([dp, vp, i32, i32, vp, vp, vp, i32, vp, i32, f32, f32, f32, vp, i32, vp,
                                   sz, vp], i32),
+        "pa_quest_clear": ([dp, vp, vp], i32),
+        "pa_quest_update": ([dp, i32, vp, vp, i32, vp, vp], i32),
+        "pa_quest_summarize": ([dp, i32, vp, vp, vp, i32, vp, vp], i32),
+        "pa_quest_select_workspace_size": ([i32, i32, i32], sz),
+        "pa_quest_select": ([dp, vp, i32, i32, vp, vp, i32, vp, i32, vp, vp, vp, sz, vp], i32),
+        "pa_decode_quest_workspace_size": ([dp, i32, i32, i32, i32], sz),
+        "pa_decode_quest": ([dp, vp, i32, i32, vp, vp, vp, i32, vp, f32, vp, i32, vp, sz, vp], i32),
+        "pa_decode_quest_fp8": ([dp, vp, i32, i32, vp, vp, vp, i32, vp, f32, f32, f32, vp, i32, vp, sz,
+                                 vp], i32),
         "pa_bm_num_free": ([vp], i32),
         "pa_bm_sequence_info": ([vp, i64, ctypes.POINTER(i32), ctypes.POINTER(i32)], i32),
         "pa_bm_block_table": ([vp, i64, ctypes.POINTER(i32), i32], i32),
@@ -451,3 +460,136 @@ def pa_decode_window_fp8(q, k_cache, v_cache, block_tables, seq_lens, window, sc
     """Sliding-window decode over an e4m3fn cache."""
     return _decode(True, q, k_cache, v_cache, block_tables, seq_lens, scale, out, num_kv_heads,
                    block_size, k_scale, v_scale, partition_tokens, workspace, window)
+
+
+# -- query-aware page selection (include/pa_quest.h) -------------------------
+
+def quest_summaries(k_cache, *, num_kv_heads, head_dim, block_size):
+    """A new summary array for the pool of ``k_cache``: int32 device tensor
+    [num_blocks, num_kv_heads, head_dim] (uint32 words, (max bf16 << 16) |
+    min bf16), every word empty."""
+    desc = make_desc(k_cache, num_kv_heads, head_dim, block_size)
+    words = torch.empty((desc.num_blocks, num_kv_heads, head_dim), dtype=torch.int32, device=k_cache.device)
+    with torch.cuda.device(k_cache.device):
+        st = _load().pa_quest_clear(ctypes.byref(desc), _ptr(words), _stream(k_cache))
+    _check("pa_quest_clear", st)
+    return words
+
+
+def _summary_args(k_cache, summaries, num_kv_heads, head_dim, block_size):
+    dev = k_cache.device
+    _need(k_cache, "k_cache", k_cache.dtype, dev)
+    desc = make_desc(k_cache, num_kv_heads, head_dim, block_size)
+    _need(summaries, "summaries", torch.int32, dev, shape=(desc.num_blocks, num_kv_heads, head_dim))
+    eb = 2 if k_cache.dtype == torch.bfloat16 else 1
+    return dev, desc, eb
+
+
+def pa_quest_update(k_cache, slot_mapping, summaries, *, num_kv_heads, head_dim, block_size):
+    """Keep the summaries current after pa_cache_write(_fp8) of slot_mapping
+    (int64 device tensor), on the same stream.  See include/pa_quest.h."""
+    dev, desc, eb = _summary_args(k_cache, summaries, num_kv_heads, head_dim, block_size)
+    _need(slot_mapping, "slot_mapping", torch.int64, dev, 1)
+    with torch.cuda.device(dev):
+        st = _load().pa_quest_update(ctypes.byref(desc), eb, _ptr(k_cache), _ptr(slot_mapping),
+                                     slot_mapping.numel(), _ptr(summaries), _stream(k_cache))
+    _check("pa_quest_update", st)
+
+
+def pa_quest_summarize(k_cache, blocks, counts, summaries, *, num_kv_heads, head_dim, block_size):
+    """Recompute the summaries of blocks[i] from their first counts[i]
+    tokens (int32 device tensors)."""
+    dev, desc, eb = _summary_args(k_cache, summaries, num_kv_heads, head_dim, block_size)
+    _need(blocks, "blocks", torch.int32, dev, 1)
+    _need(counts, "counts", torch.int32, dev, shape=tuple(blocks.shape))
+    with torch.cuda.device(dev):
+        st = _load().pa_quest_summarize(ctypes.byref(desc), eb, _ptr(k_cache), _ptr(blocks), _ptr(counts),
+                                        blocks.numel(), _ptr(summaries), _stream(k_cache))
+    _check("pa_quest_summarize", st)
+
+
+def pa_quest_select(q, summaries, block_tables, seq_lens, budget, *, num_kv_heads, block_size,
+                    sel_tables=None, sel_lens=None, workspace=None):
+    """Choose the `budget` best pages per (sequence, KV head).  Returns
+    (sel_tables [S * Hkv, budget] int32, sel_lens [S * Hkv] int32)."""
+    dev = q.device
+    _need(q, "q", torch.bfloat16, dev, 3)
+    S, Hq, D = q.shape
+    _need(summaries, "summaries", torch.int32, dev, 3)
+    if summaries.shape[1:] != (num_kv_heads, D):
+        raise ValueError("summaries must be [num_blocks, num_kv_heads, head_dim]")
+    _need(block_tables, "block_tables", torch.int32, dev, 2)
+    if block_tables.shape[0] != S:
+        raise ValueError("block_tables must have one row per sequence")
+    _need(seq_lens, "seq_lens", torch.int32, dev, shape=(S,))
+    desc = CacheDesc(summaries.shape[0], block_size, num_kv_heads, D)
+    units = S * num_kv_heads
+    if sel_tables is None:
+        sel_tables = torch.empty((units, budget), dtype=torch.int32, device=dev)
+    if sel_lens is None:
+        sel_lens = torch.empty((units,), dtype=torch.int32, device=dev)
+    _need(sel_tables, "sel_tables", torch.int32, dev, shape=(units, budget))
+    _need(sel_lens, "sel_lens", torch.int32, dev, shape=(units,))
+    maxb = block_tables.shape[1]
+    L = _load()
+    if workspace is None:
+        need = L.pa_quest_select_workspace_size(S, num_kv_heads, maxb)
+        workspace = torch.empty(max(int(need), 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, dev)
+    with torch.cuda.device(dev):
+        st = L.pa_quest_select(ctypes.byref(desc), _ptr(q), S, Hq, _ptr(summaries), _ptr(block_tables), maxb,
+                               _ptr(seq_lens), int(budget), _ptr(sel_tables), _ptr(sel_lens), _ptr(workspace),
+                               workspace.numel(), _stream(q))
+    _check("pa_quest_select", st)
+    return sel_tables, sel_lens
+
+
+def _decode_quest(fp8, q, k_cache, v_cache, sel_tables, sel_lens, scale, out, num_kv_heads, block_size,
+                  k_scale, v_scale, partition_tokens, workspace):
+    dev = q.device
+    _need(q, "q", torch.bfloat16, dev, 3)
+    S, Hq, D = q.shape
+    cdt = torch.uint8 if fp8 else torch.bfloat16
+    _need(k_cache, "k_cache", cdt, dev)
+    _need(v_cache, "v_cache", cdt, dev, shape=tuple(k_cache.shape))
+    _need(sel_tables, "sel_tables", torch.int32, dev, 2)
+    if sel_tables.shape[0] != S * num_kv_heads:
+        raise ValueError("sel_tables must have one row per (sequence, KV head)")
+    _need(sel_lens, "sel_lens", torch.int32, dev, shape=(S * num_kv_heads,))
+    if out is None:
+        out = torch.empty((S, Hq, D), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, dev, shape=(S, Hq, D))
+    desc = make_desc(k_cache, num_kv_heads, D, block_size)
+    budget = sel_tables.shape[1]
+    L = _load()
+    with torch.cuda.device(dev):
+        if workspace is None:
+            need = L.pa_decode_quest_workspace_size(ctypes.byref(desc), S, Hq, budget, partition_tokens)
+            if need == 0 and S > 0:
+                raise PagedAttentionError("pa_decode_quest_workspace_size", -6,
+                                          "no gfx950 device or invalid sizes")
+            workspace = torch.zeros(max(int(need), 1), dtype=torch.uint8, device=dev)
+        _need(workspace, "workspace", torch.uint8, dev)
+        args = [ctypes.byref(desc), _ptr(q), S, Hq, _ptr(k_cache), _ptr(v_cache), _ptr(sel_tables), budget,
+                _ptr(sel_lens), float(scale)]
+        if fp8:
+            args += [float(k_scale), float(v_scale)]
+        args += [_ptr(out), int(partition_tokens), _ptr(workspace), workspace.numel(), _stream(q)]
+        name = "pa_decode_quest" + ("_fp8" if fp8 else "")
+        st = getattr(L, name)(*args)
+    _check(name, st)
+    return out
+
+
+def pa_decode_quest(q, k_cache, v_cache, sel_tables, sel_lens, scale, out=None, *, num_kv_heads,
+                    block_size, partition_tokens=0, workspace=None):
+    """Decode over the pages pa_quest_select chose (bf16 cache)."""
+    return _decode_quest(False, q, k_cache, v_cache, sel_tables, sel_lens, scale, out, num_kv_heads,
+                         block_size, 1.0, 1.0, partition_tokens, workspace)
+
+
+def pa_decode_quest_fp8(q, k_cache, v_cache, sel_tables, sel_lens, scale, k_scale, v_scale, out=None, *,
+                        num_kv_heads, block_size, partition_tokens=0, workspace=None):
+    """Decode over the chosen pages of an e4m3fn cache."""
+    return _decode_quest(True, q, k_cache, v_cache, sel_tables, sel_lens, scale, out, num_kv_heads,
+                         block_size, k_scale, v_scale, partition_tokens, workspace)

@@ -7,6 +7,7 @@
 
 #include "../../include/pa.h"
 #include "../../include/pa_blocks.h"
+#include "../../include/pa_quest.h"
 #include "pa_internal.h"
 
 namespace {
@@ -142,11 +143,14 @@ pa_status plan(const pa_cache_desc* c, int32_t num_seqs, int32_t num_q_heads,
   return PA_OK;
 }
 
+// seq_heads > 1: `cache` describes one KV head per block and sequence s
+// reads head s % seq_heads of a cache that really holds seq_heads heads per
+// block (per-(sequence, head) block tables, as the query-aware decode uses).
 pa_status decode(const pa_cache_desc* cache, const void* q, int32_t num_seqs, int32_t num_q_heads,
                  const void* k_cache, const void* v_cache, const int32_t* block_tables,
                  int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t window, float scale,
                  float k_scale, float v_scale, bool fp8, float* out, int32_t partition_tokens,
-                 void* workspace, size_t workspace_bytes, void* stream) {
+                 void* workspace, size_t workspace_bytes, void* stream, int32_t seq_heads = 0) {
   if (!cache) return PA_ERR_NULL;
   if (!isfinite(scale) || window < 0) return PA_ERR_SHAPE;
   if (fp8 && (!good_scale(k_scale) || !good_scale(v_scale))) return PA_ERR_SHAPE;
@@ -195,7 +199,10 @@ pa_status decode(const pa_cache_desc* cache, const void* q, int32_t num_seqs, in
   p.window = window;
   p.subs = cache->block_size / pa::kSub;
   p.subs_magic = p.subs > 1 ? (uint32_t)((((uint64_t)1 << 32) + p.subs - 1) / p.subs) : 0u;
-  p.blk_stride = (int64_t)cache->num_kv_heads * p.subs * pa::kSub * cache->head_dim * (fp8 ? 1 : 2);
+  const int32_t heads_per_block = seq_heads > 1 ? seq_heads : cache->num_kv_heads;
+  p.blk_stride = (int64_t)heads_per_block * p.subs * pa::kSub * cache->head_dim * (fp8 ? 1 : 2);
+  p.seq_heads = seq_heads > 1 ? seq_heads : 0;
+  p.seq_heads_magic = seq_heads > 1 ? (uint32_t)((((uint64_t)1 << 32) + seq_heads - 1) / seq_heads) : 0u;
   p.qk_scale = scale * 1.4426950408889634f * (fp8 ? k_scale : 1.0f);
   p.out_scale = fp8 ? v_scale : 1.0f;
   if (pa::launch_decode(p, fp8, static_cast<hipStream_t>(stream)) != hipSuccess)
@@ -393,6 +400,193 @@ pa_status pa_swap_in(const pa_cache_desc* cache, int32_t elem_bytes, void* k_cac
   if (pa::launch_move_blocks(p, PA_SWAP_GROUPS, static_cast<hipStream_t>(stream)) != hipSuccess)
     return PA_ERR_LAUNCH;
   return PA_OK;
+}
+
+pa_status pa_quest_clear(const pa_cache_desc* cache, uint32_t* summaries, void* stream) {
+  if (!cache) return PA_ERR_NULL;
+  pa_status st = desc_status(cache);
+  if (st != PA_OK) return st;
+  if (!summaries) return PA_ERR_NULL;
+  int resident = 0;
+  if (!device_info(128, false, &resident)) return PA_ERR_DEVICE;
+  const int64_t words = (int64_t)cache->num_blocks * cache->num_kv_heads * cache->head_dim;
+  if (pa::launch_summary_fill(summaries, words, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return PA_ERR_LAUNCH;
+  return PA_OK;
+}
+
+namespace {
+
+// Shared checks of the summary entry points; fills the common parameters.
+pa_status summary_params(const pa_cache_desc* cache, int32_t elem_bytes, const void* k_cache,
+                         int32_t n, uint32_t* summaries, pa::SummaryParams* p) {
+  if (!cache) return PA_ERR_NULL;
+  pa_status st = desc_status(cache);
+  if (st != PA_OK) return st;
+  if (elem_bytes != 1 && elem_bytes != 2) return PA_ERR_UNSUPPORTED;
+  if (n < 0) return PA_ERR_SHAPE;
+  // Threads of the largest launch: n * Hkv * (D / 4) must fit the grid.
+  if ((int64_t)n * cache->num_kv_heads * (cache->head_dim / 4) > (int64_t)INT32_MAX * 128)
+    return PA_ERR_SHAPE;
+  if (n > 0 && (!k_cache || !summaries)) return PA_ERR_NULL;
+  *p = pa::SummaryParams{};
+  p->k_cache = static_cast<const uint8_t*>(k_cache);
+  p->words = summaries;
+  p->num_tokens = n;
+  p->num_kv_heads = cache->num_kv_heads;
+  p->head_dim = cache->head_dim;
+  p->block_size = cache->block_size;
+  p->num_blocks = cache->num_blocks;
+  return PA_OK;
+}
+
+}  // namespace
+
+pa_status pa_quest_update(const pa_cache_desc* cache, int32_t elem_bytes, const void* k_cache,
+                          const int64_t* slot_mapping, int32_t num_tokens, uint32_t* summaries,
+                          void* stream) {
+  pa::SummaryParams p;
+  pa_status st = summary_params(cache, elem_bytes, k_cache, num_tokens, summaries, &p);
+  if (st != PA_OK || num_tokens == 0) return st;
+  if (!slot_mapping) return PA_ERR_NULL;
+  int resident = 0;
+  if (!device_info(128, false, &resident)) return PA_ERR_DEVICE;
+  p.slots = slot_mapping;
+  if (pa::launch_summary_update(p, elem_bytes == 1, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return PA_ERR_LAUNCH;
+  return PA_OK;
+}
+
+pa_status pa_quest_summarize(const pa_cache_desc* cache, int32_t elem_bytes, const void* k_cache,
+                             const int32_t* blocks, const int32_t* counts, int32_t num_items,
+                             uint32_t* summaries, void* stream) {
+  pa::SummaryParams p;
+  pa_status st = summary_params(cache, elem_bytes, k_cache, num_items, summaries, &p);
+  if (st != PA_OK || num_items == 0) return st;
+  if (!blocks || !counts) return PA_ERR_NULL;
+  int resident = 0;
+  if (!device_info(128, false, &resident)) return PA_ERR_DEVICE;
+  p.blocks = blocks;
+  p.counts = counts;
+  if (pa::launch_summary_build(p, elem_bytes == 1, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return PA_ERR_LAUNCH;
+  return PA_OK;
+}
+
+size_t pa_quest_select_workspace_size(int32_t num_seqs, int32_t num_kv_heads,
+                                      int32_t max_blocks_per_seq) {
+  if (num_seqs < 0 || num_kv_heads < 1 || max_blocks_per_seq < 0) return 0;
+  return pa::align_up((size_t)num_seqs * num_kv_heads * (size_t)max_blocks_per_seq * sizeof(uint32_t),
+                      256);
+}
+
+pa_status pa_quest_select(const pa_cache_desc* cache, const void* q, int32_t num_seqs,
+                          int32_t num_q_heads, const uint32_t* summaries,
+                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* seq_lens, int32_t budget, int32_t* sel_tables,
+                          int32_t* sel_lens, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!cache) return PA_ERR_NULL;
+  pa_status st = desc_status(cache);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || num_q_heads < 1 || max_blocks_per_seq < 0 || budget < 1) return PA_ERR_SHAPE;
+  if (num_q_heads % cache->num_kv_heads != 0) return PA_ERR_SHAPE;
+  if (num_q_heads / cache->num_kv_heads > pa::kMaxGroupQuest) return PA_ERR_UNSUPPORTED;
+  if ((int64_t)max_blocks_per_seq * cache->block_size > INT32_MAX) return PA_ERR_SHAPE;
+  const int64_t units = (int64_t)num_seqs * cache->num_kv_heads;
+  const int32_t chunks = (max_blocks_per_seq + 255) / 256;
+  if (units * (chunks > 0 ? chunks : 1) > INT32_MAX || units * budget > INT32_MAX) return PA_ERR_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  if (!q || !summaries || !block_tables || !seq_lens || !sel_tables || !sel_lens) return PA_ERR_NULL;
+  const size_t need = pa_quest_select_workspace_size(num_seqs, cache->num_kv_heads, max_blocks_per_seq);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
+  int resident = 0;
+  if (!device_info(cache->head_dim, false, &resident)) return PA_ERR_DEVICE;
+  pa::SelectParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.words = summaries;
+  p.block_tables = block_tables;
+  p.seq_lens = seq_lens;
+  p.keys = static_cast<uint32_t*>(workspace);
+  p.sel_tables = sel_tables;
+  p.sel_lens = sel_lens;
+  p.num_seqs = num_seqs;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = cache->num_kv_heads;
+  p.group = num_q_heads / cache->num_kv_heads;
+  p.head_dim = cache->head_dim;
+  p.block_size = cache->block_size;
+  p.num_blocks = cache->num_blocks;
+  p.max_blocks = max_blocks_per_seq;
+  p.budget = budget;
+  p.chunks = chunks > 0 ? chunks : 1;
+  if (pa::launch_page_select(p, static_cast<hipStream_t>(stream)) != hipSuccess) return PA_ERR_LAUNCH;
+  return PA_OK;
+}
+
+namespace {
+
+// The cache as the decode over per-(sequence, head) tables sees it: one KV
+// head per block, the sequences being (s, h) pairs.
+pa_status quest_view(const pa_cache_desc* cache, int32_t num_seqs, int32_t num_q_heads,
+                     pa_cache_desc* view, int32_t* units, int32_t* group) {
+  if (!cache) return PA_ERR_NULL;
+  pa_status st = desc_status(cache);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || num_q_heads < 1 || num_q_heads % cache->num_kv_heads != 0) return PA_ERR_SHAPE;
+  if ((int64_t)num_seqs * cache->num_kv_heads > INT32_MAX) return PA_ERR_SHAPE;
+  *view = *cache;
+  view->num_kv_heads = 1;
+  *units = num_seqs * cache->num_kv_heads;
+  *group = num_q_heads / cache->num_kv_heads;
+  return PA_OK;
+}
+
+pa_status decode_quest(const pa_cache_desc* cache, const void* q, int32_t num_seqs,
+                       int32_t num_q_heads, const void* k_cache, const void* v_cache,
+                       const int32_t* sel_tables, int32_t budget, const int32_t* sel_lens,
+                       float scale, float k_scale, float v_scale, bool fp8, float* out,
+                       int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  pa_cache_desc view;
+  int32_t units = 0, group = 0;
+  pa_status st = quest_view(cache, num_seqs, num_q_heads, &view, &units, &group);
+  if (st != PA_OK) return st;
+  if (budget < 1) return PA_ERR_SHAPE;
+  // q [S][Hq][D] is [S * Hkv][G][D], and so is out.
+  return decode(&view, q, units, group, k_cache, v_cache, sel_tables, budget, sel_lens, 0, scale,
+                k_scale, v_scale, fp8, out, partition_tokens, workspace, workspace_bytes, stream,
+                cache->num_kv_heads);
+}
+
+}  // namespace
+
+size_t pa_decode_quest_workspace_size(const pa_cache_desc* cache, int32_t num_seqs,
+                                      int32_t num_q_heads, int32_t budget,
+                                      int32_t partition_tokens) {
+  pa_cache_desc view;
+  int32_t units = 0, group = 0;
+  if (quest_view(cache, num_seqs, num_q_heads, &view, &units, &group) != PA_OK || budget < 1) return 0;
+  return pa_decode_workspace_size(&view, units, group, budget, partition_tokens);
+}
+
+pa_status pa_decode_quest(const pa_cache_desc* cache, const void* q, int32_t num_seqs,
+                          int32_t num_q_heads, const void* k_cache, const void* v_cache,
+                          const int32_t* sel_tables, int32_t budget, const int32_t* sel_lens,
+                          float scale, float* out, int32_t partition_tokens, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return decode_quest(cache, q, num_seqs, num_q_heads, k_cache, v_cache, sel_tables, budget, sel_lens,
+                      scale, 1.f, 1.f, false, out, partition_tokens, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_decode_quest_fp8(const pa_cache_desc* cache, const void* q, int32_t num_seqs,
+                              int32_t num_q_heads, const void* k_cache, const void* v_cache,
+                              const int32_t* sel_tables, int32_t budget, const int32_t* sel_lens,
+                              float scale, float k_scale, float v_scale, float* out,
+                              int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  return decode_quest(cache, q, num_seqs, num_q_heads, k_cache, v_cache, sel_tables, budget, sel_lens,
+                      scale, k_scale, v_scale, true, out, partition_tokens, workspace, workspace_bytes,
+                      stream);
 }
 
 const char* pa_status_string(pa_status s) {

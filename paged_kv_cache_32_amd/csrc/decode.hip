@@ -348,6 +348,10 @@ __device__ __forceinline__ bool issue_stage(const DecodeParams& p, const Stage& 
       }
     }
   }
+  // KV head of the stage's tiles: the unit's head, or, with one head per
+  // sequence (per-head block tables), sequence s's head s % seq_heads.
+  int kvh = st.h;
+  if (p.seq_heads > 1) kvh = uni(st.s - (int)__umulhi((unsigned)st.s, p.seq_heads_magic) * p.seq_heads);
   bool bad = false;
 #pragma unroll
   for (int k = 0; k < NSUB; ++k) {
@@ -355,7 +359,7 @@ __device__ __forceinline__ bool issue_stage(const DecodeParams& p, const Stage& 
     const bool ok = (unsigned)blk[k] < (unsigned)p.num_blocks;
     bad |= in && !ok;
     const int64_t tile = (in && ok) ? (int64_t)blk[k] * p.blk_stride +
-                                          (int64_t)(st.h * subs + sub[k]) * T::TILE_BYTES
+                                          (int64_t)(kvh * subs + sub[k]) * T::TILE_BYTES
                                     : 0;
     const uint8_t* kt = p.k_cache + tile + k_off;
     const uint8_t* vt = p.v_cache + tile + v_off;

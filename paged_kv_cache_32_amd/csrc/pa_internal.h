@@ -44,6 +44,9 @@ struct DecodeParams {
   int32_t subs;                 // 16-token sub-blocks per block (block_size / 16)
   uint32_t subs_magic;          // ceil(2^32 / subs) for subs > 1: j / subs = umulhi(j, magic)
   int64_t blk_stride;           // bytes from one block's tiles to the next: Hkv * subs * tile
+  int32_t seq_heads;            // > 1: sequence s reads KV head s % seq_heads (one KV head per
+                                // sequence; its tables are per (sequence, head))
+  uint32_t seq_heads_magic;     // ceil(2^32 / seq_heads): s / seq_heads = umulhi(s, magic)
   float qk_scale;               // scale * log2(e) (* k_scale for fp8)
   float out_scale;              // 1 (bf16) or v_scale (fp8)
 };
@@ -62,6 +65,32 @@ struct BlockMoveParams {
   int32_t num_items, src_blocks, dst_blocks;
 };
 
+// Query-aware page selection: largest query group the score kernel takes.
+constexpr int kMaxGroupQuest = 16;
+
+struct SummaryParams {
+  const uint8_t* k_cache;
+  const int64_t* slots;         // update: [num_tokens] slots just written
+  const int32_t* blocks;        // build: [num_tokens] blocks to recompute ...
+  const int32_t* counts;        // ... from their first counts[i] tokens
+  uint32_t* words;              // [num_blocks][Hkv][D] (max bf16 << 16 | min bf16)
+  int32_t num_tokens;           // tokens (update) or listed blocks (build)
+  int32_t num_kv_heads, head_dim, block_size, num_blocks;
+};
+
+struct SelectParams {
+  const uint16_t* q;            // [S][Hq][D] bf16 bits
+  const uint32_t* words;        // summaries
+  const int32_t* block_tables;  // [S][max_blocks]
+  const int32_t* seq_lens;      // [S]
+  uint32_t* keys;               // workspace [S * Hkv][max_blocks] page score keys
+  int32_t* sel_tables;          // [S * Hkv][budget]
+  int32_t* sel_lens;            // [S * Hkv]
+  int32_t num_seqs, num_q_heads, num_kv_heads, group, head_dim, block_size, num_blocks, max_blocks;
+  int32_t budget;               // pages to keep per (sequence, KV head)
+  int32_t chunks;               // ceil(max_blocks / 256): score workgroups per unit
+};
+
 // Host-side launchers (defined next to their kernels).
 hipError_t launch_cache_write(const CacheWriteParams& p, bool fp8, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, bool fp8, hipStream_t stream);
@@ -69,6 +98,10 @@ hipError_t launch_zero(void* ptr, size_t bytes, hipStream_t stream);
 // max_groups > 0 caps the grid (the workgroups then stride over the
 // segments); 0 launches one workgroup per segment.
 hipError_t launch_move_blocks(const BlockMoveParams& p, int max_groups, hipStream_t stream);
+hipError_t launch_summary_fill(uint32_t* words, int64_t n_words, hipStream_t stream);
+hipError_t launch_summary_update(const SummaryParams& p, bool fp8, hipStream_t stream);
+hipError_t launch_summary_build(const SummaryParams& p, bool fp8, hipStream_t stream);
+hipError_t launch_page_select(const SelectParams& p, hipStream_t stream);
 // Resident wavefronts of the decode kernel on the current device (0 on error).
 int decode_resident_waves(int head_dim, bool fp8);
 

@@ -1,0 +1,480 @@
+// Query-aware page selection (Quest) over the paged cache ("KV Cache
+// Engineering for LLM Serving", section 7, Query-aware sparse reads).
+//
+// A page is one cache block.  Each (block, KV head) keeps, per key
+// dimension, the minimum and the maximum of the keys stored in it; a new
+// query scores every page of its sequence by the largest q.k any key inside
+// that min/max box could reach, sum_d max(q_d min_d, q_d max_d), and only the
+// best `budget` pages are then read by the decode.
+//
+// Summary words: [num_blocks][Hkv][head_dim] uint32, one per (block, head,
+// dim): bits 0-15 hold the minimum and bits 16-31 the maximum, both as bf16
+// (every stored key is exactly a bf16 value: a bf16 key, or an e4m3 code's
+// value without the per-tensor scale).  An empty summary is min = +inf,
+// max = -inf.
+//
+// Kernels:
+//   summary_fill_kernel    every word empty (a plain fill, graph-safe).
+//   summary_reset_kernel   words of blocks written at offset 0 in this call
+//                          become empty (a block's first token starts it).
+//   summary_merge_kernel   each written token's stored key widens its
+//                          block's words (compare-and-swap per word).
+//   summary_build_kernel   words of listed blocks recomputed from their
+//                          first `count` tokens (after a copy or swap-in).
+//   page_score_kernel      score of every page of every (sequence, KV head),
+//                          as an order-preserving uint32 key.
+//   page_select_kernel     per (sequence, KV head): the `budget` best pages
+//                          (equal scores: lower page first) by a radix select
+//                          on the keys, written in page order as a compacted
+//                          block table, with the token count it covers.
+// The decode over the compacted tables is the paged decode kernel itself,
+// run with one "sequence" per (sequence, KV head).
+#include "pa_internal.h"
+
+namespace pa {
+
+namespace {
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr uint32_t kEmptyWord = 0xFF807F80u;  // max = -inf (bf16 0xFF80), min = +inf (0x7F80)
+
+__device__ __forceinline__ float bf16f(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+// bf16 bits of an e4m3fn code's value (no scale): exact.  NaN codes give a
+// bf16 NaN.
+__device__ __forceinline__ uint32_t e4m3_to_bf16(uint32_t c) {
+  const uint32_t sign = (c & 0x80u) << 8;
+  const uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
+  if (e == 15u && m == 7u) return sign | 0x7FC0u;
+  if (e == 0u) return sign | (__float_as_uint((float)m * 0x1p-9f) >> 16);
+  return sign | ((e + 120u) << 7) | (m << 4);
+}
+
+// Widens one summary word by a key value (bf16 bits); NaN keys are ignored.
+// Ranges only grow inside one launch, so a word that already covers the
+// value needs no write.
+__device__ __forceinline__ void widen(uint32_t* w, uint32_t vb) {
+  const float v = bf16f(vb);
+  if (v != v) return;
+  uint32_t old = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (;;) {
+    const uint32_t lo = old & 0xFFFFu, hi = old >> 16;
+    const bool lower = v < bf16f(lo), higher = v > bf16f(hi);
+    if (!lower && !higher) return;
+    const uint32_t nw = ((higher ? vb : hi) << 16) | (lower ? vb : lo);
+    if (__hip_atomic_compare_exchange_strong(w, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT))
+      return;
+  }
+}
+
+__global__ __launch_bounds__(256) void summary_fill_kernel(u32x4* words, int64_t n4) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n4) words[i] = u32x4{kEmptyWord, kEmptyWord, kEmptyWord, kEmptyWord};
+}
+
+// One thread per (token, head, 4 words).
+__global__ __launch_bounds__(256) void summary_reset_kernel(const SummaryParams p) {
+  const int q4 = p.head_dim / 4;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t per_token = (int64_t)p.num_kv_heads * q4;
+  if (gid >= (int64_t)p.num_tokens * per_token) return;
+  const int j = (int)(gid / per_token);
+  const int rem = (int)(gid - (int64_t)j * per_token);
+  const int h = rem / q4, i = rem - h * q4;
+  const int64_t slot = p.slots[j];
+  if (slot < 0 || slot >= (int64_t)p.num_blocks * p.block_size || slot % p.block_size != 0) return;
+  const int64_t blk = slot / p.block_size;
+  u32x4* w = reinterpret_cast<u32x4*>(p.words + (blk * p.num_kv_heads + h) * p.head_dim) + i;
+  *w = u32x4{kEmptyWord, kEmptyWord, kEmptyWord, kEmptyWord};
+}
+
+// bf16 bits of element e of a 16-byte K chunk.
+template <bool FP8>
+__device__ __forceinline__ uint32_t chunk_elem(const u32x4& c, int e) {
+  if constexpr (FP8) return e4m3_to_bf16((c[e >> 2] >> (8 * (e & 3))) & 0xFFu);
+  return (c[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+}
+
+// Byte offset of the 16-byte K chunk (block, head, token, chunk dg): the
+// cache layout [blk][h][t / 16][d / X][t % 16][X elements].
+__device__ __forceinline__ int64_t k_chunk(const SummaryParams& p, int64_t blk, int h, int t, int dg,
+                                           int eb) {
+  const int subs = p.block_size / kSub;
+  const int64_t tile = ((blk * p.num_kv_heads + h) * subs + t / kSub) * (int64_t)(kSub * p.head_dim) * eb;
+  return tile + ((int64_t)dg * kSub + t % kSub) * 16;
+}
+
+// One thread per (token, head, 16-byte chunk of the key).
+template <bool FP8>
+__global__ __launch_bounds__(256) void summary_merge_kernel(const SummaryParams p) {
+  constexpr int X = FP8 ? 16 : 8;
+  const int groups = p.head_dim / X;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t per_token = (int64_t)p.num_kv_heads * groups;
+  if (gid >= (int64_t)p.num_tokens * per_token) return;
+  const int j = (int)(gid / per_token);
+  const int rem = (int)(gid - (int64_t)j * per_token);
+  const int h = rem / groups, dg = rem - h * groups;
+  const int64_t slot = p.slots[j];
+  if (slot < 0 || slot >= (int64_t)p.num_blocks * p.block_size) return;
+  const int64_t blk = slot / p.block_size;
+  const int t = (int)(slot - blk * p.block_size);
+  const u32x4 c = *reinterpret_cast<const u32x4*>(p.k_cache + k_chunk(p, blk, h, t, dg, FP8 ? 1 : 2));
+  uint32_t* w = p.words + (blk * p.num_kv_heads + h) * p.head_dim + dg * X;
+#pragma unroll
+  for (int e = 0; e < X; ++e) widen(w + e, chunk_elem<FP8>(c, e));
+}
+
+// One thread per (listed block, head, 16-byte chunk): min and max over the
+// block's first count tokens, then one store per word.
+template <bool FP8>
+__global__ __launch_bounds__(256) void summary_build_kernel(const SummaryParams p) {
+  constexpr int X = FP8 ? 16 : 8;
+  const int groups = p.head_dim / X;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t per_item = (int64_t)p.num_kv_heads * groups;
+  if (gid >= (int64_t)p.num_tokens * per_item) return;
+  const int i = (int)(gid / per_item);
+  const int rem = (int)(gid - (int64_t)i * per_item);
+  const int h = rem / groups, dg = rem - h * groups;
+  const int blk = p.blocks[i];
+  if ((unsigned)blk >= (unsigned)p.num_blocks) return;
+  int count = p.counts[i];
+  count = count < 0 ? 0 : (count > p.block_size ? p.block_size : count);
+  uint32_t lo[X], hi[X];
+#pragma unroll
+  for (int e = 0; e < X; ++e) {
+    lo[e] = 0x7F80u;
+    hi[e] = 0xFF80u;
+  }
+  for (int t = 0; t < count; ++t) {
+    const u32x4 c = *reinterpret_cast<const u32x4*>(p.k_cache + k_chunk(p, blk, h, t, dg, FP8 ? 1 : 2));
+#pragma unroll
+    for (int e = 0; e < X; ++e) {
+      const uint32_t vb = chunk_elem<FP8>(c, e);
+      const float v = bf16f(vb);
+      if (v < bf16f(lo[e])) lo[e] = vb;
+      if (v > bf16f(hi[e])) hi[e] = vb;
+    }
+  }
+  u32x4* w = reinterpret_cast<u32x4*>(p.words + ((int64_t)blk * p.num_kv_heads + h) * p.head_dim + dg * X);
+#pragma unroll
+  for (int v = 0; v < X / 4; ++v)
+    w[v] = u32x4{(hi[4 * v] << 16) | lo[4 * v], (hi[4 * v + 1] << 16) | lo[4 * v + 1],
+                 (hi[4 * v + 2] << 16) | lo[4 * v + 2], (hi[4 * v + 3] << 16) | lo[4 * v + 3]};
+}
+
+// Order-preserving uint32 of a score: a larger key is a larger score; -0 is
+// +0, and NaN takes the lowest key.
+__device__ __forceinline__ uint32_t score_key(float x) {
+  if (x != x) return 0u;
+  const uint32_t u = __float_as_uint(x + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Pages of sequence s, or -1 for a length outside [0, max_blocks * bs].
+__device__ __forceinline__ int pages_of(const SelectParams& p, int s) {
+  const int L = p.seq_lens[s];
+  if (L < 0 || (int64_t)L > (int64_t)p.max_blocks * p.block_size) return -1;
+  return (L + p.block_size - 1) / p.block_size;
+}
+
+// Work item (chunk c, unit = s * Hkv + h): pages c * 256 .. + 255 of the
+// unit, one per thread; workgroups stride over the items, chunk-major, so
+// the first chunks of all units (the only ones short sequences have) spread
+// over every XCD.  Each thread sums over the dimensions in order, in
+// float32, for every query head of the group, and keeps the largest sum.
+//
+// For a page's min <= max and a query value q, max(q * min, q * max) is
+// q * max when q >= 0 and q * min otherwise; with q+ = (q >= 0 ? q : 0) and
+// q- = (q < 0 ? q : 0) that term is added as two fused multiply-adds,
+// acc = fma(q+, max, acc) then acc = fma(q-, min, acc), one of which adds a
+// zero.  A product of two bf16 values is exact in float32 whenever its
+// magnitude is at least 2^-134 (so for any query and key values of magnitude
+// at least 2^-67, or zero), so this rounds exactly as a rounded product and a
+// rounded sum would (a zero's sign aside, which never changes a sum's
+// value), with no select and no compare in the loop.  q+ and q- of the
+// group sit in LDS (read as broadcasts); a page's row is read one 128-byte
+// line (32 dimensions) at a time and used whole, and its words are unpacked
+// once per dimension for 8 query heads.
+constexpr int kScorePages = 256;
+constexpr int kScoreGrid = 2048;
+
+template <int D>
+__global__ __launch_bounds__(256) void page_score_kernel(const SelectParams p) {
+  __shared__ float qpos[kMaxGroupQuest * D], qneg[kMaxGroupQuest * D];
+  const int Hkv = p.num_kv_heads, G = p.group;
+  const int units = p.num_seqs * Hkv;
+  const int items = units * p.chunks;
+  for (int it = blockIdx.x; it < items; it += gridDim.x) {
+    const int c = it / units, unit = it - c * units;
+    const int s = unit / Hkv, h = unit - s * Hkv;
+    const int np = pages_of(p, s);
+    if (c * kScorePages >= np) continue;                     // uniform
+    __syncthreads();                                         // previous item done with q+/q-
+    const uint16_t* qg = p.q + ((int64_t)s * p.num_q_heads + (int64_t)h * G) * D;
+    for (int i = threadIdx.x; i < G * D; i += 256) {
+      const uint32_t b = qg[i];
+      const float qf = __uint_as_float(b << 16);
+      qpos[i] = (b & 0x8000u) ? 0.f : qf;
+      qneg[i] = (b & 0x8000u) ? qf : 0.f;
+    }
+    __syncthreads();
+    const int pg = c * kScorePages + (int)threadIdx.x;
+    if (pg >= np) continue;
+    const int blk = p.block_tables[(int64_t)s * p.max_blocks + pg];
+    uint32_t key = 0u;  // a block outside the pool scores lowest
+    if ((unsigned)blk < (unsigned)p.num_blocks) {
+      const u32x4* w = reinterpret_cast<const u32x4*>(p.words + ((int64_t)blk * Hkv + h) * D);
+      float best = -__builtin_inff();
+      for (int g0 = 0; g0 < G; g0 += 8) {
+        float acc[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+#pragma unroll 1
+        for (int b = 0; b < D / 32; ++b) {
+          u32x4 line[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) line[i] = w[8 * b + i];
+#pragma unroll
+          for (int c8 = 0; c8 < 4; ++c8) {
+            float mnf[8], mxf[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const uint32_t word = line[2 * c8 + e / 4][e % 4];
+              mnf[e] = __uint_as_float(word << 16);
+              mxf[e] = __uint_as_float(word & 0xFFFF0000u);
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              if (g0 + j < G) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                  const int qi = (g0 + j) * D + 32 * b + 8 * c8 + e;
+                  acc[j] = __builtin_fmaf(qpos[qi], mxf[e], acc[j]);
+                  acc[j] = __builtin_fmaf(qneg[qi], mnf[e], acc[j]);
+                }
+              }
+            }
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (g0 + j < G) best = __builtin_fmaxf(best, acc[j]);
+      }
+      key = score_key(best);
+    }
+    p.keys[(int64_t)unit * p.max_blocks + pg] = key;
+  }
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ int wave_incl_sum(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o, 64);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
+// Sum of v over the 256 threads (red: 4 ints of LDS; two barriers).
+__device__ __forceinline__ int block_sum(int v, int* red) {
+  v = wave_sum(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  const int t = red[0] + red[1] + red[2] + red[3];
+  __syncthreads();
+  return t;
+}
+
+// Exclusive prefix sum of v over the 256 threads in thread order.
+__device__ __forceinline__ int block_excl_sum(int v, int* red) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int incl = wave_incl_sum(v, lane);
+  if (lane == 63) red[wv] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int i = 0; i < wv; ++i) before += red[i];
+  __syncthreads();
+  return before + incl - v;
+}
+
+// Keys of up to kSelectLds pages are kept in LDS, one pad word per 32 so
+// that threads walking contiguous ranges hit different banks; longer
+// sequences read them from global memory (where the score kernel just
+// wrote them).
+constexpr int kSelectLds = 12288;
+constexpr int kSelectRegs = 32;   // keys per thread held in registers (pages <= 8192)
+__device__ __forceinline__ int lds_index(int i) { return i + (i >> 5); }
+
+// Workgroup per unit (s, h): the budget best pages by key, equal keys to the
+// lower page; written in page order to sel_tables[unit][0..budget), with
+// sel_lens[unit] = tokens they hold.
+//
+// The threshold T = the budget-th largest key is found bit by bit from the
+// top (32 counting rounds: T keeps a bit when at least `budget` keys are
+// >= T with it).  Then each thread takes a contiguous range of pages: the
+// pages above T, and the first (budget - count above T) pages equal to T,
+// go to their place in page order through two prefix sums.
+template <bool LDS>
+__device__ __forceinline__ void select_unit(const SelectParams& p, int unit, int s, int np, const uint32_t* gk,
+                                            uint32_t* lk, int* red) {
+  const int tid = threadIdx.x;
+  const int B = p.budget;
+  int32_t* out = p.sel_tables + (int64_t)unit * B;
+  const int32_t* row = p.block_tables + (int64_t)s * p.max_blocks;
+  auto key = [&](int i) -> uint32_t {
+    if constexpr (LDS) return lk[lds_index(i)];
+    return gk[i];
+  };
+  uint32_t T = 0u;
+  if (np <= 256 * kSelectRegs) {
+    // Counting rounds over keys held in registers: no memory latency per round.
+    uint32_t kr[kSelectRegs];
+#pragma unroll
+    for (int k = 0; k < kSelectRegs; ++k) kr[k] = tid + 256 * k < np ? key(tid + 256 * k) : 0u;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = T | (1u << bit);   // >= 1: the padding keys 0 never count
+      int c = 0;
+#pragma unroll
+      for (int k = 0; k < kSelectRegs; ++k) c += kr[k] >= cand ? 1 : 0;
+      if (block_sum(c, red) >= B) T = cand;
+    }
+  } else {
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = T | (1u << bit);
+      int c = 0;
+      for (int i = tid; i < np; i += 256) c += key(i) >= cand ? 1 : 0;
+      if (block_sum(c, red) >= B) T = cand;
+    }
+  }
+  // Contiguous ranges: thread t owns pages [t * m, min(np, (t + 1) * m)).
+  const int m = (np + 255) / 256;
+  const int i0 = tid * m < np ? tid * m : np, i1 = (tid + 1) * m < np ? (tid + 1) * m : np;
+  int above = 0, equal = 0;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t k = key(i);
+    above += k > T ? 1 : 0;
+    equal += k == T ? 1 : 0;
+  }
+  const int need = B - block_sum(above, red);
+  const int eq_rank0 = block_excl_sum(equal, red);
+  int taken = 0;
+  {
+    int er = eq_rank0;
+    for (int i = i0; i < i1; ++i) {
+      const uint32_t k = key(i);
+      const bool eq = k == T;
+      taken += (k > T || (eq && er < need)) ? 1 : 0;
+      er += eq ? 1 : 0;
+    }
+  }
+  int pos = block_excl_sum(taken, red);
+  int er = eq_rank0;
+  const int last_valid = p.seq_lens[s] - (np - 1) * p.block_size;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t k = key(i);
+    const bool eq = k == T;
+    const bool take = k > T || (eq && er < need);
+    er += eq ? 1 : 0;
+    if (take && pos < B) {
+      out[pos] = row[i];
+      ++pos;
+    }
+    if (i == np - 1) p.sel_lens[unit] = take ? (B - 1) * p.block_size + last_valid : B * p.block_size;
+  }
+}
+
+// Units whose pages all fit the budget copy their table row; invalid
+// lengths give sel_lens = -1.
+__global__ __launch_bounds__(256) void page_select_kernel(const SelectParams p) {
+  __shared__ uint32_t lk[kSelectLds + kSelectLds / 32];
+  __shared__ int red[4];
+  const int unit = blockIdx.x;
+  const int s = unit / p.num_kv_heads;
+  const int tid = threadIdx.x;
+  const int B = p.budget;
+  const int np = pages_of(p, s);
+  if (np < 0 || np <= B) {
+    int32_t* out = p.sel_tables + (int64_t)unit * B;
+    const int32_t* row = p.block_tables + (int64_t)s * p.max_blocks;
+    for (int i = tid; i < B; i += 256) out[i] = (np >= 0 && i < np) ? row[i] : -1;
+    if (tid == 0) p.sel_lens[unit] = np < 0 ? -1 : p.seq_lens[s];
+    return;
+  }
+  const uint32_t* gk = p.keys + (int64_t)unit * p.max_blocks;
+  if (np <= kSelectLds) {
+    // Eight independent loads in flight per thread before their stores.
+    for (int i0 = tid; i0 < np; i0 += 8 * 256) {
+      uint32_t v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = i0 + 256 * k < np ? gk[i0 + 256 * k] : 0u;
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (i0 + 256 * k < np) lk[lds_index(i0 + 256 * k)] = v[k];
+    }
+    __syncthreads();
+    select_unit<true>(p, unit, s, np, gk, lk, red);
+  } else {
+    select_unit<false>(p, unit, s, np, gk, lk, red);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_summary_fill(uint32_t* words, int64_t n_words, hipStream_t stream) {
+  const int64_t n4 = n_words / 4;
+  if (n4 == 0) return hipSuccess;
+  hipLaunchKernelGGL(summary_fill_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,
+                     reinterpret_cast<u32x4*>(words), n4);
+  return hipGetLastError();
+}
+
+hipError_t launch_summary_update(const SummaryParams& p, bool fp8, hipStream_t stream) {
+  if (p.num_tokens == 0) return hipSuccess;
+  const int64_t reset_threads = (int64_t)p.num_tokens * p.num_kv_heads * (p.head_dim / 4);
+  hipLaunchKernelGGL(summary_reset_kernel, dim3((unsigned)((reset_threads + 255) / 256)), dim3(256), 0,
+                     stream, p);
+  const int64_t merge_threads = (int64_t)p.num_tokens * p.num_kv_heads * (p.head_dim / (fp8 ? 16 : 8));
+  const dim3 grid((unsigned)((merge_threads + 255) / 256));
+  if (fp8)
+    hipLaunchKernelGGL(summary_merge_kernel<true>, grid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(summary_merge_kernel<false>, grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_summary_build(const SummaryParams& p, bool fp8, hipStream_t stream) {
+  if (p.num_tokens == 0) return hipSuccess;
+  const int64_t threads = (int64_t)p.num_tokens * p.num_kv_heads * (p.head_dim / (fp8 ? 16 : 8));
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  if (fp8)
+    hipLaunchKernelGGL(summary_build_kernel<true>, grid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(summary_build_kernel<false>, grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_page_select(const SelectParams& p, hipStream_t stream) {
+  const int64_t units = (int64_t)p.num_seqs * p.num_kv_heads;
+  if (units == 0) return hipSuccess;
+  int64_t groups = units * p.chunks;
+  if (groups > kScoreGrid) groups = kScoreGrid;
+  const dim3 grid((unsigned)groups);
+  if (p.head_dim == 128)
+    hipLaunchKernelGGL(page_score_kernel<128>, grid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(page_score_kernel<64>, grid, dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(page_select_kernel, dim3((unsigned)units), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -11,7 +11,7 @@ import pytest
 import paged_kv_cache_32_amd as pa
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADERS = [os.path.join(ROOT, "include", h) for h in ("pa.h", "pa_blocks.h")]
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("pa.h", "pa_blocks.h", "pa_quest.h")]
 
 if not os.path.exists(pa.LIB_PATH):
     pytest.skip("libpa.so not built", allow_module_level=True)
@@ -38,7 +38,9 @@ def test_exports_every_declared_symbol():
     assert set(names) >= {"pa_cache_write", "pa_cache_write_fp8", "pa_decode", "pa_decode_fp8",
                           "pa_decode_workspace_size", "pa_status_string", "pa_abi_version",
                           "pa_copy_blocks", "pa_swap_out", "pa_swap_in", "pa_bm_create",
-                          "pa_bm_append_token", "pa_bm_batch", "pa_bm_swap_out", "pa_bm_swap_in"}
+                          "pa_bm_append_token", "pa_bm_batch", "pa_bm_swap_out", "pa_bm_swap_in",
+                          "pa_quest_clear", "pa_quest_update", "pa_quest_summarize", "pa_quest_select",
+                          "pa_decode_quest", "pa_decode_quest_fp8"}
     for n in names:
         assert hasattr(lib, n), n
     assert lib.pa_abi_version() == 2
@@ -141,6 +143,46 @@ def test_swap_validation(name):
     assert fn(ctypes.byref(bad), *ok[1:]) == SHAPE
 
 
+def test_quest_validation():
+    lib = pa.lib()
+    d = desc()                                         # 2 KV heads, head_dim 128, block 16
+    # summaries
+    assert lib.pa_quest_clear(None, FAKE, None) == NULL
+    assert lib.pa_quest_clear(ctypes.byref(d), None, None) == NULL
+    for fn in (lambda *a: lib.pa_quest_update(*a[:3], FAKE, *a[3:]),
+               lambda *a: lib.pa_quest_summarize(*a[:3], FAKE, FAKE, *a[3:])):
+        assert fn(None, 2, FAKE, 4, FAKE, None) == NULL
+        assert fn(ctypes.byref(d), 3, FAKE, 4, FAKE, None) == UNSUP
+        assert fn(ctypes.byref(d), 2, FAKE, -1, FAKE, None) == SHAPE
+        assert fn(ctypes.byref(d), 2, FAKE, 0, None, None) == OK
+        assert fn(ctypes.byref(d), 2, None, 4, FAKE, None) == NULL
+    assert lib.pa_quest_update(ctypes.byref(d), 2, FAKE, None, 4, FAKE, None) == NULL
+    # selection: (desc, q, S, Hq, summaries, bt, maxb, lens, budget, sel, sel_lens, ws, ws_bytes, stream)
+    ws_need = lib.pa_quest_select_workspace_size(3, 2, 8)
+    assert ws_need == 256 and lib.pa_quest_select_workspace_size(-1, 2, 8) == 0
+
+    def sel(S=3, Hq=16, maxb=8, budget=2, ws=FAKE, ws_bytes=ws_need, q=FAKE, dd=d):
+        return lib.pa_quest_select(ctypes.byref(dd) if dd else None, q, S, Hq, FAKE, FAKE, maxb, FAKE, budget,
+                                   FAKE, FAKE, ws, ws_bytes, None)
+    assert sel(dd=None) == NULL
+    assert sel(budget=0) == SHAPE
+    assert sel(Hq=15) == SHAPE
+    assert sel(Hq=2 * 17) == UNSUP
+    assert sel(S=0) == OK
+    assert sel(q=None) == NULL
+    assert sel(ws=None) == WS
+    assert sel(ws_bytes=ws_need - 1) == WS
+    # quest decode
+    assert lib.pa_decode_quest_workspace_size(ctypes.byref(d), 3, 16, 0, 0) == 0
+
+    def dq(budget=4, Hq=16, S=3):
+        return lib.pa_decode_quest(ctypes.byref(d), FAKE, S, Hq, FAKE, FAKE, FAKE, budget, FAKE, 0.1, FAKE, 0,
+                                   FAKE, 1 << 20, None)
+    assert dq(budget=0) == SHAPE
+    assert dq(Hq=15) == SHAPE
+    assert dq(S=0) == OK
+
+
 def test_device_errors_without_gpu():
     import torch
     if torch.cuda.is_available():
@@ -154,6 +196,10 @@ def test_device_errors_without_gpu():
     assert pa.lib().pa_copy_blocks(ctypes.byref(d), 2, FAKE, FAKE, FAKE, 1, None) == DEVICE
     for fn in (pa.lib().pa_swap_out, pa.lib().pa_swap_in):
         assert fn(ctypes.byref(d), 2, FAKE, FAKE, FAKE, 1, FAKE, None) == DEVICE
+    assert pa.lib().pa_quest_clear(ctypes.byref(d), FAKE, None) == DEVICE
+    assert pa.lib().pa_quest_update(ctypes.byref(d), 2, FAKE, FAKE, 4, FAKE, None) == DEVICE
+    assert pa.lib().pa_quest_select(ctypes.byref(d), FAKE, 3, 16, FAKE, FAKE, 8, FAKE, 2, FAKE, FAKE, FAKE,
+                                    256, None) == DEVICE
 
 
 def test_binding_fails_loudly_without_library(monkeypatch):

@@ -296,3 +296,23 @@ def test_write_maintained_summaries_equal_recomputed(seed):
             a, z = Q.block_summary(g, kc, b, c)
             assert np.array_equal(mn[b], a) and np.array_equal(mx[b], z), (step, b)
         assert all(np.isposinf(mn[b]).all() for b in range(g.num_blocks) if b not in count)
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_sequence_page_summaries_equal_block_summaries(kv_dtype):
+    rng = np.random.default_rng(3)
+    g = paged.Geom(num_blocks=9, block_size=32, num_kv_heads=2, head_dim=64, kv_dtype=kv_dtype)
+    if kv_dtype == "bf16":
+        kc = bf16_bits(rng.standard_normal(g.cache_elems))
+    else:
+        kc = rng.integers(0, 256, g.cache_elems).astype(np.uint8)
+        kc[(kc & 0x7F) == 0x7F] = 0x11                    # no NaN codes
+    row = [7, 2, 5, 0]
+    for L in (1, 32, 33, 100, 128):
+        for h in range(2):
+            mn, mx = Q.sequence_page_summaries(g, kc, row, L, h)
+            pages = -(-L // 32)
+            assert mn.shape == (pages, 64)
+            for p in range(pages):
+                a, z = Q.block_summary(g, kc, row[p], min(32, L - 32 * p))
+                assert np.array_equal(mn[p], a[h]) and np.array_equal(mx[p], z[h])
