@@ -197,8 +197,9 @@ __device__ __forceinline__ int pages_of(const SelectParams& p, int s) {
 // rounded sum would (a zero's sign aside, which never changes a sum's
 // value), with no select and no compare in the loop.  q+ and q- of the
 // group sit in LDS (read as broadcasts); a page's row is read one 128-byte
-// line (32 dimensions) at a time and used whole, and its words are unpacked
-// once per dimension for 8 query heads.
+// line (32 dimensions) at a time and used whole, the next line's loads in
+// flight while the current one is summed, and its words are unpacked once
+// per dimension for 8 query heads.
 constexpr int kScorePages = 256;
 constexpr int kScoreGrid = 2048;
 
@@ -233,17 +234,20 @@ __global__ __launch_bounds__(256) void page_score_kernel(const SelectParams p) {
         float acc[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+        u32x4 cur[8], nxt[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) cur[i] = w[i];
 #pragma unroll 1
         for (int b = 0; b < D / 32; ++b) {
-          u32x4 line[8];
+          const int bn = b + 1 < D / 32 ? b + 1 : b;     // last block: reload itself (never used)
 #pragma unroll
-          for (int i = 0; i < 8; ++i) line[i] = w[8 * b + i];
+          for (int i = 0; i < 8; ++i) nxt[i] = w[8 * bn + i];
 #pragma unroll
           for (int c8 = 0; c8 < 4; ++c8) {
             float mnf[8], mxf[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              const uint32_t word = line[2 * c8 + e / 4][e % 4];
+              const uint32_t word = cur[2 * c8 + e / 4][e % 4];
               mnf[e] = __uint_as_float(word << 16);
               mxf[e] = __uint_as_float(word & 0xFFFF0000u);
             }
@@ -259,6 +263,8 @@ __global__ __launch_bounds__(256) void page_score_kernel(const SelectParams p) {
               }
             }
           }
+#pragma unroll
+          for (int i = 0; i < 8; ++i) cur[i] = nxt[i];
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j)
@@ -295,6 +301,41 @@ __device__ __forceinline__ int block_sum(int v, int* red) {
   return t;
 }
 
+// Sum over the 256 threads of small counts v in [0, 64): each bit of v is
+// counted across the wavefront with a ballot and a scalar popcount, so the
+// wavefront's sum needs no cross-lane data movement.
+__device__ __forceinline__ int block_sum_small(int v, int* red) {
+  int t = 0;
+#pragma unroll
+  for (int b = 0; b < 6; ++b) t += __popcll(__ballot((v >> b) & 1)) << b;
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = t;
+  __syncthreads();
+  t = red[0] + red[1] + red[2] + red[3];
+  __syncthreads();
+  return t;
+}
+
+// Exclusive prefix sum in thread order of small counts v in [0, 64): within
+// a wavefront, each bit of v is counted over the lower lanes with a ballot
+// and mbcnt (set bits below the lane), then the wavefronts' totals are
+// combined through LDS.
+__device__ __forceinline__ int block_excl_sum_small(int v, int* red) {
+  int below = 0, total = 0;
+#pragma unroll
+  for (int b = 0; b < 6; ++b) {
+    const uint64_t m = __ballot((v >> b) & 1);
+    below += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u)) << b;
+    total += __popcll(m) << b;
+  }
+  const int wv = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wv] = total;
+  __syncthreads();
+  int before = 0;
+  for (int i = 0; i < wv; ++i) before += red[i];
+  __syncthreads();
+  return before + below;
+}
+
 // Exclusive prefix sum of v over the 256 threads in thread order.
 __device__ __forceinline__ int block_excl_sum(int v, int* red) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -324,6 +365,76 @@ __device__ __forceinline__ int lds_index(int i) { return i + (i >> 5); }
 // >= T with it).  Then each thread takes a contiguous range of pages: the
 // pages above T, and the first (budget - count above T) pages equal to T,
 // go to their place in page order through two prefix sums.
+//
+// Units of up to 256 * kSelectRegs pages keep everything in registers: the
+// keys (strided, for counting), and the keys and block ids of the thread's
+// own contiguous range (for the compaction).  All of those loads are issued
+// before the counting rounds, so their latency is paid once.  Longer units
+// read keys from LDS or global memory in each round.
+__device__ __forceinline__ void select_small(const SelectParams& p, int unit, int s, int np,
+                                             const uint32_t* gk, uint32_t* lk, int* red) {
+  const int tid = threadIdx.x;
+  const int B = p.budget;
+  int32_t* out = p.sel_tables + (int64_t)unit * B;
+  const int32_t* row = p.block_tables + (int64_t)s * p.max_blocks;
+  const int m = (np + 255) / 256;                       // <= kSelectRegs
+  const int i0 = tid * m < np ? tid * m : np;
+  const int cnt = np - i0 < m ? np - i0 : m;
+  uint32_t kr[kSelectRegs];
+  int32_t ids[kSelectRegs];
+#pragma unroll
+  for (int k = 0; k < kSelectRegs; ++k) kr[k] = tid + 256 * k < np ? gk[tid + 256 * k] : 0u;
+#pragma unroll
+  for (int k = 0; k < kSelectRegs; ++k) ids[k] = k < cnt ? row[i0 + k] : -1;
+#pragma unroll
+  for (int k = 0; k < kSelectRegs; ++k)
+    if (tid + 256 * k < np) lk[lds_index(tid + 256 * k)] = kr[k];
+  uint32_t T = 0u;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = T | (1u << bit);   // >= 1: the padding keys 0 never count
+    int c = 0;
+#pragma unroll
+    for (int k = 0; k < kSelectRegs; ++k) c += kr[k] >= cand ? 1 : 0;
+    if (block_sum_small(c, red) >= B) T = cand;   // its barriers also publish the LDS keys
+  }
+  uint32_t mine[kSelectRegs];
+  int above = 0, equal = 0;
+#pragma unroll
+  for (int k = 0; k < kSelectRegs; ++k) {
+    mine[k] = k < cnt ? lk[lds_index(i0 + k)] : 0u;
+    above += (k < cnt && mine[k] > T) ? 1 : 0;
+    equal += (k < cnt && mine[k] == T) ? 1 : 0;
+  }
+  const int need = B - block_sum_small(above, red);
+  const int eq_rank0 = block_excl_sum_small(equal, red);
+  int taken = 0;
+  {
+    int er = eq_rank0;
+#pragma unroll
+    for (int k = 0; k < kSelectRegs; ++k) {
+      const bool eq = k < cnt && mine[k] == T;
+      taken += (k < cnt && (mine[k] > T || (eq && er < need))) ? 1 : 0;
+      er += eq ? 1 : 0;
+    }
+  }
+  int pos = block_excl_sum_small(taken, red);
+  int er = eq_rank0;
+  const int last_valid = p.seq_lens[s] - (np - 1) * p.block_size;
+#pragma unroll
+  for (int k = 0; k < kSelectRegs; ++k) {
+    if (k < cnt) {
+      const bool eq = mine[k] == T;
+      const bool take = mine[k] > T || (eq && er < need);
+      er += eq ? 1 : 0;
+      if (take && pos < B) {
+        out[pos] = ids[k];
+        ++pos;
+      }
+      if (i0 + k == np - 1) p.sel_lens[unit] = take ? (B - 1) * p.block_size + last_valid : B * p.block_size;
+    }
+  }
+}
+
 template <bool LDS>
 __device__ __forceinline__ void select_unit(const SelectParams& p, int unit, int s, int np, const uint32_t* gk,
                                             uint32_t* lk, int* red) {
@@ -336,25 +447,11 @@ __device__ __forceinline__ void select_unit(const SelectParams& p, int unit, int
     return gk[i];
   };
   uint32_t T = 0u;
-  if (np <= 256 * kSelectRegs) {
-    // Counting rounds over keys held in registers: no memory latency per round.
-    uint32_t kr[kSelectRegs];
-#pragma unroll
-    for (int k = 0; k < kSelectRegs; ++k) kr[k] = tid + 256 * k < np ? key(tid + 256 * k) : 0u;
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cand = T | (1u << bit);   // >= 1: the padding keys 0 never count
-      int c = 0;
-#pragma unroll
-      for (int k = 0; k < kSelectRegs; ++k) c += kr[k] >= cand ? 1 : 0;
-      if (block_sum(c, red) >= B) T = cand;
-    }
-  } else {
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cand = T | (1u << bit);
-      int c = 0;
-      for (int i = tid; i < np; i += 256) c += key(i) >= cand ? 1 : 0;
-      if (block_sum(c, red) >= B) T = cand;
-    }
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = T | (1u << bit);
+    int c = 0;
+    for (int i = tid; i < np; i += 256) c += key(i) >= cand ? 1 : 0;
+    if (block_sum(c, red) >= B) T = cand;
   }
   // Contiguous ranges: thread t owns pages [t * m, min(np, (t + 1) * m)).
   const int m = (np + 255) / 256;
@@ -411,7 +508,9 @@ __global__ __launch_bounds__(256) void page_select_kernel(const SelectParams p) 
     return;
   }
   const uint32_t* gk = p.keys + (int64_t)unit * p.max_blocks;
-  if (np <= kSelectLds) {
+  if (np <= 256 * kSelectRegs) {
+    select_small(p, unit, s, np, gk, lk, red);
+  } else if (np <= kSelectLds) {
     // Eight independent loads in flight per thread before their stores.
     for (int i0 = tid; i0 < np; i0 += 8 * 256) {
       uint32_t v[8];
