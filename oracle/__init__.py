@@ -20,6 +20,9 @@ eye:
 * ``oracle.blocks`` - the block manager's rules (FIFO free list, reference
   counts, full-prefix keys with a model key, fork, copy-on-write) and the
   whole-block copy, and swaps to host memory and back.
+* ``oracle.cascade`` - the shared-prefix segments of a batch (maximal runs of
+  full blocks held by the same set of sequences) and decode by parts merged
+  by log-sum-exp.
 * ``oracle.quest``  - query-aware page selection: per-block min/max key
   summaries (recomputed, or kept by the cache writes), page scores, the
   top-budget choice, and attention over the chosen pages.
@@ -29,4 +32,4 @@ value the pages print, a closed form, an invariant or brute force; none is
 "parity unpinned".
 """
 
-from . import blocks, e4m3, pages, paged, quest  # noqa: F401
+from . import blocks, cascade, e4m3, pages, paged, quest  # noqa: F401

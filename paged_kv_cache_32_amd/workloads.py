@@ -390,7 +390,7 @@ def llama70b_layer(seed=2, num_seqs=64, block_size=16, kv_dtype="bf16", num_laye
 
 def prefix_shared(seed=3, num_seqs=256, block_size=32, system_tokens=900, num_pools=12,
                   pool_range=(2000, 8000), suffix_median=600.0, pool_share=0.62,
-                  max_len=32768):
+                  max_len=32768, num_q_heads=64, num_kv_heads=8, head_dim=128, kv_dtype="bf16"):
     """Prefix-shared batch on the 70B layer shape, block_size 32.
 
     Every sequence starts with the same 900-token system prompt; then one of
@@ -446,8 +446,9 @@ def prefix_shared(seed=3, num_seqs=256, block_size=32, system_tokens=900, num_po
     bt = np.full((num_seqs, maxb), -1, dtype=np.int32)
     for s, t in enumerate(tables):
         bt[s, :len(t)] = [relabel[b] for b in t]
-    w = Workload("prefix_shared_bs256", 64, 8, 128, block_size, nb, lens, bt,
-                 _slots_for_last_token(lens, bt, block_size), 1.0 / math.sqrt(128), seed=seed)
+    w = Workload("prefix_shared_bs256", num_q_heads, num_kv_heads, head_dim, block_size, nb, lens, bt,
+                 _slots_for_last_token(lens, bt, block_size), 1.0 / math.sqrt(head_dim), kv_dtype=kv_dtype,
+                 seed=seed)
     w.notes = {"suffix_sigma": float(sigma), "pool_share": float(share(sigma)),
                "prefix_hits": cache.hits, "prefix_misses": cache.misses}
     return w
