@@ -44,6 +44,13 @@ Other workloads (--workload), each on the same 70B layer shape:
                        beside it
   quest_llama70b_bs64  the same on the 70B layer bs=64 batch, 64 pages
                        (1,024 tokens) per (sequence, KV head)
+  cascade_prefix_shared_bs256  the prefix-shared batch decoded with
+                       pa_decode_cascade: its shared segments (the system
+                       prompt, the 12 pools) attended to once for all their
+                       sequences, each sequence's private tokens by the paged
+                       decode, then the merge; `value` counts distinct
+                       (physical) KV bytes like prefix_shared_bs256, and the
+                       plain decode of the same batch is timed beside it
   swap_blocks_llama70b pa_swap_out then pa_swap_in of 1,024 blocks (64 MiB of
                        K+V) through pinned host memory: `value` is bytes moved
                        per direction / time (bound by the host link, PCIe 5.0
@@ -80,7 +87,9 @@ MODEL_LAYERS = 80
 SCRUB_BYTES = 512 << 20
 WORKLOADS = {"llama70b_layer_bs64": 2, "prefix_shared_bs256": 3, "long_context_128k": 4,
              "fp8_80layer_bs128": 5, "copy_blocks_llama70b": 2, "sliding_window_llama70b": 2,
-             "swap_blocks_llama70b": 2, "quest_long_context_128k": 4, "quest_llama70b_bs64": 2}
+             "swap_blocks_llama70b": 2, "quest_long_context_128k": 4, "quest_llama70b_bs64": 2,
+             "cascade_prefix_shared_bs256": 3}
+CASCADE_CHUNK_TOKENS = 1024
 QUEST_BUDGET = {"quest_long_context_128k": 256, "quest_llama70b_bs64": 64}   # pages per (seq, KV head)
 HOST_LINK_GBS = 64.0  # PCIe 5.0 x16, per direction: 32 GT/s x 16 lanes / 8 bits
 LOCAL_WINDOW = 1024   # a local layer's window ("KV Cache Engineering for LLM Serving", section 3)
@@ -669,6 +678,101 @@ def bench_quest(args, dev):
     return res
 
 
+def bench_cascade(args, dev):
+    """Shared-prefix decode of the prefix-shared batch against its plain
+    decode (the write of the step's tokens is the same for both and timed
+    separately)."""
+    w = W.config(3)
+    log("workload:", json.dumps(w.summary()))
+    Hkv, D, BS, S = w.num_kv_heads, w.head_dim, w.block_size, w.num_seqs
+    t = w.make_tensors(dev)
+    bt = torch.from_numpy(w.block_tables).to(dev)
+    sl = torch.from_numpy(w.seq_lens).to(dev)
+    sm = torch.from_numpy(w.slot_mapping).to(dev)
+    q, kn, vn, kc, vc = t["q"][0], t["k_new"][0], t["v_new"][0], t["k_cache"][0], t["v_cache"][0]
+    t0 = time.perf_counter()
+    plan = pa.CascadePlan(w.block_tables, w.seq_lens, block_size=BS, num_kv_heads=Hkv, num_q_heads=w.num_q_heads,
+                          chunk_tokens=CASCADE_CHUNK_TOKENS, device=dev)
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    out = torch.empty((S, w.num_q_heads, D), dtype=torch.float32, device=dev)
+    full_out = torch.empty_like(out)
+    desc = pa.make_desc(kc, Hkv, D, BS)
+    cws = torch.zeros(pa.lib().pa_decode_cascade_workspace_size(ctypes.byref(desc), S, w.num_q_heads,
+                                                                w.max_blocks_per_seq, plan.info["num_slots"], 0),
+                      dtype=torch.uint8, device=dev)
+    fws = torch.zeros(pa.pa_decode_workspace_size(w.num_blocks, BS, Hkv, D, S, w.num_q_heads,
+                                                  w.max_blocks_per_seq, 0), dtype=torch.uint8, device=dev)
+    scrub = torch.ones(SCRUB_BYTES // 4, dtype=torch.float32, device=dev)
+    sink = torch.zeros((), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    kw = dict(num_kv_heads=Hkv, block_size=BS)
+
+    def write():
+        pa.pa_cache_write(kn, vn, sm, kc, vc, block_size=BS)
+
+    def cascade():
+        pa.pa_decode_cascade(q, kc, vc, plan, w.scale, out, workspace=cws, **kw)
+
+    def full():
+        pa.pa_decode(q, kc, vc, bt, sl, w.scale, full_out, workspace=fws, **kw)
+
+    for _ in range(args.warmup):
+        write()
+        cascade()
+        full()
+    torch.cuda.synchronize()
+    K = args.steps
+
+    def timed(fn):
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+        for e in ev:
+            if not args.no_scrub:
+                torch.sum(scrub, dim=0, out=sink)
+            e[0].record(stream)
+            fn()
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in ev])
+
+    write_ms = timed(write)
+    cas_ms = timed(cascade)
+    full_ms = timed(full)
+    err = float((out - full_out).abs().max().item())
+    kv_phys, alg_phys = algorithmic_bytes(w, physical=True)
+    kv_log = w.logical_kv_bytes()
+    dec_s = float(cas_ms.mean()) / 1e3
+    step_ms = float((write_ms + cas_ms).mean())
+    gbs = kv_phys / dec_s / 1e9
+    alg_gbs = alg_phys / dec_s / 1e9
+    res = base_record(args, w, K)
+    res["metric"] = "shared-prefix (cascade) decode: distinct KV GB/s and speed-up over plain decode, prefix_shared_bs256"
+    res.update({"value": round(gbs, 1), "ms_per_step": round(step_ms, 4)})
+    res["config"].update({"workload": args.workload, "kv_bytes_per_call": kv_phys,
+                          "kv_bytes_basis": "distinct (physical) tokens", "chunk_tokens": CASCADE_CHUNK_TOKENS,
+                          "scrub_mib_between_steps": 0 if args.no_scrub else SCRUB_BYTES >> 20})
+    res.update({
+        "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "decode_us": {"mean": round(dec_s * 1e6, 2), "p10": round(float(np.percentile(cas_ms, 10)) * 1e3, 2),
+                      "p90": round(float(np.percentile(cas_ms, 90)) * 1e3, 2)},
+        "plain_decode_us": round(float(full_ms.mean()) * 1e3, 2),
+        "speedup_vs_plain_decode": round(float(full_ms.mean()) / float(cas_ms.mean()), 3),
+        "cascade_vs_plain_max_abs": err,
+        "cache_write_us": round(float(write_ms.mean()) * 1e3, 2),
+        "logical_kv_gbs": round(kv_log / dec_s / 1e9, 1),
+        "plan": {k: plan.info[k] for k in ("num_segments", "num_items", "num_slots", "shared_tokens",
+                                           "segment_tokens")},
+        "plan_build_host_ms": round(plan_ms, 2),
+        "layer_tok_s": round(S / (step_ms / 1e3), 1),
+        "roofline": {"bound": "hbm", "achieved": round(alg_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(alg_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "segment_kernel + decode_kernel + combine_kernel (pa_decode_cascade)",
+                     "bytes_per_launch": alg_phys},
+    })
+    if not args.skip_cpu:
+        res["cpu_baseline"] = cpu_baseline(w, t, out)
+    return res
+
+
 def bench_swap(args, dev):
     """pa_swap_out / pa_swap_in of 1,024 blocks of the 70B layer's pool, and
     the default batch's decode with a swap running beside it on a second
@@ -804,6 +908,8 @@ def main():
         res = bench_swap(args, dev)
     elif args.workload.startswith("quest_"):
         res = bench_quest(args, dev)
+    elif args.workload == "cascade_prefix_shared_bs256":
+        res = bench_cascade(args, dev)
     else:
         res = bench_layer(args, dev)
     print(json.dumps(res), flush=True)

@@ -26,7 +26,8 @@ This module states, plainly:
 Readings: only full blocks are shared (a sequence's partly filled last block
 is its own); a segment needs at least two member sequences (a run held by
 one sequence is private); block ids are compared as given, so two tables
-share a position only if they agree on every position before it too.
+share a position only if they agree on every position before it too; a
+length outside [0, table width * block_size] is invalid and shares nothing.
 """
 
 import numpy as np
@@ -42,7 +43,8 @@ def shared_segments(block_tables, seq_lens, block_size, min_members=2):
     and prefix_tokens[s] is the number of tokens of sequence s covered by
     segments (a multiple of block_size)."""
     S = len(seq_lens)
-    full = [max(int(seq_lens[s]), 0) // block_size for s in range(S)]
+    full = [int(seq_lens[s]) // block_size if 0 <= int(seq_lens[s]) <= len(block_tables[s]) * block_size
+            else 0 for s in range(S)]
     segments = []
     prefix = [0] * S
 

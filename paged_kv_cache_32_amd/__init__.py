@@ -48,6 +48,21 @@ class CacheDesc(ctypes.Structure):
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32)]
 
 
+class CascadePlanInfo(ctypes.Structure):
+    _fields_ = [("num_segments", ctypes.c_int32), ("num_items", ctypes.c_int32), ("num_slots", ctypes.c_int32),
+                ("num_seg_blocks", ctypes.c_int32), ("num_members", ctypes.c_int32),
+                ("num_parts", ctypes.c_int32), ("members_per_workgroup", ctypes.c_int32),
+                ("chunk_blocks", ctypes.c_int32), ("shared_tokens", ctypes.c_int64),
+                ("segment_tokens", ctypes.c_int64)]
+
+
+class CascadeDevicePlan(ctypes.Structure):
+    _fields_ = [("items", ctypes.c_void_p), ("num_items", ctypes.c_int32), ("seg_blocks", ctypes.c_void_p),
+                ("members", ctypes.c_void_p), ("parts_off", ctypes.c_void_p), ("parts", ctypes.c_void_p),
+                ("num_slots", ctypes.c_int32), ("private_tables", ctypes.c_void_p),
+                ("private_lens", ctypes.c_void_p)]
+
+
 _lib = None
 
 
@@ -97,6 +112,15 @@ def _load():
         "pa_decode_quest": ([dp, vp, i32, i32, vp, vp, vp, i32, vp, f32, vp, i32, vp, sz, vp], i32),
         "pa_decode_quest_fp8": ([dp, vp, i32, i32, vp, vp, vp, i32, vp, f32, f32, f32, vp, i32, vp, sz,
                                  vp], i32),
+        "pa_cascade_plan_build": ([vp, i32, i32, vp, i32, i32, i32, i32, ctypes.POINTER(vp)], i32),
+        "pa_cascade_plan_destroy": ([vp], None),
+        "pa_cascade_plan_get_info": ([vp, ctypes.POINTER(CascadePlanInfo)], i32),
+        "pa_cascade_plan_export": ([vp, vp, vp, vp, vp, vp, vp, vp, vp], i32),
+        "pa_decode_cascade_workspace_size": ([dp, i32, i32, i32, i32, i32], sz),
+        "pa_decode_cascade": ([dp, vp, i32, i32, vp, vp, i32, ctypes.POINTER(CascadeDevicePlan), f32, vp, i32,
+                               vp, sz, vp], i32),
+        "pa_decode_cascade_fp8": ([dp, vp, i32, i32, vp, vp, i32, ctypes.POINTER(CascadeDevicePlan), f32, f32,
+                                   f32, vp, i32, vp, sz, vp], i32),
         "pa_bm_num_free": ([vp], i32),
         "pa_bm_sequence_info": ([vp, i64, ctypes.POINTER(i32), ctypes.POINTER(i32)], i32),
         "pa_bm_block_table": ([vp, i64, ctypes.POINTER(i32), i32], i32),
@@ -593,3 +617,104 @@ def pa_decode_quest_fp8(q, k_cache, v_cache, sel_tables, sel_lens, scale, k_scal
     """Decode over the chosen pages of an e4m3fn cache."""
     return _decode_quest(True, q, k_cache, v_cache, sel_tables, sel_lens, scale, out, num_kv_heads,
                          block_size, k_scale, v_scale, partition_tokens, workspace)
+
+
+# -- shared-prefix (cascade) decode (include/pa_cascade.h) --------------------
+
+class CascadePlan:
+    """Shared-prefix plan of one batch, built on the host from its block
+    tables and lengths (numpy int32 arrays, as BlockManager.batch returns
+    them) and copied to ``device``.  ``info`` holds the sizes and token
+    counts; ``segments`` is [num_segments, 4] (first block, blocks, members
+    offset, members) and ``members`` the member sequences, for inspection."""
+
+    def __init__(self, block_tables, seq_lens, *, block_size, num_kv_heads, num_q_heads, chunk_tokens=1024,
+                 device="cuda"):
+        import numpy as np
+        bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+        sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+        if bt.ndim != 2 or sl.shape != (bt.shape[0],):
+            raise ValueError("block_tables must be [S, max_blocks] and seq_lens [S]")
+        S, maxb = bt.shape
+        L = _load()
+        h = ctypes.c_void_p()
+        _check("pa_cascade_plan_build", L.pa_cascade_plan_build(
+            bt.ctypes.data_as(ctypes.c_void_p), S, maxb, sl.ctypes.data_as(ctypes.c_void_p), block_size,
+            num_kv_heads, num_q_heads, chunk_tokens, ctypes.byref(h)))
+        try:
+            info = CascadePlanInfo()
+            _check("pa_cascade_plan_get_info", L.pa_cascade_plan_get_info(h, ctypes.byref(info)))
+            arr = lambda n: np.zeros(max(int(n), 1), dtype=np.int32)
+            items, seg_blocks, members = arr(8 * info.num_items), arr(info.num_seg_blocks), arr(info.num_members)
+            parts_off, parts = arr(S + 1), arr(info.num_parts)
+            ptab, plens, segs = arr(S * maxb), arr(S), arr(4 * info.num_segments)
+            ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+            _check("pa_cascade_plan_export", L.pa_cascade_plan_export(
+                h, ptr(items), ptr(seg_blocks), ptr(members), ptr(parts_off), ptr(parts), ptr(ptab), ptr(plens),
+                ptr(segs)))
+        finally:
+            L.pa_cascade_plan_destroy(h)
+        self.info = {f: getattr(info, f) for f, _ in CascadePlanInfo._fields_}
+        self.num_seqs, self.max_blocks = S, maxb
+        self.segments = segs[:4 * info.num_segments].reshape(-1, 4)
+        self.members = members[:info.num_members]
+        self.items_host = items[:8 * info.num_items].reshape(-1, 8)
+        self.parts_off_host, self.parts_host = parts_off, parts[:info.num_parts]
+        self.private_tables_host = ptab[:S * maxb].reshape(S, maxb)
+        self.private_lens_host = plens[:S]
+        dev = torch.device(device)
+        t = lambda a: torch.from_numpy(a).to(dev)
+        self._dev = [t(items), t(seg_blocks), t(members), t(parts_off), t(parts), t(ptab), t(plens)]
+        d = self._dev
+        self.device_plan = CascadeDevicePlan(_ptr(d[0]), info.num_items, _ptr(d[1]), _ptr(d[2]), _ptr(d[3]),
+                                             _ptr(d[4]), info.num_slots, _ptr(d[5]), _ptr(d[6]))
+
+
+def _decode_cascade(fp8, q, k_cache, v_cache, plan, scale, out, num_kv_heads, block_size, k_scale, v_scale,
+                    partition_tokens, workspace):
+    dev = q.device
+    _need(q, "q", torch.bfloat16, dev, 3)
+    S, Hq, D = q.shape
+    if S != plan.num_seqs:
+        raise ValueError("the plan was built for another batch size")
+    cdt = torch.uint8 if fp8 else torch.bfloat16
+    _need(k_cache, "k_cache", cdt, dev)
+    _need(v_cache, "v_cache", cdt, dev, shape=tuple(k_cache.shape))
+    if out is None:
+        out = torch.empty((S, Hq, D), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, dev, shape=(S, Hq, D))
+    desc = make_desc(k_cache, num_kv_heads, D, block_size)
+    L = _load()
+    with torch.cuda.device(dev):
+        if workspace is None:
+            need = L.pa_decode_cascade_workspace_size(ctypes.byref(desc), S, Hq, plan.max_blocks,
+                                                      plan.info["num_slots"], partition_tokens)
+            if need == 0 and S > 0:
+                raise PagedAttentionError("pa_decode_cascade_workspace_size", -6,
+                                          "no gfx950 device or invalid sizes")
+            workspace = torch.zeros(max(int(need), 1), dtype=torch.uint8, device=dev)
+        _need(workspace, "workspace", torch.uint8, dev)
+        args = [ctypes.byref(desc), _ptr(q), S, Hq, _ptr(k_cache), _ptr(v_cache), plan.max_blocks,
+                ctypes.byref(plan.device_plan), float(scale)]
+        if fp8:
+            args += [float(k_scale), float(v_scale)]
+        args += [_ptr(out), int(partition_tokens), _ptr(workspace), workspace.numel(), _stream(q)]
+        name = "pa_decode_cascade" + ("_fp8" if fp8 else "")
+        st = getattr(L, name)(*args)
+    _check(name, st)
+    return out
+
+
+def pa_decode_cascade(q, k_cache, v_cache, plan, scale, out=None, *, num_kv_heads, block_size,
+                      partition_tokens=0, workspace=None):
+    """Decode of the batch ``plan`` (a CascadePlan) was built from, attending
+    to its shared segments once for all of their sequences (bf16 cache)."""
+    return _decode_cascade(False, q, k_cache, v_cache, plan, scale, out, num_kv_heads, block_size, 1.0, 1.0,
+                           partition_tokens, workspace)
+
+
+def pa_decode_cascade_fp8(q, k_cache, v_cache, plan, scale, k_scale, v_scale, out=None, *, num_kv_heads,
+                          block_size, partition_tokens=0, workspace=None):
+    """The same over an e4m3fn cache."""
+    return _decode_cascade(True, q, k_cache, v_cache, plan, scale, out, num_kv_heads, block_size, k_scale,
+                           v_scale, partition_tokens, workspace)

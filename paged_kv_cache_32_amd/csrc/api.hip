@@ -8,6 +8,7 @@
 #include "../../include/pa.h"
 #include "../../include/pa_blocks.h"
 #include "../../include/pa_quest.h"
+#include "../../include/pa_cascade.h"
 #include "pa_internal.h"
 
 namespace {
@@ -150,7 +151,8 @@ pa_status decode(const pa_cache_desc* cache, const void* q, int32_t num_seqs, in
                  const void* k_cache, const void* v_cache, const int32_t* block_tables,
                  int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t window, float scale,
                  float k_scale, float v_scale, bool fp8, float* out, int32_t partition_tokens,
-                 void* workspace, size_t workspace_bytes, void* stream, int32_t seq_heads = 0) {
+                 void* workspace, size_t workspace_bytes, void* stream, int32_t seq_heads = 0,
+                 float* lse = nullptr) {
   if (!cache) return PA_ERR_NULL;
   if (!isfinite(scale) || window < 0) return PA_ERR_SHAPE;
   if (fp8 && (!good_scale(k_scale) || !good_scale(v_scale))) return PA_ERR_SHAPE;
@@ -183,6 +185,7 @@ pa_status decode(const pa_cache_desc* cache, const void* q, int32_t num_seqs, in
   p.block_tables = block_tables;
   p.seq_lens = seq_lens;
   p.out = out;
+  p.lse = lse;
   p.partials = reinterpret_cast<float*>(ws + lay.partials_off);
   p.counters = reinterpret_cast<int32_t*>(ws + lay.counters_off);
   p.num_seqs = num_seqs;
@@ -587,6 +590,126 @@ pa_status pa_decode_quest_fp8(const pa_cache_desc* cache, const void* q, int32_t
   return decode_quest(cache, q, num_seqs, num_q_heads, k_cache, v_cache, sel_tables, budget, sel_lens,
                       scale, k_scale, v_scale, true, out, partition_tokens, workspace, workspace_bytes,
                       stream);
+}
+
+namespace {
+
+// Workspace of the cascade decode: the private decode's workspace first (so
+// a zero fill of the whole buffer arms its counters), then the private
+// outputs and log-sum-exps, then the partial records.
+struct CascadeLayout {
+  size_t dec_bytes, out_off, lse_off, part_off, total;
+};
+
+bool cascade_layout(const pa_cache_desc* cache, int32_t S, int32_t Hq, int32_t maxb, int32_t slots,
+                    int32_t partition_tokens, CascadeLayout* lay) {
+  if (slots < 0) return false;
+  const size_t dec = pa_decode_workspace_size(cache, S, Hq, maxb, partition_tokens);
+  if (dec == 0 && S > 0) return false;
+  const size_t D = cache->head_dim;
+  lay->dec_bytes = dec;
+  lay->out_off = pa::align_up(dec, 256);
+  lay->lse_off = pa::align_up(lay->out_off + (size_t)S * Hq * D * sizeof(float), 256);
+  lay->part_off = pa::align_up(lay->lse_off + (size_t)S * Hq * sizeof(float), 256);
+  lay->total = pa::align_up(lay->part_off + (size_t)slots * Hq * (D + 4) * sizeof(float), 256);
+  return true;
+}
+
+pa_status decode_cascade(const pa_cache_desc* cache, const void* q, int32_t S, int32_t Hq,
+                         const void* k_cache, const void* v_cache, int32_t maxb,
+                         const pa_cascade_device_plan* plan, float scale, float k_scale, float v_scale,
+                         bool fp8, float* out, int32_t partition_tokens, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (!cache || !plan) return PA_ERR_NULL;
+  pa_status st = desc_status(cache);
+  if (st != PA_OK) return st;
+  if (S < 0 || Hq < 1 || maxb < 0 || Hq % cache->num_kv_heads != 0) return PA_ERR_SHAPE;
+  const int32_t G = Hq / cache->num_kv_heads;
+  if (G > 16) return PA_ERR_UNSUPPORTED;
+  if (!isfinite(scale) || plan->num_items < 0 || plan->num_slots < 0) return PA_ERR_SHAPE;
+  if (fp8 && (!good_scale(k_scale) || !good_scale(v_scale))) return PA_ERR_SHAPE;
+  if (S == 0) return PA_OK;
+  if (!q || !k_cache || !v_cache || !out || !plan->parts_off || !plan->private_tables ||
+      !plan->private_lens || (plan->num_items > 0 && (!plan->items || !plan->seg_blocks || !plan->members)) ||
+      (plan->num_slots > 0 && !plan->parts))
+    return PA_ERR_NULL;
+  int resident = 0;
+  if (!device_info(cache->head_dim, fp8, &resident)) return PA_ERR_DEVICE;
+  CascadeLayout lay;
+  if (!cascade_layout(cache, S, Hq, maxb, plan->num_slots, partition_tokens, &lay)) return PA_ERR_SHAPE;
+  if (!workspace || workspace_bytes < lay.total) return PA_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  float* part_out = reinterpret_cast<float*>(ws + lay.out_off);
+  float* part_lse = reinterpret_cast<float*>(ws + lay.lse_off);
+  float* partials = reinterpret_cast<float*>(ws + lay.part_off);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // Private parts (and the device checks) through the paged decode.
+  st = decode(cache, q, S, Hq, k_cache, v_cache, plan->private_tables, maxb, plan->private_lens, 0, scale,
+              k_scale, v_scale, fp8, part_out, partition_tokens, ws, lay.dec_bytes, stream, 0, part_lse);
+  if (st != PA_OK) return st;
+  pa::SegmentParams sp{};
+  sp.q = static_cast<const uint16_t*>(q);
+  sp.k_cache = static_cast<const uint8_t*>(k_cache);
+  sp.v_cache = static_cast<const uint8_t*>(v_cache);
+  sp.items = plan->items;
+  sp.seg_blocks = plan->seg_blocks;
+  sp.members = plan->members;
+  sp.partials = partials;
+  sp.num_items = plan->num_items;
+  sp.num_q_heads = Hq;
+  sp.group = G;
+  sp.mpw = 16 / G;
+  sp.head_dim = cache->head_dim;
+  sp.block_size = cache->block_size;
+  sp.num_blocks = cache->num_blocks;
+  sp.num_seqs = S;
+  sp.num_slots = plan->num_slots;
+  sp.blk_stride = (int64_t)cache->num_kv_heads * cache->block_size * cache->head_dim * (fp8 ? 1 : 2);
+  sp.qk_scale = scale * 1.4426950408889634f * (fp8 ? k_scale : 1.0f);
+  if (pa::launch_segments(sp, fp8, s) != hipSuccess) return PA_ERR_LAUNCH;
+  pa::CombineParams cp{};
+  cp.part_out = part_out;
+  cp.part_lse = part_lse;
+  cp.partials = partials;
+  cp.parts_off = plan->parts_off;
+  cp.parts = plan->parts;
+  cp.out = out;
+  cp.num_seqs = S;
+  cp.num_q_heads = Hq;
+  cp.head_dim = cache->head_dim;
+  cp.num_slots = plan->num_slots;
+  cp.out_scale = fp8 ? v_scale : 1.0f;
+  if (pa::launch_combine(cp, s) != hipSuccess) return PA_ERR_LAUNCH;
+  return PA_OK;
+}
+
+}  // namespace
+
+size_t pa_decode_cascade_workspace_size(const pa_cache_desc* cache, int32_t num_seqs, int32_t num_q_heads,
+                                        int32_t max_blocks_per_seq, int32_t num_slots,
+                                        int32_t partition_tokens) {
+  if (!cache || desc_status(cache) != PA_OK) return 0;
+  CascadeLayout lay;
+  if (!cascade_layout(cache, num_seqs, num_q_heads, max_blocks_per_seq, num_slots, partition_tokens, &lay))
+    return 0;
+  return lay.total;
+}
+
+pa_status pa_decode_cascade(const pa_cache_desc* cache, const void* q, int32_t num_seqs, int32_t num_q_heads,
+                            const void* k_cache, const void* v_cache, int32_t max_blocks_per_seq,
+                            const pa_cascade_device_plan* plan, float scale, float* out,
+                            int32_t partition_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_cascade(cache, q, num_seqs, num_q_heads, k_cache, v_cache, max_blocks_per_seq, plan, scale,
+                        1.f, 1.f, false, out, partition_tokens, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_decode_cascade_fp8(const pa_cache_desc* cache, const void* q, int32_t num_seqs,
+                                int32_t num_q_heads, const void* k_cache, const void* v_cache,
+                                int32_t max_blocks_per_seq, const pa_cascade_device_plan* plan, float scale,
+                                float k_scale, float v_scale, float* out, int32_t partition_tokens,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_cascade(cache, q, num_seqs, num_q_heads, k_cache, v_cache, max_blocks_per_seq, plan, scale,
+                        k_scale, v_scale, true, out, partition_tokens, workspace, workspace_bytes, stream);
 }
 
 const char* pa_status_string(pa_status s) {

@@ -565,6 +565,9 @@ __device__ __forceinline__ void merge_unit(const DecodeParams& p, const Pending&
     for (int it = 0; it < kIt; ++it) {
       const int e = e0 + lane + 64 * it;
       if (e < groups) o[e] = num[it] * (p.out_scale / den[it]);
+      const int g = e / (D / 4);
+      if (p.lse && e < groups && e - g * (D / 4) == 0)
+        p.lse[(int64_t)pd.s * p.num_q_heads + (int64_t)pd.h * G + g] = M[it] + __builtin_amdgcn_logf(den[it]);
     }
   }
 }
@@ -636,9 +639,11 @@ __device__ __forceinline__ void finish_stage(const DecodeParams& p, const Stage&
     // The whole unit is this wavefront's: write the output directly.
     if (col < G) {
       const float inv = p.out_scale / ltot;
-      float* o = p.out + ((int64_t)st.s * p.num_q_heads + (int64_t)st.h * G + col) * D + qd * 4;
+      const int64_t row = (int64_t)st.s * p.num_q_heads + (int64_t)st.h * G + col;
+      float* o = p.out + row * D + qd * 4;
 #pragma unroll
       for (int dc = 0; dc < T::DC; ++dc) *reinterpret_cast<f32x4*>(o + dc * 16) = ws.sm.acc[dc] * inv;
+      if (p.lse && qd == 0) p.lse[row] = ws.sm.m + __builtin_amdgcn_logf(ltot);
     }
     return;
   }
@@ -713,6 +718,9 @@ __global__ __launch_bounds__(kDecodeThreads, PA_DECODE_MIN_WAVES) void decode_ke
         float* o = p.out + (int64_t)(base + l0) * p.num_q_heads * D;
         for (int e = lane; e < p.num_q_heads * D / 4; e += 64)
           reinterpret_cast<f32x4*>(o)[e] = f32x4{v, v, v, v};
+        if (p.lse)
+          for (int e = lane; e < p.num_q_heads; e += 64)
+            p.lse[(int64_t)(base + l0) * p.num_q_heads + e] = (v == 0.f) ? kNegInf : v;
       }
     }
     n = n < 0 ? 0 : n;

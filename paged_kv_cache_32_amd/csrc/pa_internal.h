@@ -34,6 +34,8 @@ struct DecodeParams {
   const int32_t* block_tables;  // [S][max_blocks]
   const int32_t* seq_lens;      // [S]
   float* out;                   // [S][Hq][D]
+  float* lse;                   // null, or [S][Hq]: log2 of each row's softmax sum in logit
+                                // units of qk_scale (m + log2 l); -inf for empty rows
   float* partials;              // [2 * num_waves][G * (D + 4)]
   int32_t* counters;            // [S * Hkv] pieces stored per unit; zero between calls
   int32_t num_seqs, num_q_heads, num_kv_heads, group, head_dim, block_size, num_blocks, max_blocks;
@@ -91,6 +93,33 @@ struct SelectParams {
   int32_t chunks;               // ceil(max_blocks / 256): score workgroups per unit
 };
 
+// Shared-prefix decode: attention over shared segments for all their members.
+struct SegmentParams {
+  const uint16_t* q;            // [S][Hq][D] bf16 bits
+  const uint8_t* k_cache;
+  const uint8_t* v_cache;
+  const int32_t* items;         // [num_items][8]: blocks offset, blocks, members offset, members,
+                                //                 KV head, first partial slot, 0, 0
+  const int32_t* seg_blocks;    // block ids of every segment chunk
+  const int32_t* members;       // member sequence ids
+  float* partials;              // [slots][Hq][D + 4]: acc[D], m, l, 0, 0 (base-2 logits)
+  int32_t num_items, num_q_heads, group, mpw, head_dim, block_size, num_blocks;
+  int32_t num_seqs, num_slots;  // members and slots outside these are skipped
+  int64_t blk_stride;           // bytes from one block's tiles to the next
+  float qk_scale;               // scale * log2(e) (* k_scale for fp8)
+};
+
+struct CombineParams {
+  const float* part_out;        // [S][Hq][D] private part, normalized and scaled
+  const float* part_lse;        // [S][Hq] its log2-sum-exp (-inf when empty)
+  const float* partials;        // shared parts
+  const int32_t* parts_off;     // [S + 1] into parts
+  const int32_t* parts;         // partial slots of each sequence
+  float* out;
+  int32_t num_seqs, num_q_heads, head_dim, num_slots;   // a slot outside num_slots makes the row NaN
+  float out_scale;              // 1 (bf16) or v_scale (fp8), applied to the shared parts
+};
+
 // Host-side launchers (defined next to their kernels).
 hipError_t launch_cache_write(const CacheWriteParams& p, bool fp8, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, bool fp8, hipStream_t stream);
@@ -102,6 +131,8 @@ hipError_t launch_summary_fill(uint32_t* words, int64_t n_words, hipStream_t str
 hipError_t launch_summary_update(const SummaryParams& p, bool fp8, hipStream_t stream);
 hipError_t launch_summary_build(const SummaryParams& p, bool fp8, hipStream_t stream);
 hipError_t launch_page_select(const SelectParams& p, hipStream_t stream);
+hipError_t launch_segments(const SegmentParams& p, bool fp8, hipStream_t stream);
+hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
 // Resident wavefronts of the decode kernel on the current device (0 on error).
 int decode_resident_waves(int head_dim, bool fp8);
 

@@ -11,7 +11,7 @@ import pytest
 import paged_kv_cache_32_amd as pa
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADERS = [os.path.join(ROOT, "include", h) for h in ("pa.h", "pa_blocks.h", "pa_quest.h")]
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("pa.h", "pa_blocks.h", "pa_quest.h", "pa_cascade.h")]
 
 if not os.path.exists(pa.LIB_PATH):
     pytest.skip("libpa.so not built", allow_module_level=True)
@@ -183,6 +183,51 @@ def test_quest_validation():
     assert dq(S=0) == OK
 
 
+def test_cascade_validation():
+    lib = pa.lib()
+    d = desc()                                         # 2 KV heads, head_dim 128, block 16
+    bt = (ctypes.c_int32 * 4)(0, 1, 0, 2)              # 2 sequences x 2 blocks
+    lens = (ctypes.c_int32 * 2)(32, 20)
+    plan = ctypes.c_void_p()
+
+    def build(S=2, maxb=2, bs=16, hkv=2, hq=16, chunk=64, b=bt, ln=lens, out=ctypes.byref(plan)):
+        return lib.pa_cascade_plan_build(b, S, maxb, ln, bs, hkv, hq, chunk, out)
+    assert build(out=None) == NULL
+    assert build(b=None) == NULL
+    assert build(bs=24) == SHAPE
+    assert build(hq=15) == SHAPE
+    assert build(chunk=0) == SHAPE
+    assert build(S=-1) == SHAPE
+    assert build(hq=2 * 17) == UNSUP
+    assert build() == OK and plan.value
+    info = pa.CascadePlanInfo()
+    assert lib.pa_cascade_plan_get_info(plan, ctypes.byref(info)) == OK
+    assert (info.num_segments, info.num_slots, info.members_per_workgroup) == (1, 2, 8 * 2)
+    assert lib.pa_cascade_plan_get_info(None, ctypes.byref(info)) == NULL
+    assert lib.pa_cascade_plan_export(plan, None, None, None, None, None, None, None, None) == NULL
+    lib.pa_cascade_plan_destroy(plan)
+    lib.pa_cascade_plan_destroy(None)
+    # decode: (desc, q, S, Hq, kc, vc, maxb, plan, scale, out, part, ws, ws_bytes, stream)
+    dp = pa.CascadeDevicePlan(FAKE.value, 1, FAKE.value, FAKE.value, FAKE.value, FAKE.value, 2, FAKE.value,
+                              FAKE.value)
+    need = 1 << 30                                     # sizes need the device (see below)
+    assert lib.pa_decode_cascade_workspace_size(ctypes.byref(d), 2, 16, 2, -1, 0) == 0
+
+    def dc(S=2, Hq=16, p=ctypes.byref(dp), scale=0.1, ws=FAKE, ws_bytes=need, q=FAKE):
+        return lib.pa_decode_cascade(ctypes.byref(d), q, S, Hq, FAKE, FAKE, 2, p, scale, FAKE, 0, ws, ws_bytes,
+                                     None)
+    assert dc(p=None) == NULL
+    assert dc(Hq=15) == SHAPE
+    assert dc(Hq=2 * 17) == UNSUP
+    assert dc(scale=float("inf")) == SHAPE
+    assert dc(S=0) == OK
+    assert dc(q=None) == NULL
+    assert lib.pa_decode_cascade_fp8(ctypes.byref(d), FAKE, 2, 16, FAKE, FAKE, 2, ctypes.byref(dp), 0.1, 0.0,
+                                     1.0, FAKE, 0, FAKE, need, None) == SHAPE
+    dp.parts = None
+    assert dc() == NULL
+
+
 def test_device_errors_without_gpu():
     import torch
     if torch.cuda.is_available():
@@ -200,6 +245,11 @@ def test_device_errors_without_gpu():
     assert pa.lib().pa_quest_update(ctypes.byref(d), 2, FAKE, FAKE, 4, FAKE, None) == DEVICE
     assert pa.lib().pa_quest_select(ctypes.byref(d), FAKE, 3, 16, FAKE, FAKE, 8, FAKE, 2, FAKE, FAKE, FAKE,
                                     256, None) == DEVICE
+    dp = pa.CascadeDevicePlan(FAKE.value, 1, FAKE.value, FAKE.value, FAKE.value, FAKE.value, 2, FAKE.value,
+                              FAKE.value)
+    assert pa.lib().pa_decode_cascade_workspace_size(ctypes.byref(d), 2, 16, 2, 2, 0) == 0
+    assert pa.lib().pa_decode_cascade(ctypes.byref(d), FAKE, 2, 16, FAKE, FAKE, 2, ctypes.byref(dp), 0.1, FAKE,
+                                      0, FAKE, 1 << 30, None) == DEVICE
 
 
 def test_binding_fails_loudly_without_library(monkeypatch):

@@ -1,0 +1,141 @@
+"""The native cascade plan (host C++ behind include/pa_cascade.h) against the
+oracle's shared segments, and the consistency of its work items, partial
+slots, per-sequence parts and private tables.  Host logic only."""
+
+import os
+import random
+
+import numpy as np
+import pytest
+
+import paged_kv_cache_32_amd as pa
+from oracle import cascade as C
+from paged_kv_cache_32_amd import workloads as W
+
+if not os.path.exists(pa.LIB_PATH):
+    pytest.skip("libpa.so not built", allow_module_level=True)
+
+
+class _CPUPlan(pa.CascadePlan):
+    """A plan whose arrays stay on the host (no device here)."""
+
+    def __init__(self, *a, **kw):
+        kw["device"] = "cpu"
+        super().__init__(*a, **kw)
+
+
+def check_plan(bt, lens, BS, Hkv, Hq, chunk_tokens):
+    bt = np.asarray(bt, np.int32)
+    lens = np.asarray(lens, np.int32)
+    plan = _CPUPlan(bt, lens, block_size=BS, num_kv_heads=Hkv, num_q_heads=Hq, chunk_tokens=chunk_tokens)
+    segs, prefix = C.shared_segments(bt, lens, BS)
+    got = sorted((int(f), tuple(int(b) for b in bt[plan.members[mo]][f:f + n]),
+                  tuple(sorted(int(x) for x in plan.members[mo:mo + m])))
+                 for f, n, mo, m in plan.segments)
+    want = sorted((s["first"], tuple(s["blocks"]), tuple(sorted(s["members"]))) for s in segs)
+    assert got == want
+    S, maxb = bt.shape
+    # private parts: the table after the last shared block, and the rest of the tokens
+    for s in range(S):
+        pb = prefix[s] // BS
+        row = plan.private_tables_host[s]
+        assert list(row[:maxb - pb]) == list(bt[s, pb:]) and (row[maxb - pb:] == -1).all()
+        assert plan.private_lens_host[s] == lens[s] - prefix[s]
+    # every (segment, chunk, member) slot: written by exactly one (item, head)
+    # per KV head, and listed in that member's parts
+    G = Hq // Hkv
+    MG = 8 * (16 // G)
+    CB = max(1, chunk_tokens // BS)
+    info = plan.info
+    assert info["members_per_workgroup"] == MG and info["chunk_blocks"] == CB
+    writes = {}
+    seg_blocks = {}
+    for it in plan.items_host:
+        off, nb, mo, nm, h, slot0 = (int(x) for x in it[:6])
+        if nm == 0:
+            assert nb == 0
+            continue
+        assert 1 <= nm <= MG and 1 <= nb <= CB and 0 <= h < Hkv
+        for k in range(nm):
+            writes.setdefault((slot0 + k, h), []).append(int(plan.members[mo + k]))
+        seg_blocks[(slot0, h)] = (off, nb, mo)
+    parts = {s: [int(x) for x in plan.parts_host[plan.parts_off_host[s]:plan.parts_off_host[s + 1]]]
+             for s in range(S)}
+    n_slots = info["num_slots"]
+    assert sorted({k[0] for k in writes}) == list(range(n_slots))
+    for (slot, h), who in writes.items():
+        assert len(who) == 1 and slot in parts[who[0]]
+    assert sum(len(v) for v in parts.values()) == n_slots
+    assert all(len(set(v)) == len(v) for v in parts.values())
+    # each member's parts cover its shared tokens exactly once
+    for s in range(S):
+        toks = 0
+        for it in plan.items_host:
+            off, nb, mo, nm, h, slot0 = (int(x) for x in it[:6])
+            if h == 0 and nm and s in [int(x) for x in plan.members[mo:mo + nm]]:
+                toks += nb * BS
+                # the chunk's blocks are the member's own blocks there
+                blocks = [int(b) for b in plan_seg_blocks(plan)[off:off + nb]]
+                first = list(bt[s]).index(blocks[0])
+                assert list(bt[s, first:first + nb]) == blocks
+        assert toks == prefix[s]
+    return plan
+
+
+def plan_seg_blocks(plan):
+    return plan._dev[1].numpy()
+
+
+def test_hand_built_batch():
+    bt = [[1, 2, 3, 4, 9, 10], [1, 2, 3, 4, 7, 0], [1, 2, 3, 5, 0, 0], [1, 2, 6, 0, 0, 0], [8, 0, 0, 0, 0, 0]]
+    lens = [5 * 16 + 1, 4 * 16 + 3, 4 * 16, 3 * 16, 2]
+    plan = check_plan(bt, lens, 16, 2, 16, 32)
+    assert plan.info["num_segments"] == 3 and plan.info["shared_tokens"] == (4 * 2 + 3 * 1 + 2 * 1) * 16
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_random_prefix_trees(seed):
+    r = random.Random(seed)
+    BS = r.choice([16, 32])
+    S = r.randrange(2, 30)
+    nid = [0]
+
+    def fresh():
+        nid[0] += 1
+        return nid[0]
+    stems = [[fresh() for _ in range(r.randrange(0, 20))] for _ in range(4)]
+    rows, lens = [], []
+    for s in range(S):
+        row = r.choice(stems)[:r.randrange(0, 25)] + [fresh() for _ in range(r.randrange(0, 5))]
+        L = len(row) * BS + r.randrange(0, BS)
+        if L % BS:
+            row.append(fresh())
+        rows.append(row)
+        lens.append(L)
+    maxb = max(len(x) for x in rows) + 2
+    bt = np.full((S, maxb), -1, np.int32)
+    for s, row in enumerate(rows):
+        bt[s, :len(row)] = row
+    for G, chunk in ((8, BS * 3), (1, 10_000), (16, BS), (3, BS * 2)):
+        check_plan(bt, lens, BS, 2, 2 * G, chunk)
+
+
+def test_prefix_shared_workload_structure():
+    """The prefix-shared generator at a reduced size: one segment for the
+    system prompt held by every sequence, one per prefix pool."""
+    w = W.prefix_shared(num_seqs=48, system_tokens=300, num_pools=4, pool_range=(200, 500), suffix_median=60,
+                        max_len=2000, block_size=32, seed=7)
+    plan = check_plan(w.block_tables, w.seq_lens, 32, 8, 64, 256)
+    n_members = sorted((int(s[3]) for s in plan.segments), reverse=True)
+    assert n_members[0] == 48 and len(n_members) >= 1 + 4
+
+
+def test_invalid_lengths_share_nothing():
+    bt = np.array([[1, 2, 3], [1, 2, 4], [1, 2, 5]], np.int32)
+    lens = [48, 3 * 16 + 1, -1]                    # the second is past its table, the third negative
+    plan = check_plan(bt, [48, 48, 40], 16, 1, 8, 64)
+    assert plan.info["num_segments"] == 1
+    plan2 = _CPUPlan(bt, np.array(lens, np.int32), block_size=16, num_kv_heads=1, num_q_heads=8)
+    assert plan2.info["num_segments"] == 0 and list(plan2.private_lens_host) == lens
+    with pytest.raises(pa.PagedAttentionError):
+        _CPUPlan(bt, np.array(lens, np.int32), block_size=16, num_kv_heads=1, num_q_heads=8 * 17)

@@ -1,0 +1,152 @@
+"""Shared-prefix (cascade) decode on the GPU (include/pa_cascade.h) against
+the oracle's plain decode: small prefix-shared batches over several group
+sizes, head sizes, block sizes, chunk sizes and both cache types; edge cases
+(empty, invalid, unshared and wholly shared sequences); and the full-size
+prefix-shared workload in the launch configuration bench.py times."""
+
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_32_amd as pa
+from oracle import cascade as C
+from oracle import paged
+from paged_kv_cache_32_amd import workloads as W
+from tests.gpu_helpers import compare, device_inputs, gpu_write, host_bits, oracle_caches
+
+pytestmark = pytest.mark.gpu
+
+
+def run(w, t, chunk_tokens, part=0, seqs=None, label=""):
+    """Write the step's tokens, decode with the cascade on the GPU; the
+    oracle decodes its own caches (plain decode, the definition)."""
+    kc0, vc0 = host_bits(t["k_cache"][0]), host_bits(t["v_cache"][0])
+    ks = float(t["k_scale"][0]) if w.kv_dtype == "fp8" else 1.0
+    vs = float(t["v_scale"][0]) if w.kv_dtype == "fp8" else 1.0
+    gpu_write(w, t)
+    kc_ref, vc_ref = oracle_caches(w, kc0, vc0, host_bits(t["k_new"][0]), host_bits(t["v_new"][0]), ks, vs)
+    plan = pa.CascadePlan(w.block_tables, w.seq_lens, block_size=w.block_size, num_kv_heads=w.num_kv_heads,
+                          num_q_heads=w.num_q_heads, chunk_tokens=chunk_tokens)
+    kw = dict(num_kv_heads=w.num_kv_heads, block_size=w.block_size, partition_tokens=part)
+    q, kc, vc = t["q"][0], t["k_cache"][0], t["v_cache"][0]
+    if w.kv_dtype == "bf16":
+        out = pa.pa_decode_cascade(q, kc, vc, plan, w.scale, **kw)
+        out2 = pa.pa_decode_cascade(q, kc, vc, plan, w.scale, **kw)
+    else:
+        out = pa.pa_decode_cascade_fp8(q, kc, vc, plan, w.scale, ks, vs, **kw)
+        out2 = pa.pa_decode_cascade_fp8(q, kc, vc, plan, w.scale, ks, vs, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) or torch.isnan(out).any(), f"{label}: not deterministic"
+    g = paged.Geom(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.kv_dtype)
+    ref = paged.decode(g, host_bits(q), kc_ref, vc_ref, w.block_tables, w.seq_lens, w.scale,
+                       k_scale=float(np.float32(ks)), v_scale=float(np.float32(vs)), seqs=seqs)
+    return plan, compare(out, ref, w.kv_dtype, seqs=seqs, label=label)
+
+
+CASES = [  # seed, S, Hq, Hkv, D, BS, system, pools, pool range, suffix median, kv, chunk tokens
+    (1, 24, 64, 8, 128, 16, 100, 3, (60, 300), 40, "bf16", (64, 1024)),
+    (2, 40, 32, 8, 128, 32, 300, 4, (100, 400), 30, "bf16", (96,)),
+    (3, 18, 16, 4, 64, 16, 50, 2, (30, 90), 20, "fp8", (32, 512)),
+    (4, 30, 16, 16, 64, 16, 80, 3, (40, 200), 25, "bf16", (48,)),
+    (5, 20, 16, 1, 128, 16, 64, 2, (50, 150), 30, "fp8", (16, 256)),
+    (6, 12, 24, 8, 64, 48, 96, 2, (48, 192), 30, "bf16", (96,)),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"{c[10]}_g{c[2] // c[3]}_d{c[4]}_bs{c[5]}" for c in CASES])
+def test_prefix_shared_batches_match_the_oracle(case):
+    seed, S, Hq, Hkv, D, BS, system, pools, prange, med, kv, chunks = case
+    w = W.prefix_shared(seed=seed, num_seqs=S, block_size=BS, system_tokens=system, num_pools=pools,
+                        pool_range=prange, suffix_median=med, max_len=2000, num_q_heads=Hq, num_kv_heads=Hkv,
+                        head_dim=D, kv_dtype=kv)
+    print(f"[cascade] {kv} G={Hq // Hkv} D={D} BS={BS} lens={list(w.seq_lens)}", flush=True)
+    for chunk in chunks:
+        for part in (0, 32):
+            t = device_inputs(w)
+            plan, _ = run(w, t, chunk, part, label=f"chunk={chunk} part={part}")
+            assert plan.info["num_segments"] >= 1 + pools and plan.info["shared_tokens"] > 0
+
+
+def test_edge_cases():
+    """Empty sequences (zeros), a length past the table (NaN rows, as
+    pa_decode), sequences sharing nothing, and sequences shared to their
+    last token (no private part), in one batch."""
+    BS, D, Hkv, Hq = 16, 64, 2, 16
+    rng = np.random.default_rng(3)
+    nb = 60
+    perm = [int(b) for b in rng.permutation(nb)]
+    common = perm[:4]                        # 4 full shared blocks
+    rows, lens = [], []
+    rows.append(common + [perm[10]]); lens.append(4 * BS + 5)    # shares, private tail
+    rows.append(common + [perm[11]]); lens.append(4 * BS + 1)
+    rows.append(common[:]); lens.append(4 * BS)                  # shared to its last token
+    rows.append(common[:]); lens.append(4 * BS)
+    rows.append([perm[20], perm[21]]); lens.append(20)           # shares nothing
+    rows.append([perm[22]]); lens.append(0)                      # empty
+    rows.append(common[:2]); lens.append(7 * BS)                 # past its table: invalid
+    maxb = 6
+    bt = np.full((len(rows), maxb), -1, np.int32)
+    for s, r in enumerate(rows):
+        bt[s, :len(r)] = r
+    lens = np.array(lens, np.int32)
+    slots = np.full(len(rows), -1, np.int64)                     # no write this step
+    w = W.Workload("edge", Hq, Hkv, D, BS, nb, lens, bt, slots, 0.125)
+    t = device_inputs(w, poison=False)
+    plan = pa.CascadePlan(bt, lens, block_size=BS, num_kv_heads=Hkv, num_q_heads=Hq, chunk_tokens=32)
+    out = pa.pa_decode_cascade(t["q"][0], t["k_cache"][0], t["v_cache"][0], plan, w.scale, num_kv_heads=Hkv,
+                               block_size=BS)
+    torch.cuda.synchronize()
+    o = out.cpu().double().numpy()
+    assert (o[5] == 0).all() and np.isnan(o[6]).all()
+    g = paged.Geom(nb, BS, Hkv, D)
+    ref = paged.decode(g, host_bits(t["q"][0]), host_bits(t["k_cache"][0]), host_bits(t["v_cache"][0]), bt,
+                       lens, w.scale, seqs=[0, 1, 2, 3, 4])
+    compare(o, ref, "bf16", seqs=[0, 1, 2, 3, 4], label="edge")
+    assert plan.info["num_segments"] >= 1 and list(plan.private_lens_host[2:4]) == [0, 0]
+
+
+def test_full_size_prefix_shared_workload():
+    """The prefix-shared batch of 256 sequences at full size (system prompt,
+    12 pools, lognormal suffixes; block 32): outputs on sampled sequences
+    from every pool against the oracle, in the launch configuration bench.py
+    times."""
+    w = W.config(3)
+    t = device_inputs(w, poison=False)
+    segs, _ = C.shared_segments(w.block_tables, w.seq_lens, w.block_size)
+    pools = [seg["members"] for seg in segs if len(seg["members"]) < w.num_seqs]
+    seqs = sorted({m[0] for m in pools} | {m[-1] for m in pools} | {0, w.num_seqs - 1})
+    print(f"[cascade] config 3 sampled {len(seqs)} sequences", flush=True)
+    plan, err = run(w, t, 1024, 0, seqs=seqs, label="config 3")
+    assert plan.info["num_segments"] == len(segs) and len(pools) >= 10
+
+
+def test_workspace_and_plan_guards():
+    """A workspace one byte short is refused before any launch; a partial
+    slot outside the plan's slot count (planted in the device copy of the
+    plan) turns only its sequence's rows into NaN, as an invalid length does."""
+    w = W.prefix_shared(seed=9, num_seqs=8, block_size=16, system_tokens=64, num_pools=1, pool_range=(16, 48),
+                        suffix_median=20, max_len=400, num_q_heads=16, num_kv_heads=2, head_dim=64)
+    t = device_inputs(w, poison=False)
+    plan = pa.CascadePlan(w.block_tables, w.seq_lens, block_size=w.block_size, num_kv_heads=w.num_kv_heads,
+                          num_q_heads=w.num_q_heads, chunk_tokens=64)
+    q, kc, vc = t["q"][0], t["k_cache"][0], t["v_cache"][0]
+    kw = dict(num_kv_heads=w.num_kv_heads, block_size=w.block_size)
+    desc = pa.make_desc(kc, w.num_kv_heads, w.head_dim, w.block_size)
+    need = pa.lib().pa_decode_cascade_workspace_size(ctypes.byref(desc), w.num_seqs, w.num_q_heads,
+                                                      plan.max_blocks, plan.info["num_slots"], 0)
+    assert need > 0
+    with pytest.raises(pa.PagedAttentionError):
+        pa.pa_decode_cascade(q, kc, vc, plan, w.scale, workspace=torch.zeros(need - 1, dtype=torch.uint8,
+                                                                             device="cuda"), **kw)
+    good = pa.pa_decode_cascade(q, kc, vc, plan, w.scale, **kw)
+    parts = plan._dev[4]
+    victim = int(np.searchsorted(plan.parts_off_host, 0, side="right") - 1)
+    assert plan.parts_off_host[victim + 1] > plan.parts_off_host[victim]
+    parts[int(plan.parts_off_host[victim])] = plan.info["num_slots"] + 7
+    bad = pa.pa_decode_cascade(q, kc, vc, plan, w.scale, **kw)
+    torch.cuda.synchronize()
+    assert torch.isnan(bad[victim]).all()
+    keep = [s for s in range(w.num_seqs) if s != victim]
+    assert torch.equal(bad[keep], good[keep])

@@ -19,11 +19,11 @@ def canon(segments):
 
 def test_hand_built_batch():
     BS = 4
-    tables = [[1, 2, 3, 4, 9],     # A
-              [1, 2, 3, 4, 7],     # B
-              [1, 2, 3, 5, 0],     # C
-              [1, 2, 6, 0, 0],     # D
-              [8, 0, 0, 0, 0]]     # E
+    tables = [[1, 2, 3, 4, 9, 10],     # A
+              [1, 2, 3, 4, 7, 0],      # B
+              [1, 2, 3, 5, 0, 0],      # C
+              [1, 2, 6, 0, 0, 0],      # D
+              [8, 0, 0, 0, 0, 0]]      # E
     lens = [5 * BS + 1, 4 * BS + 3, 4 * BS, 3 * BS, 2]
     segs, prefix = C.shared_segments(tables, lens, BS)
     assert canon(segs) == [(0, (1, 2), (0, 1, 2, 3)), (2, (3,), (0, 1, 2)), (3, (4,), (0, 1))]
