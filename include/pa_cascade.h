@@ -40,6 +40,10 @@ typedef struct pa_cascade_plan pa_cascade_plan;
  * PA_CASCADE_WAVES * (16 / G) member sequences of a segment chunk.          */
 #define PA_CASCADE_WAVES 8
 
+/* Most blocks one workgroup of the shared-segment kernel takes: the segment
+ * chunk's block ids are held in on-chip memory.                              */
+#define PA_CASCADE_MAX_CHUNK_BLOCKS 256
+
 typedef struct {
   int32_t num_segments;
   int32_t num_items;              /* workgroups of the shared part */
@@ -56,7 +60,7 @@ typedef struct {
 /* Builds the plan of a batch.  HOST inputs: block_tables [num_seqs]
  * [max_blocks_per_seq] int32, seq_lens [num_seqs] int32.  chunk_tokens (>= 1)
  * sets how many tokens of a segment one workgroup takes (rounded down to
- * whole blocks, at least one).  Lengths outside [0, max_blocks * block_size]
+ * whole blocks, at least one and at most PA_CASCADE_MAX_CHUNK_BLOCKS).  Lengths outside [0, max_blocks * block_size]
  * share nothing and keep their length (the decode turns them into NaN rows).
  * PA_ERR_SHAPE for bad sizes, PA_ERR_UNSUPPORTED for G = num_q_heads /
  * num_kv_heads > 16.                                                        */

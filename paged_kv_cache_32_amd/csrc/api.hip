@@ -665,7 +665,10 @@ pa_status decode_cascade(const pa_cache_desc* cache, const void* q, int32_t S, i
   sp.num_seqs = S;
   sp.num_slots = plan->num_slots;
   sp.blk_stride = (int64_t)cache->num_kv_heads * cache->block_size * cache->head_dim * (fp8 ? 1 : 2);
-  sp.qk_scale = scale * 1.4426950408889634f * (fp8 ? k_scale : 1.0f);
+  // scale (q . k) = |scale| ((-q) . k) for scale < 0, exactly: the kernel
+  // takes the maximum of its raw logits, which needs a non-negative scale.
+  sp.qk_scale = fabsf(scale) * 1.4426950408889634f * (fp8 ? k_scale : 1.0f);
+  sp.q_sign = scale < 0.f ? 0x80008000u : 0u;
   if (pa::launch_segments(sp, fp8, s) != hipSuccess) return PA_ERR_LAUNCH;
   pa::CombineParams cp{};
   cp.part_out = part_out;

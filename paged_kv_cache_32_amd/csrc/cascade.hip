@@ -48,7 +48,12 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
 
-// hi = p truncated to bf16, lo = (p - hi) truncated to bf16.
+// hi = p truncated to bf16, lo = (p - hi) truncated to bf16; pairs packed
+// with one byte permute each (the high halves of two words).
+__device__ __forceinline__ uint32_t high_halves(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
 __device__ __forceinline__ void split_p(const float p[4], u32x2& hi, u32x2& lo) {
   uint32_t l[4];
 #pragma unroll
@@ -56,38 +61,52 @@ __device__ __forceinline__ void split_p(const float p[4], u32x2& hi, u32x2& lo) 
     const uint32_t b = __float_as_uint(p[i]);
     l[i] = __float_as_uint(p[i] - __uint_as_float(b & 0xFFFF0000u));
   }
-  hi[0] = (__float_as_uint(p[0]) >> 16) | (__float_as_uint(p[1]) & 0xFFFF0000u);
-  hi[1] = (__float_as_uint(p[2]) >> 16) | (__float_as_uint(p[3]) & 0xFFFF0000u);
-  lo[0] = (l[0] >> 16) | (l[1] & 0xFFFF0000u);
-  lo[1] = (l[2] >> 16) | (l[3] & 0xFFFF0000u);
+  hi[0] = high_halves(__float_as_uint(p[0]), __float_as_uint(p[1]));
+  hi[1] = high_halves(__float_as_uint(p[2]), __float_as_uint(p[3]));
+  lo[0] = high_halves(l[0], l[1]);
+  lo[1] = high_halves(l[2], l[3]);
 }
 
 template <int D, bool FP8>
 struct SegTile {
   static constexpr int EB = FP8 ? 1 : 2;
-  static constexpr int BYTES = kSub * D * EB;        // one (block, head, sub-block) tile
-  static constexpr int KLD = FP8 ? D / 64 : D / 32;  // 16-byte K operand loads per lane
+  static constexpr int BYTES = kSub * D * EB;        // one (block, head, sub-block) tile of K or of V
+  static constexpr int KLD = FP8 ? D / 64 : D / 32;  // 16-byte K operand reads per lane and tile
   static constexpr int QK = D / 32;                  // 16x16x32 MFMAs per tile (K Q^T)
   static constexpr int DC = D / 16;                  // 16-row blocks of O^T
-  static constexpr int R = FP8 ? 4 : 2;              // dim blocks per 16-byte V piece
-  static constexpr int VLD = DC / R;
-  static constexpr int PIECES = BYTES / 16;          // 16-byte pieces per tile (<= 256)
-  static_assert(PIECES <= 64 * PA_CASCADE_WAVES, "one piece per thread");
+  static constexpr int R = FP8 ? 4 : 2;              // dim blocks per 16-byte V piece of the cache
+  static constexpr int VLD = DC / R;                 // 1 KB blocks of a V tile
+  static constexpr int PIECES = BYTES / 16;          // 16-byte pieces per tile
+  static constexpr int TS = 8192 / BYTES;            // tiles per stage: 2, 4 or 8
+  static constexpr int U = 16 / R;                   // bytes of 4 tokens of one dim
+  static_assert(TS * VLD == PA_CASCADE_WAVES, "one V block per wavefront and stage");
 };
 
 constexpr int kSegThreads = 64 * PA_CASCADE_WAVES;
+constexpr int kHalfStage = 8192;    // a stage: K tiles (8 KB) then V tiles (8 KB)
+constexpr int kPrefetch = 3;        // stages in flight per thread, in registers
+static_assert(kSegThreads * 16 == kHalfStage, "one K piece and one V piece per thread and stage");
 
+// LDS image of a stage.  K tiles keep the cache layout.  V tiles are stored
+// by pairs (2p, 2p + 1): unit (p, dim block dc, lane L) holds, for dim
+// 16 dc + L % 16 and tokens 4 (L / 16) .. 4 (L / 16) + 3, the U bytes of
+// tile 2p then those of tile 2p + 1.  A lane's 2U-byte read is then the
+// MFMA A operand for 8 tokens of two tiles, and the reads of a wavefront
+// are contiguous (no bank conflicts).
 template <int D, bool FP8>
 __global__ __launch_bounds__(kSegThreads) void segment_kernel(const SegmentParams p) {
   using T = SegTile<D, FP8>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][2 * T::BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][2 * kHalfStage];
+  __shared__ int32_t ids[PA_CASCADE_MAX_CHUNK_BLOCKS];
   const int32_t* it = p.items + (int64_t)blockIdx.x * 8;
-  const int blk_off = it[0], nblk = it[1], mem_off = it[2], nmem = it[3], h = it[4], slot0 = it[5];
+  const int blk_off = it[0], mem_off = it[2], nmem = it[3], h = it[4], slot0 = it[5];
+  const int nblk = it[1] <= PA_CASCADE_MAX_CHUNK_BLOCKS ? it[1] : 0;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int qd = lane >> 4, col = lane & 15;
   const int G = p.group, MPW = p.mpw;
   const int subs = p.block_size / kSub;
   const int ntiles = nblk * subs;
+  const int nst = (ntiles + T::TS - 1) / T::TS;
   if ((unsigned)h >= (unsigned)(p.num_q_heads / G)) return;   // not a KV head: the item is skipped
 
   // This lane's column: member (wave * MPW + col / G) of the item, head col % G.
@@ -102,30 +121,66 @@ __global__ __launch_bounds__(kSegThreads) void segment_kernel(const SegmentParam
 #pragma unroll
     for (int c = 0; c < T::QK; ++c) {
       const int imm = FP8 ? 128 * (c >> 1) + 16 * (c & 1) : 64 * c;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(qb + imm);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(qb + imm) ^ p.q_sign;
       qop[c] = as_bf16x8(col_ok ? v : u32x4{0u, 0u, 0u, 0u});
     }
   }
 
-  // A block id outside the pool reads tile 0 instead and marks the records
-  // NaN, as the paged decode marks such rows.
-  u32x4 kreg = {0u, 0u, 0u, 0u}, vreg = {0u, 0u, 0u, 0u};
-  bool bad = false;
-  auto gload = [&](int t) {
-    const int b = t / subs, sub = t - b * subs;
+  // The chunk's block ids, once; a block id outside the pool reads tile 0
+  // instead and marks the records NaN, as the paged decode marks such rows.
+  bool bad = it[1] != nblk;
+  for (int b = tid; b < nblk; b += kSegThreads) {
     const int blk = p.seg_blocks[blk_off + b];
     const bool ok = (unsigned)blk < (unsigned)p.num_blocks;
     bad |= !ok;
-    const int64_t tile = ok ? (int64_t)blk * p.blk_stride + (int64_t)(h * subs + sub) * T::BYTES : 0;
-    if (tid < T::PIECES) {
-      kreg = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.k_cache + tile) + tid);
-      vreg = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.v_cache + tile) + tid);
-    }
+    ids[b] = ok ? blk : 0;
+  }
+  bad = __syncthreads_or(bad);
+
+  // Per stage, thread tid brings K piece tid (tile tid / PIECES) and one
+  // 16-byte V piece: wavefront w takes 1 KB block w % VLD of tile w / VLD,
+  // lane L the piece of dims 16 (R e + r) + L % 16, tokens 4 (L / 16) ...
+  // Both tiles are the same for a whole wavefront, so their addresses are
+  // scalar.
+  const int kt = __builtin_amdgcn_readfirstlane(tid / T::PIECES);
+  const uint32_t kpc = (tid % T::PIECES) * 16;
+  const int vt = __builtin_amdgcn_readfirstlane(wave / T::VLD), ve = wave % T::VLD;
+  const uint32_t vpc = (ve * 64 + col * 4 + qd) * 16;
+  const uint32_t magic = subs > 1 ? 0xFFFFFFFFu / (uint32_t)subs + 1u : 0u;   // t / subs for t < 2^16
+  struct Pieces {
+    u32x4 k, v;
   };
-  auto lstore = [&](int b) {
-    if (tid < T::PIECES) {
-      reinterpret_cast<u32x4*>(lds[b])[tid] = kreg;
-      reinterpret_cast<u32x4*>(lds[b] + T::BYTES)[tid] = vreg;
+  // Block ids of the two tiles of stage `stage` this wavefront brings.
+  auto stage_ids = [&](int stage, int& tk, int& tv, int& bk, int& bv) {
+    tk = stage * T::TS + kt;
+    tk = tk < ntiles ? tk : ntiles - 1;               // past the end: a valid tile, never used
+    tv = stage * T::TS + vt;
+    tv = tv < ntiles ? tv : ntiles - 1;
+    const int b0 = subs > 1 ? (int)__umulhi((uint32_t)tk, magic) : tk;
+    const int b1 = subs > 1 ? (int)__umulhi((uint32_t)tv, magic) : tv;
+    bk = __builtin_amdgcn_readfirstlane(ids[b0]);
+    bv = __builtin_amdgcn_readfirstlane(ids[b1]);
+    tk -= b0 * subs;
+    tv -= b1 * subs;
+  };
+  auto gload = [&](int stage) -> Pieces {
+    int sk, sv, bk, bv;
+    stage_ids(stage, sk, sv, bk, bv);
+    const uint8_t* kb = p.k_cache + (int64_t)bk * p.blk_stride + (int64_t)(h * subs + sk) * T::BYTES;
+    const uint8_t* vb = p.v_cache + (int64_t)bv * p.blk_stride + (int64_t)(h * subs + sv) * T::BYTES;
+    Pieces r;
+    r.k = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + kpc));
+    r.v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb + vpc));
+    return r;
+  };
+  auto lstore = [&](int buf, const Pieces& pc) {
+    *reinterpret_cast<u32x4*>(lds[buf] + tid * 16) = pc.k;
+    uint8_t* vb = lds[buf] + kHalfStage + (vt >> 1) * (T::DC * 64 * 2 * T::U) + (vt & 1) * T::U;
+#pragma unroll
+    for (int r = 0; r < T::R; ++r) {
+      uint8_t* dst = vb + ((ve * T::R + r) * 64 + lane) * (2 * T::U);
+      if constexpr (FP8) *reinterpret_cast<uint32_t*>(dst) = pc.v[r];
+      else *reinterpret_cast<u32x2*>(dst) = u32x2{pc.v[2 * r], pc.v[2 * r + 1]};
     }
   };
 
@@ -134,44 +189,51 @@ __global__ __launch_bounds__(kSegThreads) void segment_kernel(const SegmentParam
 #pragma unroll
   for (int dc = 0; dc < T::DC; ++dc) acc[dc] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (ntiles > 0) {
-    gload(0);
-    lstore(0);
-  }
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    if (t + 1 < ntiles) gload(t + 1);
-    const uint8_t* kt = lds[t & 1];
-    const uint8_t* vt = lds[t & 1] + T::BYTES;
-    // Logits, base 2: lane holds tokens 4 qd + i of the tile, column col.
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  // S^T = K Q^T of one tile from LDS.
+  auto logits = [&](const uint8_t* kt_) -> f32x4 {
+    u32x4 kw[T::KLD];
+#pragma unroll
+    for (int c = 0; c < T::KLD; ++c) kw[c] = *reinterpret_cast<const u32x4*>(kt_ + c * 1024 + lane * 16);
+    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < T::KLD; ++c) {
-      const u32x4 kw = *reinterpret_cast<const u32x4*>(kt + c * 1024 + lane * 16);
       if constexpr (FP8) {
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
+        for (int hf = 0; hf < 2; ++hf) {
           u32x4 w;
-          w[0] = fp8x2_to_bf16x2<false>(kw[2 * half]);
-          w[1] = fp8x2_to_bf16x2<true>(kw[2 * half]);
-          w[2] = fp8x2_to_bf16x2<false>(kw[2 * half + 1]);
-          w[3] = fp8x2_to_bf16x2<true>(kw[2 * half + 1]);
-          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w), qop[2 * c + half], s, 0, 0, 0);
+          w[0] = fp8x2_to_bf16x2<false>(kw[c][2 * hf]);
+          w[1] = fp8x2_to_bf16x2<true>(kw[c][2 * hf]);
+          w[2] = fp8x2_to_bf16x2<false>(kw[c][2 * hf + 1]);
+          w[3] = fp8x2_to_bf16x2<true>(kw[c][2 * hf + 1]);
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w), qop[2 * c + hf], sc, 0, 0, 0);
         }
       } else {
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kw), qop[c], s, 0, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kw[c]), qop[c], sc, 0, 0, 0);
       }
     }
-    float z[4];
-    float mx = kNegInf;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      z[i] = s[i] * p.qk_scale;
-      mx = __builtin_fmaxf(mx, z[i]);
-    }
-    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32, 64));
-    if (__builtin_amdgcn_ballot_w64(mx > m + kSlack) != 0) {
+    return sc;
+  };
+
+  // Tiles 2p and 2p + 1 of a stage (the second only when `two`): online
+  // softmax in base 2 over the lane's 8 logits (tokens 4 qd + i of either
+  // tile, column col), then O^T += V^T P^T with k slots 8 qd .. 8 qd + 7
+  // pairing the A operand's 8 tokens with P split into bf16 hi and lo.
+  // qk_scale >= 0, so the maximum of the scaled logits is the scaled
+  // maximum of the raw ones.
+  auto pair = [&](const uint8_t* buf, int pp, bool two) {
+    const f32x4 s0 = logits(buf + 2 * pp * T::BYTES);
+    f32x4 s1 = logits(buf + (2 * pp + 1) * T::BYTES);
+    if (!two) s1 = f32x4{kNegInf, kNegInf, kNegInf, kNegInf};
+    const float smx = __builtin_fmaxf(
+        __builtin_fmaxf(__builtin_fmaxf(s0[0], s0[1]), __builtin_fmaxf(s0[2], s0[3])),
+        __builtin_fmaxf(__builtin_fmaxf(s1[0], s1[1]), __builtin_fmaxf(s1[2], s1[3])));
+    const float lmx = smx * p.qk_scale;
+    // The column's running maximum m is raised only when a logit exceeds
+    // it by more than kSlack, which a lane-local test and a ballot decide;
+    // then the whole column's maximum is taken.
+    if (__builtin_amdgcn_ballot_w64(lmx > m + kSlack) != 0) {
+      float mx = __builtin_fmaxf(lmx, __shfl_xor(lmx, 16, 64));
+      mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32, 64));
       const float m_new = __builtin_fmaxf(m, mx);
       const float alpha = (m == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m - m_new);
       m = m_new;
@@ -179,34 +241,72 @@ __global__ __launch_bounds__(kSegThreads) void segment_kernel(const SegmentParam
 #pragma unroll
       for (int dc = 0; dc < T::DC; ++dc) acc[dc] *= alpha;
     }
-    float pz[4];
+    float pz[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pz[i] = __builtin_amdgcn_exp2f(z[i] - m);
-    l += (pz[0] + pz[1]) + (pz[2] + pz[3]);
-    u32x2 p_hi, p_lo;
-    split_p(pz, p_hi, p_lo);
-    // O^T += V^T P^T: lane (col, qd) reads tokens 4 qd .. 4 qd + 3 of dims
-    // 16 (R e + r) + col, as the cache tile stores them.
+    for (int i = 0; i < 4; ++i) {
+      pz[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[i], p.qk_scale, -m));
+      pz[4 + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], p.qk_scale, -m));
+    }
+    if (!two) pz[4] = pz[5] = pz[6] = pz[7] = 0.f;   // also when qk_scale is 0
+    l += ((pz[0] + pz[1]) + (pz[2] + pz[3])) + ((pz[4] + pz[5]) + (pz[6] + pz[7]));
+    u32x2 h0, l0, h1, l1;
+    split_p(pz, h0, l0);
+    split_p(pz + 4, h1, l1);
+    const u32x4 bh = {h0[0], h0[1], h1[0], h1[1]}, bl = {l0[0], l0[1], l1[0], l1[1]};
+    // The products with V run at raised wave priority: a wavefront that
+    // has reached them issues its MFMAs ahead of the others' softmax
+    // arithmetic, which keeps the matrix unit fed.
+    const uint8_t* vb = buf + kHalfStage + pp * (T::DC * 64 * 2 * T::U) + lane * (2 * T::U);
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int e = 0; e < T::VLD; ++e) {
-      const u32x4 vw = *reinterpret_cast<const u32x4*>(vt + e * 1024 + (col * 4 + qd) * 16);
+    for (int dc = 0; dc < T::DC; ++dc) {
+      u32x4 a;
+      if constexpr (FP8) {
+        const u32x2 w = *reinterpret_cast<const u32x2*>(vb + dc * 64 * 2 * T::U);
+        a[0] = fp8x2_to_bf16x2<false>(w[0]);
+        a[1] = fp8x2_to_bf16x2<true>(w[0]);
+        a[2] = fp8x2_to_bf16x2<false>(w[1]);
+        a[3] = fp8x2_to_bf16x2<true>(w[1]);
+      } else {
+        a = *reinterpret_cast<const u32x4*>(vb + dc * 64 * 2 * T::U);
+      }
+      acc[dc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(bh), acc[dc], 0, 0, 0);
+      acc[dc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(bl), acc[dc], 0, 0, 0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  if (nst > 0) {
+    // Stages 0 .. kPrefetch - 1 in flight; stage s lives in register slot
+    // s % kPrefetch until it is stored to LDS buffer s & 1.  The loads,
+    // stores and barriers run for whole groups of kPrefetch stages (past
+    // the last stage they move a valid tile nobody reads), so that every
+    // path keeps the same loads in flight.
+    Pieces stg[kPrefetch];
 #pragma unroll
-      for (int r = 0; r < T::R; ++r) {
-        u32x2 a;
-        if constexpr (FP8) {
-          a[0] = fp8x2_to_bf16x2<false>(vw[r]);
-          a[1] = fp8x2_to_bf16x2<true>(vw[r]);
-        } else {
-          a[0] = vw[2 * r];
-          a[1] = vw[2 * r + 1];
+    for (int j = 0; j < kPrefetch; ++j) stg[j] = gload(j < nst ? j : nst - 1);
+    lstore(0, stg[0]);
+    stg[0] = gload(kPrefetch < nst ? kPrefetch : nst - 1);
+    __syncthreads();
+    for (int i0 = 0; i0 < nst; i0 += kPrefetch) {
+#pragma unroll
+      for (int j = 0; j < kPrefetch; ++j) {
+        const int i = i0 + j;
+        const uint8_t* buf = lds[i & 1];
+#pragma unroll
+        for (int pp = 0; pp < T::TS / 2; ++pp) {
+          const int t0 = i * T::TS + 2 * pp;
+          if (t0 < ntiles) pair(buf, pp, t0 + 1 < ntiles);
         }
-        const int dc = e * T::R + r;
-        acc[dc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_i16x4(a), as_i16x4(p_hi), acc[dc], 0, 0, 0);
-        acc[dc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_i16x4(a), as_i16x4(p_lo), acc[dc], 0, 0, 0);
+        // Stage i + 1 to the other buffer (every wavefront is past stage
+        // i - 1, which used it), then stage i + 1 + kPrefetch in flight.
+        const int jn = (j + 1) % kPrefetch;   // a constant once unrolled
+        lstore((i + 1) & 1, stg[jn]);
+        const int nx = i + 1 + kPrefetch;
+        stg[jn] = gload(nx < nst ? nx : nst - 1);
+        __syncthreads();
       }
     }
-    if (t + 1 < ntiles) lstore((t + 1) & 1);
-    __syncthreads();
   }
 
   float ltot = l + __shfl_xor(l, 16, 64);

@@ -101,7 +101,7 @@ pa_status pa_cascade_plan_build(const int32_t* block_tables, int32_t num_seqs, i
   p->num_seqs = S;
   p->max_blocks = maxb;
   p->members_per_group = PA_CASCADE_WAVES * (16 / G);
-  p->chunk_blocks = std::max<int32_t>(1, chunk_tokens / BS);
+  p->chunk_blocks = std::min<int32_t>(PA_CASCADE_MAX_CHUNK_BLOCKS, std::max<int32_t>(1, chunk_tokens / BS));
 
   std::vector<int32_t> full(S), prefix_blocks(S, 0);
   for (int32_t s = 0; s < S; ++s) {

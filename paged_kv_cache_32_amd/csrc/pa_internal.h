@@ -106,7 +106,8 @@ struct SegmentParams {
   int32_t num_items, num_q_heads, group, mpw, head_dim, block_size, num_blocks;
   int32_t num_seqs, num_slots;  // members and slots outside these are skipped
   int64_t blk_stride;           // bytes from one block's tiles to the next
-  float qk_scale;               // scale * log2(e) (* k_scale for fp8)
+  float qk_scale;               // |scale| * log2(e) (* k_scale for fp8), never negative
+  uint32_t q_sign;              // 0x80008000 when scale < 0: q is negated as it is loaded
 };
 
 struct CombineParams {

@@ -45,7 +45,7 @@ def check_plan(bt, lens, BS, Hkv, Hq, chunk_tokens):
     # per KV head, and listed in that member's parts
     G = Hq // Hkv
     MG = 8 * (16 // G)
-    CB = max(1, chunk_tokens // BS)
+    CB = min(256, max(1, chunk_tokens // BS))
     info = plan.info
     assert info["members_per_workgroup"] == MG and info["chunk_blocks"] == CB
     writes = {}

@@ -5,6 +5,7 @@ sizes, head sizes, block sizes, chunk sizes and both cache types; edge cases
 prefix-shared workload in the launch configuration bench.py times."""
 
 import ctypes
+import dataclasses
 
 import numpy as np
 import pytest
@@ -150,3 +151,18 @@ def test_workspace_and_plan_guards():
     assert torch.isnan(bad[victim]).all()
     keep = [s for s in range(w.num_seqs) if s != victim]
     assert torch.equal(bad[keep], good[keep])
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_negative_and_zero_scale(kv):
+    """A negative softmax scale (the kernel negates q and takes |scale|) and
+    a zero scale (uniform weights), against the oracle; an odd number of
+    16-token tiles per chunk (block 16, 3-block chunks) keeps a lone tile in
+    the last pair."""
+    w = W.prefix_shared(seed=11, num_seqs=10, block_size=16, system_tokens=80, num_pools=2, pool_range=(40, 90),
+                        suffix_median=25, max_len=600, num_q_heads=16, num_kv_heads=2, head_dim=128, kv_dtype=kv)
+    for scale in (-w.scale, 0.0):
+        t = device_inputs(w, poison=False)
+        w2 = dataclasses.replace(w, scale=scale)
+        print(f"[cascade] {kv} scale={scale}", flush=True)
+        run(w2, t, 48, 0, label=f"{kv} scale={scale}")
