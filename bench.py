@@ -16,7 +16,10 @@ blocks of the previous step are not served from the 256 MiB Infinity Cache
 the write and the decode are each bracketed by HIP events recorded on the
 stream they run on, so the scrub is not timed.  `value` is KV bytes read per
 decode call (sum of sequence lengths x 2 x 8 heads x 128 x 2 B) divided by
-the mean event-timed duration of pa_decode, in GB/s (1e9 B/s).
+the mean event-timed duration of pa_decode, in GB/s (1e9 B/s).  `ceilings`
+gives two practical read ceilings measured in the same run with the probes
+of include/pa_probe.h: a plain streaming read of the 512 MiB scrub buffer,
+and a read of exactly the decode's K/V tiles with no arithmetic.
 
 Other workloads (--workload), each on the same 70B layer shape:
   prefix_shared_bs256  256 sequences, block 32, a shared 900-token system
@@ -224,6 +227,47 @@ def base_record(args, w, K):
     }
 
 
+def probe_ceilings(w, kc, vc, bt, sl, scrub, sink, stream, no_scrub, reps=10, tiles=True):
+    """Practical read ceilings (include/pa_probe.h): a plain streaming read of
+    the 512 MiB scrub buffer (larger than the Infinity Cache, so every pass
+    reads HBM), and the decode's own tile loads with no arithmetic, each
+    timed with HIP events on the stream it runs on (the tile read after a
+    scrub, like the decode)."""
+    dev = kc.device
+    psink = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def tile_read():
+        pa.pa_probe_tile_read(kc, vc, bt, sl, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+                              block_size=w.block_size, sink=psink)
+    pa.pa_probe_stream_read(scrub, psink)              # warm-up: first launches load the code
+    if tiles:
+        tile_read()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+    for e in ev:
+        e[0].record(stream)
+        pa.pa_probe_stream_read(scrub, psink)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    stream_s = float(np.median([a.elapsed_time(b) for a, b in ev])) / 1e3
+    res = {"stream_read_gbs": round(scrub.numel() * 4 / stream_s / 1e9, 1)}
+    if tiles:
+        eb = 1 if w.kv_dtype == "fp8" else 2
+        ok = (w.seq_lens >= 1) & (w.seq_lens <= w.max_blocks_per_seq * w.block_size)
+        tile_bytes = int(sum(-(-int(L) // 16) for L in w.seq_lens[ok])) * 16 * w.num_kv_heads * w.head_dim * eb * 2
+        for e in ev:
+            if not no_scrub:
+                torch.sum(scrub, dim=0, out=sink)
+            e[0].record(stream)
+            tile_read()
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        tile_s = float(np.median([a.elapsed_time(b) for a, b in ev])) / 1e3
+        res.update({"tile_read_gbs": round(tile_bytes / tile_s / 1e9, 1), "tile_read_us": round(tile_s * 1e6, 2),
+                    "tile_read_bytes": tile_bytes})
+    return res
+
+
 def bench_layer(args, dev):
     """One-layer workloads: the cache write and the decode of one batch."""
     w = W.config(WORKLOADS[args.workload])
@@ -291,6 +335,8 @@ def bench_layer(args, dev):
     torch.cuda.synchronize()
     hot_ms = hot[0].elapsed_time(hot[1]) / K
 
+    ceilings = probe_ceilings(w, kc, vc, bt, sl, scrub, sink, stream, args.no_scrub, tiles=not window)
+
     kv_bytes, alg_bytes = algorithmic_bytes(w, physical=shared, window=window)
     logical_kv = w.logical_kv_bytes()
     dec_s = float(dec_ms.mean()) / 1e3
@@ -322,6 +368,12 @@ def bench_layer(args, dev):
                      "kernel": "decode_kernel (pa_decode is one launch)",
                      "bytes_per_launch": alg_bytes},
     })
+    ceilings["decode_frac_of_stream_read"] = round(kv_gbs / ceilings["stream_read_gbs"], 4)
+    if "tile_read_us" in ceilings:
+        # Both read the same tiles: the ratio of times is the fraction of the
+        # access pattern's own ceiling that the decode reaches.
+        ceilings["decode_frac_of_tile_read"] = round(ceilings["tile_read_us"] / float(np.median(dec_ms) * 1e3), 4)
+    res["ceilings"] = ceilings
     if shared:
         res["logical_kv_gbs"] = round(logical_kv / dec_s / 1e9, 1)
         res["logical_kv_bytes_per_call"] = logical_kv

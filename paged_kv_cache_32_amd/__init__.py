@@ -121,6 +121,8 @@ def _load():
                                vp, sz, vp], i32),
         "pa_decode_cascade_fp8": ([dp, vp, i32, i32, vp, vp, i32, ctypes.POINTER(CascadeDevicePlan), f32, f32,
                                    f32, vp, i32, vp, sz, vp], i32),
+        "pa_probe_stream_read": ([vp, sz, vp, vp], i32),
+        "pa_probe_tile_read": ([dp, i32, vp, vp, vp, i32, i32, vp, vp, vp], i32),
         "pa_bm_num_free": ([vp], i32),
         "pa_bm_sequence_info": ([vp, i64, ctypes.POINTER(i32), ctypes.POINTER(i32)], i32),
         "pa_bm_block_table": ([vp, i64, ctypes.POINTER(i32), i32], i32),
@@ -323,6 +325,48 @@ def pa_copy_blocks(k_cache, v_cache, pairs, *, num_kv_heads, head_dim, block_siz
                                     pairs.shape[0], _stream(k_cache))
     _check("pa_copy_blocks", st)
 
+
+
+def pa_probe_stream_read(buf, sink=None):
+    """Read a contiguous device tensor once (include/pa_probe.h): returns the
+    int32 device tensor ``sink`` (zeroed when not given) into which the XOR
+    of all the buffer's 32-bit words is folded."""
+    dev = buf.device
+    if dev.type != "cuda" or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    _need(sink, "sink", torch.int32, dev)
+    nbytes = buf.numel() * buf.element_size()
+    with torch.cuda.device(dev):
+        st = _load().pa_probe_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(buf))
+    _check("pa_probe_stream_read", st)
+    return sink
+
+
+def pa_probe_tile_read(k_cache, v_cache, block_tables, seq_lens, *, num_kv_heads, head_dim, block_size,
+                       sink=None):
+    """Read the cache tiles pa_decode reads for these tables and lengths,
+    with no arithmetic (include/pa_probe.h); bf16 or uint8 (e4m3fn) caches.
+    Returns the int32 device tensor ``sink`` holding the XOR of their words."""
+    dev = k_cache.device
+    if k_cache.dtype not in (torch.bfloat16, torch.uint8):
+        raise TypeError("caches must be bfloat16 or uint8 (e4m3fn codes)")
+    _need(k_cache, "k_cache", k_cache.dtype, dev)
+    _need(v_cache, "v_cache", k_cache.dtype, dev, shape=tuple(k_cache.shape))
+    _need(block_tables, "block_tables", torch.int32, dev, 2)
+    S, maxb = block_tables.shape
+    _need(seq_lens, "seq_lens", torch.int32, dev, shape=(S,))
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    _need(sink, "sink", torch.int32, dev)
+    desc = make_desc(k_cache, num_kv_heads, head_dim, block_size)
+    eb = 2 if k_cache.dtype == torch.bfloat16 else 1
+    with torch.cuda.device(dev):
+        st = _load().pa_probe_tile_read(ctypes.byref(desc), eb, _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                        S, maxb, _ptr(seq_lens), _ptr(sink), _stream(k_cache))
+    _check("pa_probe_tile_read", st)
+    return sink
 
 def _swap(out, k_cache, v_cache, blocks, host, num_kv_heads, head_dim, block_size):
     dev = k_cache.device

@@ -9,6 +9,7 @@
 #include "../../include/pa_blocks.h"
 #include "../../include/pa_quest.h"
 #include "../../include/pa_cascade.h"
+#include "../../include/pa_probe.h"
 #include "pa_internal.h"
 
 namespace {
@@ -713,6 +714,67 @@ pa_status pa_decode_cascade_fp8(const pa_cache_desc* cache, const void* q, int32
                                 void* workspace, size_t workspace_bytes, void* stream) {
   return decode_cascade(cache, q, num_seqs, num_q_heads, k_cache, v_cache, max_blocks_per_seq, plan, scale,
                         k_scale, v_scale, true, out, partition_tokens, workspace, workspace_bytes, stream);
+}
+
+namespace {
+
+// Workgroups of a probe: 4 per CU of the current device (16 wavefronts).
+int probe_grid() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return 4 * cus;
+}
+
+}  // namespace
+
+pa_status pa_probe_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  if (!sink || (bytes > 0 && !buf)) return PA_ERR_NULL;
+  if (bytes % 16 != 0 || reinterpret_cast<uintptr_t>(buf) % 16 != 0) return PA_ERR_SHAPE;
+  int resident = 0;
+  if (!device_info(128, false, &resident)) return PA_ERR_DEVICE;
+  if (bytes == 0) return PA_OK;
+  const int grid = probe_grid();
+  if (grid <= 0) return PA_ERR_DEVICE;
+  if (pa::launch_stream_read(buf, bytes, sink, grid, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return PA_ERR_LAUNCH;
+  return PA_OK;
+}
+
+pa_status pa_probe_tile_read(const pa_cache_desc* cache, int32_t elem_bytes, const void* k_cache,
+                             const void* v_cache, const int32_t* block_tables, int32_t num_seqs,
+                             int32_t max_blocks_per_seq, const int32_t* seq_lens, uint32_t* sink,
+                             void* stream) {
+  if (!cache) return PA_ERR_NULL;
+  pa_status st = desc_status(cache);
+  if (st != PA_OK) return st;
+  if (elem_bytes != 1 && elem_bytes != 2) return PA_ERR_UNSUPPORTED;
+  if (num_seqs < 0 || max_blocks_per_seq < 0) return PA_ERR_SHAPE;
+  if ((int64_t)max_blocks_per_seq * cache->block_size > INT32_MAX) return PA_ERR_SHAPE;
+  if ((int64_t)num_seqs * cache->num_kv_heads * max_blocks_per_seq > INT32_MAX) return PA_ERR_SHAPE;
+  if (!sink) return PA_ERR_NULL;
+  if (num_seqs == 0 || max_blocks_per_seq == 0) return PA_OK;
+  if (!k_cache || !v_cache || !block_tables || !seq_lens) return PA_ERR_NULL;
+  int resident = 0;
+  if (!device_info(cache->head_dim, elem_bytes == 1, &resident)) return PA_ERR_DEVICE;
+  const int grid = probe_grid();
+  if (grid <= 0) return PA_ERR_DEVICE;
+  pa::TileProbeParams p{};
+  p.k_cache = static_cast<const uint8_t*>(k_cache);
+  p.v_cache = static_cast<const uint8_t*>(v_cache);
+  p.block_tables = block_tables;
+  p.seq_lens = seq_lens;
+  p.sink = sink;
+  p.num_seqs = num_seqs;
+  p.num_kv_heads = cache->num_kv_heads;
+  p.max_blocks = max_blocks_per_seq;
+  p.block_size = cache->block_size;
+  p.num_blocks = cache->num_blocks;
+  p.head_dim = cache->head_dim;
+  p.elem_bytes = elem_bytes;
+  p.blk_stride = (int64_t)cache->num_kv_heads * cache->block_size * cache->head_dim * elem_bytes;
+  if (pa::launch_tile_read(p, grid, static_cast<hipStream_t>(stream)) != hipSuccess) return PA_ERR_LAUNCH;
+  return PA_OK;
 }
 
 const char* pa_status_string(pa_status s) {

@@ -110,6 +110,16 @@ struct SegmentParams {
   uint32_t q_sign;              // 0x80008000 when scale < 0: q is negated as it is loaded
 };
 
+struct TileProbeParams {
+  const uint8_t* k_cache;
+  const uint8_t* v_cache;
+  const int32_t* block_tables;  // [num_seqs][max_blocks]
+  const int32_t* seq_lens;
+  uint32_t* sink;               // XOR of every word read is folded in
+  int32_t num_seqs, num_kv_heads, max_blocks, block_size, num_blocks, head_dim, elem_bytes;
+  int64_t blk_stride;           // bytes per block of one cache
+};
+
 struct CombineParams {
   const float* part_out;        // [S][Hq][D] private part, normalized and scaled
   const float* part_lse;        // [S][Hq] its log2-sum-exp (-inf when empty)
@@ -134,6 +144,8 @@ hipError_t launch_summary_build(const SummaryParams& p, bool fp8, hipStream_t st
 hipError_t launch_page_select(const SelectParams& p, hipStream_t stream);
 hipError_t launch_segments(const SegmentParams& p, bool fp8, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int grid, hipStream_t stream);
+hipError_t launch_tile_read(const TileProbeParams& p, int grid, hipStream_t stream);
 // Resident wavefronts of the decode kernel on the current device (0 on error).
 int decode_resident_waves(int head_dim, bool fp8);
 

@@ -11,7 +11,7 @@ import pytest
 import paged_kv_cache_32_amd as pa
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADERS = [os.path.join(ROOT, "include", h) for h in ("pa.h", "pa_blocks.h", "pa_quest.h", "pa_cascade.h")]
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("pa.h", "pa_blocks.h", "pa_quest.h", "pa_cascade.h", "pa_probe.h")]
 
 if not os.path.exists(pa.LIB_PATH):
     pytest.skip("libpa.so not built", allow_module_level=True)
@@ -228,6 +228,27 @@ def test_cascade_validation():
     assert dc() == NULL
 
 
+def test_probe_validation():
+    lib = pa.lib()
+    d = desc()
+    assert lib.pa_probe_stream_read(FAKE, 64, None, None) == NULL
+    assert lib.pa_probe_stream_read(None, 64, FAKE, None) == NULL
+    assert lib.pa_probe_stream_read(FAKE, 63, FAKE, None) == SHAPE
+    assert lib.pa_probe_stream_read(ctypes.c_void_p(0x1008), 64, FAKE, None) == SHAPE
+
+    def tr(eb=2, S=2, maxb=4, sink=FAKE, bt=FAKE, dd=d):
+        return lib.pa_probe_tile_read(ctypes.byref(dd) if dd else None, eb, FAKE, FAKE, bt, S, maxb, FAKE, sink,
+                                      None)
+    assert tr(dd=None) == NULL
+    assert tr(eb=4) == UNSUP
+    assert tr(S=-1) == SHAPE
+    assert tr(sink=None) == NULL
+    assert tr(S=0) == OK
+    assert tr(bt=None) == NULL
+    bad = pa.CacheDesc(10, 24, 2, 128)
+    assert tr(dd=bad) == UNSUP
+
+
 def test_device_errors_without_gpu():
     import torch
     if torch.cuda.is_available():
@@ -247,6 +268,8 @@ def test_device_errors_without_gpu():
                                     256, None) == DEVICE
     dp = pa.CascadeDevicePlan(FAKE.value, 1, FAKE.value, FAKE.value, FAKE.value, FAKE.value, 2, FAKE.value,
                               FAKE.value)
+    assert pa.lib().pa_probe_stream_read(FAKE, 64, FAKE, None) == DEVICE
+    assert pa.lib().pa_probe_tile_read(ctypes.byref(d), 2, FAKE, FAKE, FAKE, 2, 4, FAKE, FAKE, None) == DEVICE
     assert pa.lib().pa_decode_cascade_workspace_size(ctypes.byref(d), 2, 16, 2, 2, 0) == 0
     assert pa.lib().pa_decode_cascade(ctypes.byref(d), FAKE, 2, 16, FAKE, FAKE, 2, ctypes.byref(dp), 0.1, FAKE,
                                       0, FAKE, 1 << 30, None) == DEVICE
