@@ -362,7 +362,9 @@ __device__ __forceinline__ int lds_index(int i) { return i + (i >> 5); }
 //
 // The threshold T = the budget-th largest key is found bit by bit from the
 // top (32 counting rounds: T keeps a bit when at least `budget` keys are
-// >= T with it).  Then each thread takes a contiguous range of pages: the
+// >= T with it; for units held in registers a wavefront counts with one
+// ballot per key slot and scalar popcounts).  Then each thread takes a
+// contiguous range of pages: the
 // pages above T, and the first (budget - count above T) pages equal to T,
 // go to their place in page order through two prefix sums.
 //
@@ -392,10 +394,15 @@ __device__ __forceinline__ void select_small(const SelectParams& p, int unit, in
   uint32_t T = 0u;
   for (int bit = 31; bit >= 0; --bit) {
     const uint32_t cand = T | (1u << bit);   // >= 1: the padding keys 0 never count
+    // The wavefront's count: one ballot per key slot, counted on the scalar unit.
     int c = 0;
 #pragma unroll
-    for (int k = 0; k < kSelectRegs; ++k) c += kr[k] >= cand ? 1 : 0;
-    if (block_sum_small(c, red) >= B) T = cand;   // its barriers also publish the LDS keys
+    for (int k = 0; k < kSelectRegs; ++k) c += __popcll(__ballot(kr[k] >= cand));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = c;
+    __syncthreads();                          // also publishes the LDS keys
+    const int total = red[0] + red[1] + red[2] + red[3];
+    __syncthreads();
+    if (total >= B) T = cand;
   }
   uint32_t mine[kSelectRegs];
   int above = 0, equal = 0;
