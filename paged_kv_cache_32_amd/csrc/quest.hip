@@ -196,19 +196,31 @@ __device__ __forceinline__ int pages_of(const SelectParams& p, int s) {
 // at least 2^-67, or zero), so this rounds exactly as a rounded product and a
 // rounded sum would (a zero's sign aside, which never changes a sum's
 // value), with no select and no compare in the loop.  q+ and q- of the
-// group sit in LDS (read as broadcasts); a page's row is read one 128-byte
-// line (32 dimensions) at a time and used whole, the next line's loads in
-// flight while the current one is summed, and its words are unpacked once
-// per dimension for 8 query heads.
+// group sit in LDS (read as broadcasts); a page's row is summed one
+// 128-byte line (32 dimensions) at a time, the next line's loads in flight
+// while the current one is summed, and its words are unpacked once per
+// dimension for all query heads.
 constexpr int kScorePages = 256;
 constexpr int kScoreGrid = 2048;
+
+// Each wavefront stages its own 64 rows through LDS one line at a time: 8
+// lanes bring one row's line, so each load instruction covers 8 whole lines
+// instead of pieces of 64 lines (64 cache tag lookups per instruction,
+// which measured as the cost of the lane-per-row loads); rows sit 144 bytes
+// apart, so a lane's reads of its own row fall in distinct banks.  No
+// workgroup barrier: a wavefront only reads what it wrote (wavefront-scope
+// fences keep the compiler from moving its LDS accesses across each other).
+constexpr int kRowWords = 36;   // 32 words of a line + 4 of pad
 
 template <int D>
 __global__ __launch_bounds__(256) void page_score_kernel(const SelectParams p) {
   __shared__ float qpos[kMaxGroupQuest * D], qneg[kMaxGroupQuest * D];
+  __shared__ __attribute__((aligned(16))) uint32_t stage[4][64 * kRowWords];
   const int Hkv = p.num_kv_heads, G = p.group;
   const int units = p.num_seqs * Hkv;
   const int items = units * p.chunks;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  uint32_t* rows = stage[wv];
   for (int it = blockIdx.x; it < items; it += gridDim.x) {
     const int c = it / units, unit = it - c * units;
     const int s = unit / Hkv, h = unit - s * Hkv;
@@ -216,63 +228,81 @@ __global__ __launch_bounds__(256) void page_score_kernel(const SelectParams p) {
     if (c * kScorePages >= np) continue;                     // uniform
     __syncthreads();                                         // previous item done with q+/q-
     const uint16_t* qg = p.q + ((int64_t)s * p.num_q_heads + (int64_t)h * G) * D;
-    for (int i = threadIdx.x; i < G * D; i += 256) {
+    for (int i = tid; i < G * D; i += 256) {
       const uint32_t b = qg[i];
       const float qf = __uint_as_float(b << 16);
       qpos[i] = (b & 0x8000u) ? 0.f : qf;
       qneg[i] = (b & 0x8000u) ? qf : 0.f;
     }
     __syncthreads();
-    const int pg = c * kScorePages + (int)threadIdx.x;
-    if (pg >= np) continue;
-    const int blk = p.block_tables[(int64_t)s * p.max_blocks + pg];
-    uint32_t key = 0u;  // a block outside the pool scores lowest
-    if ((unsigned)blk < (unsigned)p.num_blocks) {
-      const u32x4* w = reinterpret_cast<const u32x4*>(p.words + ((int64_t)blk * Hkv + h) * D);
-      float best = -__builtin_inff();
-      for (int g0 = 0; g0 < G; g0 += 8) {
-        float acc[8];
+    const int pg0 = c * kScorePages + 64 * wv;               // this wavefront's first page
+    if (pg0 >= np) continue;                                 // wave-uniform; no barrier follows
+    const int pg = pg0 + lane;
+    int blk = pg < np ? p.block_tables[(int64_t)s * p.max_blocks + pg] : -1;
+    if ((unsigned)blk >= (unsigned)p.num_blocks) blk = -1;
+    // Lane brings piece lane % 8 of the lines of rows lane / 8 + 8 i, i < 8.
+    int rb[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] = 0.f;
-        u32x4 cur[8], nxt[8];
+    for (int i = 0; i < 8; ++i) rb[i] = __shfl(blk, lane / 8 + 8 * i, 64);
+    auto gload = [&](int b, u32x4 (&v)[8]) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) cur[i] = w[i];
+      for (int i = 0; i < 8; ++i)
+        v[i] = rb[i] >= 0 ? reinterpret_cast<const u32x4*>(p.words + ((int64_t)rb[i] * Hkv + h) * D + 32 * b)[lane % 8]
+                          : u32x4{0u, 0u, 0u, 0u};
+    };
+    u32x4 v[8];
+    gload(0, v);
+    float acc[kMaxGroupQuest];
+#pragma unroll
+    for (int j = 0; j < kMaxGroupQuest; ++j) acc[j] = 0.f;
 #pragma unroll 1
-        for (int b = 0; b < D / 32; ++b) {
-          const int bn = b + 1 < D / 32 ? b + 1 : b;     // last block: reload itself (never used)
+    for (int b = 0; b < D / 32; ++b) {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) nxt[i] = w[8 * bn + i];
+      for (int i = 0; i < 8; ++i)
+        *reinterpret_cast<u32x4*>(rows + (lane / 8 + 8 * i) * kRowWords + 4 * (lane % 8)) = v[i];
+      if (b + 1 < D / 32) gload(b + 1, v);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      u32x4 line[8];
 #pragma unroll
-          for (int c8 = 0; c8 < 4; ++c8) {
-            float mnf[8], mxf[8];
+      for (int k = 0; k < 8; ++k) line[k] = *reinterpret_cast<const u32x4*>(rows + lane * kRowWords + 4 * k);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const uint32_t word = cur[2 * c8 + e / 4][e % 4];
-              mnf[e] = __uint_as_float(word << 16);
-              mxf[e] = __uint_as_float(word & 0xFFFF0000u);
-            }
+      for (int c8 = 0; c8 < 4; ++c8) {
+        float mnf[8], mxf[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              if (g0 + j < G) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                  const int qi = (g0 + j) * D + 32 * b + 8 * c8 + e;
-                  acc[j] = __builtin_fmaf(qpos[qi], mxf[e], acc[j]);
-                  acc[j] = __builtin_fmaf(qneg[qi], mnf[e], acc[j]);
-                }
-              }
-            }
-          }
-#pragma unroll
-          for (int i = 0; i < 8; ++i) cur[i] = nxt[i];
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t word = line[2 * c8 + e / 4][e % 4];
+          mnf[e] = __uint_as_float(word << 16);
+          mxf[e] = __uint_as_float(word & 0xFFFF0000u);
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (g0 + j < G) best = __builtin_fmaxf(best, acc[j]);
+        for (int j = 0; j < kMaxGroupQuest; ++j) {
+          if (j < G) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int qi = j * D + 32 * b + 8 * c8 + e;
+              acc[j] = __builtin_fmaf(qpos[qi], mxf[e], acc[j]);
+              acc[j] = __builtin_fmaf(qneg[qi], mnf[e], acc[j]);
+            }
+          }
+        }
       }
-      key = score_key(best);
     }
-    p.keys[(int64_t)unit * p.max_blocks + pg] = key;
+    if (pg < np) {
+      uint32_t key = 0u;  // a block outside the pool scores lowest
+      if (blk >= 0) {
+        float best = -__builtin_inff();
+#pragma unroll
+        for (int j = 0; j < kMaxGroupQuest; ++j)
+          if (j < G) best = __builtin_fmaxf(best, acc[j]);
+        key = score_key(best);
+      }
+      p.keys[(int64_t)unit * p.max_blocks + pg] = key;
+    }
   }
 }
 
