@@ -20,6 +20,8 @@ the mean event-timed duration of pa_decode, in GB/s (1e9 B/s).  `ceilings`
 gives two practical read ceilings measured in the same run with the probes
 of include/pa_probe.h: a plain streaming read of the 512 MiB scrub buffer,
 and a read of exactly the decode's K/V tiles with no arithmetic.
+`fused_append_decode` times the same step as one pa_decode_append launch (the
+write folded into the decode), after the same scrub, beside the two launches.
 
 Other workloads (--workload), each on the same 70B layer shape:
   prefix_shared_bs256  256 sequences, block 32, a shared 900-token system
@@ -268,6 +270,19 @@ def probe_ceilings(w, kc, vc, bt, sl, scrub, sink, stream, no_scrub, reps=10, ti
     return res
 
 
+def new_token_blocks_private(w):
+    """Whether every sequence's new token (position L - 1) sits in a block no
+    other sequence's table names, as the fused append requires."""
+    bt, BS = w.block_tables, w.block_size
+    used = bt[bt >= 0]
+    ids, counts = np.unique(used, return_counts=True)
+    refs = dict(zip(ids.tolist(), counts.tolist()))
+    for s, L in enumerate(w.seq_lens):
+        if L > 0 and refs.get(int(bt[s, (int(L) - 1) // BS]), 0) > 1:
+            return False
+    return True
+
+
 def bench_layer(args, dev):
     """One-layer workloads: the cache write and the decode of one batch."""
     w = W.config(WORKLOADS[args.workload])
@@ -335,6 +350,28 @@ def bench_layer(args, dev):
     torch.cuda.synchronize()
     hot_ms = hot[0].elapsed_time(hot[1]) / K
 
+    # The same step as one fused launch (pa_decode_append: the write of the
+    # new tokens folded into the decode), timed the same way.
+    fused = None
+    if new_token_blocks_private(w):
+        def fused_step():
+            pa.pa_decode_append(q, kn, vn, kc, vc, bt, sl, w.scale, out, num_kv_heads=w.num_kv_heads,
+                                block_size=w.block_size, window=window,
+                                partition_tokens=args.partition_tokens, workspace=ws)
+        for _ in range(args.warmup):
+            if not args.no_scrub:
+                torch.sum(scrub, dim=0, out=sink)
+            fused_step()
+        fev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+        for i in range(K):
+            if not args.no_scrub:
+                torch.sum(scrub, dim=0, out=sink)
+            fev[i][0].record(stream)
+            fused_step()
+            fev[i][1].record(stream)
+        torch.cuda.synchronize()
+        fused = np.array([e[0].elapsed_time(e[1]) for e in fev])
+
     ceilings = probe_ceilings(w, kc, vc, bt, sl, scrub, sink, stream, args.no_scrub, tiles=not window)
 
     kv_bytes, alg_bytes = algorithmic_bytes(w, physical=shared, window=window)
@@ -374,6 +411,15 @@ def bench_layer(args, dev):
         # access pattern's own ceiling that the decode reaches.
         ceilings["decode_frac_of_tile_read"] = round(ceilings["tile_read_us"] / float(np.median(dec_ms) * 1e3), 4)
     res["ceilings"] = ceilings
+    if fused is not None:
+        f_ms = float(fused.mean())
+        res["fused_append_decode"] = {
+            "entry_point": "pa_decode_append", "us_mean": round(f_ms * 1e3, 2),
+            "us_p50": round(float(np.median(fused)) * 1e3, 2),
+            "layer_tok_s": round(w.num_seqs / (f_ms / 1e3), 1),
+            "step_saving_us": round((step_ms - f_ms) * 1e3, 2)}
+    else:
+        res["fused_append_decode"] = "not timed: a new token's block is read by another sequence"
     if shared:
         res["logical_kv_gbs"] = round(logical_kv / dec_s / 1e9, 1)
         res["logical_kv_bytes_per_call"] = logical_kv
@@ -447,6 +493,27 @@ def bench_model_step(args, dev):
     wall = time.perf_counter() - tw
     graph_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
 
+    # The same step with each layer's write and decode as one fused launch
+    # (pa_decode_append_fp8): 80 launches in its graph instead of 160.
+    fused_ms = None
+    if new_token_blocks_private(w):
+        fstep = DecodeStep(q=t["q"], k_new=t["k_new"], v_new=t["v_new"], k_cache=t["k_cache"],
+                           v_cache=t["v_cache"], out=out, block_tables=bt, seq_lens=sl, slot_mapping=sm,
+                           scale=w.scale, num_kv_heads=w.num_kv_heads, block_size=w.block_size,
+                           k_scale=t["k_scale"].tolist(), v_scale=t["v_scale"].tolist(),
+                           partition_tokens=args.partition_tokens, workspace=step.workspace, fused=True)
+        fstep.capture()
+        for _ in range(args.warmup):
+            fstep.replay()
+        torch.cuda.synchronize()
+        fev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+        for i in range(K):
+            fev[i][0].record(stream)
+            fstep.replay()
+            fev[i][1].record(stream)
+        torch.cuda.synchronize()
+        fused_ms = np.array([e[0].elapsed_time(e[1]) for e in fev])
+
     kv_layer, alg_layer = algorithmic_bytes(w)
     step_s = float(graph_ms.mean()) / 1e3
     dec_s = float(dec_ms.mean()) / 1e3
@@ -476,6 +543,13 @@ def bench_model_step(args, dev):
                      "kernel": "decode_kernel fp8 (one layer's pa_decode_fp8)",
                      "bytes_per_launch": alg_layer},
     })
+    if fused_ms is not None:
+        f_s = float(fused_ms.mean()) / 1e3
+        res["fused_append_decode"] = {
+            "entry_point": "pa_decode_append_fp8, one launch per layer, one HIP graph",
+            "step_ms_mean": round(f_s * 1e3, 4), "step_ms_p10": round(float(np.percentile(fused_ms, 10)), 4),
+            "step_ms_p90": round(float(np.percentile(fused_ms, 90)), 4),
+            "decode_tok_s": round(w.num_seqs / f_s, 1), "kv_gbs": round(n * kv_layer / f_s / 1e9, 1)}
     if not args.skip_cpu:
         res["cpu_baseline"] = cpu_baseline(w, t, out[0], layer=0)
     return res

@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 2
+#define PA_ABI_VERSION 3
 
 typedef enum pa_status {
   PA_OK = 0,
@@ -203,6 +203,43 @@ pa_status pa_decode_window_fp8(const pa_cache_desc* cache, const void* q, int32_
                                const int32_t* seq_lens, int32_t window, float scale,
                                float k_scale, float v_scale, float* out, int32_t partition_tokens,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Fused append and decode: one launch that does what pa_cache_write (or
+ * pa_cache_write_fp8) of each sequence's new token followed by
+ * pa_decode_window (or pa_decode_window_fp8) does.  The new token of
+ * sequence s is its last position, L - 1 with L = seq_lens[s] (the length
+ * counts it): it is written at offset (L - 1) % block_size of block
+ * block_tables[s][(L - 1) / block_size], for every KV head, and attended to
+ * with the rest.  A decode step appends the token's K and V to the sequence's
+ * cache and then attends over all of it ("Taming the token torrent", "The
+ * Block Table Logic"; "KV Cache Engineering for LLM Serving", section 1).
+ *   k_new, v_new  [num_seqs][num_kv_heads][head_dim] bf16, contiguous
+ *   k_cache, v_cache  written in place (the new token's row only)
+ *   window        as for pa_decode_window (0 = every token)
+ *   fp8: k_scale, v_scale serve both the write (codes of x / scale, rounded
+ *   as pa_cache_write_fp8 rounds them) and the read.
+ * The caches and `out` are bit for bit those of the two calls it replaces
+ * (same partition_tokens, same workspace size).  Sequences with L == 0 write
+ * nothing and give zeros; an invalid L, or a block id outside the pool,
+ * writes nothing and gives NaN rows, as for pa_decode.
+ * The block that receives a sequence's new token must not appear in another
+ * sequence's block table in the same call (a sequence appends into a block
+ * it owns alone, as copy-on-write ensures); if it does, the outputs of the
+ * sequences that share it are undefined.
+ * workspace: as for pa_decode (pa_decode_workspace_size).                   */
+pa_status pa_decode_append(const pa_cache_desc* cache, const void* q, const void* k_new,
+                           const void* v_new, int32_t num_seqs, int32_t num_q_heads,
+                           void* k_cache, void* v_cache, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t window,
+                           float scale, float* out, int32_t partition_tokens, void* workspace,
+                           size_t workspace_bytes, void* stream);
+pa_status pa_decode_append_fp8(const pa_cache_desc* cache, const void* q, const void* k_new,
+                               const void* v_new, int32_t num_seqs, int32_t num_q_heads,
+                               void* k_cache, void* v_cache, const int32_t* block_tables,
+                               int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                               int32_t window, float scale, float k_scale, float v_scale,
+                               float* out, int32_t partition_tokens, void* workspace,
+                               size_t workspace_bytes, void* stream);
 
 /* Human-readable name of a status code (static string, never NULL).        */
 const char* pa_status_string(pa_status status);

@@ -103,6 +103,10 @@ def _load():
         "pa_decode_window": ([dp, vp, i32, i32, vp, vp, vp, i32, vp, i32, f32, vp, i32, vp, sz, vp], i32),
         "pa_decode_window_fp8": ([dp, vp, i32, i32, vp, vp, vp, i32, vp, i32, f32, f32, f32, vp, i32, vp,
                                   sz, vp], i32),
+        "pa_decode_append": ([dp, vp, vp, vp, i32, i32, vp, vp, vp, i32, vp, i32, f32, vp, i32, vp, sz, vp],
+                             i32),
+        "pa_decode_append_fp8": ([dp, vp, vp, vp, i32, i32, vp, vp, vp, i32, vp, i32, f32, f32, f32, vp, i32,
+                                  vp, sz, vp], i32),
         "pa_quest_clear": ([dp, vp, vp], i32),
         "pa_quest_update": ([dp, i32, vp, vp, i32, vp, vp], i32),
         "pa_quest_summarize": ([dp, i32, vp, vp, vp, i32, vp, vp], i32),
@@ -528,6 +532,66 @@ def pa_decode_window_fp8(q, k_cache, v_cache, block_tables, seq_lens, window, sc
     """Sliding-window decode over an e4m3fn cache."""
     return _decode(True, q, k_cache, v_cache, block_tables, seq_lens, scale, out, num_kv_heads,
                    block_size, k_scale, v_scale, partition_tokens, workspace, window)
+
+
+def _decode_append(fp8, q, k_new, v_new, k_cache, v_cache, block_tables, seq_lens, scale, out,
+                   num_kv_heads, block_size, k_scale, v_scale, window, partition_tokens, workspace):
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("pa_decode_append needs device tensors")
+    _need(q, "q", torch.bfloat16, dev, 3)
+    S, Hq, D = q.shape
+    _need(k_new, "k_new", torch.bfloat16, dev, shape=(S, num_kv_heads, D))
+    _need(v_new, "v_new", torch.bfloat16, dev, shape=(S, num_kv_heads, D))
+    cdt = torch.uint8 if fp8 else torch.bfloat16
+    _need(k_cache, "k_cache", cdt, dev)
+    _need(v_cache, "v_cache", cdt, dev, shape=tuple(k_cache.shape))
+    _need(block_tables, "block_tables", torch.int32, dev, 2)
+    if block_tables.shape[0] != S:
+        raise ValueError("block_tables must have one row per sequence")
+    _need(seq_lens, "seq_lens", torch.int32, dev, shape=(S,))
+    if out is None:
+        out = torch.empty((S, Hq, D), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, dev, shape=(S, Hq, D))
+    desc = make_desc(k_cache, num_kv_heads, D, block_size)
+    maxb = block_tables.shape[1]
+    L = _load()
+    with torch.cuda.device(dev):
+        if workspace is None:
+            need = L.pa_decode_workspace_size(ctypes.byref(desc), S, Hq, maxb, partition_tokens)
+            if need == 0 and S > 0:
+                raise PagedAttentionError("pa_decode_workspace_size", -6,
+                                          "no gfx950 device or invalid sizes")
+            workspace = torch.zeros(max(int(need), 1), dtype=torch.uint8, device=dev)
+        _need(workspace, "workspace", torch.uint8, dev)
+        args = [ctypes.byref(desc), _ptr(q), _ptr(k_new), _ptr(v_new), S, Hq, _ptr(k_cache), _ptr(v_cache),
+                _ptr(block_tables), maxb, _ptr(seq_lens), int(window), float(scale)]
+        if fp8:
+            args += [float(k_scale), float(v_scale)]
+        args += [_ptr(out), int(partition_tokens), _ptr(workspace), workspace.numel(), _stream(q)]
+        name = "pa_decode_append" + ("_fp8" if fp8 else "")
+        st = getattr(L, name)(*args)
+    _check(name, st)
+    return out
+
+
+def pa_decode_append(q, k_new, v_new, k_cache, v_cache, block_tables, seq_lens, scale, out=None, *,
+                     num_kv_heads, block_size, window=0, partition_tokens=0, workspace=None):
+    """Write each sequence's new token (k_new, v_new [S, Hkv, D] bf16) at
+    position seq_lens[s] - 1 and decode, in one launch: the same caches and
+    output as pa_cache_write then pa_decode_window.  See pa_decode_append in
+    include/pa.h."""
+    return _decode_append(False, q, k_new, v_new, k_cache, v_cache, block_tables, seq_lens, scale, out,
+                          num_kv_heads, block_size, 1.0, 1.0, window, partition_tokens, workspace)
+
+
+def pa_decode_append_fp8(q, k_new, v_new, k_cache, v_cache, block_tables, seq_lens, scale, k_scale,
+                         v_scale, out=None, *, num_kv_heads, block_size, window=0, partition_tokens=0,
+                         workspace=None):
+    """pa_decode_append over an e4m3fn cache: the new token is stored as
+    codes of x / scale, as pa_cache_write_fp8 stores it."""
+    return _decode_append(True, q, k_new, v_new, k_cache, v_cache, block_tables, seq_lens, scale, out,
+                          num_kv_heads, block_size, k_scale, v_scale, window, partition_tokens, workspace)
 
 
 # -- query-aware page selection (include/pa_quest.h) -------------------------

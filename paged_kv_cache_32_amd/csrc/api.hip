@@ -153,7 +153,8 @@ pa_status decode(const pa_cache_desc* cache, const void* q, int32_t num_seqs, in
                  int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t window, float scale,
                  float k_scale, float v_scale, bool fp8, float* out, int32_t partition_tokens,
                  void* workspace, size_t workspace_bytes, void* stream, int32_t seq_heads = 0,
-                 float* lse = nullptr) {
+                 float* lse = nullptr, bool append = false, const void* k_new = nullptr,
+                 const void* v_new = nullptr) {
   if (!cache) return PA_ERR_NULL;
   if (!isfinite(scale) || window < 0) return PA_ERR_SHAPE;
   if (fp8 && (!good_scale(k_scale) || !good_scale(v_scale))) return PA_ERR_SHAPE;
@@ -170,6 +171,7 @@ pa_status decode(const pa_cache_desc* cache, const void* q, int32_t num_seqs, in
   }
   if (num_seqs == 0) return PA_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !out) return PA_ERR_NULL;
+  if (append && (!k_new || !v_new)) return PA_ERR_NULL;
   if (!workspace) return PA_ERR_WORKSPACE;
   pa_status st = plan(cache, num_seqs, num_q_heads, max_blocks_per_seq, partition_tokens, fp8,
                       &num_waves, &chunk_fixed);
@@ -209,6 +211,15 @@ pa_status decode(const pa_cache_desc* cache, const void* q, int32_t num_seqs, in
   p.seq_heads_magic = seq_heads > 1 ? (uint32_t)((((uint64_t)1 << 32) + seq_heads - 1) / seq_heads) : 0u;
   p.qk_scale = scale * 1.4426950408889634f * (fp8 ? k_scale : 1.0f);
   p.out_scale = fp8 ? v_scale : 1.0f;
+  // Fused append: the caches are the caller's writable memory.
+  p.k_new = static_cast<const uint16_t*>(k_new);
+  p.v_new = static_cast<const uint16_t*>(v_new);
+  p.k_store = append ? const_cast<uint8_t*>(p.k_cache) : nullptr;
+  p.v_store = append ? const_cast<uint8_t*>(p.v_cache) : nullptr;
+  // The cache write's reciprocals: correctly rounded float32 (IEEE division).
+  volatile float one = 1.0f;
+  p.k_inv = fp8 ? one / k_scale : 1.0f;
+  p.v_inv = fp8 ? one / v_scale : 1.0f;
   if (pa::launch_decode(p, fp8, static_cast<hipStream_t>(stream)) != hipSuccess)
     return PA_ERR_LAUNCH;
   return PA_OK;
@@ -336,6 +347,31 @@ pa_status pa_decode_window_fp8(const pa_cache_desc* cache, const void* q, int32_
   return decode(cache, q, num_seqs, num_q_heads, k_cache, v_cache, block_tables,
                 max_blocks_per_seq, seq_lens, window, scale, k_scale, v_scale, true, out,
                 partition_tokens, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_decode_append(const pa_cache_desc* cache, const void* q, const void* k_new,
+                           const void* v_new, int32_t num_seqs, int32_t num_q_heads, void* k_cache,
+                           void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* seq_lens, int32_t window, float scale, float* out,
+                           int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  return decode(cache, q, num_seqs, num_q_heads, k_cache, v_cache, block_tables,
+                max_blocks_per_seq, seq_lens, window, scale, 1.f, 1.f, false, out,
+                partition_tokens, workspace, workspace_bytes, stream, 0, nullptr, true, k_new,
+                v_new);
+}
+
+pa_status pa_decode_append_fp8(const pa_cache_desc* cache, const void* q, const void* k_new,
+                               const void* v_new, int32_t num_seqs, int32_t num_q_heads,
+                               void* k_cache, void* v_cache, const int32_t* block_tables,
+                               int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t window,
+                               float scale, float k_scale, float v_scale, float* out,
+                               int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  return decode(cache, q, num_seqs, num_q_heads, k_cache, v_cache, block_tables,
+                max_blocks_per_seq, seq_lens, window, scale, k_scale, v_scale, true, out,
+                partition_tokens, workspace, workspace_bytes, stream, 0, nullptr, true, k_new,
+                v_new);
 }
 
 pa_status pa_copy_blocks(const pa_cache_desc* cache, int32_t elem_bytes, void* k_cache,

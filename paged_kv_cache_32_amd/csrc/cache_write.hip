@@ -19,27 +19,6 @@ namespace {
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-// e4m3fn code of float32(x * inv): round to nearest even, saturate to
-// +-448, NaN -> 0x7F with x's sign.  Clamping first keeps the hardware
-// conversion inside the finite range, where it rounds to nearest even.
-__device__ __forceinline__ uint32_t e4m3_code(float x, float inv) {
-  if (__builtin_isnan(x)) return (__float_as_uint(x) >> 24 & 0x80u) | 0x7Fu;
-  float y = x * inv;
-  y = __builtin_fminf(__builtin_fmaxf(y, -448.0f), 448.0f);
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y, y, 0, false) & 0xFFu;
-}
-
-// Element index of V (token r of a 16-token tile, dim d) inside its tile:
-// [d / 16R][d % 16][r / 4][(d / 16) % R][r % 4].
-template <int R>
-__device__ __forceinline__ int v_elem(int d, int r) {
-  return ((((d / (16 * R)) * 16 + d % 16) * 4 + r / 4) * R + (d / 16) % R) * 4 + r % 4;
-}
-
-__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
-  return __uint_as_float(bits16 << 16);
-}
-
 // One thread per (token, kv head, group of X elements), X = 16 bytes of
 // cache: 8 bf16 values or 16 fp8 codes.
 template <bool FP8>

@@ -41,6 +41,16 @@
 //    l_p) and re-arms the counter to zero, so one kernel launch does the
 //    whole decode.  Every wavefront scans seq_lens itself, so there is no
 //    planning kernel and no host synchronisation.
+//  * Fused append (the APPEND instantiation): the step's new token of a
+//    sequence is its position L - 1, in the last chunk of each of its units.
+//    Before its first tile load, a wavefront stores the new tokens of the
+//    units whose last chunk lies in its range (it is the only reader of
+//    those tiles), 8 units per memory round trip, and waits for the stores;
+//    its loads then read them like any other token.  All of the append's memory traffic thus happens
+//    before the load pipeline starts: a load or store issued inside the
+//    pipeline on some stages only would make the waits of the following
+//    stages cover it, and under full load each such wait costs about one
+//    memory latency.
 #include "pa_internal.h"
 
 // Sub-blocks loaded per online-softmax step, and the fewest wavefronts per
@@ -255,6 +265,69 @@ __device__ __forceinline__ void next_unit(const DecodeParams& p, int max_len, in
   }
 }
 
+// Fused append: store the new tokens of up to 8 units at once, unit g by the
+// 8 lanes 8g .. 8g + 7 (u_s >= 0 marks a lane whose group has a unit): the
+// token of sequence u_s (position u_L - 1) of KV head u_h, rows [u_s][u_h][:]
+// of k_new / v_new, goes into its tile as the cache write stores it (bf16
+// bits, or e4m3fn codes of x / scale).  Lane j writes K pieces j and j + 8 of
+// the row (16 bytes, X dims each) and V dims (D / 8) j .. + D / 8 - 1 one
+// element each.  Every load of the batch is issued before the first store,
+// so the batch costs one memory round trip.  Nothing is written for a token
+// whose block lies outside the pool.
+template <int D, bool FP8>
+__device__ __forceinline__ void write_new_tokens(const DecodeParams& p, int u_s, int u_h, int u_L, int lane) {
+  using T = Tile<D, FP8>;
+  constexpr int X = FP8 ? 16 : 8;    // elements per 16-byte K piece
+  constexpr int KP = D / X;          // K pieces per row
+  constexpr int VE = D / 8;          // V elements per lane
+  if (u_s < 0) return;
+  const int j = lane & 7;
+  const int pos = u_L - 1, chunk = pos / kSub, r = pos % kSub;
+  const int bi = pos / p.block_size;
+  const int blk = p.block_tables[(int64_t)u_s * p.max_blocks + bi];
+  const int64_t row = ((int64_t)u_s * p.num_kv_heads + u_h) * D;
+  u32x4 kin[2][FP8 ? 2 : 1];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int hf = 0; hf < (FP8 ? 2 : 1); ++hf)
+      kin[i][hf] = (j + 8 * i < KP) ? *reinterpret_cast<const u32x4*>(p.k_new + row + (j + 8 * i) * X + 8 * hf)
+                                    : u32x4{0u, 0u, 0u, 0u};
+  u32x4 vin[VE / 8];
+#pragma unroll
+  for (int i = 0; i < VE / 8; ++i) vin[i] = *reinterpret_cast<const u32x4*>(p.v_new + row + VE * j + 8 * i);
+  if ((unsigned)blk >= (unsigned)p.num_blocks) return;
+  const int64_t tile = (int64_t)blk * p.blk_stride + (int64_t)(u_h * p.subs + (chunk - bi * p.subs)) * T::TILE_BYTES;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int pc = j + 8 * i;
+    if (pc < KP) {
+      u32x4 out;
+      if constexpr (FP8) {
+        out = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const uint32_t w = kin[i][e >> 3][(e >> 1) & 3];
+          out[e >> 2] |= e4m3_code(bf16_to_f32((e & 1) ? (w >> 16) : (w & 0xFFFFu)), p.k_inv) << (8 * (e & 3));
+        }
+      } else {
+        out = kin[i][0];
+      }
+      *reinterpret_cast<u32x4*>(p.k_store + tile + ((int64_t)pc * kSub + r) * 16) = out;   // [d/X][t%16][X]
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < VE; ++e) {
+    const uint32_t w = vin[e >> 3][(e >> 1) & 3];
+    const uint32_t x = (e & 1) ? (w >> 16) : (w & 0xFFFFu);
+    const int d = VE * j + e;
+    if constexpr (FP8)
+      p.v_store[tile + v_elem<4>(d, r)] = (uint8_t)e4m3_code(bf16_to_f32(x), p.v_inv);
+    else
+      reinterpret_cast<uint16_t*>(p.v_store + tile)[v_elem<2>(d, r)] = (uint16_t)x;
+  }
+}
+
 // Next stage of the cursor's range; moves the cursor past it.
 template <int NSUB>
 __device__ __forceinline__ Stage next_stage(Cursor& c, const DecodeParams& p, int max_len) {
@@ -300,6 +373,42 @@ __device__ __forceinline__ Stage next_stage(Cursor& c, const DecodeParams& p, in
   st = Stage{uni(pc.s), uni(pc.h), uni(pc.n), uni(pc.L), uni(pc.u0), uni(c0 + c.j), uni(cnt), uni(f)};
   c.j += cnt;
   return st;
+}
+
+// Fused append: store the new tokens of the units whose last chunk lies in
+// this wavefront's range [a, b) (called before the first stage, while the
+// cursor still stands at piece A), 8 units per batch, then wait for the
+// stores.  Those units are unit A when it ends inside the range, every
+// middle unit, and unit Z when its last chunk is b - 1.
+template <int D, bool FP8>
+__device__ __forceinline__ void append_range(const DecodeParams& p, const Cursor& c, int b, int max_len,
+                                             int lane) {
+  int u_s = -1, u_h = 0, u_L = 0, cnt = 0;
+  auto add = [&](int s, int h, int L) {
+    if ((lane >> 3) == cnt) {
+      u_s = s;
+      u_h = h;
+      u_L = L;
+    }
+    if (++cnt == 8) {
+      write_new_tokens<D, FP8>(p, u_s, u_h, u_L, lane);
+      u_s = -1;
+      cnt = 0;
+    }
+  };
+  if (c.a_end <= b) add(c.cur.s, c.cur.h, c.cur.L);
+  if (c.a_end < c.z.u0) {
+    int s = c.a_s, h = c.a_h, n = c.cur.n, L = c.cur.L;
+    int u0 = c.a_end;
+    do {
+      next_unit(p, max_len, s, h, n, L);
+      add(s, h, L);
+      u0 += n;
+    } while (u0 < c.z.u0);
+  }
+  if (c.z.j1 > 0 && c.z.u0 + c.z.n == b) add(c.z.s, c.z.h, c.z.L);
+  if (cnt > 0) write_new_tokens<D, FP8>(p, u_s, u_h, u_L, lane);
+  wait_vmcnt<0>();
 }
 
 // Issue every load of a stage: exactly StageBuf::kLoads vector loads, always,
@@ -684,7 +793,7 @@ __device__ __forceinline__ void settle(const DecodeParams& p, WaveState<D, FP8>&
   }
 }
 
-template <int D, bool FP8, int NSUB>
+template <int D, bool FP8, int NSUB, bool APPEND>
 __global__ __launch_bounds__(kDecodeThreads, PA_DECODE_MIN_WAVES) void decode_kernel(const DecodeParams p) {
   using Buf = StageBuf<D, FP8, NSUB>;
   static_assert(Buf::kLoads <= 63, "a stage must fit the vector-memory counter");
@@ -789,6 +898,7 @@ __global__ __launch_bounds__(kDecodeThreads, PA_DECODE_MIN_WAVES) void decode_ke
       cur.z = Piece{sz, hz, nz, Lz, u0z, 0, b - u0z};
     }
   }
+  if constexpr (APPEND) append_range<D, FP8>(p, cur, b, max_len, lane);
 
   // Lane offsets of the stage loads (constant per lane): query row of head
   // col (clamped into the group) at k-group qd; K lane = 16 bytes; V lane
@@ -841,7 +951,10 @@ __global__ __launch_bounds__(256) void zero_kernel(uint32_t* p, size_t words) {
 template <int D, bool FP8>
 hipError_t launch_typed(const DecodeParams& p, hipStream_t stream) {
   const unsigned groups = (unsigned)((p.num_waves + kWavesPerGroup - 1) / kWavesPerGroup);
-  hipLaunchKernelGGL((decode_kernel<D, FP8, kStage<FP8>>), dim3(groups), dim3(kDecodeThreads), 0, stream, p);
+  if (p.k_new)
+    hipLaunchKernelGGL((decode_kernel<D, FP8, kStage<FP8>, true>), dim3(groups), dim3(kDecodeThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_kernel<D, FP8, kStage<FP8>, false>), dim3(groups), dim3(kDecodeThreads), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -850,7 +963,7 @@ int resident_waves_typed() {
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<D, FP8, kStage<FP8>>, kDecodeThreads, 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<D, FP8, kStage<FP8>, false>, kDecodeThreads, 0) !=
       hipSuccess)
     return 0;
   return cus * per_cu * kWavesPerGroup;

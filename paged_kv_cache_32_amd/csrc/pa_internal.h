@@ -16,6 +16,29 @@ constexpr int kSub = 16;
 constexpr int kWavesPerGroup = PA_DECODE_WAVES_PER_GROUP;
 constexpr int kDecodeThreads = 64 * kWavesPerGroup;
 
+// e4m3fn code of float32(x * inv): round to nearest even, saturate to
+// +-448, NaN -> 0x7F with x's sign ("KV Cache Engineering for LLM Serving",
+// section 8, Quantization: divide by the scale, round, clip).  Clamping
+// first keeps the hardware conversion inside the finite range, where it
+// rounds to nearest even (a NaN clamps to -448 and its code is replaced).
+// Branch-free, so loops over it unroll into straight-line code.
+__device__ __forceinline__ uint32_t e4m3_code(float x, float inv) {
+  float y = x * inv;
+  y = __builtin_fminf(__builtin_fmaxf(y, -448.0f), 448.0f);
+  const uint32_t code = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y, y, 0, false) & 0xFFu;
+  const uint32_t nan_code = (__float_as_uint(x) >> 24 & 0x80u) | 0x7Fu;
+  return __builtin_isnan(x) ? nan_code : code;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// Element index of V (token r of a 16-token tile, dim d) inside its tile:
+// [d / 16R][d % 16][r / 4][(d / 16) % R][r % 4].
+template <int R>
+__device__ __forceinline__ int v_elem(int d, int r) {
+  return ((((d / (16 * R)) * 16 + d % 16) * 4 + r / 4) * R + (d / 16) % R) * 4 + r % 4;
+}
+
 struct CacheWriteParams {
   const uint16_t* k;          // [T][Hkv][D] bf16 bits
   const uint16_t* v;
@@ -51,6 +74,15 @@ struct DecodeParams {
   uint32_t seq_heads_magic;     // ceil(2^32 / seq_heads): s / seq_heads = umulhi(s, magic)
   float qk_scale;               // scale * log2(e) (* k_scale for fp8)
   float out_scale;              // 1 (bf16) or v_scale (fp8)
+  // Fused append (all null otherwise): sequence s's new token, rows
+  // [s][h][:] of k_new / v_new ([S][Hkv][D] bf16), is position L - 1; it is
+  // stored into the caches (k_store / v_store, the same memory as k_cache /
+  // v_cache) and attended to from registers.
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  uint8_t* k_store;
+  uint8_t* v_store;
+  float k_inv, v_inv;           // fp8 append: 1 / k_scale, 1 / v_scale
 };
 
 struct BlockMoveParams {

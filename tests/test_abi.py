@@ -40,10 +40,11 @@ def test_exports_every_declared_symbol():
                           "pa_copy_blocks", "pa_swap_out", "pa_swap_in", "pa_bm_create",
                           "pa_bm_append_token", "pa_bm_batch", "pa_bm_swap_out", "pa_bm_swap_in",
                           "pa_quest_clear", "pa_quest_update", "pa_quest_summarize", "pa_quest_select",
-                          "pa_decode_quest", "pa_decode_quest_fp8"}
+                          "pa_decode_quest", "pa_decode_quest_fp8", "pa_decode_append",
+                          "pa_decode_append_fp8"}
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.pa_abi_version() == 2
+    assert lib.pa_abi_version() == 3
 
 
 def test_status_strings():
@@ -108,6 +109,33 @@ def test_decode_validation():
     assert dec(desc(), ws=None) == WS
     assert dec(desc(), fp8=True, ks=0.0) == SHAPE
     assert dec(desc(), fp8=True, vs=float("inf")) == SHAPE
+
+
+def app(d, S=2, Hq=16, maxb=4, window=0, scale=0.1, q=FAKE, kn=FAKE, vn=FAKE, ws=FAKE, wsb=1 << 30,
+        fp8=False, ks=1.0, vs=1.0):
+    lib = pa.lib()
+    dp = ctypes.byref(d) if d else None
+    if fp8:
+        return lib.pa_decode_append_fp8(dp, q, kn, vn, S, Hq, FAKE, FAKE, FAKE, maxb, FAKE, window, scale,
+                                        ks, vs, FAKE, 0, ws, wsb, None)
+    return lib.pa_decode_append(dp, q, kn, vn, S, Hq, FAKE, FAKE, FAKE, maxb, FAKE, window, scale, FAKE, 0,
+                                ws, wsb, None)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_decode_append_validation(fp8):
+    assert app(None, fp8=fp8) == NULL
+    assert app(desc(d=32), kn=None, fp8=fp8) == UNSUP    # shape checks come before pointers
+    assert app(desc(), Hq=3, fp8=fp8) == SHAPE
+    assert app(desc(), window=-1, fp8=fp8) == SHAPE
+    assert app(desc(), S=0, kn=None, vn=None, fp8=fp8) == OK
+    assert app(desc(), kn=None, fp8=fp8) == NULL
+    assert app(desc(), vn=None, fp8=fp8) == NULL
+    assert app(desc(), q=None, fp8=fp8) == NULL
+    assert app(desc(), ws=None, fp8=fp8) == WS
+    if fp8:
+        assert app(desc(), fp8=True, ks=0.0) == SHAPE
+        assert app(desc(), fp8=True, vs=float("nan")) == SHAPE
 
 
 def test_workspace_init_validation():

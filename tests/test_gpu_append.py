@@ -1,0 +1,195 @@
+"""Fused append and decode (pa_decode_append / pa_decode_append_fp8,
+include/pa.h) on the GPU.  Each case runs the fused call on one copy of the
+caches and the two calls it replaces (pa_cache_write then pa_decode_window)
+on another, from the same seeded inputs, and checks
+
+  * the caches: byte for byte equal to each other and to the oracle's write
+    of the new tokens ("Taming the token torrent", "The Block Table Logic");
+  * the outputs: bit for bit equal to each other (the fused kernel attends
+    to the same values in the same order), and within the decode tolerance
+    of the oracle's decode of the written caches.
+
+The generator poisons each new token's slot with NaN before the step, so a
+token the fused kernel did not store before reading its tile shows up as
+NaN."""
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_32_amd as pa
+from paged_kv_cache_32_amd import workloads as W
+from oracle import paged
+from tests.gpu_helpers import compare, device_inputs, geom, host_bits, oracle_caches
+
+pytestmark = pytest.mark.gpu
+
+
+def scales(w, t):
+    if w.kv_dtype == "fp8":
+        return float(t["k_scale"][0]), float(t["v_scale"][0])
+    return 1.0, 1.0
+
+
+def two_calls(w, t, kc, vc, slots, seq_lens, window, part, ws):
+    ks, vs = scales(w, t)
+    kw = dict(num_kv_heads=w.num_kv_heads, block_size=w.block_size, partition_tokens=part, workspace=ws)
+    if w.kv_dtype == "bf16":
+        pa.pa_cache_write(t["k_new"][0], t["v_new"][0], slots, kc, vc, block_size=w.block_size)
+        return pa.pa_decode_window(t["q"][0], kc, vc, t["block_tables"], seq_lens, window, w.scale, **kw)
+    pa.pa_cache_write_fp8(t["k_new"][0], t["v_new"][0], slots, kc, vc, ks, vs, block_size=w.block_size)
+    return pa.pa_decode_window_fp8(t["q"][0], kc, vc, t["block_tables"], seq_lens, window, w.scale, ks, vs,
+                                   **kw)
+
+
+def fused(w, t, kc, vc, seq_lens, window, part, ws):
+    ks, vs = scales(w, t)
+    kw = dict(num_kv_heads=w.num_kv_heads, block_size=w.block_size, window=window, partition_tokens=part,
+              workspace=ws)
+    if w.kv_dtype == "bf16":
+        return pa.pa_decode_append(t["q"][0], t["k_new"][0], t["v_new"][0], kc, vc, t["block_tables"], seq_lens,
+                                   w.scale, **kw)
+    return pa.pa_decode_append_fp8(t["q"][0], t["k_new"][0], t["v_new"][0], kc, vc, t["block_tables"],
+                                   seq_lens, w.scale, ks, vs, **kw)
+
+
+def workspace(w, part):
+    need = pa.pa_decode_workspace_size(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.num_seqs,
+                                       w.num_q_heads, w.max_blocks_per_seq, part)
+    return torch.zeros(need, dtype=torch.uint8, device="cuda")
+
+
+def shared_new_token_blocks(w):
+    """For each sequence, whether the block receiving its new token (position
+    L - 1) is named by another sequence's table too (the fused call requires
+    that it is not)."""
+    refs = {}
+    for s in range(w.num_seqs):
+        for b in set(int(x) for x in w.block_tables[s] if x >= 0):
+            refs[b] = refs.get(b, 0) + 1
+    out = []
+    for s, L in enumerate(w.seq_lens):
+        L = int(L)
+        out.append(L > 0 and refs[int(w.block_tables[s, (L - 1) // w.block_size])] > 1)
+    return out
+
+
+def run_pair(w, t, window, part, seq_lens=None, slots=None):
+    """The fused call and the two calls on separate cache copies; returns
+    (fused out, two-call out, fused caches, two-call caches)."""
+    seq_lens = t["seq_lens"] if seq_lens is None else seq_lens
+    slots = t["slot_mapping"] if slots is None else slots
+    kc_a, vc_a = t["k_cache"][0].clone(), t["v_cache"][0].clone()
+    kc_b, vc_b = t["k_cache"][0].clone(), t["v_cache"][0].clone()
+    out_a = fused(w, t, kc_a, vc_a, seq_lens, window, part, workspace(w, part))
+    out_b = two_calls(w, t, kc_b, vc_b, slots, seq_lens, window, part, workspace(w, part))
+    torch.cuda.synchronize()
+    return out_a, out_b, (kc_a, vc_a), (kc_b, vc_b)
+
+
+def assert_same(out_a, out_b, caches_a, caches_b, label):
+    for name, a, b in (("K", caches_a[0], caches_b[0]), ("V", caches_a[1], caches_b[1])):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"{label}: {name} cache differs"
+    assert torch.equal(out_a.view(torch.int32), out_b.view(torch.int32)), f"{label}: outputs differ in bits"
+
+
+CASES = [  # seed, S, Hq, Hkv, D, BS, max_len, kv, window, partition_tokens
+    (41, 9, 32, 4, 128, 16, 700, "bf16", 0, 0),
+    (42, 7, 16, 2, 64, 32, 900, "bf16", 0, 32),
+    (43, 8, 8, 8, 128, 48, 600, "fp8", 0, 0),
+    (44, 6, 64, 8, 128, 16, 1500, "fp8", 0, 48),
+    (45, 10, 12, 1, 64, 16, 500, "bf16", 100, 0),
+    (46, 5, 40, 8, 128, 256, 2000, "fp8", 300, 16),
+    (47, 12, 16, 1, 128, 32, 400, "bf16", 0, 16),
+    (48, 6, 8, 4, 64, 64, 800, "fp8", 64, 0),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"{c[7]}_d{c[4]}_bs{c[5]}_w{c[8]}_p{c[9]}" for c in CASES])
+def test_append_matches_two_calls_and_oracle(case):
+    seed, S, Hq, Hkv, D, BS, max_len, kv, window, part = case
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(1, max_len + 1, size=S).astype(np.int32)
+    lens[:4] = [1, 16, 17, 0]                 # only the new token; a full chunk; one past it; empty
+    w = W.random_workload(seed, S, Hq, Hkv, D, BS, max_len, kv_dtype=kv, lens=lens)
+    assert not any(shared_new_token_blocks(w))
+    t = device_inputs(w)                      # new-token slots poisoned with NaN
+    print(f"[append] {kv} D={D} BS={BS} window={window} part={part} lens={list(w.seq_lens)}", flush=True)
+    out_a, out_b, ca, cb = run_pair(w, t, window, part)
+    assert_same(out_a, out_b, ca, cb, "fused vs two calls")
+
+    ks, vs = scales(w, t)
+    kc_ref, vc_ref = oracle_caches(w, host_bits(t["k_cache"][0]), host_bits(t["v_cache"][0]),
+                                   host_bits(t["k_new"][0]), host_bits(t["v_new"][0]), ks, vs)
+    assert np.array_equal(host_bits(ca[0]), kc_ref), "K cache differs from the oracle's write"
+    assert np.array_equal(host_bits(ca[1]), vc_ref), "V cache differs from the oracle's write"
+    ref = paged.decode(geom(w), host_bits(t["q"][0]), kc_ref, vc_ref, w.block_tables, w.seq_lens, w.scale,
+                       k_scale=ks, v_scale=vs, window=window)
+    assert float(out_a[3].abs().max()) == 0.0            # L = 0: zeros
+    compare(out_a, ref, kv, label="fused vs oracle")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_append_invalid_rows(kv):
+    """A length past the table and a last block outside the pool: nothing is
+    written for those sequences, their rows are NaN, and every other
+    sequence is unaffected; the two calls get slot -1 / an out-of-range slot
+    for them, which writes nothing either."""
+    w = W.random_workload(51, 8, 16, 2, 128, 16, 300, kv_dtype=kv, min_len=1)
+    t = device_inputs(w)
+    lens = w.seq_lens.copy()
+    lens[2] = w.max_blocks_per_seq * w.block_size + 1
+    bad_s = 5
+    L5 = int(lens[bad_s])
+    bt = w.block_tables.copy()
+    bt[bad_s, (L5 - 1) // w.block_size] = w.num_blocks + 7
+    t["block_tables"] = torch.from_numpy(bt).cuda()
+    slots = w.slot_mapping.copy()
+    slots[2] = -1
+    slots[bad_s] = (w.num_blocks + 7) * w.block_size + (L5 - 1) % w.block_size
+    print(f"[append] invalid rows {kv}: lens={list(lens)}", flush=True)
+    out_a, out_b, ca, cb = run_pair(w, t, 0, 0, seq_lens=torch.from_numpy(lens).cuda(),
+                                    slots=torch.from_numpy(slots).cuda())
+    assert_same(out_a, out_b, ca, cb, "invalid rows")
+    assert torch.isnan(out_a[2]).all() and torch.isnan(out_a[bad_s]).all()
+    good = [s for s in range(w.num_seqs) if s not in (2, bad_s)]
+    assert torch.isfinite(out_a[good]).all()
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_append_full_size_layer(kv):
+    """The 70B-shaped layer at batch 64 (lognormal lengths up to 32,768), in
+    the launch configuration the benchmark times: bit-equal to the two
+    calls, and sampled sequences (the shortest, the median and the longest)
+    against the oracle."""
+    w = W.llama70b_layer(kv_dtype=kv)
+    assert not any(shared_new_token_blocks(w))
+    t = device_inputs(w, poison=False)
+    print(f"[append] full size {kv}: {int(w.seq_lens.sum())} tokens", flush=True)
+    out_a, out_b, ca, cb = run_pair(w, t, 0, 0)
+    assert_same(out_a, out_b, ca, cb, "full size")
+    order = np.argsort(w.seq_lens)
+    seqs = sorted({int(order[0]), int(order[len(order) // 2]), int(order[-1])})
+    ks, vs = scales(w, t)
+    kc_ref, vc_ref = host_bits(ca[0]), host_bits(ca[1])
+    # The written caches were checked against the two calls above; check the
+    # new tokens' rows of the sampled sequences against the oracle's write.
+    kc0, vc0 = host_bits(t["k_cache"][0]), host_bits(t["v_cache"][0])
+    kn, vn = host_bits(t["k_new"][0]), host_bits(t["v_new"][0])
+    sub = W.Workload(w.name, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size, w.num_blocks, w.seq_lens,
+                     w.block_tables, np.where(np.isin(np.arange(w.num_seqs), seqs), w.slot_mapping, -1),
+                     w.scale, kv_dtype=kv)
+    k_or, v_or = oracle_caches(sub, kc0, vc0, kn, vn, ks, vs)
+    g = geom(w)
+    for s in seqs:
+        pos = int(w.seq_lens[s]) - 1
+        blk = int(w.block_tables[s, pos // w.block_size])
+        for h in range(w.num_kv_heads):
+            for d in range(w.head_dim):
+                assert kc_ref[paged.k_offset(g, blk, h, pos % w.block_size, d)] == \
+                    k_or[paged.k_offset(g, blk, h, pos % w.block_size, d)]
+                assert vc_ref[paged.v_offset(g, blk, h, pos % w.block_size, d)] == \
+                    v_or[paged.v_offset(g, blk, h, pos % w.block_size, d)]
+    ref = paged.decode(g, host_bits(t["q"][0]), kc_ref, vc_ref, w.block_tables, w.seq_lens, w.scale,
+                       k_scale=ks, v_scale=vs, seqs=seqs)
+    compare(out_a, ref, kv, seqs=seqs, label="full size vs oracle")

@@ -1,5 +1,5 @@
-"""A multi-layer step (cache write + decode per layer) captured once as a HIP
-graph and replayed several times, with the program's own eager work and
+"""A multi-layer step (cache write + decode per layer, as two launches or as
+one fused append-and-decode launch) captured once as a HIP graph and replayed several times, with the program's own eager work and
 synchronisations between replays: every replay must reproduce the eager
 result bit for bit (the kernels issue no memset, allocate nothing, and the
 decode re-arms its workspace counters itself), and the result must match the
@@ -17,12 +17,14 @@ from tests.gpu_helpers import compare, device_inputs, host_bits, oracle_caches, 
 pytestmark = pytest.mark.gpu
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["two_calls", "fused"])
 @pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
-def test_graph_replays_match_eager_and_oracle(kv_dtype):
+def test_graph_replays_match_eager_and_oracle(kv_dtype, fused):
     w = W.random_workload(seed=77, num_seqs=24, num_q_heads=32, num_kv_heads=4, head_dim=128,
                           block_size=16, max_len=3000, kv_dtype=kv_dtype)
     w.num_layers = 3
-    print(f"[graph] {kv_dtype}: {int(w.seq_lens.sum())} tokens x {w.num_layers} layers", flush=True)
+    print(f"[graph] {kv_dtype} fused={fused}: {int(w.seq_lens.sum())} tokens x {w.num_layers} layers",
+          flush=True)
     t = device_inputs(w)
     before = [(host_bits(t["k_cache"][i]), host_bits(t["v_cache"][i])) for i in range(w.num_layers)]
     out = torch.empty((w.num_layers, w.num_seqs, w.num_q_heads, w.head_dim), dtype=torch.float32,
@@ -33,7 +35,7 @@ def test_graph_replays_match_eager_and_oracle(kv_dtype):
     step = DecodeStep(q=t["q"], k_new=t["k_new"], v_new=t["v_new"], k_cache=t["k_cache"],
                       v_cache=t["v_cache"], out=out, block_tables=t["block_tables"],
                       seq_lens=t["seq_lens"], slot_mapping=t["slot_mapping"], scale=w.scale,
-                      num_kv_heads=w.num_kv_heads, block_size=w.block_size, **kw)
+                      num_kv_heads=w.num_kv_heads, block_size=w.block_size, fused=fused, **kw)
     step.run()
     torch.cuda.synchronize()
     eager = out.clone()
