@@ -102,6 +102,11 @@ CASES = [  # seed, S, Hq, Hkv, D, BS, max_len, kv, window, partition_tokens
     (46, 5, 40, 8, 128, 256, 2000, "fp8", 300, 16),
     (47, 12, 16, 1, 128, 32, 400, "bf16", 0, 16),
     (48, 6, 8, 4, 64, 64, 800, "fp8", 64, 0),
+    # Many short sequences and long partitions: each wavefront finishes 20-40
+    # units, so their new tokens go out in several batches of 8.
+    (49, 40, 16, 4, 128, 16, 48, "bf16", 0, 1024),
+    (50, 40, 32, 8, 64, 32, 60, "fp8", 0, 2048),
+    (52, 30, 8, 2, 128, 16, 90, "fp8", 40, 0),
 ]
 
 
