@@ -182,10 +182,14 @@ __device__ __forceinline__ int pages_of(const SelectParams& p, int s) {
 }
 
 // Work item (chunk c, unit = s * Hkv + h): pages c * 256 .. + 255 of the
-// unit, one per thread; workgroups stride over the items, chunk-major, so
-// the first chunks of all units (the only ones short sequences have) spread
-// over every XCD.  Each thread sums over the dimensions in order, in
-// float32, for every query head of the group, and keeps the largest sum.
+// unit, two per thread (a workgroup of two wavefronts, 128 pages each:
+// lane l takes pages l and l + 64 of its wavefront's, so every read of the
+// query from LDS serves two pages); workgroups stride over the items,
+// chunk-major, so the first chunks of all units (the only ones short
+// sequences have) spread over every XCD.  Each thread sums over the
+// dimensions in order, in float32, for every query head of the group, and
+// keeps the largest sum of each of its pages.  The block ids are loaded
+// before the query, so the two loads' latencies overlap.
 //
 // For a page's min <= max and a query value q, max(q * min, q * max) is
 // q * max when q >= 0 and q * min otherwise; with q+ = (q >= 0 ? q : 0) and
@@ -201,10 +205,11 @@ __device__ __forceinline__ int pages_of(const SelectParams& p, int s) {
 // while the current one is summed, and its words are unpacked once per
 // dimension for all query heads.
 constexpr int kScorePages = 256;
-constexpr int kScoreGrid = 2048;
+constexpr int kScoreGrid = 4096;
 
-// Each wavefront stages its own 64 rows through LDS one line at a time: 8
-// lanes bring one row's line, so each load instruction covers 8 whole lines
+// Each wavefront stages its rows through LDS one line at a time, 64 rows
+// (one per lane) per pass, two passes per line: 8 lanes bring one row's
+// line, so each load instruction covers 8 whole lines
 // instead of pieces of 64 lines (64 cache tag lookups per instruction,
 // which measured as the cost of the lane-per-row loads); rows sit 144 bytes
 // apart, so a lane's reads of its own row fall in distinct banks.  No
@@ -213,71 +218,86 @@ constexpr int kScoreGrid = 2048;
 constexpr int kRowWords = 36;   // 32 words of a line + 4 of pad
 
 template <int D>
-__global__ __launch_bounds__(256) void page_score_kernel(const SelectParams p) {
+__global__ __launch_bounds__(128) void page_score_kernel(const SelectParams p) {
   __shared__ float qpos[kMaxGroupQuest * D], qneg[kMaxGroupQuest * D];
-  __shared__ __attribute__((aligned(16))) uint32_t stage[4][64 * kRowWords];
+  __shared__ __attribute__((aligned(16))) uint32_t stage[2][64 * kRowWords];
   const int Hkv = p.num_kv_heads, G = p.group;
   const int units = p.num_seqs * Hkv;
-  const int items = units * p.chunks;
+  const int chunks = p.chunks;                              // items of 256 pages
+  const int items = units * chunks;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   uint32_t* rows = stage[wv];
   for (int it = blockIdx.x; it < items; it += gridDim.x) {
     const int c = it / units, unit = it - c * units;
     const int s = unit / Hkv, h = unit - s * Hkv;
     const int np = pages_of(p, s);
-    if (c * kScorePages >= np) continue;                     // uniform
-    __syncthreads();                                         // previous item done with q+/q-
+    if (c * 256 >= np) continue;                             // uniform
+    const int pg0 = c * 256 + 128 * wv;                      // this wavefront's first page
+    int blk[2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int pg = pg0 + 64 * x + lane;
+      blk[x] = pg < np ? p.block_tables[(int64_t)s * p.max_blocks + pg] : -1;
+    }
+    __syncthreads();
     const uint16_t* qg = p.q + ((int64_t)s * p.num_q_heads + (int64_t)h * G) * D;
-    for (int i = tid; i < G * D; i += 256) {
+    for (int i = tid; i < G * D; i += 128) {
       const uint32_t b = qg[i];
       const float qf = __uint_as_float(b << 16);
       qpos[i] = (b & 0x8000u) ? 0.f : qf;
       qneg[i] = (b & 0x8000u) ? qf : 0.f;
     }
     __syncthreads();
-    const int pg0 = c * kScorePages + 64 * wv;               // this wavefront's first page
-    if (pg0 >= np) continue;                                 // wave-uniform; no barrier follows
-    const int pg = pg0 + lane;
-    int blk = pg < np ? p.block_tables[(int64_t)s * p.max_blocks + pg] : -1;
-    if ((unsigned)blk >= (unsigned)p.num_blocks) blk = -1;
-    // Lane brings piece lane % 8 of the lines of rows lane / 8 + 8 i, i < 8.
-    int rb[8];
+    if (pg0 >= np) continue;
+    int rb[2][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) rb[i] = __shfl(blk, lane / 8 + 8 * i, 64);
-    auto gload = [&](int b, u32x4 (&v)[8]) {
+    for (int x = 0; x < 2; ++x) {
+      if ((unsigned)blk[x] >= (unsigned)p.num_blocks) blk[x] = -1;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) rb[x][i] = __shfl(blk[x], lane / 8 + 8 * i, 64);
+    }
+    auto gload = [&](int x, int b, u32x4 (&v)[8]) {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        v[i] = rb[i] >= 0 ? reinterpret_cast<const u32x4*>(p.words + ((int64_t)rb[i] * Hkv + h) * D + 32 * b)[lane % 8]
-                          : u32x4{0u, 0u, 0u, 0u};
+        v[i] = rb[x][i] >= 0 ? reinterpret_cast<const u32x4*>(p.words + ((int64_t)rb[x][i] * Hkv + h) * D + 32 * b)[lane % 8]
+                             : u32x4{0u, 0u, 0u, 0u};
     };
-    u32x4 v[8];
-    gload(0, v);
-    float acc[kMaxGroupQuest];
-#pragma unroll
-    for (int j = 0; j < kMaxGroupQuest; ++j) acc[j] = 0.f;
-#pragma unroll 1
-    for (int b = 0; b < D / 32; ++b) {
+    auto stage_line = [&](const u32x4 (&v)[8], u32x4 (&line)[8]) {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         *reinterpret_cast<u32x4*>(rows + (lane / 8 + 8 * i) * kRowWords + 4 * (lane % 8)) = v[i];
-      if (b + 1 < D / 32) gload(b + 1, v);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      u32x4 line[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) line[k] = *reinterpret_cast<const u32x4*>(rows + lane * kRowWords + 4 * k);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+    u32x4 va[8], vb[8];
+    gload(0, 0, va);
+    gload(1, 0, vb);
+    float acc[2][kMaxGroupQuest];
+#pragma unroll
+    for (int j = 0; j < kMaxGroupQuest; ++j) acc[0][j] = acc[1][j] = 0.f;
+#pragma unroll 1
+    for (int b = 0; b < D / 32; ++b) {
+      u32x4 la[8], lb[8];
+      stage_line(va, la);
+      if (b + 1 < D / 32) gload(0, b + 1, va);
+      stage_line(vb, lb);
+      if (b + 1 < D / 32) gload(1, b + 1, vb);
 #pragma unroll
       for (int c8 = 0; c8 < 4; ++c8) {
-        float mnf[8], mxf[8];
+        float mna[8], mxa[8], mnb[8], mxb[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const uint32_t word = line[2 * c8 + e / 4][e % 4];
-          mnf[e] = __uint_as_float(word << 16);
-          mxf[e] = __uint_as_float(word & 0xFFFF0000u);
+          const uint32_t wa = la[2 * c8 + e / 4][e % 4], wb = lb[2 * c8 + e / 4][e % 4];
+          mna[e] = __uint_as_float(wa << 16);
+          mxa[e] = __uint_as_float(wa & 0xFFFF0000u);
+          mnb[e] = __uint_as_float(wb << 16);
+          mxb[e] = __uint_as_float(wb & 0xFFFF0000u);
         }
 #pragma unroll
         for (int j = 0; j < kMaxGroupQuest; ++j) {
@@ -285,23 +305,30 @@ __global__ __launch_bounds__(256) void page_score_kernel(const SelectParams p) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
               const int qi = j * D + 32 * b + 8 * c8 + e;
-              acc[j] = __builtin_fmaf(qpos[qi], mxf[e], acc[j]);
-              acc[j] = __builtin_fmaf(qneg[qi], mnf[e], acc[j]);
+              const float qp = qpos[qi], qn = qneg[qi];
+              acc[0][j] = __builtin_fmaf(qp, mxa[e], acc[0][j]);
+              acc[0][j] = __builtin_fmaf(qn, mna[e], acc[0][j]);
+              acc[1][j] = __builtin_fmaf(qp, mxb[e], acc[1][j]);
+              acc[1][j] = __builtin_fmaf(qn, mnb[e], acc[1][j]);
             }
           }
         }
       }
     }
-    if (pg < np) {
-      uint32_t key = 0u;  // a block outside the pool scores lowest
-      if (blk >= 0) {
-        float best = -__builtin_inff();
 #pragma unroll
-        for (int j = 0; j < kMaxGroupQuest; ++j)
-          if (j < G) best = __builtin_fmaxf(best, acc[j]);
-        key = score_key(best);
+    for (int x = 0; x < 2; ++x) {
+      const int pg = pg0 + 64 * x + lane;
+      if (pg < np) {
+        uint32_t key = 0u;  // a block outside the pool scores lowest
+        if (blk[x] >= 0) {
+          float best = -__builtin_inff();
+#pragma unroll
+          for (int j = 0; j < kMaxGroupQuest; ++j)
+            if (j < G) best = __builtin_fmaxf(best, acc[x][j]);
+          key = score_key(best);
+        }
+        p.keys[(int64_t)unit * p.max_blocks + pg] = key;
       }
-      p.keys[(int64_t)unit * p.max_blocks + pg] = key;
     }
   }
 }
@@ -606,9 +633,9 @@ hipError_t launch_page_select(const SelectParams& p, hipStream_t stream) {
   if (groups > kScoreGrid) groups = kScoreGrid;
   const dim3 grid((unsigned)groups);
   if (p.head_dim == 128)
-    hipLaunchKernelGGL(page_score_kernel<128>, grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(page_score_kernel<128>, grid, dim3(128), 0, stream, p);
   else
-    hipLaunchKernelGGL(page_score_kernel<64>, grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(page_score_kernel<64>, grid, dim3(128), 0, stream, p);
   hipLaunchKernelGGL(page_select_kernel, dim3((unsigned)units), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
