@@ -417,11 +417,12 @@ __device__ __forceinline__ int lds_index(int i) { return i + (i >> 5); }
 // lower page; written in page order to sel_tables[unit][0..budget), with
 // sel_lens[unit] = tokens they hold.
 //
-// The threshold T = the budget-th largest key is found bit by bit from the
-// top (32 counting rounds: T keeps a bit when at least `budget` keys are
-// >= T with it; for units held in registers a wavefront counts with one
-// ballot per key slot and scalar popcounts).  Then each thread takes a
-// contiguous range of pages: the
+// The threshold T = the budget-th largest key is found from the top: 8 bits
+// per round with an LDS histogram for units held in registers with at most
+// 16 keys per thread, else bit by bit (32 counting rounds: T keeps a bit
+// when at least `budget` keys are >= T with it; for units held in registers
+// a wavefront counts with one ballot per key slot and scalar popcounts).
+// Then each thread takes a contiguous range of pages: the
 // pages above T, and the first (budget - count above T) pages equal to T,
 // go to their place in page order through two prefix sums.
 //
@@ -431,7 +432,7 @@ __device__ __forceinline__ int lds_index(int i) { return i + (i >> 5); }
 // before the counting rounds, so their latency is paid once.  Longer units
 // read keys from LDS or global memory in each round.
 __device__ __forceinline__ void select_small(const SelectParams& p, int unit, int s, int np,
-                                             const uint32_t* gk, uint32_t* lk, int* red) {
+                                             const uint32_t* gk, uint32_t* lk, int* red, uint32_t* hist) {
   const int tid = threadIdx.x;
   const int B = p.budget;
   int32_t* out = p.sel_tables + (int64_t)unit * B;
@@ -448,18 +449,78 @@ __device__ __forceinline__ void select_small(const SelectParams& p, int unit, in
 #pragma unroll
   for (int k = 0; k < kSelectRegs; ++k)
     if (tid + 256 * k < np) lk[lds_index(tid + 256 * k)] = kr[k];
+  // T = the budget-th largest key.  Units of at most 16 key slots per
+  // thread find it 8 bits per round from the top: the keys that agree with T
+  // above the round's digit are counted per digit value (LDS histogram); T
+  // takes the largest digit with at least `want` of them at or above it,
+  // and `want` drops by those strictly above.  Fuller units, whose keys
+  // crowd the histogram's first-round bins (sign and top exponent bits),
+  // find it bit by bit: T keeps a bit when at least `budget` keys are >= T
+  // with it, counted with one ballot per key slot and scalar popcounts.
+  const int slots = (np + 255) / 256;       // key slots that hold any page
   uint32_t T = 0u;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = T | (1u << bit);   // >= 1: the padding keys 0 never count
-    // The wavefront's count: one ballot per key slot, counted on the scalar unit.
-    int c = 0;
+  if (slots <= 16) {
+    int want = B;
+    for (int r = 0; r < 4; ++r) {
+      const int shift = 24 - 8 * r;
+      hist[tid] = 0u;
+      __syncthreads();                          // also publishes the LDS keys (first round)
 #pragma unroll
-    for (int k = 0; k < kSelectRegs; ++k) c += __popcll(__ballot(kr[k] >= cand));
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = c;
-    __syncthreads();                          // also publishes the LDS keys
-    const int total = red[0] + red[1] + red[2] + red[3];
-    __syncthreads();
-    if (total >= B) T = cand;
+      for (int k = 0; k < kSelectRegs; ++k) {
+        if (k < slots && tid + 256 * k < np) {
+          const bool match = r == 0 || ((kr[k] ^ T) >> (shift + 8)) == 0u;
+          if (match) atomicAdd(&hist[(kr[k] >> shift) & 255u], 1u);
+        }
+      }
+      __syncthreads();
+      if (tid < 64) {
+        // Lane l holds digits 4l .. 4l + 3; suffix sums from the top digit.
+        uint32_t h[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) h[i] = hist[4 * tid + i];
+        const int own = (int)(h[0] + h[1] + h[2] + h[3]);
+        int suf = own;                          // sum over lanes >= tid
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int u = __shfl_down(suf, o, 64);
+          if (tid + o < 64) suf += u;
+        }
+        // S(d) for this lane's digits, top first; the largest d with S(d) >= want.
+        int above = suf - own;                  // keys in digits above 4 tid + 3
+        int dbest = -1, above_best = 0;
+#pragma unroll
+        for (int i = 3; i >= 0; --i) {
+          const int Sd = above + (int)h[i];
+          if (dbest < 0 && Sd >= want) {
+            dbest = 4 * tid + i;
+            above_best = above;
+          }
+          above = Sd;
+        }
+        const uint64_t hit = __ballot(dbest >= 0);
+        const int l = 63 - __builtin_clzll(hit);  // the highest lane with a qualifying digit
+        if (tid == l) {
+          red[0] = dbest;
+          red[1] = want - above_best;
+        }
+      }
+      __syncthreads();
+      T |= (uint32_t)red[0] << shift;
+      want = red[1];
+      __syncthreads();
+    }
+  } else {
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = T | (1u << bit);   // >= 1: the padding keys 0 never count
+      int c = 0;
+#pragma unroll
+      for (int k = 0; k < kSelectRegs; ++k) c += __popcll(__ballot(kr[k] >= cand));
+      if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = c;
+      __syncthreads();                        // also publishes the LDS keys
+      const int total = red[0] + red[1] + red[2] + red[3];
+      __syncthreads();
+      if (total >= B) T = cand;
+    }
   }
   uint32_t mine[kSelectRegs];
   int above = 0, equal = 0;
@@ -559,6 +620,7 @@ __device__ __forceinline__ void select_unit(const SelectParams& p, int unit, int
 __global__ __launch_bounds__(256) void page_select_kernel(const SelectParams p) {
   __shared__ uint32_t lk[kSelectLds + kSelectLds / 32];
   __shared__ int red[4];
+  __shared__ uint32_t hist[256];
   const int unit = blockIdx.x;
   const int s = unit / p.num_kv_heads;
   const int tid = threadIdx.x;
@@ -573,7 +635,7 @@ __global__ __launch_bounds__(256) void page_select_kernel(const SelectParams p) 
   }
   const uint32_t* gk = p.keys + (int64_t)unit * p.max_blocks;
   if (np <= 256 * kSelectRegs) {
-    select_small(p, unit, s, np, gk, lk, red);
+    select_small(p, unit, s, np, gk, lk, red, hist);
   } else if (np <= kSelectLds) {
     // Eight independent loads in flight per thread before their stores.
     for (int i0 = tid; i0 < np; i0 += 8 * 256) {
