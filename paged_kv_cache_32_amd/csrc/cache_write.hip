@@ -10,7 +10,11 @@
 //
 // The write is a few hundred bytes per token: it is latency bound, so the
 // kernel is one thread per 16-byte K chunk of a (token, kv head) row, with
-// the matching V elements, and no attempt at more.
+// the matching V elements, and no attempt at more.  A token's K row and V
+// column write many cache lines in part (16-byte K pieces 256 bytes apart, V
+// elements spread over the whole V tile); the stores carry the non-temporal
+// hint so that those lines are not kept in L2 as partly written lines when
+// the decode then streams the cache through it.
 #include "pa_internal.h"
 
 namespace pa {
@@ -49,13 +53,13 @@ __global__ __launch_bounds__(256) void cache_write_kernel(const CacheWriteParams
   uint8_t* vtile = p.v_cache + tile;  // [d/16R][d%16][(t%16)/4][(d/16)%R][t%4], R = 4 / eb
   if (!FP8) {
     const u32x4 kv = *reinterpret_cast<const u32x4*>(p.k + src);
-    *reinterpret_cast<u32x4*>(kdst) = kv;
+    __builtin_nontemporal_store(kv, reinterpret_cast<u32x4*>(kdst));
     const u32x4 vv = *reinterpret_cast<const u32x4*>(p.v + src);
     uint16_t* vdst = reinterpret_cast<uint16_t*>(vtile);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const uint32_t w = vv[e >> 1];
-      vdst[v_elem<2>(dg * 8 + e, r)] = (uint16_t)((e & 1) ? (w >> 16) : (w & 0xFFFFu));
+      __builtin_nontemporal_store((uint16_t)((e & 1) ? (w >> 16) : (w & 0xFFFFu)), vdst + v_elem<2>(dg * 8 + e, r));
     }
   } else {
     u32x4 kin[2], vin[2];
@@ -70,12 +74,12 @@ __global__ __launch_bounds__(256) void cache_write_kernel(const CacheWriteParams
       const uint32_t code = e4m3_code(bf16_to_f32((e & 1) ? (w >> 16) : (w & 0xFFFFu)), p.k_inv);
       kout[e >> 2] |= code << (8 * (e & 3));
     }
-    *reinterpret_cast<u32x4*>(kdst) = kout;
+    __builtin_nontemporal_store(kout, reinterpret_cast<u32x4*>(kdst));
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const uint32_t w = vin[e >> 3][(e >> 1) & 3];
       const uint32_t code = e4m3_code(bf16_to_f32((e & 1) ? (w >> 16) : (w & 0xFFFFu)), p.v_inv);
-      vtile[v_elem<4>(dg * 16 + e, r)] = (uint8_t)code;
+      __builtin_nontemporal_store((uint8_t)code, vtile + v_elem<4>(dg * 16 + e, r));
     }
   }
 }
