@@ -27,18 +27,21 @@ extern "C" {
  * is not a multiple of 16, PA_ERR_DEVICE without a gfx950.                  */
 pa_status pa_probe_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 
-/* Reads what pa_decode (bf16 cache, elem_bytes 2) or pa_decode_fp8
- * (elem_bytes 1) reads of the caches for the same arguments: for every
- * sequence s with 1 <= seq_lens[s] <= max_blocks_per_seq * block_size and
- * KV head h, the K and V tiles of 16 tokens covering tokens
- * [0, seq_lens[s]) through block_tables (block ids outside the pool are
- * skipped).  *sink ^= XOR of all 32-bit words of those tiles, each tile
- * counted once per (sequence, head) that reads it.  Validation as
- * pa_decode's (PA_ERR_UNSUPPORTED for elem_bytes other than 1 and 2).      */
+/* Reads what pa_decode_window (bf16 cache, elem_bytes 2) or
+ * pa_decode_window_fp8 (elem_bytes 1) reads of the caches for the same
+ * arguments (window 0: what pa_decode / pa_decode_fp8 read): for every
+ * sequence s with 1 <= L = seq_lens[s] <= max_blocks_per_seq * block_size
+ * and KV head h, the K and V tiles of 16 tokens covering tokens
+ * [max(0, L - window), L) (window > 0) or [0, L) (window 0) through
+ * block_tables (block ids outside the pool are skipped; table entries of
+ * tiles before the window are not read).  *sink ^= XOR of all 32-bit words
+ * of those tiles, each tile counted once per (sequence, head) that reads it.
+ * Validation as pa_decode's (PA_ERR_UNSUPPORTED for elem_bytes other than 1
+ * and 2; PA_ERR_SHAPE for window < 0).                                     */
 pa_status pa_probe_tile_read(const pa_cache_desc* cache, int32_t elem_bytes, const void* k_cache,
                              const void* v_cache, const int32_t* block_tables, int32_t num_seqs,
-                             int32_t max_blocks_per_seq, const int32_t* seq_lens, uint32_t* sink,
-                             void* stream);
+                             int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t window,
+                             uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

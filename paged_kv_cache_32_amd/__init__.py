@@ -126,7 +126,7 @@ def _load():
         "pa_decode_cascade_fp8": ([dp, vp, i32, i32, vp, vp, i32, ctypes.POINTER(CascadeDevicePlan), f32, f32,
                                    f32, vp, i32, vp, sz, vp], i32),
         "pa_probe_stream_read": ([vp, sz, vp, vp], i32),
-        "pa_probe_tile_read": ([dp, i32, vp, vp, vp, i32, i32, vp, vp, vp], i32),
+        "pa_probe_tile_read": ([dp, i32, vp, vp, vp, i32, i32, vp, i32, vp, vp], i32),
         "pa_bm_num_free": ([vp], i32),
         "pa_bm_sequence_info": ([vp, i64, ctypes.POINTER(i32), ctypes.POINTER(i32)], i32),
         "pa_bm_block_table": ([vp, i64, ctypes.POINTER(i32), i32], i32),
@@ -349,10 +349,11 @@ def pa_probe_stream_read(buf, sink=None):
 
 
 def pa_probe_tile_read(k_cache, v_cache, block_tables, seq_lens, *, num_kv_heads, head_dim, block_size,
-                       sink=None):
-    """Read the cache tiles pa_decode reads for these tables and lengths,
-    with no arithmetic (include/pa_probe.h); bf16 or uint8 (e4m3fn) caches.
-    Returns the int32 device tensor ``sink`` holding the XOR of their words."""
+                       window=0, sink=None):
+    """Read the cache tiles pa_decode (pa_decode_window with a window) reads
+    for these tables and lengths, with no arithmetic (include/pa_probe.h);
+    bf16 or uint8 (e4m3fn) caches.  Returns the int32 device tensor ``sink``
+    holding the XOR of their words."""
     dev = k_cache.device
     if k_cache.dtype not in (torch.bfloat16, torch.uint8):
         raise TypeError("caches must be bfloat16 or uint8 (e4m3fn codes)")
@@ -368,7 +369,7 @@ def pa_probe_tile_read(k_cache, v_cache, block_tables, seq_lens, *, num_kv_heads
     eb = 2 if k_cache.dtype == torch.bfloat16 else 1
     with torch.cuda.device(dev):
         st = _load().pa_probe_tile_read(ctypes.byref(desc), eb, _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
-                                        S, maxb, _ptr(seq_lens), _ptr(sink), _stream(k_cache))
+                                        S, maxb, _ptr(seq_lens), int(window), _ptr(sink), _stream(k_cache))
     _check("pa_probe_tile_read", st)
     return sink
 

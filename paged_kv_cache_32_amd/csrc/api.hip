@@ -779,13 +779,13 @@ pa_status pa_probe_stream_read(const void* buf, size_t bytes, uint32_t* sink, vo
 
 pa_status pa_probe_tile_read(const pa_cache_desc* cache, int32_t elem_bytes, const void* k_cache,
                              const void* v_cache, const int32_t* block_tables, int32_t num_seqs,
-                             int32_t max_blocks_per_seq, const int32_t* seq_lens, uint32_t* sink,
-                             void* stream) {
+                             int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t window,
+                             uint32_t* sink, void* stream) {
   if (!cache) return PA_ERR_NULL;
   pa_status st = desc_status(cache);
   if (st != PA_OK) return st;
   if (elem_bytes != 1 && elem_bytes != 2) return PA_ERR_UNSUPPORTED;
-  if (num_seqs < 0 || max_blocks_per_seq < 0) return PA_ERR_SHAPE;
+  if (num_seqs < 0 || max_blocks_per_seq < 0 || window < 0) return PA_ERR_SHAPE;
   if ((int64_t)max_blocks_per_seq * cache->block_size > INT32_MAX) return PA_ERR_SHAPE;
   if ((int64_t)num_seqs * cache->num_kv_heads * max_blocks_per_seq > INT32_MAX) return PA_ERR_SHAPE;
   if (!sink) return PA_ERR_NULL;
@@ -808,6 +808,7 @@ pa_status pa_probe_tile_read(const pa_cache_desc* cache, int32_t elem_bytes, con
   p.num_blocks = cache->num_blocks;
   p.head_dim = cache->head_dim;
   p.elem_bytes = elem_bytes;
+  p.window = window;
   p.blk_stride = (int64_t)cache->num_kv_heads * cache->block_size * cache->head_dim * elem_bytes;
   if (pa::launch_tile_read(p, grid, static_cast<hipStream_t>(stream)) != hipSuccess) return PA_ERR_LAUNCH;
   return PA_OK;

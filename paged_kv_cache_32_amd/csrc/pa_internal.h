@@ -149,6 +149,7 @@ struct TileProbeParams {
   const int32_t* seq_lens;
   uint32_t* sink;               // XOR of every word read is folded in
   int32_t num_seqs, num_kv_heads, max_blocks, block_size, num_blocks, head_dim, elem_bytes;
+  int32_t window;               // > 0: only the tiles of the last `window` tokens
   int64_t blk_stride;           // bytes per block of one cache
 };
 

@@ -6,8 +6,8 @@
 //
 // tile_read_kernel: the loads of a paged decode and nothing else.  For every
 // (sequence, KV head) it reads the K and V tiles (16 tokens each) that cover
-// the sequence's tokens, through the block table, in the cache layout the
-// decode kernel reads ("Taming the token torrent", "The Block Table Logic");
+// the sequence's tokens (with a window, its last `window` tokens), through
+// the block table, in the cache layout the decode kernel reads ("Taming the token torrent", "The Block Table Logic");
 // the tiles are split evenly over the wavefronts, 16 KB of loads in flight
 // per wavefront.  No arithmetic on the data.
 //
@@ -67,7 +67,9 @@ __global__ __launch_bounds__(kProbeThreads) void stream_read_kernel(const u32x4*
 // sequences with 1 <= len <= max_blocks * block_size; wavefront w reads
 // tiles [w T / W, (w + 1) T / W) of the T in all, B tiles (K and V) at a
 // time.  Each wavefront finds its first sequence by a scan of the lengths.
-// Block ids outside the pool read block 0 and are not folded.
+// Block ids outside the pool read block 0 and are not folded.  Tile t of a
+// sequence is its chunk c0 + t, c0 the chunk holding its first attended
+// token (0 without a window).
 template <int BYTES>
 __global__ __launch_bounds__(kProbeThreads) void tile_read_kernel(const TileProbeParams p) {
   constexpr int NL = BYTES / 1024;              // 16-byte loads per lane and tile
@@ -75,9 +77,10 @@ __global__ __launch_bounds__(kProbeThreads) void tile_read_kernel(const TileProb
   const int lane = threadIdx.x & 63;
   const int subs = p.block_size / kSub;
   const int lmax = p.max_blocks * p.block_size;
+  auto first_chunk = [&](int L) -> int { return (p.window > 0 && L > p.window) ? (L - p.window) / kSub : 0; };
   auto ntiles = [&](int s) -> int {
     const int L = p.seq_lens[s];
-    return (L >= 1 && L <= lmax) ? (L + kSub - 1) / kSub : 0;
+    return (L >= 1 && L <= lmax) ? (L + kSub - 1) / kSub - first_chunk(L) : 0;
   };
   int64_t total = 0;
   for (int s = lane; s < p.num_seqs; s += 64) total += ntiles(s);
@@ -97,16 +100,18 @@ __global__ __launch_bounds__(kProbeThreads) void tile_read_kernel(const TileProb
       base += (int64_t)nt * p.num_kv_heads;
     }
     int h = (int)((i0 - base) / nt), t = (int)((i0 - base) % nt);
+    int c0 = first_chunk(p.seq_lens[s]);
     for (int64_t i = i0; i < i1; i += B) {
       u32x4 r[B][2 * NL];
       bool ok[B];
 #pragma unroll
       for (int k = 0; k < B; ++k) {
         ok[k] = i + k < i1;
-        const int blk = __builtin_amdgcn_readfirstlane(p.block_tables[(int64_t)s * p.max_blocks + t / subs]);
+        const int tc = c0 + t;
+        const int blk = __builtin_amdgcn_readfirstlane(p.block_tables[(int64_t)s * p.max_blocks + tc / subs]);
         const bool in_pool = (unsigned)blk < (unsigned)p.num_blocks;
         ok[k] = ok[k] && in_pool;
-        const int64_t off = (int64_t)(in_pool ? blk : 0) * p.blk_stride + (int64_t)(h * subs + t % subs) * BYTES;
+        const int64_t off = (int64_t)(in_pool ? blk : 0) * p.blk_stride + (int64_t)(h * subs + tc % subs) * BYTES;
         const u32x4* kp = reinterpret_cast<const u32x4*>(p.k_cache + off) + lane;
         const u32x4* vp = reinterpret_cast<const u32x4*>(p.v_cache + off) + lane;
 #pragma unroll
@@ -122,6 +127,7 @@ __global__ __launch_bounds__(kProbeThreads) void tile_read_kernel(const TileProb
             h = 0;
             do nt = ntiles(++s);
             while (nt == 0);
+            c0 = first_chunk(p.seq_lens[s]);
           }
         }
       }

@@ -264,12 +264,13 @@ def test_probe_validation():
     assert lib.pa_probe_stream_read(FAKE, 63, FAKE, None) == SHAPE
     assert lib.pa_probe_stream_read(ctypes.c_void_p(0x1008), 64, FAKE, None) == SHAPE
 
-    def tr(eb=2, S=2, maxb=4, sink=FAKE, bt=FAKE, dd=d):
-        return lib.pa_probe_tile_read(ctypes.byref(dd) if dd else None, eb, FAKE, FAKE, bt, S, maxb, FAKE, sink,
-                                      None)
+    def tr(eb=2, S=2, maxb=4, sink=FAKE, bt=FAKE, dd=d, window=0):
+        return lib.pa_probe_tile_read(ctypes.byref(dd) if dd else None, eb, FAKE, FAKE, bt, S, maxb, FAKE, window,
+                                      sink, None)
     assert tr(dd=None) == NULL
     assert tr(eb=4) == UNSUP
     assert tr(S=-1) == SHAPE
+    assert tr(window=-1) == SHAPE
     assert tr(sink=None) == NULL
     assert tr(S=0) == OK
     assert tr(bt=None) == NULL
@@ -297,7 +298,7 @@ def test_device_errors_without_gpu():
     dp = pa.CascadeDevicePlan(FAKE.value, 1, FAKE.value, FAKE.value, FAKE.value, FAKE.value, 2, FAKE.value,
                               FAKE.value)
     assert pa.lib().pa_probe_stream_read(FAKE, 64, FAKE, None) == DEVICE
-    assert pa.lib().pa_probe_tile_read(ctypes.byref(d), 2, FAKE, FAKE, FAKE, 2, 4, FAKE, FAKE, None) == DEVICE
+    assert pa.lib().pa_probe_tile_read(ctypes.byref(d), 2, FAKE, FAKE, FAKE, 2, 4, FAKE, 0, FAKE, None) == DEVICE
     assert pa.lib().pa_decode_cascade_workspace_size(ctypes.byref(d), 2, 16, 2, 2, 0) == 0
     assert pa.lib().pa_decode_cascade(ctypes.byref(d), FAKE, 2, 16, FAKE, FAKE, 2, ctypes.byref(dp), 0.1, FAKE,
                                       0, FAKE, 1 << 30, None) == DEVICE

@@ -33,9 +33,10 @@ def test_stream_read_reads_every_word_once(nbytes):
     assert sink_value(sink) == xor_words(host.numpy())
 
 
-def expected_tile_xor(w, kc, vc, bt, lens):
+def expected_tile_xor(w, kc, vc, bt, lens, window=0):
     """XOR over the K and V tiles (16 tokens) covering [0, L) of every valid
-    (sequence, head), through the tables; block ids outside the pool skip."""
+    (sequence, head), or [L - window, L) when L > window > 0, through the
+    tables; block ids outside the pool skip."""
     eb = 1 if w.kv_dtype == "fp8" else 2
     words = 16 * w.head_dim * eb // 4
     subs = w.block_size // 16
@@ -47,7 +48,8 @@ def expected_tile_xor(w, kc, vc, bt, lens):
     for s, L in enumerate(lens):
         if not 1 <= L <= maxb * w.block_size:
             continue
-        t = np.arange(-(-int(L) // 16))
+        c0 = (int(L) - window) // 16 if 0 < window < int(L) else 0
+        t = np.arange(c0, -(-int(L) // 16))
         blk = bt[s, t // subs].astype(np.int64)
         keep = (blk >= 0) & (blk < w.num_blocks)
         sel = per_tile[blk[keep], :, (t % subs)[keep]]        # [tiles, heads]
@@ -83,6 +85,27 @@ def test_tile_read_reads_the_decode_tiles(case):
     want = expected_tile_xor(w, kb.numpy(), vb.numpy(), bt, lens)
     print(f"[probe] {kv} D={D} BS={BS} lens={list(lens)}", flush=True)
     assert sink_value(sink) == want
+
+
+@pytest.mark.parametrize("window", [1, 16, 40, 100])
+def test_tile_read_window(window):
+    """With a window only the tiles of the last `window` tokens are read; the
+    table entries before them are set to -1 (as after pa_bm_trim) and must
+    not be read."""
+    w = W.random_workload(9, 8, 8, 2, 128, 16, 400, min_len=1)
+    t = device_inputs(w, poison=False)
+    kc, vc = t["k_cache"][0], t["v_cache"][0]
+    bt, lens = w.block_tables.copy(), w.seq_lens.copy()
+    for s, L in enumerate(lens):
+        if L > window:
+            bt[s, :(int(L) - window) // w.block_size] = -1
+    sink = pa.pa_probe_tile_read(kc, vc, torch.from_numpy(bt).cuda(), torch.from_numpy(lens).cuda(),
+                                 num_kv_heads=w.num_kv_heads, head_dim=w.head_dim, block_size=w.block_size,
+                                 window=window)
+    torch.cuda.synchronize()
+    kb, vb = kc.cpu().view(torch.int16).numpy(), vc.cpu().view(torch.int16).numpy()
+    print(f"[probe] window {window} lens={list(lens)}", flush=True)
+    assert sink_value(sink) == expected_tile_xor(w, kb, vb, bt, lens, window)
 
 
 def test_tile_read_full_size_workload():
