@@ -111,9 +111,12 @@ pa_status cache_write(const pa_cache_desc* cache, const void* k, const void* v,
 }
 
 // Wavefronts to launch and the fixed chunk count per wavefront (0 = auto).
+// With fixed partitions the wavefront count covers an upper bound of the
+// chunks: every sequence's whole table, or with a window of W tokens at most
+// (W + 15) / 16 + 1 chunks per sequence.
 pa_status plan(const pa_cache_desc* c, int32_t num_seqs, int32_t num_q_heads,
                int32_t max_blocks_per_seq, int32_t partition_tokens, bool fp8,
-               int64_t* num_waves, int32_t* chunk_fixed) {
+               int64_t* num_waves, int32_t* chunk_fixed, int32_t window = 0) {
   if (!c) return PA_ERR_NULL;
   pa_status st = desc_status(c);
   if (st != PA_OK) return st;
@@ -134,7 +137,9 @@ pa_status plan(const pa_cache_desc* c, int32_t num_seqs, int32_t num_q_heads,
     *chunk_fixed = 0;
   } else {
     const int64_t per = partition_tokens / pa::kSub;
-    const int64_t chunks_per_seq = ((int64_t)max_blocks_per_seq * c->block_size + pa::kSub - 1) / pa::kSub;
+    int64_t chunks_per_seq = ((int64_t)max_blocks_per_seq * c->block_size + pa::kSub - 1) / pa::kSub;
+    if (window > 0 && ((int64_t)window + pa::kSub - 1) / pa::kSub + 1 < chunks_per_seq)
+      chunks_per_seq = ((int64_t)window + pa::kSub - 1) / pa::kSub + 1;
     const int64_t upper = (int64_t)num_seqs * c->num_kv_heads * chunks_per_seq;
     int64_t w = (upper + per - 1) / per;
     if (w < 1) w = 1;
@@ -174,7 +179,7 @@ pa_status decode(const pa_cache_desc* cache, const void* q, int32_t num_seqs, in
   if (append && (!k_new || !v_new)) return PA_ERR_NULL;
   if (!workspace) return PA_ERR_WORKSPACE;
   pa_status st = plan(cache, num_seqs, num_q_heads, max_blocks_per_seq, partition_tokens, fp8,
-                      &num_waves, &chunk_fixed);
+                      &num_waves, &chunk_fixed, window);
   if (st != PA_OK) return st;
   const int group = num_q_heads / cache->num_kv_heads;
   const pa::WorkspaceLayout lay =
