@@ -144,7 +144,8 @@ pa_status pa_decode_workspace_init(void* workspace, size_t workspace_bytes, void
  *   w = softmax_t(scale * dot(q[s][i][:], K_s[t][h][:])), t in [0, L),
  * where K_s[t] / V_s[t] are read from block block_tables[s][t / block_size]
  * at offset t % block_size.  L == 0 gives zeros.  seq_lens includes the
- * token written this step (write it with pa_cache_write first).
+ * token written this step (write it with pa_cache_write first, or write and
+ * decode in one launch with pa_decode_append).
  *   q             [num_seqs][num_q_heads][head_dim] bf16
  *   block_tables  [num_seqs][max_blocks_per_seq] int32; entries past
  *                 ceil(L / block_size) are never read
