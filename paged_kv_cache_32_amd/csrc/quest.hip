@@ -349,25 +349,31 @@ __device__ __forceinline__ int wave_incl_sum(int v, int lane) {
 }
 
 // Sum of v over the 256 threads (red: 4 ints of LDS; two barriers).
+template <int NW>
 __device__ __forceinline__ int block_sum(int v, int* red) {
   v = wave_sum(v);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
-  const int t = red[0] + red[1] + red[2] + red[3];
+  int t = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) t += red[i];
   __syncthreads();
   return t;
 }
 
-// Sum over the 256 threads of small counts v in [0, 64): each bit of v is
+// Sum over the NW wavefronts' threads of small counts v in [0, 64): each bit of v is
 // counted across the wavefront with a ballot and a scalar popcount, so the
 // wavefront's sum needs no cross-lane data movement.
+template <int NW>
 __device__ __forceinline__ int block_sum_small(int v, int* red) {
   int t = 0;
 #pragma unroll
   for (int b = 0; b < 6; ++b) t += __popcll(__ballot((v >> b) & 1)) << b;
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = t;
   __syncthreads();
-  t = red[0] + red[1] + red[2] + red[3];
+  t = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) t += red[i];
   __syncthreads();
   return t;
 }
@@ -426,29 +432,32 @@ __device__ __forceinline__ int lds_index(int i) { return i + (i >> 5); }
 // pages above T, and the first (budget - count above T) pages equal to T,
 // go to their place in page order through two prefix sums.
 //
-// Units of up to 256 * kSelectRegs pages keep everything in registers: the
+// The workgroup has NT threads: 256, or 1,024 when the tables are wider than
+// 2,048 pages (a long unit's keys then spread over four times the threads).
+// Units of up to NT * REGS pages keep everything in registers: the
 // keys (strided, for counting), and the keys and block ids of the thread's
 // own contiguous range (for the compaction).  All of those loads are issued
 // before the counting rounds, so their latency is paid once.  Longer units
 // read keys from LDS or global memory in each round.
+template <int NT, int REGS>
 __device__ __forceinline__ void select_small(const SelectParams& p, int unit, int s, int np,
                                              const uint32_t* gk, uint32_t* lk, int* red, uint32_t* hist) {
   const int tid = threadIdx.x;
   const int B = p.budget;
   int32_t* out = p.sel_tables + (int64_t)unit * B;
   const int32_t* row = p.block_tables + (int64_t)s * p.max_blocks;
-  const int m = (np + 255) / 256;                       // <= kSelectRegs
+  const int m = (np + NT - 1) / NT;                     // <= REGS
   const int i0 = tid * m < np ? tid * m : np;
   const int cnt = np - i0 < m ? np - i0 : m;
-  uint32_t kr[kSelectRegs];
-  int32_t ids[kSelectRegs];
+  uint32_t kr[REGS];
+  int32_t ids[REGS];
 #pragma unroll
-  for (int k = 0; k < kSelectRegs; ++k) kr[k] = tid + 256 * k < np ? gk[tid + 256 * k] : 0u;
+  for (int k = 0; k < REGS; ++k) kr[k] = tid + NT * k < np ? gk[tid + NT * k] : 0u;
 #pragma unroll
-  for (int k = 0; k < kSelectRegs; ++k) ids[k] = k < cnt ? row[i0 + k] : -1;
+  for (int k = 0; k < REGS; ++k) ids[k] = k < cnt ? row[i0 + k] : -1;
 #pragma unroll
-  for (int k = 0; k < kSelectRegs; ++k)
-    if (tid + 256 * k < np) lk[lds_index(tid + 256 * k)] = kr[k];
+  for (int k = 0; k < REGS; ++k)
+    if (tid + NT * k < np) lk[lds_index(tid + NT * k)] = kr[k];
   // T = the budget-th largest key.  Units of at most 16 key slots per
   // thread find it 8 bits per round from the top: the keys that agree with T
   // above the round's digit are counted per digit value (LDS histogram); T
@@ -457,17 +466,17 @@ __device__ __forceinline__ void select_small(const SelectParams& p, int unit, in
   // crowd the histogram's first-round bins (sign and top exponent bits),
   // find it bit by bit: T keeps a bit when at least `budget` keys are >= T
   // with it, counted with one ballot per key slot and scalar popcounts.
-  const int slots = (np + 255) / 256;       // key slots that hold any page
+  const int slots = (np + NT - 1) / NT;     // key slots that hold any page
   uint32_t T = 0u;
   if (slots <= 16) {
     int want = B;
     for (int r = 0; r < 4; ++r) {
       const int shift = 24 - 8 * r;
-      hist[tid] = 0u;
+      if (tid < 256) hist[tid] = 0u;
       __syncthreads();                          // also publishes the LDS keys (first round)
 #pragma unroll
-      for (int k = 0; k < kSelectRegs; ++k) {
-        if (k < slots && tid + 256 * k < np) {
+      for (int k = 0; k < REGS; ++k) {
+        if (k < slots && tid + NT * k < np) {
           const bool match = r == 0 || ((kr[k] ^ T) >> (shift + 8)) == 0u;
           if (match) atomicAdd(&hist[(kr[k] >> shift) & 255u], 1u);
         }
@@ -514,29 +523,31 @@ __device__ __forceinline__ void select_small(const SelectParams& p, int unit, in
       const uint32_t cand = T | (1u << bit);   // >= 1: the padding keys 0 never count
       int c = 0;
 #pragma unroll
-      for (int k = 0; k < kSelectRegs; ++k) c += __popcll(__ballot(kr[k] >= cand));
+      for (int k = 0; k < REGS; ++k) c += __popcll(__ballot(kr[k] >= cand));
       if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = c;
       __syncthreads();                        // also publishes the LDS keys
-      const int total = red[0] + red[1] + red[2] + red[3];
+      int total = 0;
+#pragma unroll
+      for (int i = 0; i < NT / 64; ++i) total += red[i];
       __syncthreads();
       if (total >= B) T = cand;
     }
   }
-  uint32_t mine[kSelectRegs];
+  uint32_t mine[REGS];
   int above = 0, equal = 0;
 #pragma unroll
-  for (int k = 0; k < kSelectRegs; ++k) {
+  for (int k = 0; k < REGS; ++k) {
     mine[k] = k < cnt ? lk[lds_index(i0 + k)] : 0u;
     above += (k < cnt && mine[k] > T) ? 1 : 0;
     equal += (k < cnt && mine[k] == T) ? 1 : 0;
   }
-  const int need = B - block_sum_small(above, red);
+  const int need = B - block_sum_small<NT / 64>(above, red);
   const int eq_rank0 = block_excl_sum_small(equal, red);
   int taken = 0;
   {
     int er = eq_rank0;
 #pragma unroll
-    for (int k = 0; k < kSelectRegs; ++k) {
+    for (int k = 0; k < REGS; ++k) {
       const bool eq = k < cnt && mine[k] == T;
       taken += (k < cnt && (mine[k] > T || (eq && er < need))) ? 1 : 0;
       er += eq ? 1 : 0;
@@ -546,7 +557,7 @@ __device__ __forceinline__ void select_small(const SelectParams& p, int unit, in
   int er = eq_rank0;
   const int last_valid = p.seq_lens[s] - (np - 1) * p.block_size;
 #pragma unroll
-  for (int k = 0; k < kSelectRegs; ++k) {
+  for (int k = 0; k < REGS; ++k) {
     if (k < cnt) {
       const bool eq = mine[k] == T;
       const bool take = mine[k] > T || (eq && er < need);
@@ -560,7 +571,7 @@ __device__ __forceinline__ void select_small(const SelectParams& p, int unit, in
   }
 }
 
-template <bool LDS>
+template <int NT, bool LDS>
 __device__ __forceinline__ void select_unit(const SelectParams& p, int unit, int s, int np, const uint32_t* gk,
                                             uint32_t* lk, int* red) {
   const int tid = threadIdx.x;
@@ -575,11 +586,11 @@ __device__ __forceinline__ void select_unit(const SelectParams& p, int unit, int
   for (int bit = 31; bit >= 0; --bit) {
     const uint32_t cand = T | (1u << bit);
     int c = 0;
-    for (int i = tid; i < np; i += 256) c += key(i) >= cand ? 1 : 0;
-    if (block_sum(c, red) >= B) T = cand;
+    for (int i = tid; i < np; i += NT) c += key(i) >= cand ? 1 : 0;
+    if (block_sum<NT / 64>(c, red) >= B) T = cand;
   }
   // Contiguous ranges: thread t owns pages [t * m, min(np, (t + 1) * m)).
-  const int m = (np + 255) / 256;
+  const int m = (np + NT - 1) / NT;
   const int i0 = tid * m < np ? tid * m : np, i1 = (tid + 1) * m < np ? (tid + 1) * m : np;
   int above = 0, equal = 0;
   for (int i = i0; i < i1; ++i) {
@@ -587,7 +598,7 @@ __device__ __forceinline__ void select_unit(const SelectParams& p, int unit, int
     above += k > T ? 1 : 0;
     equal += k == T ? 1 : 0;
   }
-  const int need = B - block_sum(above, red);
+  const int need = B - block_sum<NT / 64>(above, red);
   const int eq_rank0 = block_excl_sum(equal, red);
   int taken = 0;
   {
@@ -617,9 +628,11 @@ __device__ __forceinline__ void select_unit(const SelectParams& p, int unit, int
 
 // Units whose pages all fit the budget copy their table row; invalid
 // lengths give sel_lens = -1.
-__global__ __launch_bounds__(256) void page_select_kernel(const SelectParams p) {
+template <int NT>
+__global__ __launch_bounds__(NT) void page_select_kernel(const SelectParams p) {
+  constexpr int REGS = NT == 1024 ? 12 : kSelectRegs;   // NT * REGS <= kSelectLds keys held in LDS
   __shared__ uint32_t lk[kSelectLds + kSelectLds / 32];
-  __shared__ int red[4];
+  __shared__ int red[NT / 64];
   __shared__ uint32_t hist[256];
   const int unit = blockIdx.x;
   const int s = unit / p.num_kv_heads;
@@ -629,27 +642,27 @@ __global__ __launch_bounds__(256) void page_select_kernel(const SelectParams p) 
   if (np < 0 || np <= B) {
     int32_t* out = p.sel_tables + (int64_t)unit * B;
     const int32_t* row = p.block_tables + (int64_t)s * p.max_blocks;
-    for (int i = tid; i < B; i += 256) out[i] = (np >= 0 && i < np) ? row[i] : -1;
+    for (int i = tid; i < B; i += NT) out[i] = (np >= 0 && i < np) ? row[i] : -1;
     if (tid == 0) p.sel_lens[unit] = np < 0 ? -1 : p.seq_lens[s];
     return;
   }
   const uint32_t* gk = p.keys + (int64_t)unit * p.max_blocks;
-  if (np <= 256 * kSelectRegs) {
-    select_small(p, unit, s, np, gk, lk, red, hist);
+  if (np <= NT * REGS) {
+    select_small<NT, REGS>(p, unit, s, np, gk, lk, red, hist);
   } else if (np <= kSelectLds) {
     // Eight independent loads in flight per thread before their stores.
-    for (int i0 = tid; i0 < np; i0 += 8 * 256) {
+    for (int i0 = tid; i0 < np; i0 += 8 * NT) {
       uint32_t v[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = i0 + 256 * k < np ? gk[i0 + 256 * k] : 0u;
+      for (int k = 0; k < 8; ++k) v[k] = i0 + NT * k < np ? gk[i0 + NT * k] : 0u;
 #pragma unroll
       for (int k = 0; k < 8; ++k)
-        if (i0 + 256 * k < np) lk[lds_index(i0 + 256 * k)] = v[k];
+        if (i0 + NT * k < np) lk[lds_index(i0 + NT * k)] = v[k];
     }
     __syncthreads();
-    select_unit<true>(p, unit, s, np, gk, lk, red);
+    select_unit<NT, true>(p, unit, s, np, gk, lk, red);
   } else {
-    select_unit<false>(p, unit, s, np, gk, lk, red);
+    select_unit<NT, false>(p, unit, s, np, gk, lk, red);
   }
 }
 
@@ -698,7 +711,11 @@ hipError_t launch_page_select(const SelectParams& p, hipStream_t stream) {
     hipLaunchKernelGGL(page_score_kernel<128>, grid, dim3(128), 0, stream, p);
   else
     hipLaunchKernelGGL(page_score_kernel<64>, grid, dim3(128), 0, stream, p);
-  hipLaunchKernelGGL(page_select_kernel, dim3((unsigned)units), dim3(256), 0, stream, p);
+  // Wide tables: a 1,024-thread workgroup per unit (fewer keys per thread).
+  if (p.max_blocks > 2048)
+    hipLaunchKernelGGL(page_select_kernel<1024>, dim3((unsigned)units), dim3(1024), 0, stream, p);
+  else
+    hipLaunchKernelGGL(page_select_kernel<256>, dim3((unsigned)units), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

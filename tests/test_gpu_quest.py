@@ -252,6 +252,31 @@ def test_equal_scores_go_to_the_lower_page():
         run_select_and_decode(w2, t, budget, label=f"ties budget={budget}")
 
 
+@pytest.mark.parametrize("budget", [3, 100, 5000])
+def test_wide_tables(budget):
+    """Tables wider than 2,048 pages take the 1,024-thread choice kernel.
+    Sequences 0 and 1 are short (keys held in registers; their rows padded
+    with -1); sequence 2 has 13,000 pages (more keys than LDS holds) whose
+    table cycles over its own 25-40 blocks, so that equal scores decide at
+    the threshold."""
+    w0 = W.random_workload(12, 3, 16, 2, 64, 16, 640, min_len=400)
+    maxb = 13000
+    bt = np.full((3, maxb), -1, dtype=np.int32)
+    for s in range(2):
+        n = -(-int(w0.seq_lens[s]) // 16)
+        bt[s, :n] = w0.block_tables[s, :n]
+    n2 = -(-int(w0.seq_lens[2]) // 16)
+    bt[2, :] = np.resize(w0.block_tables[2, :n2], maxb)
+    lens = w0.seq_lens.copy()
+    lens[2] = maxb * 16 - 5
+    slots = np.array([int(bt[s, (int(L) - 1) // 16]) * 16 + (int(L) - 1) % 16 for s, L in enumerate(lens)],
+                     dtype=np.int64)
+    w = W.Workload("wide_tables", 16, 2, 64, 16, w0.num_blocks, lens, bt, slots, w0.scale, seed=12)
+    t = device_inputs(w, poison=False)
+    print(f"[quest] wide tables budget={budget} lens={list(lens)}", flush=True)
+    run_select_and_decode(w, t, budget, label=f"wide budget={budget}")
+
+
 def test_invalid_and_empty_rows():
     """Length 0 gives zeros, a length past the table gives NaN rows (as
     pa_decode), and neither disturbs the other sequences."""
