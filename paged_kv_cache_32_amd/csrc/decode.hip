@@ -68,6 +68,10 @@
 #ifndef PA_DECODE_NT
 #define PA_DECODE_NT 1
 #endif
+// Pieces whose partial records the merging wavefront loads per round trip.
+#ifndef PA_DECODE_MERGE_BATCH
+#define PA_DECODE_MERGE_BATCH 8
+#endif
 
 namespace pa {
 
@@ -624,9 +628,11 @@ __device__ __forceinline__ int piece_slot(int w, int w0, int u0, int C) {
 // Merge the partial softmax states of unit (s, h), pieces from wavefronts
 // w0..w1, into out (run by the wavefront that counted in the last piece):
 // out = sum_p e^(m_p - M) acc_p / sum_p e^(m_p - M) l_p, M = max_p m_p, taken
-// one piece at a time with a running maximum.  Lane l handles the 4-float
-// groups e = l + 64 i of the G x D output, kIt of them per pass; the loads of
-// kBatch pieces are issued together.
+// one piece at a time with a running maximum.  Lane l handles kIt adjacent
+// 4-float groups of one query head's output row per pass, so one load of a
+// piece's (m, l) serves all of them; the loads of kBatch pieces are issued
+// together (one memory round trip per kBatch pieces: this merge is the tail
+// of the launch when a unit is split over many wavefronts).
 template <int D, int kIt, int kBatch>
 __device__ __forceinline__ void merge_unit(const DecodeParams& p, const Pending& pd, int C, int lane) {
   const int G = p.group;
@@ -635,52 +641,41 @@ __device__ __forceinline__ void merge_unit(const DecodeParams& p, const Pending&
   const int w0 = pd.u0 / C, w1 = (pd.u0 + pd.n - 1) / C;
   f32x4* o = reinterpret_cast<f32x4*>(p.out + ((int64_t)pd.s * p.num_q_heads + (int64_t)pd.h * G) * D);
   for (int e0 = 0; e0 < groups; e0 += 64 * kIt) {
-    float M[kIt], den[kIt];
+    const int e_first = e0 + lane * kIt;
+    const int g = e_first / (D / 4), d40 = e_first - g * (D / 4);
+    const bool in = e_first < groups;
+    float M = kNegInf, den = 0.f;
     f32x4 num[kIt];
 #pragma unroll
-    for (int it = 0; it < kIt; ++it) {
-      M[it] = kNegInf;
-      den[it] = 0.f;
-      num[it] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int it = 0; it < kIt; ++it) num[it] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int wb = w0; wb <= w1; wb += kBatch) {
-      f32x4 ml[kBatch][kIt], acc[kBatch][kIt];
+      f32x4 ml[kBatch], acc[kBatch][kIt];
 #pragma unroll
       for (int b = 0; b < kBatch; ++b) {
         const int w = (wb + b <= w1) ? wb + b : w1;
         const auto r = record_rsrc(p.partials + (int64_t)piece_slot(w, w0, pd.u0, C) * (rec_bytes / 4), rec_bytes);
+        ml[b] = load_record(r, in ? (G * D + g * 4) * 4 : 0);
 #pragma unroll
-        for (int it = 0; it < kIt; ++it) {
-          const int e = e0 + lane + 64 * it;
-          const int g = e / (D / 4), d4 = e - g * (D / 4);
-          const bool in = e < groups;
-          ml[b][it] = load_record(r, in ? (G * D + g * 4) * 4 : 0);
-          acc[b][it] = load_record(r, in ? (d4 * G + g) * 16 : 0);
-        }
+        for (int it = 0; it < kIt; ++it) acc[b][it] = load_record(r, in ? ((d40 + it) * G + g) * 16 : 0);
       }
 #pragma unroll
       for (int b = 0; b < kBatch; ++b) {
         if (wb + b <= w1) {
+          const float m_new = __builtin_fmaxf(M, ml[b][0]);
+          const float a = (M == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(M - m_new);
+          const float f = (ml[b][0] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(ml[b][0] - m_new);
 #pragma unroll
-          for (int it = 0; it < kIt; ++it) {
-            const float m_new = __builtin_fmaxf(M[it], ml[b][it][0]);
-            const float a = (M[it] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(M[it] - m_new);
-            const float f = (ml[b][it][0] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(ml[b][it][0] - m_new);
-            num[it] = num[it] * a + acc[b][it] * f;
-            den[it] = den[it] * a + ml[b][it][1] * f;
-            M[it] = m_new;
-          }
+          for (int it = 0; it < kIt; ++it) num[it] = num[it] * a + acc[b][it] * f;
+          den = den * a + ml[b][1] * f;
+          M = m_new;
         }
       }
     }
 #pragma unroll
-    for (int it = 0; it < kIt; ++it) {
-      const int e = e0 + lane + 64 * it;
-      if (e < groups) o[e] = num[it] * (p.out_scale / den[it]);
-      const int g = e / (D / 4);
-      if (p.lse && e < groups && e - g * (D / 4) == 0)
-        p.lse[(int64_t)pd.s * p.num_q_heads + (int64_t)pd.h * G + g] = M[it] + __builtin_amdgcn_logf(den[it]);
-    }
+    for (int it = 0; it < kIt; ++it)
+      if (in) o[e_first + it] = num[it] * (p.out_scale / den);
+    if (p.lse && in && d40 == 0)
+      p.lse[(int64_t)pd.s * p.num_q_heads + (int64_t)pd.h * G + g] = M + __builtin_amdgcn_logf(den);
   }
 }
 
@@ -703,7 +698,7 @@ __device__ __forceinline__ void resolve_piece(Pending& pd, int C) {
 
 template <int D>
 __device__ __forceinline__ void merge_and_rearm(const DecodeParams& p, Pending& pd, int C, int lane) {
-  merge_unit<D, D / 32, 4>(p, pd, C, lane);
+  merge_unit<D, D / 32, PA_DECODE_MERGE_BATCH>(p, pd, C, lane);
   if (lane == 0)
     __hip_atomic_store(p.counters + (int64_t)pd.s * p.num_kv_heads + pd.h, 0, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
