@@ -143,3 +143,16 @@ def test_workspace_reuse_and_too_small():
     with pytest.raises(pa.PagedAttentionError) as e:
         H.gpu_decode(w, t, partition_tokens=16, workspace=ws[: need - 1])
     assert e.value.status == -4
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_merge_two_passes_and_batch_edges(kv):
+    """Head dim 64 with 16 query heads per KV head: the merging wavefront
+    covers the 16 x 64 output in two passes.  With 16-token partitions each
+    unit is split into one piece per 16-token chunk, so these lengths give
+    1, 7, 8, 9 and 17 pieces (one memory round trip takes 8), plus ragged
+    tails."""
+    lens = [16, 112, 128, 144, 272, 100, 135, 257]
+    w = W.random_workload(78, len(lens), 32, 2, 64, 16, 0, kv_dtype=kv, lens=lens)
+    t = H.device_inputs(w)
+    H.step_and_check(w, t, partition_tokens=16, label=f"merge passes {kv}")
