@@ -104,8 +104,12 @@ typedef struct {
 } pa_cascade_device_plan;
 
 /* DEVICE workspace bytes of pa_decode_cascade(_fp8): the private decode's
- * workspace (zero-filled once, as pa_decode's), its outputs, and the partial
- * records.  0 for invalid sizes.                                             */
+ * workspace first (its merge counters in the first max(U, 16384) * 4 bytes,
+ * U = num_seqs * num_kv_heads), then the private outputs and the partial
+ * records, which each call writes before reading.  Zero-fill it once (as
+ * pa_decode's); it then serves any number of calls with any plan and sizes
+ * that fit while U <= 16384, exactly as pa_decode's workspace does.  0 for
+ * invalid sizes.                                                             */
 size_t pa_decode_cascade_workspace_size(const pa_cache_desc* cache, int32_t num_seqs, int32_t num_q_heads,
                                         int32_t max_blocks_per_seq, int32_t num_slots,
                                         int32_t partition_tokens);

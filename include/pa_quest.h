@@ -95,8 +95,9 @@ pa_status pa_quest_select(const pa_cache_desc* cache, const void* q, int32_t num
                           const int32_t* seq_lens, int32_t budget, int32_t* sel_tables,
                           int32_t* sel_lens, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Decode workspace for pa_decode_quest(_fp8) (zero-filled once, as for
- * pa_decode); 0 for invalid sizes.                                           */
+/* Decode workspace for pa_decode_quest(_fp8): zero-filled once, and reused
+ * under pa_decode's rule, with one merge counter per (sequence, KV head), so
+ * U = num_seqs * num_kv_heads.  0 for invalid sizes.                        */
 size_t pa_decode_quest_workspace_size(const pa_cache_desc* cache, int32_t num_seqs,
                                       int32_t num_q_heads, int32_t budget,
                                       int32_t partition_tokens);

@@ -182,18 +182,30 @@ hipError_t launch_tile_read(const TileProbeParams& p, int grid, hipStream_t stre
 // Resident wavefronts of the decode kernel on the current device (0 on error).
 int decode_resident_waves(int head_dim, bool fp8);
 
-// Workspace carve-up shared by the size query and the launcher.
+// Workspace carve-up shared by the size query and the launchers.  The
+// per-unit counters come first, in a region of at least kMinCounterUnits
+// entries: for every call with num_seqs * num_kv_heads <= kMinCounterUnits
+// the counters then occupy the same first 64 KiB, which nothing else in the
+// workspace is ever used for, whatever the other sizes (wave count, group,
+// head_dim, partition) of the calls sharing it.  Each call leaves its
+// counters at zero, so such calls can share one workspace that was zero-
+// filled once.  The partial records follow; they are always written before
+// they are read, so their contents between calls do not matter.
+constexpr int64_t kMinCounterUnits = 16384;
 struct WorkspaceLayout {
-  size_t partials_off, counters_off, total;
+  size_t counters_off, partials_off, total;
 };
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline size_t counter_region_bytes(int64_t units) {
+  return align_up((size_t)(units > kMinCounterUnits ? units : kMinCounterUnits) * sizeof(int32_t), 256);
+}
 inline WorkspaceLayout workspace_layout(int64_t num_waves, int group, int head_dim,
                                         int num_seqs, int num_kv_heads) {
   WorkspaceLayout w;
-  w.partials_off = 0;
-  size_t part = (size_t)(2 * num_waves) * (size_t)group * (size_t)(head_dim + 4) * sizeof(float);
-  w.counters_off = align_up(part, 256);
-  w.total = align_up(w.counters_off + (size_t)num_seqs * (size_t)num_kv_heads * sizeof(int32_t), 256);
+  w.counters_off = 0;
+  w.partials_off = counter_region_bytes((int64_t)num_seqs * num_kv_heads);
+  const size_t part = (size_t)(2 * num_waves) * (size_t)group * (size_t)(head_dim + 4) * sizeof(float);
+  w.total = align_up(w.partials_off + part, 256);
   return w;
 }
 
