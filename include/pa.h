@@ -28,7 +28,8 @@
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers, allocated, owned and freed by
  *     the caller.  The library never allocates or frees device memory and
- *     keeps no per-call state; sizes are element counts unless named _bytes.
+ *     keeps no per-call state (the one exception is pa_decode_noalloc's
+ *     static scratch array); sizes are element counts unless named _bytes.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Work is enqueued on it and the call returns without synchronising.
  *   - Arguments are validated on the host before anything is launched; on
@@ -192,6 +193,26 @@ pa_status pa_decode_fp8(const pa_cache_desc* cache, const void* q, int32_t num_s
                         const int32_t* seq_lens, float scale, float k_scale, float v_scale,
                         float* out, int32_t partition_tokens, void* workspace,
                         size_t workspace_bytes, void* stream);
+
+/* pa_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same decode, with no workspace argument.  Its workspace is a scratch array
+ * of 32 MiB inside the library's device code: each GPU the library's code is
+ * loaded on holds its own copy until the process ends, and the call itself
+ * calls no allocator.  Each call first clears the array's merge counters with a
+ * fill kernel on `stream` (two launches per call).  Calls whose workspace
+ * (pa_decode_workspace_size, bf16) exceeds 32 MiB return PA_ERR_WORKSPACE
+ * and launch nothing: with the automatic split every shape pa_decode takes
+ * fits, and fixed partitions fit up to about 30 MiB of partial records.
+ * Every call on one GPU shares that GPU's array: calls that may overlap on
+ * one GPU (different streams, or different host threads) race and give
+ * undefined results.  Arguments and results are pa_decode's, bit for bit
+ * with the same partition_tokens.                                          */
+pa_status pa_decode_noalloc(const pa_cache_desc* cache, const void* q, int32_t num_seqs,
+                            int32_t num_q_heads, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* seq_lens, float scale, float* out,
+                            int32_t partition_tokens, void* stream);
 
 /* Sliding-window decode: as pa_decode / pa_decode_fp8, except that each
  * sequence attends only to its last `window` tokens, positions

@@ -84,6 +84,7 @@ def _load():
         "pa_decode": ([dp, vp, i32, i32, vp, vp, vp, i32, vp, f32, vp, i32, vp, sz, vp], i32),
         "pa_decode_fp8": ([dp, vp, i32, i32, vp, vp, vp, i32, vp, f32, f32, f32, vp, i32, vp, sz,
                            vp], i32),
+        "pa_decode_noalloc": ([dp, vp, i32, i32, vp, vp, vp, i32, vp, f32, vp, i32, vp], i32),
         "pa_status_string": ([i32], ctypes.c_char_p),
         "pa_abi_version": ([], i32),
         "pa_copy_blocks": ([dp, i32, vp, vp, vp, i32, vp], i32),
@@ -306,6 +307,31 @@ def pa_decode_fp8(q, k_cache, v_cache, block_tables, seq_lens, scale, k_scale, v
     """Paged decode over an e4m3fn cache with per-tensor scales."""
     return _decode(True, q, k_cache, v_cache, block_tables, seq_lens, scale, out, num_kv_heads,
                    block_size, k_scale, v_scale, partition_tokens, workspace)
+
+
+def pa_decode_noalloc(q, k_cache, v_cache, block_tables, seq_lens, scale, out=None, *, num_kv_heads,
+                      block_size, partition_tokens=0):
+    """pa_decode with no workspace: the library's own per-GPU scratch array
+    serves as one (include/pa.h).  Calls on one GPU must not overlap."""
+    dev = q.device
+    _need(q, "q", torch.bfloat16, dev, 3)
+    S, Hq, D = q.shape
+    _need(k_cache, "k_cache", torch.bfloat16, dev)
+    _need(v_cache, "v_cache", torch.bfloat16, dev, shape=tuple(k_cache.shape))
+    _need(block_tables, "block_tables", torch.int32, dev, 2)
+    _need(seq_lens, "seq_lens", torch.int32, dev, shape=(S,))
+    if block_tables.shape[0] != S:
+        raise ValueError("block_tables must have one row per sequence")
+    if out is None:
+        out = torch.empty((S, Hq, D), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, dev, shape=(S, Hq, D))
+    desc = make_desc(k_cache, num_kv_heads, D, block_size)
+    with torch.cuda.device(dev):
+        st = _load().pa_decode_noalloc(ctypes.byref(desc), _ptr(q), S, Hq, _ptr(k_cache), _ptr(v_cache),
+                                       _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), float(scale),
+                                       _ptr(out), int(partition_tokens), _stream(q))
+    _check("pa_decode_noalloc", st)
+    return out
 
 
 def pa_copy_blocks(k_cache, v_cache, pairs, *, num_kv_heads, head_dim, block_size):

@@ -269,6 +269,36 @@ pa::BlockMoveParams block_move_params(int64_t block_bytes, int32_t n) {
 
 }  // namespace
 
+// Device scratch of pa_decode_noalloc: the decode workspace of callers that
+// cannot allocate (merge counters first, then the partial records).  Each
+// device the library runs on holds its own copy, until the process ends.
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+
+void* g_scratch[kMaxDevices];  // per device: the device address of `scratch`
+
+// The device address of this device's copy of `scratch`, looked up once per
+// device with that device current (the array's name is a host-side stand-in,
+// not a device address).  Null on failure.
+void* noalloc_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch[dev] = ptr;
+  }
+  return g_scratch[dev];
+}
+
+}  // namespace
+
 extern "C" {
 
 pa_status pa_cache_write(const pa_cache_desc* cache, const void* k, const void* v,
@@ -319,6 +349,43 @@ pa_status pa_decode(const pa_cache_desc* cache, const void* q, int32_t num_seqs,
   return decode(cache, q, num_seqs, num_q_heads, k_cache, v_cache, block_tables,
                 max_blocks_per_seq, seq_lens, 0, scale, 1.f, 1.f, false, out, partition_tokens,
                 workspace, workspace_bytes, stream);
+}
+
+pa_status pa_decode_noalloc(const pa_cache_desc* cache, const void* q, int32_t num_seqs,
+                            int32_t num_q_heads, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* seq_lens, float scale, float* out,
+                            int32_t partition_tokens, void* stream) {
+  // Every check pa_decode makes comes before anything is launched.
+  if (!cache) return PA_ERR_NULL;
+  if (!isfinite(scale)) return PA_ERR_SHAPE;
+  int64_t num_waves = 0;
+  int32_t chunk_fixed = 0;
+  {
+    pa_status st = desc_status(cache);
+    if (st != PA_OK) return st;
+    if (num_seqs < 0 || num_q_heads < 1 || max_blocks_per_seq < 0) return PA_ERR_SHAPE;
+    if (num_q_heads % cache->num_kv_heads != 0) return PA_ERR_SHAPE;
+    if (num_q_heads / cache->num_kv_heads > kMaxGroup) return PA_ERR_UNSUPPORTED;
+    if (partition_tokens < 0 || partition_tokens % pa::kSub != 0) return PA_ERR_SHAPE;
+  }
+  if (num_seqs == 0) return PA_OK;
+  if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !out) return PA_ERR_NULL;
+  pa_status st = plan(cache, num_seqs, num_q_heads, max_blocks_per_seq, partition_tokens, false,
+                      &num_waves, &chunk_fixed);
+  if (st != PA_OK) return st;
+  const pa::WorkspaceLayout lay = pa::workspace_layout(num_waves, num_q_heads / cache->num_kv_heads,
+                                                       cache->head_dim, num_seqs, cache->num_kv_heads);
+  if (lay.total > kNoAllocScratchBytes) return PA_ERR_WORKSPACE;
+  void* ws = noalloc_scratch();
+  if (!ws) return PA_ERR_DEVICE;
+  // The array keeps the previous call's contents: clear the merge counters
+  // (a fill kernel on the caller's stream, ahead of the decode).
+  if (pa::launch_zero(ws, lay.partials_off, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return PA_ERR_LAUNCH;
+  return decode(cache, q, num_seqs, num_q_heads, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                seq_lens, 0, scale, 1.f, 1.f, false, out, partition_tokens, ws, kNoAllocScratchBytes,
+                stream);
 }
 
 pa_status pa_decode_window(const pa_cache_desc* cache, const void* q, int32_t num_seqs,
