@@ -11,7 +11,7 @@ import torch
 import paged_kv_cache_32_amd as pa
 from oracle import blocks as B
 from oracle import paged
-from tests.gpu_helpers import BF16_TOL, host_bits
+from tests.gpu_helpers import BF16_ENVELOPE, BF16_TOL, host_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -111,5 +111,5 @@ def test_decode_steps_driven_by_the_block_manager():
         assert np.array_equal(host_bits(kc), k_ref) and np.array_equal(host_bits(vc), v_ref), step
         ref = paged.decode(g, host_bits(q), k_ref, v_ref, bt_o, sl_o, scale)
         err = np.abs(out.cpu().double().numpy() - ref)
-        assert err.max() <= BF16_TOL[0] and err.mean() <= BF16_TOL[1], (step, err.max())
+        assert err.max() <= min(BF16_TOL[0], BF16_ENVELOPE) and err.mean() <= BF16_TOL[1], (step, err.max())
     assert copies == 3          # one copy per sequence that wrote first into a shared partial block

@@ -3,8 +3,9 @@ configuration bench.py times: partition_tokens = 0 (the kernel sizes its
 split from the device's resident-wave count), one decode launch per layer,
 and one zero-filled workspace reused across calls.  Caches are compared bit
 for bit with the oracle's write; outputs element by element with the fp64
-oracle on every sequence of the batch (every sequence of three layers for the
-80-layer step)."""
+oracle on every sequence of the batch (for the 80-layer step: every sequence
+of three layers, and a seeded sample of sequences plus the new-token rows on
+every layer)."""
 
 import gc
 
@@ -13,6 +14,7 @@ import pytest
 import torch
 
 import paged_kv_cache_32_amd as pa
+from oracle import e4m3, paged
 from paged_kv_cache_32_amd import workloads as W
 from paged_kv_cache_32_amd.step import DecodeStep
 
@@ -87,9 +89,30 @@ def test_long_context_128k_partitions(parts):
         print(f"[configs] {w.name}: part={part} max-abs {mx:.2e} mean-abs {mean:.2e}", flush=True)
 
 
+def _layer_sample(w, t, i, kc_dev, vc_dev, seqs):
+    """The cache bytes of the blocks the given sequences read, gathered on
+    the device and renumbered from 0, with the sequences' tables and
+    lengths: a compact pool the oracle decodes in place of the whole
+    layer."""
+    blocks = sorted({int(b) for s in seqs for b in w.block_tables[s, :-(-int(w.seq_lens[s]) // w.block_size)]})
+    remap = {b: j for j, b in enumerate(blocks)}
+    idx = torch.tensor(blocks, dtype=torch.int64, device=kc_dev.device)
+    kc = host_bits(kc_dev.view(w.num_blocks, -1).index_select(0, idx)).reshape(-1)
+    vc = host_bits(vc_dev.view(w.num_blocks, -1).index_select(0, idx)).reshape(-1)
+    bt = np.full((len(seqs), w.max_blocks_per_seq), -1, dtype=np.int32)
+    for r, s in enumerate(seqs):
+        n = -(-int(w.seq_lens[s]) // w.block_size)
+        bt[r, :n] = [remap[int(b)] for b in w.block_tables[s, :n]]
+    return len(blocks), kc, vc, bt, w.seq_lens[list(seqs)]
+
+
 def test_fp8_80_layers_step_as_graph():
     """The 80-layer fp8 step (per layer: fp8 write, fp8 decode) captured as
-    one HIP graph and replayed twice; layers 0, 39 and 79 checked in full."""
+    one HIP graph and replayed twice.  Layers 0, 39 and 79 are checked in
+    full (caches bit for bit, every sequence's output).  Every layer's
+    new-token rows are checked bit for bit against the oracle's e4m3
+    encoding with that layer's scales, and on every layer a seeded sample of
+    6 sequences (a different one per layer) is decoded by the oracle."""
     w = W.config(5)
     print(f"[configs] {w.name}: drawing {w.num_layers} layers", flush=True)
     t = device_inputs(w)
@@ -117,3 +140,29 @@ def test_fp8_80_layers_step_as_graph():
         ref = oracle_decode(w, host_bits(t["q"][i]), kc_ref, vc_ref, ks, vs)
         mx, mean = compare(out[i], ref, w.kv_dtype, label=f"{w.name} layer {i}")
         print(f"[configs] {w.name}: layer {i} max-abs {mx:.2e} mean-abs {mean:.2e}", flush=True)
+    del before
+    g = paged.Geom(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.kv_dtype)
+    hh, dd = np.meshgrid(np.arange(w.num_kv_heads), np.arange(w.head_dim), indexing="ij")
+    blk, off = np.divmod(w.slot_mapping.astype(np.int64), w.block_size)
+    k_idx = np.stack([paged.k_offset(g, b, hh, o, dd) for b, o in zip(blk, off)])
+    v_idx = np.stack([paged.v_offset(g, b, hh, o, dd) for b, o in zip(blk, off)])
+    k_idx_d = torch.from_numpy(k_idx.reshape(-1)).cuda()
+    v_idx_d = torch.from_numpy(v_idx.reshape(-1)).cuda()
+    worst = 0.0
+    for i in range(w.num_layers):
+        ks, vs = float(t["k_scale"][i]), float(t["v_scale"][i])
+        kn = paged.bf16_bits_to_f64(host_bits(t["k_new"][i])).astype(np.float32)
+        vn = paged.bf16_bits_to_f64(host_bits(t["v_new"][i])).astype(np.float32)
+        got_k = host_bits(t["k_cache"][i][k_idx_d]).reshape(k_idx.shape)
+        got_v = host_bits(t["v_cache"][i][v_idx_d]).reshape(v_idx.shape)
+        assert np.array_equal(got_k, e4m3.quantize(kn, np.float32(ks))), f"layer {i}: new K rows"
+        assert np.array_equal(got_v, e4m3.quantize(vn, np.float32(vs))), f"layer {i}: new V rows"
+        seqs = sorted(np.random.default_rng(500 + i).choice(w.num_seqs, 6, replace=False).tolist())
+        nb, kc, vc, bt, sl = _layer_sample(w, t, i, t["k_cache"][i], t["v_cache"][i], seqs)
+        gs = paged.Geom(nb, w.block_size, w.num_kv_heads, w.head_dim, w.kv_dtype)
+        ref = paged.decode(gs, host_bits(t["q"][i][seqs]), kc, vc, bt, sl, w.scale,
+                           k_scale=float(np.float32(ks)), v_scale=float(np.float32(vs)))
+        mx, _ = compare(out[i][seqs], ref, w.kv_dtype, label=f"{w.name} layer {i} sequences {seqs}")
+        worst = max(worst, mx)
+    print(f"[configs] {w.name}: new-token rows of all {w.num_layers} layers bit-exact; sampled sequences "
+          f"on every layer max-abs {worst:.2e}", flush=True)

@@ -10,7 +10,7 @@ import torch
 import paged_kv_cache_32_amd as pa
 from oracle import blocks as B
 from oracle import paged
-from tests.gpu_helpers import BF16_TOL, host_bits
+from tests.gpu_helpers import BF16_ENVELOPE, BF16_TOL, host_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -113,7 +113,7 @@ def test_decode_around_a_swap_driven_by_the_block_manager():
         torch.cuda.synchronize()
         ref = paged.decode(g, host_bits(q), k_ref, v_ref, bt_o, sl, scale)
         err = np.abs(out.cpu().double().numpy() - ref)
-        assert err.max() <= BF16_TOL[0] and err.mean() <= BF16_TOL[1], err.max()
+        assert err.max() <= min(BF16_TOL[0], BF16_ENVELOPE) and err.mean() <= BF16_TOL[1], err.max()
 
     decode([0, 1])
     t0 = model.table(0)
@@ -185,4 +185,4 @@ def test_swap_on_a_second_stream_overlaps_a_decode():
     ref = paged.decode(g, host_bits(q)[rows], k0, v0, bt[rows], sl[rows], 0.088)
     for o in outs:
         err = np.abs(o.cpu().double().numpy()[rows] - ref)
-        assert err.max() <= BF16_TOL[0] and err.mean() <= BF16_TOL[1], err.max()
+        assert err.max() <= min(BF16_TOL[0], BF16_ENVELOPE) and err.mean() <= BF16_TOL[1], err.max()

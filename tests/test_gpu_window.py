@@ -12,7 +12,7 @@ import paged_kv_cache_32_amd as pa
 from oracle import blocks as B
 from oracle import paged
 from paged_kv_cache_32_amd import workloads as W
-from tests.gpu_helpers import (BF16_TOL, compare, device_inputs, gpu_write, host_bits, oracle_caches)
+from tests.gpu_helpers import (BF16_ENVELOPE, BF16_TOL, compare, device_inputs, gpu_write, host_bits, oracle_caches)
 
 pytestmark = pytest.mark.gpu
 
@@ -114,7 +114,7 @@ def test_window_decode_with_manager_trims():
         assert np.array_equal(bt, bt_o)
         ref = paged.decode(g, host_bits(q), k_ref, v_ref, bt_o, sl, 0.125, window=WIN)
         err = np.abs(out.cpu().double().numpy() - ref)
-        assert err.max() <= BF16_TOL[0] and err.mean() <= BF16_TOL[1], (step, err.max())
+        assert err.max() <= min(BF16_TOL[0], BF16_ENVELOPE) and err.mean() <= BF16_TOL[1], (step, err.max())
     # the pool stays bounded: each sequence holds at most ceil(WIN / BS) + 1 blocks
     assert all(sum(b >= 0 for b in model.table(s)) <= -(-WIN // BS) + 1 for s in seqs)
     assert model.num_free() >= NB - len(seqs) * (-(-WIN // BS) + 1)

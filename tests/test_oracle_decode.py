@@ -334,3 +334,30 @@ def test_window_of_one_returns_the_last_value_and_ignores_released_blocks():
     for s, L in enumerate(lens):
         bt2[s, :max(0, L - W) // 16] = -1
     assert np.array_equal(paged.decode(g, q, kc, vc, bt2, sl, 0.3, window=W), ref)
+
+
+def test_a_lost_or_doubled_piece_leaves_the_parity_envelope():
+    """Why the GPU parity tests check an accuracy envelope beside the
+    contract bounds.  Planted in the oracle: a long unit (9,000 tokens, the
+    length the many-piece GPU test uses) merged by log-sum-exp with one
+    16-token piece dropped, or counted twice.  With N(0, 1) queries, keys and
+    values the output moves by about 1/563 of a value, which the contract's
+    max-abs 1e-2 can miss but the envelope's 1e-4 cannot."""
+    from tests.gpu_helpers import BF16_ENVELOPE, BF16_TOL
+    rng = np.random.default_rng(7)
+    L, G, D, P = 9000, 8, 128, 16
+    q = rng.standard_normal((G, D))
+    K = rng.standard_normal((L, D))
+    V = rng.standard_normal((L, D))
+    scale = 1 / math.sqrt(D)
+    pieces = [paged.partial_state(q, K[i:i + P], V[i:i + P], scale) for i in range(0, L, P)]
+    whole = paged.lse_merge(pieces)
+    assert np.abs(whole - paged.softmax_attention(q, K, V, scale)).max() < 1e-12
+    moved = []
+    for j in (0, 100, 400, len(pieces) - 1):
+        lost = paged.lse_merge(pieces[:j] + pieces[j + 1:])
+        twice = paged.lse_merge(pieces + [pieces[j]])
+        for bad in (lost, twice):
+            moved.append(np.abs(bad - whole).max())
+    assert min(moved) > 10 * BF16_ENVELOPE
+    assert min(moved) < BF16_TOL[0]          # the contract bound alone would not have caught some
