@@ -41,12 +41,14 @@ Other workloads (--workload), each on the same 70B layer shape:
                        manager's add_sequence / append_token rates
   quest_long_context_128k  the long-context batch (4 x 131,072 tokens) decoded
                        with query-aware page selection, 256 pages (4,096
-                       tokens) per (sequence, KV head): a step is the cache
-                       write, pa_quest_update, pa_quest_select and
+                       tokens) per (sequence, KV head): a step is
+                       pa_quest_cache_write (the cache write keeping the page
+                       summaries in the same launch), pa_quest_select and
                        pa_decode_quest; `value` counts the bytes the step
                        must read (page summaries, chosen K/V, q, out,
                        tables); the plain decode of the same batch is timed
-                       beside it
+                       beside it.  The write is pa_quest_cache_write: the
+                       summary update in the write's own launch
   quest_llama70b_bs64  the same on the 70B layer bs=64 batch, 64 pages
                        (1,024 tokens) per (sequence, KV head)
   cascade_prefix_shared_bs256  the prefix-shared batch decoded with
@@ -737,9 +739,9 @@ def bench_quest(args, dev):
     stream = torch.cuda.current_stream(dev)
 
     def phases():
-        pa.pa_cache_write(kn, vn, sm, kc, vc, block_size=BS)
-        yield
-        pa.pa_quest_update(kc, sm, summ, num_kv_heads=Hkv, head_dim=D, block_size=BS)
+        # The step's write keeps the summaries in the same launch (one new
+        # token per sequence, each in a block of its own).
+        pa.pa_quest_cache_write(kn, vn, sm, kc, vc, summ, block_size=BS)
         yield
         pa.pa_quest_select(q, summ, bt, sl, budget, sel_tables=sel_t, sel_lens=sel_l, workspace=sel_ws, **kw)
         yield
@@ -755,7 +757,7 @@ def bench_quest(args, dev):
         full()
     torch.cuda.synchronize()
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
     fev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
     t0 = time.perf_counter()
     for i in range(K):
@@ -773,14 +775,14 @@ def bench_quest(args, dev):
         full()
         fev[i][1].record(stream)
     torch.cuda.synchronize()
-    ph = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in ev])   # ms
+    ph = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in ev])   # ms
     full_ms = np.array([e[0].elapsed_time(e[1]) for e in fev])
     step_ms = float(ph.sum(axis=1).mean())
     qb = quest_bytes(w, budget)
     kept = int(sel_l.clamp(min=0).sum().item())
     qb["decode"] -= (qb["kept_tokens_upper"] - kept) * 2 * D * w.elem_bytes     # the exact kept tokens
     total = qb["update"] + qb["select"] + qb["decode"] + S * Hkv * D * 2 * w.elem_bytes
-    names = ["cache_write", "quest_update", "quest_select", "decode_quest"]
+    names = ["quest_cache_write", "quest_select", "decode_quest"]
     means = {n: float(ph[:, j].mean()) for j, n in enumerate(names)}
     dom = max(("quest_select", "decode_quest"), key=lambda n: means[n])
     dom_bytes = qb["select"] if dom == "quest_select" else qb["decode"]

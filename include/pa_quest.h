@@ -11,17 +11,23 @@
  *
  * Here a page is one cache block, and pages are chosen per (sequence, KV
  * head): the query heads of a group share their KV head's K/V, and a page's
- * score for the group is the largest of its query heads' scores.  A step is
- *   pa_cache_write(_fp8)  -> pa_quest_update   (summaries follow the writes)
- *   pa_quest_select       -> pa_decode_quest(_fp8)
- * all on one stream.
+ * score for the group is the largest of its query heads' scores.  A decode
+ * step is
+ *   pa_quest_cache_write(_fp8)   (the write, keeping the summaries current)
+ *   pa_quest_select -> pa_decode_quest(_fp8)
+ * all on one stream.  Writes with several tokens per block (a prompt) use
+ * pa_cache_write(_fp8) followed by pa_quest_update instead.
  *
  * Summaries: a DEVICE array of num_blocks * num_kv_heads * head_dim uint32
- * words, word [blk][h][d] = (max << 16) | min, both bf16 bit patterns of the
- * keys' stored values (bf16 keys as stored; fp8 keys as their e4m3 code
- * values without the per-tensor scale - a positive scale changes no
- * minimum, maximum or ranking).  An empty summary is min = +inf, max = -inf.
- * NaN keys are ignored.  Start a pool with pa_quest_clear.
+ * words, one per (block b, KV head h, dimension d) at index
+ *   ((b * (head_dim / 4) + d / 4) * num_kv_heads + h) * 4 + d % 4
+ * (for each block and 4 dimensions, the 16-byte quads of all heads are
+ * contiguous: the score kernel reads them as one run per page).  A word is
+ * (max << 16) | min, both bf16 bit patterns of the keys' stored values (bf16
+ * keys as stored; fp8 keys as their e4m3 code values without the per-tensor
+ * scale - a positive scale changes no minimum, maximum or ranking).  An
+ * empty summary is min = +inf, max = -inf.  NaN keys are ignored.  Start a
+ * pool with pa_quest_clear.
  */
 #ifndef PA_QUEST_H_
 #define PA_QUEST_H_
@@ -35,6 +41,29 @@ extern "C" {
 /* Sets every summary word of the pool empty (a fill kernel on `stream`).
  * summaries: DEVICE, num_blocks * num_kv_heads * head_dim uint32.           */
 pa_status pa_quest_clear(const pa_cache_desc* cache, uint32_t* summaries, void* stream);
+
+/* pa_cache_write in one launch with the summary update: the caches are
+ * written exactly as pa_cache_write writes them, and the summaries end as
+ * pa_cache_write followed by pa_quest_update leaves them (a token at offset
+ * 0 starts its block's summary afresh, every token widens its block's).
+ * Contract: no two tokens of one call go to the same block - a decode
+ * step's new tokens, one per sequence, each appended to a block that its
+ * sequence alone holds (copy-on-write guarantees that).  Several tokens in
+ * one block give undefined summaries (the caches are still written as
+ * pa_cache_write writes them).
+ *   summaries  DEVICE, as for pa_quest_update; NULL -> PA_ERR_NULL (unless
+ *              num_tokens == 0)
+ * Other arguments and errors as pa_cache_write.                            */
+pa_status pa_quest_cache_write(const pa_cache_desc* cache, const void* k, const void* v,
+                               const int64_t* slot_mapping, int32_t num_tokens, void* k_cache,
+                               void* v_cache, uint32_t* summaries, void* stream);
+
+/* The same into an fp8 (e4m3fn) cache, as pa_cache_write_fp8: the summaries
+ * take the stored codes' values.                                             */
+pa_status pa_quest_cache_write_fp8(const pa_cache_desc* cache, const void* k, const void* v,
+                                   const int64_t* slot_mapping, int32_t num_tokens, void* k_cache,
+                                   void* v_cache, float k_scale, float v_scale, uint32_t* summaries,
+                                   void* stream);
 
 /* Keeps the summaries current after a cache write of the same tokens
  * (call it after pa_cache_write / pa_cache_write_fp8 on the same stream):

@@ -110,6 +110,8 @@ def _load():
                                   vp, sz, vp], i32),
         "pa_quest_clear": ([dp, vp, vp], i32),
         "pa_quest_update": ([dp, i32, vp, vp, i32, vp, vp], i32),
+        "pa_quest_cache_write": ([dp, vp, vp, vp, i32, vp, vp, vp, vp], i32),
+        "pa_quest_cache_write_fp8": ([dp, vp, vp, vp, i32, vp, vp, f32, f32, vp, vp], i32),
         "pa_quest_summarize": ([dp, i32, vp, vp, vp, i32, vp, vp], i32),
         "pa_quest_select_workspace_size": ([i32, i32, i32], sz),
         "pa_quest_select": ([dp, vp, i32, i32, vp, vp, i32, vp, i32, vp, vp, vp, sz, vp], i32),
@@ -623,12 +625,19 @@ def pa_decode_append_fp8(q, k_new, v_new, k_cache, v_cache, block_tables, seq_le
 
 # -- query-aware page selection (include/pa_quest.h) -------------------------
 
+def summary_shape(num_blocks, num_kv_heads, head_dim):
+    """Shape of a pool's summary array: [num_blocks, head_dim / 4,
+    num_kv_heads, 4] (include/pa_quest.h)."""
+    return (num_blocks, head_dim // 4, num_kv_heads, 4)
+
+
 def quest_summaries(k_cache, *, num_kv_heads, head_dim, block_size):
     """A new summary array for the pool of ``k_cache``: int32 device tensor
-    [num_blocks, num_kv_heads, head_dim] (uint32 words, (max bf16 << 16) |
-    min bf16), every word empty."""
+    of summary_shape() (uint32 words, (max bf16 << 16) | min bf16), every
+    word empty."""
     desc = make_desc(k_cache, num_kv_heads, head_dim, block_size)
-    words = torch.empty((desc.num_blocks, num_kv_heads, head_dim), dtype=torch.int32, device=k_cache.device)
+    words = torch.empty(summary_shape(desc.num_blocks, num_kv_heads, head_dim), dtype=torch.int32,
+                        device=k_cache.device)
     with torch.cuda.device(k_cache.device):
         st = _load().pa_quest_clear(ctypes.byref(desc), _ptr(words), _stream(k_cache))
     _check("pa_quest_clear", st)
@@ -639,9 +648,42 @@ def _summary_args(k_cache, summaries, num_kv_heads, head_dim, block_size):
     dev = k_cache.device
     _need(k_cache, "k_cache", k_cache.dtype, dev)
     desc = make_desc(k_cache, num_kv_heads, head_dim, block_size)
-    _need(summaries, "summaries", torch.int32, dev, shape=(desc.num_blocks, num_kv_heads, head_dim))
+    _need(summaries, "summaries", torch.int32, dev, shape=summary_shape(desc.num_blocks, num_kv_heads, head_dim))
     eb = 2 if k_cache.dtype == torch.bfloat16 else 1
     return dev, desc, eb
+
+
+def _quest_cache_write(fp8, k, v, slot_mapping, k_cache, v_cache, summaries, block_size, k_scale, v_scale):
+    dev = k.device
+    _need(k, "k", torch.bfloat16, dev, 3)
+    T, Hkv, D = k.shape
+    _need(v, "v", torch.bfloat16, dev, shape=k.shape)
+    _need(slot_mapping, "slot_mapping", torch.int64, dev, shape=(T,))
+    _need(k_cache, "k_cache", torch.uint8 if fp8 else torch.bfloat16, dev)
+    _need(v_cache, "v_cache", k_cache.dtype, dev, shape=tuple(k_cache.shape))
+    desc = make_desc(k_cache, Hkv, D, block_size)
+    _need(summaries, "summaries", torch.int32, dev, shape=summary_shape(desc.num_blocks, Hkv, D))
+    L = _load()
+    with torch.cuda.device(dev):
+        if fp8:
+            st = L.pa_quest_cache_write_fp8(ctypes.byref(desc), _ptr(k), _ptr(v), _ptr(slot_mapping), T,
+                                            _ptr(k_cache), _ptr(v_cache), float(k_scale), float(v_scale),
+                                            _ptr(summaries), _stream(k))
+        else:
+            st = L.pa_quest_cache_write(ctypes.byref(desc), _ptr(k), _ptr(v), _ptr(slot_mapping), T,
+                                        _ptr(k_cache), _ptr(v_cache), _ptr(summaries), _stream(k))
+    _check("pa_quest_cache_write" + ("_fp8" if fp8 else ""), st)
+
+
+def pa_quest_cache_write(k, v, slot_mapping, k_cache, v_cache, summaries, *, block_size):
+    """pa_cache_write and the summary update in one launch (no two tokens of
+    the call in one block).  See include/pa_quest.h."""
+    _quest_cache_write(False, k, v, slot_mapping, k_cache, v_cache, summaries, block_size, 1.0, 1.0)
+
+
+def pa_quest_cache_write_fp8(k, v, slot_mapping, k_cache, v_cache, k_scale, v_scale, summaries, *, block_size):
+    """The same into an e4m3fn cache."""
+    _quest_cache_write(True, k, v, slot_mapping, k_cache, v_cache, summaries, block_size, k_scale, v_scale)
 
 
 def pa_quest_update(k_cache, slot_mapping, summaries, *, num_kv_heads, head_dim, block_size):
@@ -674,9 +716,9 @@ def pa_quest_select(q, summaries, block_tables, seq_lens, budget, *, num_kv_head
     dev = q.device
     _need(q, "q", torch.bfloat16, dev, 3)
     S, Hq, D = q.shape
-    _need(summaries, "summaries", torch.int32, dev, 3)
-    if summaries.shape[1:] != (num_kv_heads, D):
-        raise ValueError("summaries must be [num_blocks, num_kv_heads, head_dim]")
+    _need(summaries, "summaries", torch.int32, dev, 4)
+    if tuple(summaries.shape[1:]) != summary_shape(1, num_kv_heads, D)[1:]:
+        raise ValueError("summaries must be [num_blocks, head_dim / 4, num_kv_heads, 4]")
     _need(block_tables, "block_tables", torch.int32, dev, 2)
     if block_tables.shape[0] != S:
         raise ValueError("block_tables must have one row per sequence")

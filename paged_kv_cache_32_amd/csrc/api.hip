@@ -80,7 +80,8 @@ bool good_scale(float s) { return isfinite(s) && s > 0.f; }
 
 pa_status cache_write(const pa_cache_desc* cache, const void* k, const void* v,
                       const int64_t* slot_mapping, int32_t num_tokens, void* k_cache,
-                      void* v_cache, bool fp8, float k_scale, float v_scale, void* stream) {
+                      void* v_cache, bool fp8, float k_scale, float v_scale, void* stream,
+                      uint32_t* summaries = nullptr) {
   if (!cache) return PA_ERR_NULL;
   pa_status st = desc_status(cache);
   if (st != PA_OK) return st;
@@ -96,6 +97,7 @@ pa_status cache_write(const pa_cache_desc* cache, const void* k, const void* v,
   p.slots = slot_mapping;
   p.k_cache = static_cast<uint8_t*>(k_cache);
   p.v_cache = static_cast<uint8_t*>(v_cache);
+  p.summaries = summaries;
   p.num_tokens = num_tokens;
   p.num_kv_heads = cache->num_kv_heads;
   p.head_dim = cache->head_dim;
@@ -554,6 +556,23 @@ pa_status summary_params(const pa_cache_desc* cache, int32_t elem_bytes, const v
 
 }  // namespace
 
+pa_status pa_quest_cache_write(const pa_cache_desc* cache, const void* k, const void* v,
+                               const int64_t* slot_mapping, int32_t num_tokens, void* k_cache,
+                               void* v_cache, uint32_t* summaries, void* stream) {
+  if (num_tokens > 0 && !summaries) return PA_ERR_NULL;
+  return cache_write(cache, k, v, slot_mapping, num_tokens, k_cache, v_cache, false, 1.f, 1.f, stream,
+                     summaries);
+}
+
+pa_status pa_quest_cache_write_fp8(const pa_cache_desc* cache, const void* k, const void* v,
+                                   const int64_t* slot_mapping, int32_t num_tokens, void* k_cache,
+                                   void* v_cache, float k_scale, float v_scale, uint32_t* summaries,
+                                   void* stream) {
+  if (num_tokens > 0 && !summaries) return PA_ERR_NULL;
+  return cache_write(cache, k, v, slot_mapping, num_tokens, k_cache, v_cache, true, k_scale, v_scale, stream,
+                     summaries);
+}
+
 pa_status pa_quest_update(const pa_cache_desc* cache, int32_t elem_bytes, const void* k_cache,
                           const int64_t* slot_mapping, int32_t num_tokens, uint32_t* summaries,
                           void* stream) {
@@ -605,8 +624,9 @@ pa_status pa_quest_select(const pa_cache_desc* cache, const void* q, int32_t num
   if (num_q_heads / cache->num_kv_heads > pa::kMaxGroupQuest) return PA_ERR_UNSUPPORTED;
   if ((int64_t)max_blocks_per_seq * cache->block_size > INT32_MAX) return PA_ERR_SHAPE;
   const int64_t units = (int64_t)num_seqs * cache->num_kv_heads;
-  const int32_t chunks = (max_blocks_per_seq + 255) / 256;
-  if (units * (chunks > 0 ? chunks : 1) > INT32_MAX || units * budget > INT32_MAX) return PA_ERR_SHAPE;
+  if (units * (int64_t)(max_blocks_per_seq > 0 ? max_blocks_per_seq : 1) > INT32_MAX ||
+      units * budget > INT32_MAX)
+    return PA_ERR_SHAPE;
   if (num_seqs == 0) return PA_OK;
   if (!q || !summaries || !block_tables || !seq_lens || !sel_tables || !sel_lens) return PA_ERR_NULL;
   const size_t need = pa_quest_select_workspace_size(num_seqs, cache->num_kv_heads, max_blocks_per_seq);
@@ -630,7 +650,6 @@ pa_status pa_quest_select(const pa_cache_desc* cache, const void* q, int32_t num
   p.num_blocks = cache->num_blocks;
   p.max_blocks = max_blocks_per_seq;
   p.budget = budget;
-  p.chunks = chunks > 0 ? chunks : 1;
   if (pa::launch_page_select(p, static_cast<hipStream_t>(stream)) != hipSuccess) return PA_ERR_LAUNCH;
   return PA_OK;
 }

@@ -8,6 +8,14 @@
 // to nearest even and saturated ("KV Cache Engineering for LLM Serving",
 // section 8, Quantization).
 //
+// With a summary array (the query-aware page selection of "KV Cache
+// Engineering for LLM Serving", section 7), the same threads keep each
+// block's per-dimension key minimum and maximum current: a token at offset 0
+// starts its block's summary, any other token widens it.  That is a plain
+// read-modify-write of the words, valid because no two tokens of one such
+// call share a block (the caller's contract: a decode step's new tokens,
+// one per sequence, each in a block its sequence owns alone).
+//
 // The write is a few hundred bytes per token: it is latency bound, so the
 // kernel is one thread per 16-byte K chunk of a (token, kv head) row, with
 // the matching V elements, and no attempt at more.  A token's K row and V
@@ -23,9 +31,44 @@ namespace {
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
+// bf16 bits of an e4m3fn code's value (no scale): exact; a NaN code gives
+// a bf16 NaN.
+__device__ __forceinline__ uint32_t e4m3_bf16_bits(uint32_t c) {
+  const uint32_t sign = (c & 0x80u) << 8;
+  const uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
+  if (e == 15u && m == 7u) return sign | 0x7FC0u;
+  if (e == 0u) return sign | (__float_as_uint((float)m * 0x1p-9f) >> 16);
+  return sign | ((e + 120u) << 7) | (m << 4);
+}
+
+// The summary words of X consecutive key dimensions (dg * X ..) of one
+// (block, head): a token at offset 0 sets them from its own key (a NaN key
+// leaves a dimension empty), any other token widens them.  `key` holds the
+// stored keys' bf16 bits.
+template <int X>
+__device__ __forceinline__ void update_summary(const CacheWriteParams& p, int64_t blk, int h, int dg, bool first,
+                                               const uint32_t (&key)[X]) {
+#pragma unroll
+  for (int qd = 0; qd < X / 4; ++qd) {
+    u32x4* w = reinterpret_cast<u32x4*>(p.summaries + summary_word(blk, h, dg * X + 4 * qd, p.num_kv_heads, p.head_dim));
+    u32x4 cur = first ? u32x4{kEmptySummaryWord, kEmptySummaryWord, kEmptySummaryWord, kEmptySummaryWord} : *w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t vb = key[4 * qd + e];
+      const float v = bf16_to_f32(vb);
+      const uint32_t lo = cur[e] & 0xFFFFu, hi = cur[e] >> 16;
+      const uint32_t nlo = v < bf16_to_f32(lo) ? vb : lo;   // a NaN compares false: unchanged
+      const uint32_t nhi = v > bf16_to_f32(hi) ? vb : hi;
+      cur[e] = (nhi << 16) | nlo;
+    }
+    *w = cur;
+  }
+}
+
 // One thread per (token, kv head, group of X elements), X = 16 bytes of
-// cache: 8 bf16 values or 16 fp8 codes.
-template <bool FP8>
+// cache: 8 bf16 values or 16 fp8 codes.  QUEST: also the summary words of
+// those X dimensions.
+template <bool FP8, bool QUEST>
 __global__ __launch_bounds__(256) void cache_write_kernel(const CacheWriteParams p) {
   constexpr int X = FP8 ? 16 : 8;
   const int groups = p.head_dim / X;
@@ -54,6 +97,12 @@ __global__ __launch_bounds__(256) void cache_write_kernel(const CacheWriteParams
   if (!FP8) {
     const u32x4 kv = *reinterpret_cast<const u32x4*>(p.k + src);
     __builtin_nontemporal_store(kv, reinterpret_cast<u32x4*>(kdst));
+    if constexpr (QUEST) {
+      uint32_t key[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) key[e] = (e & 1) ? (kv[e >> 1] >> 16) : (kv[e >> 1] & 0xFFFFu);
+      update_summary<8>(p, blk, h, dg, off == 0, key);
+    }
     const u32x4 vv = *reinterpret_cast<const u32x4*>(p.v + src);
     uint16_t* vdst = reinterpret_cast<uint16_t*>(vtile);
 #pragma unroll
@@ -75,6 +124,12 @@ __global__ __launch_bounds__(256) void cache_write_kernel(const CacheWriteParams
       kout[e >> 2] |= code << (8 * (e & 3));
     }
     __builtin_nontemporal_store(kout, reinterpret_cast<u32x4*>(kdst));
+    if constexpr (QUEST) {
+      uint32_t key[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) key[e] = e4m3_bf16_bits((kout[e >> 2] >> (8 * (e & 3))) & 0xFFu);
+      update_summary<16>(p, blk, h, dg, off == 0, key);
+    }
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const uint32_t w = vin[e >> 3][(e >> 1) & 3];
@@ -90,11 +145,18 @@ hipError_t launch_cache_write(const CacheWriteParams& p, bool fp8, hipStream_t s
   const int X = fp8 ? 16 : 8;
   const int64_t threads = (int64_t)p.num_tokens * p.num_kv_heads * (p.head_dim / X);
   if (threads == 0) return hipSuccess;
-  const int64_t blocks = (threads + 255) / 256;
-  if (fp8)
-    hipLaunchKernelGGL(cache_write_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
-  else
-    hipLaunchKernelGGL(cache_write_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  if (p.summaries) {
+    if (fp8)
+      hipLaunchKernelGGL((cache_write_kernel<true, true>), grid, dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((cache_write_kernel<false, true>), grid, dim3(256), 0, stream, p);
+  } else {
+    if (fp8)
+      hipLaunchKernelGGL((cache_write_kernel<true, false>), grid, dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((cache_write_kernel<false, false>), grid, dim3(256), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

@@ -39,12 +39,22 @@ __device__ __forceinline__ int v_elem(int d, int r) {
   return ((((d / (16 * R)) * 16 + d % 16) * 4 + r / 4) * R + (d / 16) % R) * 4 + r % 4;
 }
 
+// Query-aware page summaries: one uint32 word per (block, KV head, key
+// dimension), (max bf16 << 16) | min bf16, laid out [block][d / 4][head][4]
+// so that the 16-byte quads of all heads for 4 dimensions of a block are
+// contiguous (the score kernel reads one such run per page and step).
+__host__ __device__ __forceinline__ int64_t summary_word(int64_t blk, int h, int d, int num_kv_heads, int head_dim) {
+  return ((blk * (head_dim / 4) + d / 4) * num_kv_heads + h) * 4 + d % 4;
+}
+constexpr uint32_t kEmptySummaryWord = 0xFF807F80u;  // max = -inf (bf16 0xFF80), min = +inf (0x7F80)
+
 struct CacheWriteParams {
   const uint16_t* k;          // [T][Hkv][D] bf16 bits
   const uint16_t* v;
   const int64_t* slots;       // [T]
   uint8_t* k_cache;
   uint8_t* v_cache;
+  uint32_t* summaries;        // null, or the pool's page summaries, kept current by the write
   int32_t num_tokens, num_kv_heads, head_dim, block_size;
   int64_t num_slots;          // num_blocks * block_size
   float k_inv, v_inv;         // 1 / scale (fp8 only)
@@ -107,7 +117,7 @@ struct SummaryParams {
   const int64_t* slots;         // update: [num_tokens] slots just written
   const int32_t* blocks;        // build: [num_tokens] blocks to recompute ...
   const int32_t* counts;        // ... from their first counts[i] tokens
-  uint32_t* words;              // [num_blocks][Hkv][D] (max bf16 << 16 | min bf16)
+  uint32_t* words;              // summaries, laid out as summary_word() says
   int32_t num_tokens;           // tokens (update) or listed blocks (build)
   int32_t num_kv_heads, head_dim, block_size, num_blocks;
 };
@@ -122,7 +132,8 @@ struct SelectParams {
   int32_t* sel_lens;            // [S * Hkv]
   int32_t num_seqs, num_q_heads, num_kv_heads, group, head_dim, block_size, num_blocks, max_blocks;
   int32_t budget;               // pages to keep per (sequence, KV head)
-  int32_t chunks;               // ceil(max_blocks / 256): score workgroups per unit
+  int32_t slice_heads;          // KV heads whose queries a score workgroup holds at once
+  int32_t item_pages;           // pages a score workgroup takes per item
 };
 
 // Shared-prefix decode: attention over shared segments for all their members.

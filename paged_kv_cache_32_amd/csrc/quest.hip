@@ -7,11 +7,12 @@
 // that min/max box could reach, sum_d max(q_d min_d, q_d max_d), and only the
 // best `budget` pages are then read by the decode.
 //
-// Summary words: [num_blocks][Hkv][head_dim] uint32, one per (block, head,
-// dim): bits 0-15 hold the minimum and bits 16-31 the maximum, both as bf16
-// (every stored key is exactly a bf16 value: a bf16 key, or an e4m3 code's
-// value without the per-tensor scale).  An empty summary is min = +inf,
-// max = -inf.
+// Summary words: one uint32 per (block, head, dim), bits 0-15 the minimum
+// and bits 16-31 the maximum, both as bf16 (every stored key is exactly a
+// bf16 value: a bf16 key, or an e4m3 code's value without the per-tensor
+// scale), laid out [block][dim / 4][head][4] (summary_word in
+// pa_internal.h).  An empty summary is min = +inf, max = -inf.  The cache
+// write can keep them itself (pa_quest_cache_write, cache_write.hip).
 //
 // Kernels:
 //   summary_fill_kernel    every word empty (a plain fill, graph-safe).
@@ -22,7 +23,8 @@
 //   summary_build_kernel   words of listed blocks recomputed from their
 //                          first `count` tokens (after a copy or swap-in).
 //   page_score_kernel      score of every page of every (sequence, KV head),
-//                          as an order-preserving uint32 key.
+//                          as an order-preserving uint32 key (a workgroup
+//                          per run of a sequence's pages, all KV heads).
 //   page_select_kernel     per (sequence, KV head): the `budget` best pages
 //                          (equal scores: lower page first) by a radix select
 //                          on the keys, written in page order as a compacted
@@ -37,7 +39,7 @@ namespace {
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr uint32_t kEmptyWord = 0xFF807F80u;  // max = -inf (bf16 0xFF80), min = +inf (0x7F80)
+constexpr uint32_t kEmptyWord = kEmptySummaryWord;
 
 __device__ __forceinline__ float bf16f(uint32_t b16) { return __uint_as_float(b16 << 16); }
 
@@ -86,7 +88,7 @@ __global__ __launch_bounds__(256) void summary_reset_kernel(const SummaryParams 
   const int64_t slot = p.slots[j];
   if (slot < 0 || slot >= (int64_t)p.num_blocks * p.block_size || slot % p.block_size != 0) return;
   const int64_t blk = slot / p.block_size;
-  u32x4* w = reinterpret_cast<u32x4*>(p.words + (blk * p.num_kv_heads + h) * p.head_dim) + i;
+  u32x4* w = reinterpret_cast<u32x4*>(p.words + summary_word(blk, h, 4 * i, p.num_kv_heads, p.head_dim));
   *w = u32x4{kEmptyWord, kEmptyWord, kEmptyWord, kEmptyWord};
 }
 
@@ -122,9 +124,9 @@ __global__ __launch_bounds__(256) void summary_merge_kernel(const SummaryParams 
   const int64_t blk = slot / p.block_size;
   const int t = (int)(slot - blk * p.block_size);
   const u32x4 c = *reinterpret_cast<const u32x4*>(p.k_cache + k_chunk(p, blk, h, t, dg, FP8 ? 1 : 2));
-  uint32_t* w = p.words + (blk * p.num_kv_heads + h) * p.head_dim + dg * X;
 #pragma unroll
-  for (int e = 0; e < X; ++e) widen(w + e, chunk_elem<FP8>(c, e));
+  for (int e = 0; e < X; ++e)
+    widen(p.words + summary_word(blk, h, dg * X + e, p.num_kv_heads, p.head_dim), chunk_elem<FP8>(c, e));
 }
 
 // One thread per (listed block, head, 16-byte chunk): min and max over the
@@ -159,11 +161,11 @@ __global__ __launch_bounds__(256) void summary_build_kernel(const SummaryParams 
       if (v > bf16f(hi[e])) hi[e] = vb;
     }
   }
-  u32x4* w = reinterpret_cast<u32x4*>(p.words + ((int64_t)blk * p.num_kv_heads + h) * p.head_dim + dg * X);
 #pragma unroll
   for (int v = 0; v < X / 4; ++v)
-    w[v] = u32x4{(hi[4 * v] << 16) | lo[4 * v], (hi[4 * v + 1] << 16) | lo[4 * v + 1],
-                 (hi[4 * v + 2] << 16) | lo[4 * v + 2], (hi[4 * v + 3] << 16) | lo[4 * v + 3]};
+    *reinterpret_cast<u32x4*>(p.words + summary_word(blk, h, dg * X + 4 * v, p.num_kv_heads, p.head_dim)) =
+        u32x4{(hi[4 * v] << 16) | lo[4 * v], (hi[4 * v + 1] << 16) | lo[4 * v + 1],
+              (hi[4 * v + 2] << 16) | lo[4 * v + 2], (hi[4 * v + 3] << 16) | lo[4 * v + 3]};
 }
 
 // Order-preserving uint32 of a score: a larger key is a larger score; -0 is
@@ -181,153 +183,229 @@ __device__ __forceinline__ int pages_of(const SelectParams& p, int s) {
   return (L + p.block_size - 1) / p.block_size;
 }
 
-// Work item (chunk c, unit = s * Hkv + h): pages c * 256 .. + 255 of the
-// unit, two per thread (a workgroup of two wavefronts, 128 pages each:
-// lane l takes pages l and l + 64 of its wavefront's, so every read of the
-// query from LDS serves two pages); workgroups stride over the items,
-// chunk-major, so the first chunks of all units (the only ones short
-// sequences have) spread over every XCD.  Each thread sums over the
-// dimensions in order, in float32, for every query head of the group, and
-// keeps the largest sum of each of its pages.  The block ids are loaded
-// before the query, so the two loads' latencies overlap.
-//
-// For a page's min <= max and a query value q, max(q * min, q * max) is
-// q * max when q >= 0 and q * min otherwise; with q+ = (q >= 0 ? q : 0) and
-// q- = (q < 0 ? q : 0) that term is added as two fused multiply-adds,
-// acc = fma(q+, max, acc) then acc = fma(q-, min, acc), one of which adds a
-// zero.  A product of two bf16 values is exact in float32 whenever its
-// magnitude is at least 2^-134 (so for any query and key values of magnitude
-// at least 2^-67, or zero), so this rounds exactly as a rounded product and a
+__device__ __forceinline__ int wave_incl_sum(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o, 64);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
+// Score workgroups: kScoreWaves wavefronts that share the staged queries of
+// one sequence.  A lane scores kScorePages pages of one KV head; lanes
+// (slot, head) with the heads fastest, so the lanes of a page read one run
+// of the block's summary words (all heads' quads of 4 dimensions, 128 bytes
+// at 8 heads) per load instruction.  kScoreAhead dimension quads of every
+// page are in flight while the previous ones are summed.
+constexpr int kScoreWaves = 4;
+constexpr int kScoreThreads = 64 * kScoreWaves;
+constexpr int kScorePages = 2;
+constexpr int kScoreAhead = 8;
+constexpr int kScoreLdsFloats = 16384;   // q+ and q- of the staged heads: 64 KiB
+
+// Work item: the item_pages pages c * item_pages .. of sequence s (a
+// sequence of n pages has ceil(n / item_pages) items, numbered in sequence
+// order); workgroups stride over the items.  Per item and slice of
+// slice_heads KV heads, the workgroup stages q+ = max(q, 0) and q- =
+// min(q, 0) of the slice's query heads in LDS as float32, the group padded
+// to GP heads with zeros: q+ in the first half of the array and q- in the
+// second, each as [KV head][query head][quad of 4 dimensions], the quad
+// index XORed with the KV head, so that the 8 heads' lanes of one read land
+// in 8 different 16-byte slots of every 128 bytes (no bank conflicts) while
+// a lane's reads of one step differ by constant offsets.  Each lane then sums, for every query head of its group,
+// over the dimensions in order, in float32: for a page's min <= max and a
+// query value q, max(q * min, q * max) is q * max when q >= 0 and q * min
+// otherwise, so the term is added as two fused multiply-adds, acc =
+// fma(q+, max, acc) then acc = fma(q-, min, acc), one of which adds a zero.
+// A product of two bf16 values is exact in float32 whenever its magnitude
+// is at least 2^-134, so this rounds exactly as a rounded product and a
 // rounded sum would (a zero's sign aside, which never changes a sum's
-// value), with no select and no compare in the loop.  q+ and q- of the
-// group sit in LDS (read as broadcasts); a page's row is summed one
-// 128-byte line (32 dimensions) at a time, the next line's loads in flight
-// while the current one is summed, and its words are unpacked once per
-// dimension for all query heads.
-constexpr int kScorePages = 256;
-constexpr int kScoreGrid = 4096;
-
-// Each wavefront stages its rows through LDS one line at a time, 64 rows
-// (one per lane) per pass, two passes per line: 8 lanes bring one row's
-// line, so each load instruction covers 8 whole lines
-// instead of pieces of 64 lines (64 cache tag lookups per instruction,
-// which measured as the cost of the lane-per-row loads); rows sit 144 bytes
-// apart, so a lane's reads of its own row fall in distinct banks.  No
-// workgroup barrier: a wavefront only reads what it wrote (wavefront-scope
-// fences keep the compiler from moving its LDS accesses across each other).
-constexpr int kRowWords = 36;   // 32 words of a line + 4 of pad
-
-template <int D>
-__global__ __launch_bounds__(128) void page_score_kernel(const SelectParams p) {
-  __shared__ float qpos[kMaxGroupQuest * D], qneg[kMaxGroupQuest * D];
-  __shared__ __attribute__((aligned(16))) uint32_t stage[2][64 * kRowWords];
-  const int Hkv = p.num_kv_heads, G = p.group;
-  const int units = p.num_seqs * Hkv;
-  const int chunks = p.chunks;                              // items of 256 pages
-  const int items = units * chunks;
+// value).  The page's score is the largest sum of the group.
+template <int D, int GP>
+__global__ __launch_bounds__(kScoreThreads) void page_score_kernel(const SelectParams p) {
+  __shared__ __attribute__((aligned(16))) float qs[kScoreLdsFloats];
+  constexpr int Q4 = D / 4;                       // dimension quads
+  // Quads per batch: at most kScoreAhead, fewer for 16 query heads (more
+  // registers per quad), and at most a quarter of a page so that the loop
+  // below runs at least twice (a loop of one pass becomes straight-line code
+  // whose hoisted addresses the compiler then spills).
+  constexpr int PP = kScorePages;
+  constexpr int PF0 = GP >= 16 ? kScoreAhead / 2 : kScoreAhead;
+  constexpr int PF = PF0 < Q4 / 4 ? PF0 : Q4 / 4;
+  static_assert(Q4 % (2 * PF) == 0 && Q4 / (2 * PF) >= 2, "the batch loop runs at least twice");
+  const int Hkv = p.num_kv_heads, G = p.group, Hs = p.slice_heads, PI = p.item_pages;
+  const int S = p.num_seqs;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  uint32_t* rows = stage[wv];
-  for (int it = blockIdx.x; it < items; it += gridDim.x) {
-    const int c = it / units, unit = it - c * units;
-    const int s = unit / Hkv, h = unit - s * Hkv;
-    const int np = pages_of(p, s);
-    if (c * 256 >= np) continue;                             // uniform
-    const int pg0 = c * 256 + 128 * wv;                      // this wavefront's first page
-    int blk[2];
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const int pg = pg0 + 64 * x + lane;
-      blk[x] = pg < np ? p.block_tables[(int64_t)s * p.max_blocks + pg] : -1;
-    }
-    __syncthreads();
-    const uint16_t* qg = p.q + ((int64_t)s * p.num_q_heads + (int64_t)h * G) * D;
-    for (int i = tid; i < G * D; i += 128) {
-      const uint32_t b = qg[i];
-      const float qf = __uint_as_float(b << 16);
-      qpos[i] = (b & 0x8000u) ? 0.f : qf;
-      qneg[i] = (b & 0x8000u) ? qf : 0.f;
-    }
-    __syncthreads();
-    if (pg0 >= np) continue;
-    int rb[2][8];
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      if ((unsigned)blk[x] >= (unsigned)p.num_blocks) blk[x] = -1;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) rb[x][i] = __shfl(blk[x], lane / 8 + 8 * i, 64);
-    }
-    auto gload = [&](int x, int b, u32x4 (&v)[8]) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        v[i] = rb[x][i] >= 0 ? reinterpret_cast<const u32x4*>(p.words + ((int64_t)rb[x][i] * Hkv + h) * D + 32 * b)[lane % 8]
-                             : u32x4{0u, 0u, 0u, 0u};
-    };
-    auto stage_line = [&](const u32x4 (&v)[8], u32x4 (&line)[8]) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        *reinterpret_cast<u32x4*>(rows + (lane / 8 + 8 * i) * kRowWords + 4 * (lane % 8)) = v[i];
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-      for (int k = 0; k < 8; ++k) line[k] = *reinterpret_cast<const u32x4*>(rows + lane * kRowWords + 4 * k);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    };
-    u32x4 va[8], vb[8];
-    gload(0, 0, va);
-    gload(1, 0, vb);
-    float acc[2][kMaxGroupQuest];
-#pragma unroll
-    for (int j = 0; j < kMaxGroupQuest; ++j) acc[0][j] = acc[1][j] = 0.f;
-#pragma unroll 1
-    for (int b = 0; b < D / 32; ++b) {
-      u32x4 la[8], lb[8];
-      stage_line(va, la);
-      if (b + 1 < D / 32) gload(0, b + 1, va);
-      stage_line(vb, lb);
-      if (b + 1 < D / 32) gload(1, b + 1, vb);
-#pragma unroll
-      for (int c8 = 0; c8 < 4; ++c8) {
-        float mna[8], mxa[8], mnb[8], mxb[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t wa = la[2 * c8 + e / 4][e % 4], wb = lb[2 * c8 + e / 4][e % 4];
-          mna[e] = __uint_as_float(wa << 16);
-          mxa[e] = __uint_as_float(wa & 0xFFFF0000u);
-          mnb[e] = __uint_as_float(wb << 16);
-          mxb[e] = __uint_as_float(wb & 0xFFFF0000u);
+  const int slots = 64 / Hs;                      // page slots per wavefront
+  const int hh = lane % Hs, slot = lane / Hs;
+  const int gq = GP * Q4;                         // quads per staged KV head (in each of q+ and q-)
+  for (int it = blockIdx.x;; it += gridDim.x) {
+    // The item's sequence (every wavefront finds the same one).
+    int s = -1, c = 0, np = 0;
+    {
+      int carry = 0;
+      for (int base = 0; base < S; base += 64) {
+        const int si = base + lane;
+        int npl = 0, n = 0;
+        if (si < S) {
+          npl = pages_of(p, si);
+          n = npl > 0 ? (npl + PI - 1) / PI : 0;
         }
+        const int incl = wave_incl_sum(n, lane);
+        const uint64_t hit = __ballot(n > 0 && carry + incl - n <= it && it < carry + incl);
+        if (hit) {
+          const int l0 = __builtin_ctzll(hit);
+          s = base + l0;
+          c = it - (carry + __builtin_amdgcn_readlane(incl - n, l0));
+          np = __builtin_amdgcn_readlane(npl, l0);
+          break;
+        }
+        carry += __builtin_amdgcn_readlane(incl, 63);
+      }
+    }
+    if (s < 0) break;                              // past the last item: the same for the whole workgroup
+    const int pg0 = c * PI + wv * slots * PP;      // this wavefront's first page
+    int blk[PP];
+    bool live[PP], ok[PP];
 #pragma unroll
-        for (int j = 0; j < kMaxGroupQuest; ++j) {
-          if (j < G) {
+    for (int k = 0; k < PP; ++k) {
+      const int pg = pg0 + k * slots + slot;
+      live[k] = slot < slots && pg < np;
+      blk[k] = live[k] ? p.block_tables[(int64_t)s * p.max_blocks + pg] : 0;
+      ok[k] = (unsigned)blk[k] < (unsigned)p.num_blocks;
+      if (!ok[k]) blk[k] = 0;                      // read block 0 in its place; the page scores lowest
+    }
+    for (int h0 = 0; h0 < Hkv; h0 += Hs) {
+      const int hn = Hkv - h0 < Hs ? Hkv - h0 : Hs;
+      const int h = h0 + (hh < hn ? hh : 0);
+      const u32x4* row[PP];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int qi = j * D + 32 * b + 8 * c8 + e;
-              const float qp = qpos[qi], qn = qneg[qi];
-              acc[0][j] = __builtin_fmaf(qp, mxa[e], acc[0][j]);
-              acc[0][j] = __builtin_fmaf(qn, mna[e], acc[0][j]);
-              acc[1][j] = __builtin_fmaf(qp, mxb[e], acc[1][j]);
-              acc[1][j] = __builtin_fmaf(qn, mnb[e], acc[1][j]);
+      for (int k = 0; k < PP; ++k)
+        row[k] = reinterpret_cast<const u32x4*>(p.words + summary_word(blk[k], h, 0, Hkv, D));
+      // Quad j of a page's head h sits Hkv quads after quad j - 1.
+      auto load = [&](u32x4 (&v)[PF][PP], int j0) {
+#pragma unroll
+        for (int jj = 0; jj < PF; ++jj) {
+          const int j = j0 + jj < Q4 ? j0 + jj : Q4 - 1;   // past the end: a repeat, never summed
+#pragma unroll
+          for (int k = 0; k < PP; ++k) v[jj][k] = row[k][(int64_t)j * Hkv];
+        }
+      };
+      float acc[PP][GP];
+#pragma unroll
+      for (int k = 0; k < PP; ++k)
+#pragma unroll
+        for (int g = 0; g < GP; ++g) acc[k][g] = 0.f;
+      const float* qh = qs + (hh < hn ? hh : 0) * gq * 4;
+      const int sw = (hh < hn ? hh : 0) & 7;
+      auto sum = [&](const u32x4 (&v)[PF][PP], int j0) {
+#pragma unroll
+        for (int jj = 0; jj < PF; ++jj) {
+          const int j = j0 + jj;
+          const int jx = (j ^ sw) * 4;
+          float mn[PP][4], mx[PP][4];
+#pragma unroll
+          for (int k = 0; k < PP; ++k)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              mn[k][e] = __uint_as_float(v[jj][k][e] << 16);
+              mx[k][e] = __uint_as_float(v[jj][k][e] & 0xFFFF0000u);
+            }
+#pragma unroll
+          for (int g = 0; g < GP; ++g) {
+            const float* qq = qh + g * Q4 * 4 + jx;
+            const float4 qp = *reinterpret_cast<const float4*>(qq);
+            const float4 qn = *reinterpret_cast<const float4*>(qq + kScoreLdsFloats / 2);
+            const float qpa[4] = {qp.x, qp.y, qp.z, qp.w}, qna[4] = {qn.x, qn.y, qn.z, qn.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+              for (int k = 0; k < PP; ++k) {
+                acc[k][g] = __builtin_fmaf(qpa[e], mx[k][e], acc[k][g]);
+                acc[k][g] = __builtin_fmaf(qna[e], mn[k][e], acc[k][g]);
+              }
+          }
+        }
+      };
+      // The first batch of this slice's summary loads is issued before the
+      // queries are staged, so their latencies overlap.  The scheduling
+      // barriers keep each batch of loads where it is issued (without them
+      // the compiler sinks every load to just before its use, and each quad
+      // then waits a whole memory latency).
+      u32x4 va[PF][PP], vb[PF][PP];
+      load(va, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();                             // the previous slice's reads of qs are done
+      // Staging: each thread takes 8 dimensions (16 bytes of q) at a time,
+      // kStageLoads of them with all loads issued before the first is used.
+      const uint16_t* qseq = p.q + (int64_t)s * p.num_q_heads * D;
+      constexpr int kStageLoads = 4;
+      const int octs = hn * gq / 2;                 // 8-dimension runs of the slice's query heads
+      for (int i0 = tid; i0 < octs; i0 += kScoreThreads * kStageLoads) {
+        u32x4 raw[kStageLoads];
+#pragma unroll
+        for (int u = 0; u < kStageLoads; ++u) {
+          const int i = i0 + u * kScoreThreads;
+          const int hs = i / (gq / 2), rem = i - hs * (gq / 2), g = rem / (Q4 / 2), jp = rem - g * (Q4 / 2);
+          // Runs past the slice or the group read the sequence's first run
+          // instead (always inside q) and are zeroed below.
+          const bool in = i < octs && g < G;
+          raw[u] = *reinterpret_cast<const u32x4*>(qseq + (in ? ((h0 + hs) * G + g) * D + 8 * jp : 0));
+          if (!in) raw[u] = u32x4{0u, 0u, 0u, 0u};
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < kStageLoads; ++u) {
+          const int i = i0 + u * kScoreThreads;
+          if (i < octs) {
+            const int hs = i / (gq / 2), rem = i - hs * (gq / 2), g = rem / (Q4 / 2), jp = rem - g * (Q4 / 2);
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+              const int j = 2 * jp + half;
+              const uint32_t w0 = raw[u][2 * half], w1 = raw[u][2 * half + 1];
+              const uint32_t b[4] = {w0 & 0xFFFFu, w0 >> 16, w1 & 0xFFFFu, w1 >> 16};
+              float4 qp, qn;
+              float* pp = &qp.x;
+              float* pn = &qn.x;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float qf = __uint_as_float(b[e] << 16);
+                pp[e] = (b[e] & 0x8000u) ? 0.f : qf;
+                pn[e] = (b[e] & 0x8000u) ? qf : 0.f;
+              }
+              float* dst = qs + ((hs * GP + g) * Q4 + (j ^ (hs & 7))) * 4;
+              *reinterpret_cast<float4*>(dst) = qp;
+              *reinterpret_cast<float4*>(dst + kScoreLdsFloats / 2) = qn;
             }
           }
         }
       }
-    }
+      __syncthreads();
+#pragma unroll 1
+      for (int j0 = 0; j0 < Q4; j0 += 2 * PF) {
+        load(vb, j0 + PF);
+        __builtin_amdgcn_sched_barrier(0);
+        sum(va, j0);
+        __builtin_amdgcn_sched_barrier(0);
+        load(va, j0 + 2 * PF);
+        __builtin_amdgcn_sched_barrier(0);
+        sum(vb, j0 + PF);
+        __builtin_amdgcn_sched_barrier(0);
+      }
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const int pg = pg0 + 64 * x + lane;
-      if (pg < np) {
-        uint32_t key = 0u;  // a block outside the pool scores lowest
-        if (blk[x] >= 0) {
-          float best = -__builtin_inff();
+      for (int k = 0; k < PP; ++k) {
+        if (live[k] && hh < hn) {
+          uint32_t key = 0u;  // a block outside the pool scores lowest
+          if (ok[k]) {
+            float best = -__builtin_inff();
 #pragma unroll
-          for (int j = 0; j < kMaxGroupQuest; ++j)
-            if (j < G) best = __builtin_fmaxf(best, acc[x][j]);
-          key = score_key(best);
+            for (int g = 0; g < GP; ++g)
+              if (g < G) best = __builtin_fmaxf(best, acc[k][g]);
+            key = score_key(best);
+          }
+          p.keys[((int64_t)s * Hkv + h) * p.max_blocks + pg0 + k * slots + slot] = key;
         }
-        p.keys[(int64_t)unit * p.max_blocks + pg] = key;
       }
     }
   }
@@ -336,15 +414,6 @@ __global__ __launch_bounds__(128) void page_score_kernel(const SelectParams p) {
 __device__ __forceinline__ int wave_sum(int v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-
-__device__ __forceinline__ int wave_incl_sum(int v, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(v, o, 64);
-    if (lane >= o) v += u;
-  }
   return v;
 }
 
@@ -701,16 +770,45 @@ hipError_t launch_summary_build(const SummaryParams& p, bool fp8, hipStream_t st
   return hipGetLastError();
 }
 
-hipError_t launch_page_select(const SelectParams& p, hipStream_t stream) {
-  const int64_t units = (int64_t)p.num_seqs * p.num_kv_heads;
+template <int D>
+void launch_score(const SelectParams& p, int gp, dim3 grid, hipStream_t stream) {
+  switch (gp) {
+    case 1: hipLaunchKernelGGL((page_score_kernel<D, 1>), grid, dim3(kScoreThreads), 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((page_score_kernel<D, 2>), grid, dim3(kScoreThreads), 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((page_score_kernel<D, 4>), grid, dim3(kScoreThreads), 0, stream, p); break;
+    case 8: hipLaunchKernelGGL((page_score_kernel<D, 8>), grid, dim3(kScoreThreads), 0, stream, p); break;
+    default: hipLaunchKernelGGL((page_score_kernel<D, 16>), grid, dim3(kScoreThreads), 0, stream, p); break;
+  }
+}
+
+hipError_t launch_page_select(const SelectParams& p_in, hipStream_t stream) {
+  const int64_t units = (int64_t)p_in.num_seqs * p_in.num_kv_heads;
   if (units == 0) return hipSuccess;
-  int64_t groups = units * p.chunks;
-  if (groups > kScoreGrid) groups = kScoreGrid;
-  const dim3 grid((unsigned)groups);
-  if (p.head_dim == 128)
-    hipLaunchKernelGGL(page_score_kernel<128>, grid, dim3(128), 0, stream, p);
-  else
-    hipLaunchKernelGGL(page_score_kernel<64>, grid, dim3(128), 0, stream, p);
+  SelectParams p = p_in;
+  // Query heads per group padded to a power of two; KV heads whose queries
+  // fit the 64 KiB of LDS at once (and a page's heads fit a wavefront).
+  int gp = 1;
+  while (gp < p.group) gp *= 2;
+  int hs = kScoreLdsFloats / (2 * gp * p.head_dim);   // q+ and q- of hs KV heads
+  if (hs > 64) hs = 64;
+  if (hs > p.num_kv_heads) hs = p.num_kv_heads;
+  p.slice_heads = hs;
+  p.item_pages = kScoreWaves * (64 / hs) * kScorePages;
+  // Two workgroups per CU (their LDS fills 128 KiB of the 160); no more than
+  // the items there can be.
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return hipErrorInvalidDevice;
+  const int64_t most = (int64_t)p.num_seqs * ((p.max_blocks + p.item_pages - 1) / p.item_pages);
+  int64_t groups = 2 * (int64_t)cus;
+  if (groups > most) groups = most;
+  if (groups > 0) {
+    const dim3 grid((unsigned)groups);
+    if (p.head_dim == 128)
+      launch_score<128>(p, gp, grid, stream);
+    else
+      launch_score<64>(p, gp, grid, stream);
+  }
   // Wide tables: a 1,024-thread workgroup per unit (fewer keys per thread).
   if (p.max_blocks > 2048)
     hipLaunchKernelGGL(page_select_kernel<1024>, dim3((unsigned)units), dim3(1024), 0, stream, p);

@@ -185,6 +185,18 @@ def test_quest_validation():
         assert fn(ctypes.byref(d), 2, FAKE, 0, None, None) == OK
         assert fn(ctypes.byref(d), 2, None, 4, FAKE, None) == NULL
     assert lib.pa_quest_update(ctypes.byref(d), 2, FAKE, None, 4, FAKE, None) == NULL
+    # the write that keeps the summaries: pa_cache_write's checks, and a summary array
+    qcw = lambda dd, T=4, summ=FAKE: lib.pa_quest_cache_write(ctypes.byref(dd) if dd else None, FAKE, FAKE, FAKE,
+                                                               T, FAKE, FAKE, summ, None)
+    qcw8 = lambda dd, T=4, summ=FAKE, ks=1.0: lib.pa_quest_cache_write_fp8(
+        ctypes.byref(dd) if dd else None, FAKE, FAKE, FAKE, T, FAKE, FAKE, ks, 1.0, summ, None)
+    for fn in (qcw, qcw8):
+        assert fn(None) == NULL
+        assert fn(d, summ=None) == NULL
+        assert fn(d, T=0, summ=None) == OK
+        assert fn(d, T=-1) == SHAPE
+        assert fn(desc(d=96)) == UNSUP
+    assert qcw8(d, ks=0.0) == SHAPE
     # selection: (desc, q, S, Hq, summaries, bt, maxb, lens, budget, sel, sel_lens, ws, ws_bytes, stream)
     ws_need = lib.pa_quest_select_workspace_size(3, 2, 8)
     assert ws_need == 256 and lib.pa_quest_select_workspace_size(-1, 2, 8) == 0

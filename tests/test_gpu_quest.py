@@ -23,8 +23,12 @@ def bf16_bits(x):
 
 
 def words_to_values(words):
-    """Summary words (int32 device tensor) -> (min, max) float64 arrays."""
+    """Summary words (int32 device tensor, [blocks, D / 4, Hkv, 4] as
+    include/pa_quest.h lays them out) -> (min, max) float64 arrays
+    [blocks, Hkv, D], the oracle's order."""
     u = words.cpu().numpy().view(np.uint32)
+    nb, q4, hkv, _ = u.shape
+    u = u.transpose(0, 2, 1, 3).reshape(nb, hkv, 4 * q4)
     return (paged.bf16_bits_to_f64((u & 0xFFFF).astype(np.uint16)),
             paged.bf16_bits_to_f64((u >> 16).astype(np.uint16)))
 
@@ -144,6 +148,91 @@ def test_summaries_kept_by_the_writes(kv_dtype):
         torch.cuda.synchronize()
         gm, gx = words_to_values(summ)
         assert np.array_equal(gm, mn) and np.array_equal(gx, mx), step
+
+
+@pytest.mark.parametrize("kv_dtype,block_size", [("bf16", 16), ("fp8", 16), ("bf16", 48)])
+def test_summaries_kept_by_the_fused_write(kv_dtype, block_size):
+    """pa_quest_cache_write(_fp8): sequences start with a prompt (several
+    tokens per block: pa_cache_write + pa_quest_update), then grow by one
+    token per step through the fused write, crossing block boundaries (a
+    token at offset 0 restarts its block's summary), while others end and
+    their blocks are reused; padding and out-of-pool slots are mixed in.
+    After every step the caches equal the oracle's write bit for bit and the
+    summaries equal the oracle's write-maintained ones value for value."""
+    rng = np.random.default_rng(3)
+    BS, D, Hkv = block_size, 128, 4
+    g = paged.Geom(num_blocks=40, block_size=BS, num_kv_heads=Hkv, head_dim=D, kv_dtype=kv_dtype)
+    ks, vs = np.float32(2.0 / 448), np.float32(1.5 / 448)
+    if kv_dtype == "bf16":
+        kc0 = bf16_bits(rng.standard_normal(g.cache_elems) * 5)
+        kc = torch.from_numpy(kc0.view(np.int16).copy()).view(torch.bfloat16).cuda()
+    else:
+        kc0 = rng.integers(0, 126, g.cache_elems).astype(np.uint8)
+        kc = torch.from_numpy(kc0.copy()).cuda()
+    vc = torch.zeros_like(kc)
+    k_ref, v_ref = kc0.copy(), host_bits(vc).copy()
+    summ = pa.quest_summaries(kc, num_kv_heads=Hkv, head_dim=D, block_size=BS)
+    mn, mx = Q.empty_summaries(g)
+    free, seqs = list(range(g.num_blocks)), {}
+    to_dev = lambda b: torch.from_numpy(b.view(np.int16).copy()).view(torch.bfloat16).cuda()
+    fused_steps = 0
+    for step in range(60):
+        prompt = not seqs or rng.random() < 0.15
+        slots = []
+        if prompt:
+            L = int(rng.integers(1, 3 * BS))
+            nb = -(-L // BS)
+            if nb > len(free):
+                continue
+            table = [free.pop(0) for _ in range(nb)]
+            seqs[step] = [table, L]
+            slots = [table[i // BS] * BS + i % BS for i in range(L)]
+        elif rng.random() < 0.15:
+            s = list(seqs)[int(rng.integers(len(seqs)))]
+            free.extend(seqs.pop(s)[0])
+            continue
+        else:
+            for s, (table, L) in list(seqs.items()):
+                if L % BS == 0:
+                    if not free:
+                        continue
+                    table.append(free.pop(0))
+                slots.append(table[L // BS] * BS + L % BS)
+                seqs[s][1] = L + 1
+            for _ in range(int(rng.integers(0, 3))):
+                slots.insert(int(rng.integers(len(slots) + 1)), int(rng.choice([-1, g.num_blocks * BS])))
+        if not slots:
+            continue
+        T = len(slots)
+        kn = bf16_bits(rng.standard_normal((T, Hkv, D)) * rng.uniform(0.2, 2))
+        vn = bf16_bits(rng.standard_normal((T, Hkv, D)))
+        if rng.random() < 0.1:
+            kn[0, 0, :7] = 0x7FC0                    # NaN keys: ignored by the summaries
+        sd = torch.tensor(slots, dtype=torch.int64, device="cuda")
+        if kv_dtype == "bf16":
+            paged.cache_write_bf16(g, kn, vn, slots, k_ref, v_ref)
+        else:
+            paged.cache_write_fp8(g, kn, vn, slots, k_ref, v_ref, ks, vs)
+        if prompt:
+            if kv_dtype == "bf16":
+                pa.pa_cache_write(to_dev(kn), to_dev(vn), sd, kc, vc, block_size=BS)
+            else:
+                pa.pa_cache_write_fp8(to_dev(kn), to_dev(vn), sd, kc, vc, float(ks), float(vs), block_size=BS)
+            pa.pa_quest_update(kc, sd, summ, num_kv_heads=Hkv, head_dim=D, block_size=BS)
+        else:
+            fused_steps += 1
+            if kv_dtype == "bf16":
+                pa.pa_quest_cache_write(to_dev(kn), to_dev(vn), sd, kc, vc, summ, block_size=BS)
+            else:
+                pa.pa_quest_cache_write_fp8(to_dev(kn), to_dev(vn), sd, kc, vc, float(ks), float(vs), summ,
+                                            block_size=BS)
+        Q.update_summaries(g, k_ref, slots, mn, mx)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(kc), k_ref), f"step {step}: K cache"
+        assert np.array_equal(host_bits(vc), v_ref), f"step {step}: V cache"
+        gm, gx = words_to_values(summ)
+        assert np.array_equal(gm, mn) and np.array_equal(gx, mx), f"step {step}: summaries"
+    assert fused_steps > 20
 
 
 @pytest.mark.parametrize("kv_dtype,block_size,head_dim", [("bf16", 16, 128), ("fp8", 32, 64),
