@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 3
+#define PA_ABI_VERSION 4
 
 typedef enum pa_status {
   PA_OK = 0,
@@ -272,6 +272,47 @@ pa_status pa_decode_append_fp8(const pa_cache_desc* cache, const void* q, const 
                                int32_t window, float scale, float k_scale, float v_scale,
                                float* out, int32_t partition_tokens, void* workspace,
                                size_t workspace_bytes, void* stream);
+
+/* Local-layer decode from ring tables ("KV Cache Engineering for LLM
+ * Serving", section 3, sliding windows: a local layer keeps only its most
+ * recent `window` positions, each new one displacing the oldest).  Each
+ * sequence's table row is a ring of ring_entries block ids: logical block
+ * b of the sequence (positions b * block_size ..) is
+ * ring_tables[s][b % ring_entries], so the row stays ring_entries wide
+ * however long the sequence grows, and the block that falls out of the
+ * window is the one its next block reuses (pa_bm_add_ring_sequence keeps
+ * such rows).  Otherwise as pa_decode_window / pa_decode_window_fp8: each
+ * sequence attends to positions [max(0, L - window), L).
+ *   ring_tables   [num_seqs][ring_entries] int32; only the entries of the
+ *                 blocks holding a position of the window are read
+ *   ring_entries  >= ceil(window / block_size) + 1 (every block a window
+ *                 can span has its own entry), else PA_ERR_SHAPE
+ *   window        >= 1, else PA_ERR_SHAPE
+ *   seq_lens      any L >= 0 up to INT32_MAX - 16 (no table bound); larger
+ *                 or negative L gives NaN rows
+ *   k_new, v_new  both NULL: decode only, the caches are not written.  Both
+ *                 non-NULL ([num_seqs][num_kv_heads][head_dim] bf16): fused
+ *                 append as pa_decode_append, the new token (position L - 1)
+ *                 going to offset (L - 1) % block_size of block
+ *                 ring_tables[s][((L - 1) / block_size) % ring_entries].  One
+ *                 NULL and one not: PA_ERR_NULL.
+ *   workspace     as for pa_decode, sized by pa_decode_workspace_size with
+ *                 max_blocks_per_seq = ring_entries.
+ * The output is pa_decode_window's on the linear table the ring stands for,
+ * bit for bit with the same partition_tokens and workspace size.            */
+pa_status pa_decode_ring(const pa_cache_desc* cache, const void* q, const void* k_new,
+                         const void* v_new, int32_t num_seqs, int32_t num_q_heads, void* k_cache,
+                         void* v_cache, const int32_t* ring_tables, int32_t ring_entries,
+                         const int32_t* seq_lens, int32_t window, float scale, float* out,
+                         int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                         void* stream);
+pa_status pa_decode_ring_fp8(const pa_cache_desc* cache, const void* q, const void* k_new,
+                             const void* v_new, int32_t num_seqs, int32_t num_q_heads,
+                             void* k_cache, void* v_cache, const int32_t* ring_tables,
+                             int32_t ring_entries, const int32_t* seq_lens, int32_t window,
+                             float scale, float k_scale, float v_scale, float* out,
+                             int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                             void* stream);
 
 /* Human-readable name of a status code (static string, never NULL).        */
 const char* pa_status_string(pa_status status);

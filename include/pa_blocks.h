@@ -57,6 +57,37 @@ void pa_bm_destroy(pa_block_manager* bm);
 pa_status pa_bm_add_sequence(pa_block_manager* bm, int64_t seq, const int32_t* tokens,
                              int32_t n, uint64_t model_key, int32_t* reused);
 
+/* A local layer's sequence with a ring table ("KV Cache Engineering for LLM
+ * Serving", section 3, sliding windows: a local layer keeps its most recent
+ * `window` positions only, each new one displacing the oldest).  The table
+ * has *ring_entries = ceil(window / block_size) + 1 entries, and logical
+ * block b (positions b * block_size ..) is entry b % ring_entries, so a
+ * window's blocks never share an entry.  The sequence starts with n tokens
+ * (n >= 0, a prompt whose K/V the caller writes to the slots pa_bm_slots
+ * gives): blocks are taken for its last min(ceil(n / block_size),
+ * ring_entries) logical blocks, the other entries are -1.  Afterwards
+ * pa_bm_append_token (its `token` argument is not kept) fills the ring:
+ * where a new block starts, the entry's old block, which has left the
+ * window, is written over in place when no other sequence holds it, so a
+ * full ring takes no more blocks from the pool; a block a fork still shares
+ * is let go and a fresh one taken, and a shared partial block is copied
+ * first as for plain tables.  Ring sequences keep no token ids and share no
+ * prefix blocks.  Use pa_decode_ring on their tables; pa_bm_batch needs
+ * max_blocks == ring_entries for them.  window >= 1, else PA_ERR_SHAPE;
+ * PA_ERR_NOT_FOUND if seq exists; PA_ERR_NO_BLOCKS, with nothing changed,
+ * if the free list is too short.                                            */
+pa_status pa_bm_add_ring_sequence(pa_block_manager* bm, int64_t seq, int32_t n, int32_t window,
+                                  int32_t* ring_entries);
+
+/* Slots of positions first .. first + count - 1 of `seq` (plain or ring):
+ * slots[i] = block * block_size + offset of position first + i, or -1 when
+ * the sequence holds no block for it any more (a trimmed entry, or a ring
+ * entry that has moved on).  PA_ERR_SHAPE unless 0 <= first, 0 <= count and
+ * first + count <= the sequence's token count; PA_ERR_SWAPPED while the
+ * sequence is swapped out.                                                  */
+pa_status pa_bm_slots(const pa_block_manager* bm, int64_t seq, int32_t first, int32_t count,
+                      int64_t* slots);
+
 /* Sequence `child` shares every block of `parent` (reference counts + 1),
  * with the same tokens and model key.  PA_ERR_NOT_FOUND if parent is unknown
  * or child exists.                                                           */
@@ -82,7 +113,8 @@ pa_status pa_bm_free_sequence(pa_block_manager* bm, int64_t seq);
  * tokens (keep_tokens >= 1) each lose one reference, and their table entries
  * become -1; the table keeps its length, so later positions keep their
  * logical blocks.  pa_decode_window with window <= keep_tokens never reads
- * the released entries.  *released (may be NULL) receives the count.        */
+ * the released entries.  *released (may be NULL) receives the count.  On a
+ * ring sequence the same holds for the blocks its ring still lists.        */
 pa_status pa_bm_trim(pa_block_manager* bm, int64_t seq, int32_t keep_tokens, int32_t* released);
 
 /* Swap-out bookkeeping: the blocks of `seq` that no other sequence holds
@@ -130,7 +162,8 @@ pa_status pa_bm_stats(const pa_block_manager* bm, int64_t* hits, int64_t* misses
 /* Host arrays for one decode batch of the sequences seqs[0..n):
  * block_tables[n][max_blocks] (entries past a sequence's blocks set to -1)
  * and seq_lens[n] (token counts).  PA_ERR_SHAPE if a sequence has more than
- * max_blocks blocks.                                                         */
+ * max_blocks blocks, or is a ring sequence with ring_entries != max_blocks
+ * (its row must be the ring itself).                                        */
 pa_status pa_bm_batch(const pa_block_manager* bm, const int64_t* seqs, int32_t n,
                       int32_t max_blocks, int32_t* block_tables, int32_t* seq_lens);
 

@@ -18,7 +18,11 @@ What a block manager does, from the pages:
   different K and V under different weights (rajatmohan.com, same section).
 * A local (sliding-window) layer keeps only its most recent positions, so the
   blocks that hold nothing newer can go back to the pool ("KV Cache
-  Engineering for LLM Serving", section 3): ``trim``.
+  Engineering for LLM Serving", section 3): ``trim``.  Such a layer's window
+  works as a ring, each new entry displacing the oldest (same section):
+  ``add_ring_sequence`` gives a sequence a table of ceil(W / block_size) + 1
+  entries, logical block b at entry b % entries, and a new block reuses the
+  block its entry held, which has just left the window.
 * Blocks a paused sequence does not need can move to host memory and come
   back when it resumes ("KV Cache Engineering for LLM Serving", section 12,
   Cache Offloading); the blocks of a shared prefix stay on the GPU ("Taming
@@ -56,7 +60,7 @@ class BlockManager:
         self.ref = [0] * num_blocks
         self.key_block = {}                   # prefix key -> block
         self.block_key = {}                   # block -> prefix key it is stored under
-        self.seqs = {}                        # seq id -> {"tokens", "table", "model"}
+        self.seqs = {}                        # seq id -> {"tokens", "table", "model", "swapped", "ring"}
         self.hits = 0
         self.misses = 0
 
@@ -114,8 +118,32 @@ class BlockManager:
             table.append(self._take())
         self.hits += reused
         self.misses += len(table) - reused
-        self.seqs[seq] = {"tokens": list(tokens), "table": table, "model": model, "swapped": False}
+        self.seqs[seq] = {"tokens": list(tokens), "table": table, "model": model, "swapped": False, "ring": 0}
         return reused
+
+    def add_ring_sequence(self, seq, n, window):
+        """A local layer's sequence of n tokens whose table is a ring of
+        E = ceil(window / block_size) + 1 entries: logical block b lives at
+        entry b % E, so the blocks of any ``window`` consecutive positions
+        have distinct entries.  Blocks are taken for the last min(blocks, E)
+        logical blocks of the n tokens; other entries are -1.  No prefix
+        keys: a ring block is rewritten as the window moves.  Returns E."""
+        if seq in self.seqs:
+            raise KeyError(seq)
+        if window < 1:
+            raise ValueError("window must be >= 1")
+        bs = self.block_size
+        E = -(-window // bs) + 1
+        nb = -(-n // bs)
+        held = min(nb, E)
+        if held > len(self.free):
+            raise OutOfBlocks(f"need {held} blocks, {len(self.free)} free")
+        table = [-1] * E
+        for b in range(nb - held, nb):
+            table[b % E] = self._take()
+        self.misses += held
+        self.seqs[seq] = {"tokens": [0] * n, "table": table, "model": None, "swapped": False, "ring": E}
+        return E
 
     def fork(self, parent, child):
         """``child`` shares every block of ``parent``, partial last block
@@ -129,7 +157,7 @@ class BlockManager:
             if b >= 0:
                 self.ref[b] += 1
         self.seqs[child] = {"tokens": list(p["tokens"]), "table": list(p["table"]),
-                            "model": p["model"], "swapped": False}
+                            "model": p["model"], "swapped": False, "ring": p["ring"]}
 
     def append_token(self, seq, token):
         """One generated token.  Returns (slot, copy_src, copy_dst): the slot
@@ -141,6 +169,8 @@ class BlockManager:
         bs = self.block_size
         pos = len(s["tokens"])
         src = dst = -1
+        if s["ring"]:
+            return self._append_ring(s, pos, token)
         if (pos % bs == 0 or self.ref[s["table"][-1]] > 1) and not self.free:
             raise OutOfBlocks("no free block")
         if pos % bs == 0:
@@ -158,6 +188,54 @@ class BlockManager:
             self._store(blk, self._key(s["model"], s["tokens"], pos + 1))
         return blk * bs + pos % bs, src, dst
 
+    def _append_ring(self, s, pos, token):
+        """append_token on a ring table.  The new position's entry is
+        e = (pos // block_size) % E.  Starting a block: the entry's old block
+        has left the window, so it is written over in place if this
+        sequence alone holds it; if a fork still shares it, or the entry is
+        empty, a fresh block is taken (the shared one loses a reference).
+        Inside a block: a shared block is copied first (copy-on-write)."""
+        bs = self.block_size
+        e = (pos // bs) % s["ring"]
+        old = s["table"][e]
+        fresh = old < 0 or (pos % bs == 0 and self.ref[old] > 1)
+        copy = not fresh and pos % bs != 0 and self.ref[old] > 1
+        if (fresh or copy) and not self.free:
+            raise OutOfBlocks("no free block")
+        src = dst = -1
+        if fresh:
+            if old >= 0:
+                self._release(old)
+            s["table"][e] = self._take()
+        elif copy:
+            src, dst = old, self._take()
+            self.ref[old] -= 1
+            s["table"][e] = dst
+        s["tokens"].append(token)
+        return s["table"][e] * bs + pos % bs, src, dst
+
+    def slots(self, seq, first, count):
+        """Slots of positions first .. first + count - 1 (block * block_size
+        + offset), -1 where no table entry holds the position's block any
+        more (released by a trim, or a ring entry that has moved on)."""
+        s = self.seqs[seq]
+        if s["swapped"]:
+            raise Swapped(seq)
+        n = len(s["tokens"])
+        if first < 0 or count < 0 or first + count > n:
+            raise ValueError("positions outside the sequence")
+        bs = self.block_size
+        nb = -(-n // bs)
+        out = []
+        for pos in range(first, first + count):
+            b = pos // bs
+            if s["ring"]:
+                blk = s["table"][b % s["ring"]] if b >= nb - s["ring"] else -1
+            else:
+                blk = s["table"][b]
+            out.append(blk * bs + pos % bs if blk >= 0 else -1)
+        return out
+
     def trim(self, seq, keep):
         """Sliding window: release the blocks of ``seq`` that hold only
         positions before its last ``keep`` tokens (keep >= 1); their table
@@ -170,8 +248,11 @@ class BlockManager:
             raise Swapped(seq)
         bs = self.block_size
         first = max(len(s["tokens"]) - keep, 0) // bs   # first block with a kept position
+        E = s["ring"]
+        start = max(-(-len(s["tokens"]) // bs) - E, 0) if E else 0   # oldest block a ring still lists
         n = 0
-        for i in range(first):
+        for b in range(start, first):
+            i = b % E if E else b
             if s["table"][i] >= 0:
                 self._release(s["table"][i])
                 s["table"][i] = -1
@@ -209,7 +290,7 @@ class BlockManager:
             b = self._take()
             s["table"][i] = b
             out.append(b)
-            if (i + 1) * bs <= len(s["tokens"]):
+            if not s["ring"] and (i + 1) * bs <= len(s["tokens"]):
                 self._store(b, self._key(s["model"], s["tokens"], (i + 1) * bs))
         s["swapped"] = False
         return out

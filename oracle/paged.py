@@ -194,31 +194,37 @@ def window_positions(L, window):
 
 
 def decode(g, q_bits, k_cache, v_cache, block_tables, seq_lens, scale,
-           k_scale=1.0, v_scale=1.0, seqs=None, heads=None, window=0):
+           k_scale=1.0, v_scale=1.0, seqs=None, heads=None, window=0, ring=False):
     """Paged decode: out[s, i, :] = softmax(scale * q[s, i] K_s^T) V_s with
     K_s, V_s gathered for KV head i // (Hq / Hkv); with a window, K_s and V_s
     are the rows of ``window_positions(L, window)`` only.
 
     q_bits: [S, Hq, D] bf16 bit patterns.  Returns float64 [S, Hq, D]; when
     ``seqs`` (and optionally ``heads``, a list of KV heads) restrict the work,
-    rows that were not computed are NaN.  With a window, block-table entries
-    of blocks holding no kept position are not read."""
+    rows that were not computed are NaN.  Only the blocks holding a kept
+    position are looked up.  With ``ring`` each table row is a ring of
+    len(row) entries (a local layer that keeps only its window, section 3 of
+    "KV Cache Engineering for LLM Serving"): logical block b of the sequence
+    is row[b % len(row)]."""
     q = bf16_bits_to_f64(q_bits)
     S, Hq, D = q.shape
     G = Hq // g.num_kv_heads
+    bs = g.block_size
     out = np.full((S, Hq, D), np.nan)
     seqs = range(S) if seqs is None else seqs
     heads = range(g.num_kv_heads) if heads is None else heads
     for s in seqs:
         L = max(int(seq_lens[s]), 0)
-        keep = window_positions(L, window)
-        first_block = keep[0] // g.block_size if keep else 0
-        row = np.asarray(block_tables[s]).copy()
-        row[:first_block] = row[first_block] if keep else 0   # entries never read
+        keep = np.asarray(window_positions(L, window), dtype=np.int64)
+        first_block = int(keep[0]) // bs if keep.size else 0
+        row = np.asarray(block_tables[s])
+        logical = np.arange(first_block, -(-L // bs))
+        span = row[logical % row.size] if ring else row[logical]
+        base = first_block * bs
         for h in heads:
-            K, V = gather(g, k_cache, v_cache, row, L, h, k_scale, v_scale)
-            out[s, h * G:(h + 1) * G] = softmax_attention(q[s, h * G:(h + 1) * G], K[keep], V[keep],
-                                                          scale)
+            K, V = gather(g, k_cache, v_cache, span, L - base, h, k_scale, v_scale)
+            out[s, h * G:(h + 1) * G] = softmax_attention(q[s, h * G:(h + 1) * G], K[keep - base],
+                                                          V[keep - base], scale)
     return out
 
 

@@ -108,6 +108,11 @@ def _load():
                              i32),
         "pa_decode_append_fp8": ([dp, vp, vp, vp, i32, i32, vp, vp, vp, i32, vp, i32, f32, f32, f32, vp, i32,
                                   vp, sz, vp], i32),
+        "pa_decode_ring": ([dp, vp, vp, vp, i32, i32, vp, vp, vp, i32, vp, i32, f32, vp, i32, vp, sz, vp], i32),
+        "pa_decode_ring_fp8": ([dp, vp, vp, vp, i32, i32, vp, vp, vp, i32, vp, i32, f32, f32, f32, vp, i32,
+                                vp, sz, vp], i32),
+        "pa_bm_add_ring_sequence": ([vp, i64, i32, i32, ctypes.POINTER(i32)], i32),
+        "pa_bm_slots": ([vp, i64, i32, i32, ctypes.POINTER(i64)], i32),
         "pa_quest_clear": ([dp, vp, vp], i32),
         "pa_quest_update": ([dp, i32, vp, vp, i32, vp, vp], i32),
         "pa_quest_cache_write": ([dp, vp, vp, vp, i32, vp, vp, vp, vp], i32),
@@ -468,6 +473,23 @@ class BlockManager:
             self._h, seq, arr, len(tokens), model_key, ctypes.byref(reused)))
         return reused.value
 
+    def add_ring_sequence(self, seq, n, window):
+        """A local layer's sequence of n tokens with a ring table for a
+        window of `window` tokens; returns the ring's entry count."""
+        e = ctypes.c_int32()
+        _check("pa_bm_add_ring_sequence", _load().pa_bm_add_ring_sequence(
+            self._h, seq, int(n), int(window), ctypes.byref(e)))
+        return e.value
+
+    def slots(self, seq, first, count):
+        """numpy int64 slots of positions first .. first + count - 1 (-1
+        where the sequence holds no block for a position)."""
+        import numpy as np
+        out = np.empty(max(int(count), 1), dtype=np.int64)
+        _check("pa_bm_slots", _load().pa_bm_slots(
+            self._h, seq, int(first), int(count), out.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))))
+        return out[:int(count)]
+
     def fork(self, parent, child):
         _check("pa_bm_fork", _load().pa_bm_fork(self._h, parent, child))
 
@@ -564,14 +586,18 @@ def pa_decode_window_fp8(q, k_cache, v_cache, block_tables, seq_lens, window, sc
 
 
 def _decode_append(fp8, q, k_new, v_new, k_cache, v_cache, block_tables, seq_lens, scale, out,
-                   num_kv_heads, block_size, k_scale, v_scale, window, partition_tokens, workspace):
+                   num_kv_heads, block_size, k_scale, v_scale, window, partition_tokens, workspace,
+                   ring=False):
     dev = q.device
     if dev.type != "cuda":
         raise ValueError("pa_decode_append needs device tensors")
     _need(q, "q", torch.bfloat16, dev, 3)
     S, Hq, D = q.shape
-    _need(k_new, "k_new", torch.bfloat16, dev, shape=(S, num_kv_heads, D))
-    _need(v_new, "v_new", torch.bfloat16, dev, shape=(S, num_kv_heads, D))
+    if ring and (k_new is None) != (v_new is None):
+        raise ValueError("k_new and v_new go together")
+    if not ring or k_new is not None:
+        _need(k_new, "k_new", torch.bfloat16, dev, shape=(S, num_kv_heads, D))
+        _need(v_new, "v_new", torch.bfloat16, dev, shape=(S, num_kv_heads, D))
     cdt = torch.uint8 if fp8 else torch.bfloat16
     _need(k_cache, "k_cache", cdt, dev)
     _need(v_cache, "v_cache", cdt, dev, shape=tuple(k_cache.shape))
@@ -593,12 +619,14 @@ def _decode_append(fp8, q, k_new, v_new, k_cache, v_cache, block_tables, seq_len
                                           "no gfx950 device or invalid sizes")
             workspace = torch.zeros(max(int(need), 1), dtype=torch.uint8, device=dev)
         _need(workspace, "workspace", torch.uint8, dev)
-        args = [ctypes.byref(desc), _ptr(q), _ptr(k_new), _ptr(v_new), S, Hq, _ptr(k_cache), _ptr(v_cache),
+        kn = _ptr(k_new) if k_new is not None else None
+        vn = _ptr(v_new) if v_new is not None else None
+        args = [ctypes.byref(desc), _ptr(q), kn, vn, S, Hq, _ptr(k_cache), _ptr(v_cache),
                 _ptr(block_tables), maxb, _ptr(seq_lens), int(window), float(scale)]
         if fp8:
             args += [float(k_scale), float(v_scale)]
         args += [_ptr(out), int(partition_tokens), _ptr(workspace), workspace.numel(), _stream(q)]
-        name = "pa_decode_append" + ("_fp8" if fp8 else "")
+        name = ("pa_decode_ring" if ring else "pa_decode_append") + ("_fp8" if fp8 else "")
         st = getattr(L, name)(*args)
     _check(name, st)
     return out
@@ -621,6 +649,25 @@ def pa_decode_append_fp8(q, k_new, v_new, k_cache, v_cache, block_tables, seq_le
     codes of x / scale, as pa_cache_write_fp8 stores it."""
     return _decode_append(True, q, k_new, v_new, k_cache, v_cache, block_tables, seq_lens, scale, out,
                           num_kv_heads, block_size, k_scale, v_scale, window, partition_tokens, workspace)
+
+
+def pa_decode_ring(q, k_cache, v_cache, ring_tables, seq_lens, window, scale, out=None, *, num_kv_heads,
+                   block_size, k_new=None, v_new=None, partition_tokens=0, workspace=None):
+    """Local-layer decode from ring tables ([S, ring_entries] int32, logical
+    block b at entry b % ring_entries) over a bf16 cache; with k_new / v_new
+    the new tokens are written first in the same launch.  See pa_decode_ring
+    in include/pa.h."""
+    return _decode_append(False, q, k_new, v_new, k_cache, v_cache, ring_tables, seq_lens, scale, out,
+                          num_kv_heads, block_size, 1.0, 1.0, window, partition_tokens, workspace, ring=True)
+
+
+def pa_decode_ring_fp8(q, k_cache, v_cache, ring_tables, seq_lens, window, scale, k_scale, v_scale, out=None,
+                       *, num_kv_heads, block_size, k_new=None, v_new=None, partition_tokens=0,
+                       workspace=None):
+    """pa_decode_ring over an e4m3fn cache."""
+    return _decode_append(True, q, k_new, v_new, k_cache, v_cache, ring_tables, seq_lens, scale, out,
+                          num_kv_heads, block_size, k_scale, v_scale, window, partition_tokens, workspace,
+                          ring=True)
 
 
 # -- query-aware page selection (include/pa_quest.h) -------------------------

@@ -161,9 +161,13 @@ pa_status decode(const pa_cache_desc* cache, const void* q, int32_t num_seqs, in
                  float k_scale, float v_scale, bool fp8, float* out, int32_t partition_tokens,
                  void* workspace, size_t workspace_bytes, void* stream, int32_t seq_heads = 0,
                  float* lse = nullptr, bool append = false, const void* k_new = nullptr,
-                 const void* v_new = nullptr) {
+                 const void* v_new = nullptr, bool ring = false) {
   if (!cache) return PA_ERR_NULL;
   if (!isfinite(scale) || window < 0) return PA_ERR_SHAPE;
+  // Ring rows must hold every block a window can span: ceil(W / BS) + 1.
+  if (ring && (window < 1 || cache->block_size < 1 ||
+               (int64_t)max_blocks_per_seq < ((int64_t)window + cache->block_size - 1) / cache->block_size + 1))
+    return PA_ERR_SHAPE;
   if (fp8 && (!good_scale(k_scale) || !good_scale(v_scale))) return PA_ERR_SHAPE;
   int64_t num_waves = 0;
   int32_t chunk_fixed = 0;
@@ -210,6 +214,7 @@ pa_status decode(const pa_cache_desc* cache, const void* q, int32_t num_seqs, in
   p.chunk_min = kChunkMinAuto;
   p.chunk_fixed = chunk_fixed;
   p.window = window;
+  p.ring = ring ? 1 : 0;
   p.subs = cache->block_size / pa::kSub;
   p.subs_magic = p.subs > 1 ? (uint32_t)((((uint64_t)1 << 32) + p.subs - 1) / p.subs) : 0u;
   const int32_t heads_per_block = seq_heads > 1 ? seq_heads : cache->num_kv_heads;
@@ -446,6 +451,31 @@ pa_status pa_decode_append_fp8(const pa_cache_desc* cache, const void* q, const 
                 max_blocks_per_seq, seq_lens, window, scale, k_scale, v_scale, true, out,
                 partition_tokens, workspace, workspace_bytes, stream, 0, nullptr, true, k_new,
                 v_new);
+}
+
+pa_status pa_decode_ring(const pa_cache_desc* cache, const void* q, const void* k_new,
+                         const void* v_new, int32_t num_seqs, int32_t num_q_heads, void* k_cache,
+                         void* v_cache, const int32_t* ring_tables, int32_t ring_entries,
+                         const int32_t* seq_lens, int32_t window, float scale, float* out,
+                         int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  if ((k_new == nullptr) != (v_new == nullptr)) return PA_ERR_NULL;
+  return decode(cache, q, num_seqs, num_q_heads, k_cache, v_cache, ring_tables, ring_entries,
+                seq_lens, window, scale, 1.f, 1.f, false, out, partition_tokens, workspace,
+                workspace_bytes, stream, 0, nullptr, k_new != nullptr, k_new, v_new, true);
+}
+
+pa_status pa_decode_ring_fp8(const pa_cache_desc* cache, const void* q, const void* k_new,
+                             const void* v_new, int32_t num_seqs, int32_t num_q_heads,
+                             void* k_cache, void* v_cache, const int32_t* ring_tables,
+                             int32_t ring_entries, const int32_t* seq_lens, int32_t window,
+                             float scale, float k_scale, float v_scale, float* out,
+                             int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  if ((k_new == nullptr) != (v_new == nullptr)) return PA_ERR_NULL;
+  return decode(cache, q, num_seqs, num_q_heads, k_cache, v_cache, ring_tables, ring_entries,
+                seq_lens, window, scale, k_scale, v_scale, true, out, partition_tokens, workspace,
+                workspace_bytes, stream, 0, nullptr, k_new != nullptr, k_new, v_new, true);
 }
 
 pa_status pa_copy_blocks(const pa_cache_desc* cache, int32_t elem_bytes, void* k_cache,

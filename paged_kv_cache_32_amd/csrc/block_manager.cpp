@@ -8,6 +8,16 @@
 // reference count when another sequence has that exact prefix; a write into
 // a block someone else holds goes to a private copy first.
 //
+// A local (sliding-window) layer's sequence can instead keep a ring table
+// ("KV Cache Engineering for LLM Serving", section 3, sliding windows): a
+// fixed number of entries, ceil(W / block_size) + 1 for a window of W
+// tokens, logical block b at entry b % entries.  When a new block starts,
+// the entry it lands on holds the block that has just left the window, and
+// that block is written over in place: the sequence holds at most `entries`
+// blocks however long it grows, and takes none from the pool once its ring
+// is full.  Ring sequences keep no token ids and take part in no prefix
+// sharing, since their blocks are rewritten as the window moves on.
+//
 // Prefix keys are interned: a full-block prefix is the pair (id of the prefix
 // one block shorter, the block's tokens) under a model key, looked up in a
 // hash map with exact key comparison, so equal prefixes always get the same
@@ -65,11 +75,23 @@ constexpr int32_t kReleased = -1;  // table entry released by a sliding-window t
 constexpr int32_t kSwapped = -2;   // table entry whose block was swapped out
 
 struct Sequence {
-  std::vector<int32_t> tokens;
-  std::vector<int32_t> table;       // physical block of each logical block (or kReleased / kSwapped)
-  std::vector<uint64_t> prefixes;   // prefix id of each full block
-  uint64_t model;
+  std::vector<int32_t> tokens;      // token ids (plain sequences only)
+  std::vector<int32_t> table;       // physical block of each logical block (or kReleased / kSwapped);
+                                    // ring sequences: of logical block b at entry b % ring
+  std::vector<uint64_t> prefixes;   // prefix id of each full block (plain sequences only)
+  uint64_t model = 0;
+  int64_t len = 0;                  // tokens held
+  int32_t ring = 0;                 // ring entries, 0 for a plain table
   bool swapped = false;
+
+  // Table entry of the block holding position pos, or -1 when no entry
+  // holds it any more (a ring whose entry has moved on).
+  int64_t entry(int64_t pos, int32_t bs) const {
+    const int64_t b = pos / bs;
+    if (!ring) return b;
+    const int64_t nb = (len + bs - 1) / bs;
+    return b < nb - ring ? -1 : b % ring;
+  }
 };
 
 }  // namespace
@@ -199,6 +221,7 @@ pa_status pa_bm_add_sequence(pa_block_manager* bm, int64_t seq, const int32_t* t
   Sequence s;
   s.model = model_key;
   s.tokens.assign(tokens, tokens + n);
+  s.len = n;
   int32_t hit_count = 0;
   uint64_t parent = kRoot;
   for (int32_t i = 0; i < full; ++i) {
@@ -225,6 +248,46 @@ pa_status pa_bm_add_sequence(pa_block_manager* bm, int64_t seq, const int32_t* t
   return PA_OK;
 }
 
+pa_status pa_bm_add_ring_sequence(pa_block_manager* bm, int64_t seq, int32_t n, int32_t window,
+                                  int32_t* ring_entries) {
+  if (!bm) return PA_ERR_NULL;
+  if (n < 0 || window < 1 || n >= INT32_MAX - 16) return PA_ERR_SHAPE;
+  if (bm->seqs.count(seq)) return PA_ERR_NOT_FOUND;
+  const int32_t bs = bm->block_size;
+  const int64_t ring = ((int64_t)window + bs - 1) / bs + 1;
+  if (ring > INT32_MAX / 2) return PA_ERR_SHAPE;
+  const int64_t nb = ((int64_t)n + bs - 1) / bs;
+  const int64_t held = std::min<int64_t>(nb, ring);
+  if (held > (int64_t)bm->free_list.size()) return PA_ERR_NO_BLOCKS;
+  Sequence s;
+  s.len = n;
+  s.ring = (int32_t)ring;
+  s.table.assign((size_t)ring, kReleased);
+  for (int64_t b = nb - held; b < nb; ++b) s.table[b % ring] = bm->take();
+  bm->misses += held;
+  bm->seqs.emplace(seq, std::move(s));
+  if (ring_entries) *ring_entries = (int32_t)ring;
+  return PA_OK;
+}
+
+pa_status pa_bm_slots(const pa_block_manager* bm, int64_t seq, int32_t first, int32_t count,
+                      int64_t* slots) {
+  if (!bm || (!slots && count > 0)) return PA_ERR_NULL;
+  auto it = bm->seqs.find(seq);
+  if (it == bm->seqs.end()) return PA_ERR_NOT_FOUND;
+  const Sequence& s = it->second;
+  if (s.swapped) return PA_ERR_SWAPPED;
+  if (first < 0 || count < 0 || (int64_t)first + count > s.len) return PA_ERR_SHAPE;
+  const int32_t bs = bm->block_size;
+  for (int32_t i = 0; i < count; ++i) {
+    const int64_t pos = (int64_t)first + i;
+    const int64_t e = s.entry(pos, bs);
+    const int32_t b = e < 0 ? -1 : s.table[e];
+    slots[i] = b < 0 ? -1 : (int64_t)b * bs + pos % bs;
+  }
+  return PA_OK;
+}
+
 pa_status pa_bm_fork(pa_block_manager* bm, int64_t parent, int64_t child) {
   if (!bm) return PA_ERR_NULL;
   auto it = bm->seqs.find(parent);
@@ -246,7 +309,34 @@ pa_status pa_bm_append_token(pa_block_manager* bm, int64_t seq, int32_t token, i
   Sequence& s = it->second;
   if (s.swapped) return PA_ERR_SWAPPED;
   const int32_t bs = bm->block_size;
-  const int64_t pos = (int64_t)s.tokens.size();
+  const int64_t pos = s.len;
+  if (pos >= INT32_MAX - 16) return PA_ERR_SHAPE;
+  if (s.ring) {
+    // The entry of the new position's block.  A new block reuses the
+    // entry's old block in place when only this sequence holds it; a shared
+    // one (after a fork) is let go and a fresh block taken.  Inside a block,
+    // a shared block is copied first, as for plain tables.
+    const int64_t e = (pos / bs) % s.ring;
+    const int32_t old = s.table[e];
+    const bool fresh = old < 0 || (pos % bs == 0 && bm->ref[old] > 1);
+    const bool copy = !fresh && pos % bs != 0 && bm->ref[old] > 1;
+    if ((fresh || copy) && bm->free_list.empty()) return PA_ERR_NO_BLOCKS;
+    int32_t src = -1, dst = -1;
+    if (fresh) {
+      if (old >= 0) bm->release(old);
+      s.table[e] = bm->take();
+    } else if (copy) {
+      src = old;
+      dst = bm->take();
+      bm->ref[src]--;
+      s.table[e] = dst;
+    }
+    s.len = pos + 1;
+    *slot = (int64_t)s.table[e] * bs + pos % bs;
+    *copy_src = src;
+    *copy_dst = dst;
+    return PA_OK;
+  }
   const bool new_block = pos % bs == 0;
   if ((new_block || bm->ref[s.table.back()] > 1) && bm->free_list.empty()) return PA_ERR_NO_BLOCKS;
   int32_t src = -1, dst = -1;
@@ -259,6 +349,7 @@ pa_status pa_bm_append_token(pa_block_manager* bm, int64_t seq, int32_t token, i
     s.table.back() = dst;
   }
   s.tokens.push_back(token);
+  s.len = pos + 1;
   const int32_t blk = s.table[pos / bs];
   if ((pos + 1) % bs == 0) {
     const uint64_t parent = s.prefixes.empty() ? kRoot : s.prefixes.back();
@@ -290,13 +381,17 @@ pa_status pa_bm_trim(pa_block_manager* bm, int64_t seq, int32_t keep_tokens, int
   if (it == bm->seqs.end()) return PA_ERR_NOT_FOUND;
   Sequence& s = it->second;
   if (s.swapped) return PA_ERR_SWAPPED;
-  const int64_t n = (int64_t)s.tokens.size();
-  const int64_t first = (n > keep_tokens ? n - keep_tokens : 0) / bm->block_size;
+  const int32_t bs = bm->block_size;
+  const int64_t n = s.len;
+  const int64_t first = (n > keep_tokens ? n - keep_tokens : 0) / bs;
+  // Logical blocks before `first` that still have an entry.
+  const int64_t start = s.ring ? std::max<int64_t>(0, (n + bs - 1) / bs - s.ring) : 0;
   int32_t count = 0;
-  for (int64_t i = 0; i < first; ++i) {
-    if (s.table[i] >= 0) {
-      bm->release(s.table[i]);
-      s.table[i] = kReleased;
+  for (int64_t i = start; i < first; ++i) {
+    const int64_t e = s.ring ? i % s.ring : i;
+    if (s.table[e] >= 0) {
+      bm->release(s.table[e]);
+      s.table[e] = kReleased;
       ++count;
     }
   }
@@ -362,7 +457,7 @@ pa_status pa_bm_sequence_info(const pa_block_manager* bm, int64_t seq, int32_t* 
   if (!bm || !num_tokens || !num_blocks) return PA_ERR_NULL;
   auto it = bm->seqs.find(seq);
   if (it == bm->seqs.end()) return PA_ERR_NOT_FOUND;
-  *num_tokens = (int32_t)it->second.tokens.size();
+  *num_tokens = (int32_t)it->second.len;
   *num_blocks = (int32_t)it->second.table.size();
   return PA_OK;
 }
@@ -403,13 +498,14 @@ pa_status pa_bm_batch(const pa_block_manager* bm, const int64_t* seqs, int32_t n
     if (it == bm->seqs.end()) return PA_ERR_NOT_FOUND;
     if (it->second.swapped) return PA_ERR_SWAPPED;
     if ((int64_t)it->second.table.size() > max_blocks) return PA_ERR_SHAPE;
+    if (it->second.ring && it->second.ring != max_blocks) return PA_ERR_SHAPE;
   }
   for (int32_t i = 0; i < n; ++i) {
     const Sequence& s = bm->seqs.find(seqs[i])->second;
     int32_t* row = block_tables + (int64_t)i * max_blocks;
     std::fill(row, row + max_blocks, -1);
     std::copy(s.table.begin(), s.table.end(), row);
-    seq_lens[i] = (int32_t)s.tokens.size();
+    seq_lens[i] = (int32_t)s.len;
   }
   return PA_OK;
 }

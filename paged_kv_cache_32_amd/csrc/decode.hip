@@ -291,7 +291,7 @@ __device__ __forceinline__ void write_new_tokens(const DecodeParams& p, int u_s,
   const int j = lane & 7;
   const int pos = u_L - 1, chunk = pos / kSub, r = pos % kSub;
   const int bi = pos / p.block_size;
-  const int blk = p.block_tables[(int64_t)u_s * p.max_blocks + bi];
+  const int blk = p.block_tables[(int64_t)u_s * p.max_blocks + (p.ring ? bi % p.max_blocks : bi)];
   const int64_t row = ((int64_t)u_s * p.num_kv_heads + u_h) * D;
   u32x4 kin[2][FP8 ? 2 : 1];
 #pragma unroll
@@ -445,18 +445,23 @@ __device__ __forceinline__ bool issue_stage(const DecodeParams& p, const Stage& 
   // Block ids of the stage's chunks: chunk j lies in block j / subs at
   // sub-block j % subs.  All ids are loaded first (scalar loads); ids past
   // the stage repeat its last one, so no table entry past the sequence's
-  // blocks is read.
+  // blocks is read.  With ring rows, logical block b sits at entry
+  // b % max_blocks: a stage's blocks all lie in the window's span, fewer
+  // than max_blocks consecutive blocks, so they wrap at most once.
   const int subs = p.subs;
   const int jlast = st.j + (st.cnt > 0 ? st.cnt - 1 : 0);
   const int bi0 = (subs == 1) ? st.j : (int)__umulhi((unsigned)st.j, p.subs_magic);
   const int bil = (subs == 1) ? jlast : (int)__umulhi((unsigned)jlast, p.subs_magic);
   const int32_t* bt = p.block_tables + (int64_t)st.s * p.max_blocks;
+  const int e0 = p.ring ? uni(bi0 % p.max_blocks) : bi0;   // entry of block bi0
   int blk[NSUB], sub[NSUB];
   {
     int bi = bi0, sb = st.j - bi0 * subs;
 #pragma unroll
     for (int k = 0; k < NSUB; ++k) {
-      blk[k] = sload(bt, bi < bil ? bi : bil);
+      int e = e0 + ((bi < bil ? bi : bil) - bi0);
+      if (e >= p.max_blocks) e -= p.max_blocks;
+      blk[k] = sload(bt, e);
       sub[k] = sb;
       if (++sb == subs) {
         sb = 0;
@@ -807,7 +812,9 @@ __global__ __launch_bounds__(kDecodeThreads, PA_DECODE_MIN_WAVES) void decode_ke
   const int wave = uni(g * kWavesPerGroup + (threadIdx.x >> 6));
   if (wave >= p.num_waves) return;
   const int S = p.num_seqs, Hkv = p.num_kv_heads;
-  const int max_len = p.max_blocks * p.block_size;
+  // Longest valid sequence: the table's reach, or with ring rows any length
+  // whose chunk count stays inside int range.
+  const int max_len = p.ring ? INT32_MAX - kSub : p.max_blocks * p.block_size;
 
   // Pass 1: total chunks.  Wavefront 0 also writes the rows no other
   // wavefront will touch: zeros for empty sequences, NaN for invalid ones.

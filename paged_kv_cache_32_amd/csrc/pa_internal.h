@@ -76,6 +76,8 @@ struct DecodeParams {
   int32_t chunk_min;            // auto split: fewest chunks a wavefront takes
   int32_t chunk_fixed;          // > 0: every wavefront takes this many chunks
   int32_t window;               // > 0: attend to the last `window` tokens only
+  int32_t ring;                 // != 0: each table row is a ring of max_blocks entries, logical
+                                // block b at entry b % max_blocks (local layers, window > 0)
   int32_t subs;                 // 16-token sub-blocks per block (block_size / 16)
   uint32_t subs_magic;          // ceil(2^32 / subs) for subs > 1: j / subs = umulhi(j, magic)
   int64_t blk_stride;           // bytes from one block's tiles to the next: Hkv * subs * tile

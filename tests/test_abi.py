@@ -41,10 +41,12 @@ def test_exports_every_declared_symbol():
                           "pa_bm_append_token", "pa_bm_batch", "pa_bm_swap_out", "pa_bm_swap_in",
                           "pa_quest_clear", "pa_quest_update", "pa_quest_summarize", "pa_quest_select",
                           "pa_decode_quest", "pa_decode_quest_fp8", "pa_decode_append",
-                          "pa_decode_append_fp8"}
+                          "pa_decode_append_fp8", "pa_decode_ring", "pa_decode_ring_fp8",
+                          "pa_bm_add_ring_sequence", "pa_bm_slots", "pa_decode_noalloc"}
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.pa_abi_version() == 3
+    version = re.search(r"#define PA_ABI_VERSION (\d+)", open(HEADERS[0]).read())
+    assert lib.pa_abi_version() == int(version.group(1)) == 4
 
 
 def test_status_strings():
@@ -136,6 +138,35 @@ def test_decode_append_validation(fp8):
     if fp8:
         assert app(desc(), fp8=True, ks=0.0) == SHAPE
         assert app(desc(), fp8=True, vs=float("nan")) == SHAPE
+
+
+def ring(d, S=2, Hq=16, entries=5, window=64, scale=0.1, q=FAKE, kn=None, vn=None, ws=FAKE, wsb=1 << 30,
+         fp8=False, ks=1.0, vs=1.0):
+    lib = pa.lib()
+    dp = ctypes.byref(d) if d else None
+    if fp8:
+        return lib.pa_decode_ring_fp8(dp, q, kn, vn, S, Hq, FAKE, FAKE, FAKE, entries, FAKE, window, scale,
+                                      ks, vs, FAKE, 0, ws, wsb, None)
+    return lib.pa_decode_ring(dp, q, kn, vn, S, Hq, FAKE, FAKE, FAKE, entries, FAKE, window, scale, FAKE, 0,
+                              ws, wsb, None)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_decode_ring_validation(fp8):
+    assert ring(None, fp8=fp8) == NULL
+    assert ring(desc(), S=0, fp8=fp8) == OK               # 64-token window, 16-token blocks: 5 entries
+    assert ring(desc(), S=0, entries=4, fp8=fp8) == SHAPE
+    assert ring(desc(), S=0, window=65, fp8=fp8) == SHAPE  # 65 tokens can span 6 blocks
+    assert ring(desc(), S=0, window=65, entries=6, fp8=fp8) == OK
+    assert ring(desc(bs=32), S=0, window=64, entries=3, fp8=fp8) == OK
+    assert ring(desc(), S=0, window=0, fp8=fp8) == SHAPE    # a ring needs a window
+    assert ring(desc(), S=0, window=-1, fp8=fp8) == SHAPE
+    assert ring(desc(), kn=FAKE, fp8=fp8) == NULL           # k_new and v_new go together
+    assert ring(desc(), vn=FAKE, fp8=fp8) == NULL
+    assert ring(desc(), q=None, fp8=fp8) == NULL
+    assert ring(desc(), ws=None, fp8=fp8) == WS
+    if fp8:
+        assert ring(desc(), fp8=True, ks=0.0) == SHAPE
 
 
 def test_workspace_init_validation():

@@ -16,6 +16,7 @@ if not os.path.exists(pa.LIB_PATH):
     pytest.skip("libpa.so not built", allow_module_level=True)
 
 NO_BLOCKS, NOT_FOUND, SWAPPED = -7, -8, -9
+SHAPE = -2
 
 
 def test_page_traces(pages):
@@ -186,3 +187,120 @@ def run_both(seed, num_blocks, block_size, steps, vocab, max_prompt):
     (0, 40, 4, 2), (1, 40, 4, 3), (2, 25, 3, 2), (3, 64, 8, 2), (4, 12, 2, 2), (5, 200, 16, 2)])
 def test_random_operations_match_the_oracle(seed, num_blocks, block_size, vocab):
     run_both(seed, num_blocks, block_size, 1500, vocab, 4 * block_size + 3)
+
+
+def run_ring_both(seed, num_blocks, block_size, steps):
+    """Ring (local-layer) sequences on both managers: random ring adds,
+    forks, appends, trims, swaps and frees, comparing every result, the
+    tables, the slots of every window position and the pool after each
+    operation."""
+    rng = random.Random(seed)
+    ref = B.BlockManager(num_blocks, block_size)
+    got = pa.BlockManager(num_blocks, block_size)
+    live, swapped, window, nxt = [], set(), {}, 0
+    seen = {"cow": 0, "no_blocks": 0, "swap": 0}
+    for step in range(steps):
+        op = rng.random()
+        resident = [s for s in live if s not in swapped]
+        if op < 0.12 or not resident:
+            n, W = rng.randrange(0, 6 * block_size), rng.randrange(1, 3 * block_size)
+            try:
+                e = ref.add_ring_sequence(nxt, n, W)
+            except B.OutOfBlocks:
+                seen["no_blocks"] += 1
+                with pytest.raises(pa.PagedAttentionError) as err:
+                    got.add_ring_sequence(nxt, n, W)
+                assert err.value.status == NO_BLOCKS
+                continue
+            assert got.add_ring_sequence(nxt, n, W) == e
+            window[nxt] = W
+            live.append(nxt)
+            nxt += 1
+        elif op < 0.2:
+            p = rng.choice(resident)
+            ref.fork(p, nxt)
+            got.fork(p, nxt)
+            window[nxt] = window[p]
+            live.append(nxt)
+            nxt += 1
+        elif op < 0.75:
+            s = rng.choice(resident)
+            try:
+                r = ref.append_token(s, 0)
+            except B.OutOfBlocks:
+                seen["no_blocks"] += 1
+                with pytest.raises(pa.PagedAttentionError) as err:
+                    got.append_token(s, 0)
+                assert err.value.status == NO_BLOCKS
+                continue
+            seen["cow"] += r[1] >= 0
+            assert got.append_token(s, 0) == r, step
+        elif op < 0.8:
+            s = rng.choice(resident)
+            keep = rng.randrange(1, 3 * block_size)
+            assert got.trim(s, keep) == ref.trim(s, keep), step
+        elif op < 0.86:
+            s = rng.choice(resident)
+            assert got.swap_out(s) == ref.swap_out(s), step
+            swapped.add(s)
+        elif op < 0.93 and swapped:
+            s = rng.choice(sorted(swapped))
+            try:
+                r = ref.swap_in(s)
+            except B.OutOfBlocks:
+                with pytest.raises(pa.PagedAttentionError):
+                    got.swap_in(s)
+                continue
+            assert got.swap_in(s) == r, step
+            swapped.discard(s)
+            seen["swap"] += 1
+        else:
+            s = live.pop(rng.randrange(len(live)))
+            swapped.discard(s)
+            ref.free_sequence(s)
+            got.free_sequence(s)
+        assert got.num_free() == ref.num_free(), step
+        for s in live:
+            assert got.table(s) == ref.table(s), (step, s)
+            assert got.length(s) == ref.length(s)
+            if s not in swapped:
+                L = ref.length(s)
+                assert list(got.slots(s, 0, L)) == ref.slots(s, 0, L), (step, s)
+        if step % 10 == 0:
+            assert [got.refcount(b) for b in range(num_blocks)] == ref.ref
+    assert got.stats() == (ref.hits, ref.misses)
+    assert min(seen.values()) > 0, seen
+    resident = [s for s in live if s not in swapped]
+    for s in resident:
+        E = len(ref.table(s))
+        bt, sl = got.batch([s], E)
+        assert list(bt[0]) == ref.table(s) and sl[0] == ref.length(s)
+        with pytest.raises(pa.PagedAttentionError) as err:
+            got.batch([s], E + 1)                     # a ring row must be the ring itself
+        assert err.value.status == SHAPE
+
+
+@pytest.mark.parametrize("seed,num_blocks,block_size", [(0, 40, 4), (1, 25, 3), (2, 64, 16), (3, 12, 2)])
+def test_ring_operations_match_the_oracle(seed, num_blocks, block_size):
+    run_ring_both(seed, num_blocks, block_size, 1200)
+
+
+def test_ring_errors():
+    bm = pa.BlockManager(8, 16)
+    with pytest.raises(pa.PagedAttentionError) as e:
+        bm.add_ring_sequence(0, 10, 0)
+    assert e.value.status == SHAPE
+    assert bm.add_ring_sequence(0, 100, 1024) == 65   # a 1,024-token window over 16-token blocks
+    with pytest.raises(pa.PagedAttentionError) as e:
+        bm.add_ring_sequence(0, 10, 16)
+    assert e.value.status == NOT_FOUND
+    with pytest.raises(pa.PagedAttentionError) as e:
+        bm.add_ring_sequence(1, 1000, 1024)           # 63 blocks needed, 1 free
+    assert e.value.status == NO_BLOCKS and bm.num_free() == 1
+    with pytest.raises(pa.PagedAttentionError) as e:
+        bm.slots(0, 90, 11)                           # past the sequence's 100 tokens
+    assert e.value.status == SHAPE
+    with pytest.raises(pa.PagedAttentionError) as e:
+        bm.slots(0, -1, 1)
+    assert e.value.status == SHAPE
+    assert list(bm.slots(0, 99, 1)) == [bm.table(0)[6] * 16 + 3]

@@ -2,7 +2,10 @@
 oracle: windows shorter than a chunk, not a multiple of 16, longer than every
 sequence, with table entries before the window released (-1), several
 partition sizes, and decode steps whose tables come from the block manager
-with trims."""
+with trims.  Local layers with ring tables (pa_decode_ring /
+pa_decode_ring_fp8): bit for bit the linear-table window decode, against the
+oracle's ring decode, and a step loop of 100,000-token sequences whose
+65-entry rings the block manager keeps, with plain and fused writes."""
 
 import numpy as np
 import pytest
@@ -10,7 +13,7 @@ import torch
 
 import paged_kv_cache_32_amd as pa
 from oracle import blocks as B
-from oracle import paged
+from oracle import e4m3, paged
 from paged_kv_cache_32_amd import workloads as W
 from tests.gpu_helpers import (BF16_ENVELOPE, BF16_TOL, compare, device_inputs, gpu_write, host_bits, oracle_caches)
 
@@ -118,3 +121,165 @@ def test_window_decode_with_manager_trims():
     # the pool stays bounded: each sequence holds at most ceil(WIN / BS) + 1 blocks
     assert all(sum(b >= 0 for b in model.table(s)) <= -(-WIN // BS) + 1 for s in seqs)
     assert model.num_free() >= NB - len(seqs) * (-(-WIN // BS) + 1)
+
+
+def ring_rows(w, win):
+    """The ring tables (ceil(win / BS) + 1 entries) standing for the
+    workload's linear tables: logical block b of the window's span at entry
+    b % entries, -1 elsewhere."""
+    BS = w.block_size
+    E = -(-win // BS) + 1
+    rt = np.full((w.num_seqs, E), -1, dtype=np.int32)
+    for s, L in enumerate(w.seq_lens):
+        L = int(L)
+        for b in range(max(0, L - win) // BS, -(-L // BS)):
+            rt[s, b % E] = w.block_tables[s, b]
+    return rt
+
+
+def ring_decode(w, t, rt, win, part=0, k_new=None, v_new=None, workspace=None):
+    kc, vc = t["k_cache"][0], t["v_cache"][0]
+    if w.kv_dtype == "bf16":
+        return pa.pa_decode_ring(t["q"][0], kc, vc, rt, t["seq_lens"], win, w.scale,
+                                 num_kv_heads=w.num_kv_heads, block_size=w.block_size, k_new=k_new,
+                                 v_new=v_new, partition_tokens=part, workspace=workspace)
+    return pa.pa_decode_ring_fp8(t["q"][0], kc, vc, rt, t["seq_lens"], win, w.scale, float(t["k_scale"][0]),
+                                 float(t["v_scale"][0]), num_kv_heads=w.num_kv_heads, block_size=w.block_size,
+                                 k_new=k_new, v_new=v_new, partition_tokens=part, workspace=workspace)
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"{c[7]}_d{c[4]}_bs{c[5]}" for c in CASES])
+def test_ring_decode_is_the_window_decode_of_its_linear_table(case):
+    """Ring rows holding the same blocks as the linear rows give the same
+    output bit for bit (same split, same merge order) at the automatic and
+    at fixed partitions, and match the oracle's ring decode."""
+    seed, S, Hq, Hkv, D, BS, max_len, kv, windows = case
+    w = W.random_workload(seed, S, Hq, Hkv, D, BS, max_len, kv_dtype=kv, min_len=1)
+    print(f"[ring] {w.name} {kv} lens={list(w.seq_lens)}", flush=True)
+    t = device_inputs(w)
+    kc0, vc0 = host_bits(t["k_cache"][0]), host_bits(t["v_cache"][0])
+    ks = float(t["k_scale"][0]) if kv == "fp8" else 1.0
+    vs = float(t["v_scale"][0]) if kv == "fp8" else 1.0
+    gpu_write(w, t)
+    kc_ref, vc_ref = oracle_caches(w, kc0, vc0, host_bits(t["k_new"][0]), host_bits(t["v_new"][0]), ks, vs)
+    g = paged.Geom(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.kv_dtype)
+    q = host_bits(t["q"][0])
+    for win in windows:
+        rt = ring_rows(w, win)
+        ref = paged.decode(g, q, kc_ref, vc_ref, rt, w.seq_lens, w.scale, k_scale=ks, v_scale=vs,
+                           window=win, ring=True)
+        rt_d = torch.from_numpy(rt).cuda()
+        for part in (0, 16, 64):
+            lin = window_decode(w, t, win, part)
+            out = ring_decode(w, t, rt_d, win, part)
+            torch.cuda.synchronize()
+            assert torch.equal(out.view(torch.int32), lin.view(torch.int32)), f"window={win} part={part}"
+            compare(out, ref, kv, label=f"ring window={win} part={part} entries={rt.shape[1]}")
+
+
+def _rows(gen, n, Hkv, D):
+    return torch.randn((n, Hkv, D), generator=gen, device="cuda").to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_ring_step_loop_of_100k_token_sequences_from_65_entries(kv):
+    """A local layer with a 1,024-token window over 16-token blocks: the
+    manager gives each sequence a ring of 65 entries.  Sequences of about
+    100,000, 50,000, 1,000, 3 and 0 prompt tokens (only the prompt rows the
+    ring holds are written) then take 40 decode steps, writing the new token
+    either with pa_cache_write at the manager's slot followed by
+    pa_decode_ring, or with the fused write of pa_decode_ring itself.  After
+    every step the caches equal the oracle's bit for bit, the output matches
+    the oracle's ring decode, and that in turn is dense attention over the
+    raw rows of the last 1,024 positions."""
+    Hq, Hkv, D, BS, WIN = 64, 8, 128, 16, 1024
+    fp8 = kv == "fp8"
+    prompts = [99_990, 50_007, 1_000, 3, 0]
+    S = len(prompts)
+    NB = S * 65 + 11
+    g = paged.Geom(NB, BS, Hkv, D, kv)
+    ks, vs = (np.float32(0.05), np.float32(0.04)) if fp8 else (1.0, 1.0)
+    bm = pa.BlockManager(NB, BS)
+    ents = [bm.add_ring_sequence(s, n, WIN) for s, n in enumerate(prompts)]
+    assert ents == [65] * S
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(77)
+    cdt = torch.uint8 if fp8 else torch.bfloat16
+    poison = 0x7F if fp8 else 0x7FC0
+    kc = torch.full((g.cache_elems,), poison, dtype=torch.int16 if not fp8 else torch.uint8, device="cuda")
+    kc = kc.view(cdt) if not fp8 else kc
+    vc = kc.clone()
+    k_ref, v_ref = host_bits(kc).copy(), host_bits(vc).copy()
+    raw_k = [[] for _ in range(S)]   # bf16 bits of every written position, [pos, Hkv, D]
+    raw_v = [[] for _ in range(S)]
+    held_from = []
+
+    def write(rows_k, rows_v, slots, fused=False):
+        sl_d = torch.from_numpy(np.asarray(slots, dtype=np.int64)).cuda()
+        if not fused:
+            if fp8:
+                pa.pa_cache_write_fp8(rows_k, rows_v, sl_d, kc, vc, float(ks), float(vs), block_size=BS)
+            else:
+                pa.pa_cache_write(rows_k, rows_v, sl_d, kc, vc, block_size=BS)
+        if fp8:
+            paged.cache_write_fp8(g, host_bits(rows_k), host_bits(rows_v), np.asarray(slots), k_ref, v_ref, ks, vs)
+        else:
+            paged.cache_write_bf16(g, host_bits(rows_k), host_bits(rows_v), np.asarray(slots), k_ref, v_ref)
+
+    for s, n in enumerate(prompts):
+        slots = bm.slots(s, 0, n)
+        first = int(np.argmax(slots >= 0)) if n else 0
+        held_from.append(first)
+        assert (slots[:first] == -1).all() and (slots[first:] >= 0).all()
+        assert n - first <= 65 * BS
+        if n > first:
+            rk, rv = _rows(gen, n - first, Hkv, D), _rows(gen, n - first, Hkv, D)
+            write(rk, rv, slots[first:])
+            raw_k[s].append(host_bits(rk))
+            raw_v[s].append(host_bits(rv))
+    torch.cuda.synchronize()
+    free0 = bm.num_free()
+    seqs = list(range(S))
+    for step in range(40):
+        slots = np.array([bm.append_token(s, 0)[0] for s in seqs], dtype=np.int64)
+        rk, rv, q = _rows(gen, S, Hkv, D), _rows(gen, S, Hkv, D), _rows(gen, S, Hq, D)
+        bt, sl = bm.batch(seqs, 65)
+        assert bt.shape == (S, 65)
+        rt_d, sl_d = torch.from_numpy(bt).cuda(), torch.from_numpy(sl).cuda()
+        fused = step % 2 == 1
+        write(rk, rv, slots, fused=fused)
+        kn, vn = (rk, rv) if fused else (None, None)
+        if fp8:
+            out = pa.pa_decode_ring_fp8(q, kc, vc, rt_d, sl_d, WIN, 0.088, float(ks), float(vs),
+                                        num_kv_heads=Hkv, block_size=BS, k_new=kn, v_new=vn)
+        else:
+            out = pa.pa_decode_ring(q, kc, vc, rt_d, sl_d, WIN, 0.088, num_kv_heads=Hkv, block_size=BS,
+                                    k_new=kn, v_new=vn)
+        torch.cuda.synchronize()
+        for s in seqs:
+            raw_k[s].append(host_bits(rk)[s:s + 1])
+            raw_v[s].append(host_bits(rv)[s:s + 1])
+        label = f"{kv} step {step} ({'fused' if fused else 'write + decode'})"
+        print(f"[ring] {label}", flush=True)
+        assert np.array_equal(host_bits(kc), k_ref), f"{label}: K cache"
+        assert np.array_equal(host_bits(vc), v_ref), f"{label}: V cache"
+        ref = paged.decode(g, host_bits(q), k_ref, v_ref, bt, sl, 0.088, k_scale=float(ks),
+                           v_scale=float(vs), window=WIN, ring=True)
+        compare(out, ref, kv, label=label)
+        if step % 13 == 0:
+            # the oracle's ring decode is dense attention over the last WIN raw rows
+            qf = paged.bf16_bits_to_f64(host_bits(q))
+            for s in seqs:
+                K = np.concatenate(raw_k[s])[-WIN:]
+                V = np.concatenate(raw_v[s])[-WIN:]
+                if fp8:
+                    Kf = e4m3.dequantize(e4m3.quantize(paged.bf16_bits_to_f64(K).astype(np.float32), ks), ks)
+                    Vf = e4m3.dequantize(e4m3.quantize(paged.bf16_bits_to_f64(V).astype(np.float32), vs), vs)
+                else:
+                    Kf, Vf = paged.bf16_bits_to_f64(K), paged.bf16_bits_to_f64(V)
+                for h in range(Hkv):
+                    want = paged.softmax_attention(qf[s, 8 * h:8 * h + 8], Kf[:, h], Vf[:, h], 0.088)
+                    assert np.max(np.abs(ref[s, 8 * h:8 * h + 8] - want)) < 1e-9, (label, s, h)
+    # full rings take no blocks: only the short sequences' rings grew
+    assert all(sum(b >= 0 for b in bm.table(s)) <= 65 for s in seqs)
+    assert bm.num_free() == free0 - sum(min(-(-(n + 40) // BS), 65) - min(-(-n // BS), 65) for n in prompts)

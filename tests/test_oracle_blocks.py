@@ -348,3 +348,182 @@ def test_swap_image_round_trip():
         assert np.array_equal(v2[dst * E:(dst + 1) * E], v[src * E:(src + 1) * E])
     assert not k2[E:2 * E].any() and not v2[3 * E:6 * E].any()
     assert B.swap_image(k, v, [], E).size == 0
+
+
+# ---------------------------------------------------------------- ring tables
+def test_ring_sequence_keeps_its_window_and_takes_no_blocks_once_full():
+    """A local layer's sequence in a ring of ceil(W / BS) + 1 entries ("KV
+    Cache Engineering for LLM Serving", section 3: each new entry displaces
+    the oldest).  After every append, each of the last W positions still
+    reads back the value it wrote (no later token wrote over its slot), the
+    ring's blocks are the only blocks it holds, and once the ring is full
+    the pool no longer changes."""
+    bs, W = 4, 8
+    bm = B.BlockManager(30, bs)
+    E = bm.add_ring_sequence("a", 0, W)
+    assert E == 3 and bm.table("a") == [-1, -1, -1]
+    content = {}                                    # slot -> position written there last
+    written = []
+    for p in range(60):
+        slot, src, dst = bm.append_token("a", 7)
+        assert (src, dst) == (-1, -1)
+        content[slot] = p
+        written.append(slot)
+        L = p + 1
+        lo = max(0, L - W)
+        got = bm.slots("a", lo, L - lo)
+        assert got == written[lo:L]
+        assert all(content[s] == q for q, s in zip(range(lo, L), got)), p
+        assert len(bm.table("a")) == E
+        held = [b for b in bm.table("a") if b >= 0]
+        assert len(held) == min(-(-L // bs), E) and 30 - bm.num_free() == len(held)
+    # positions whose block has left the ring have no slot
+    nb = -(-60 // bs)
+    assert bm.slots("a", 0, (nb - E) * bs) == [-1] * ((nb - E) * bs)
+    assert bm.slots("a", (nb - E) * bs, 1)[0] >= 0
+    bm.free_sequence("a")
+    assert bm.num_free() == 30
+
+
+def test_ring_prompt_holds_its_last_blocks():
+    bm = B.BlockManager(10, 4)
+    assert bm.add_ring_sequence("b", 23, 8) == 3    # 6 logical blocks; the last 3 are held
+    t = bm.table("b")
+    assert sorted(t) == [0, 1, 2] and t == [0, 1, 2]  # logical 3, 4, 5 at entries 0, 1, 2
+    s = bm.slots("b", 0, 23)
+    assert s[:12] == [-1] * 12 and s[12:] == [0 * 4 + i for i in range(4)] + [4 + i for i in range(4)] + [8, 9, 10]
+    with pytest.raises(B.OutOfBlocks):
+        bm.add_ring_sequence("c", 100, 40)          # 11 entries, 7 free blocks
+    assert bm.num_free() == 7 and "c" not in bm.seqs
+    with pytest.raises(ValueError):
+        bm.add_ring_sequence("d", 5, 0)
+
+
+def test_ring_fork_copies_shared_blocks_before_writing_them():
+    bm = B.BlockManager(12, 4)
+    bm.add_ring_sequence("c", 10, 8)                # logical blocks 0, 1, 2 at entries 0, 1, 2
+    t0 = bm.table("c")
+    bm.fork("c", "d")
+    assert all(bm.ref[b] == 2 for b in t0)
+    # c writes position 10 into shared logical block 2: copy first
+    slot, src, dst = bm.append_token("c", 1)
+    assert src == t0[2] and dst not in t0 and slot == dst * 4 + 2
+    # d now holds block t0[2] alone: written in place
+    assert bm.append_token("d", 1) == (t0[2] * 4 + 2, -1, -1)
+    bm.append_token("c", 1)
+    # c starts logical block 3 on entry 0, whose block d still shares: a fresh block
+    slot, src, dst = bm.append_token("c", 1)
+    assert (src, dst) == (-1, -1) and slot // 4 not in t0 and bm.ref[t0[0]] == 1
+    bm.append_token("d", 1)
+    # d starts logical block 3 on entry 0, whose block only d holds now: reused in place
+    assert bm.append_token("d", 1) == (t0[0] * 4, -1, -1)
+    check_invariants_with_trims(bm, 12)
+
+
+def test_ring_trim_releases_blocks_before_the_kept_tokens():
+    bm = B.BlockManager(10, 4)
+    bm.add_ring_sequence("e", 20, 8)                # logical 2, 3, 4 held
+    t = bm.table("e")
+    assert bm.trim("e", 3) == 2                     # keeps positions 17..19: logical block 4 only
+    assert bm.table("e") == [-1, t[1], -1]          # entries 2 % 3 and 3 % 3 released; 4 % 3 kept
+    assert bm.slots("e", 16, 4) == [t[1] * 4 + i for i in range(4)]
+    assert bm.slots("e", 12, 4) == [-1] * 4
+    slot, _, _ = bm.append_token("e", 0)            # position 20: logical 5, entry 2: a fresh block
+    assert slot % 4 == 0 and bm.table("e")[2] == slot // 4
+    check_invariants_with_trims(bm, 10)
+
+
+def ring_ops_with_contents(seed, num_blocks, bs, steps):
+    """Random ring adds, forks, appends (with their copy-on-write copies),
+    trims, swaps out and in and frees on the model, simulating what each
+    slot holds: every token written gets a unique id, block copies and swap
+    images move the ids, and after each operation every live sequence's
+    window positions must read back their own ids."""
+    rng = random.Random(seed)
+    bm = B.BlockManager(num_blocks, bs)
+    content = {}                 # slot -> token id
+    ids = {}                     # seq -> token id of every position
+    window = {}
+    images = {}
+    nid = [0]
+
+    def fresh_id():
+        nid[0] += 1
+        return nid[0]
+
+    def copy_block(src, dst):
+        for o in range(bs):
+            if src * bs + o in content:
+                content[dst * bs + o] = content[src * bs + o]
+
+    live, swapped, nxt = [], set(), 0
+    for step in range(steps):
+        op = rng.random()
+        resident = [s for s in live if s not in swapped]
+        if op < 0.12 or not resident:
+            n, W = rng.randrange(0, 6 * bs), rng.randrange(1, 3 * bs)
+            try:
+                bm.add_ring_sequence(nxt, n, W)
+            except B.OutOfBlocks:
+                continue
+            ids[nxt] = [fresh_id() for _ in range(n)]
+            window[nxt] = W
+            for p, s in enumerate(bm.slots(nxt, 0, n)):
+                if s >= 0:
+                    content[s] = ids[nxt][p]
+            live.append(nxt)
+            nxt += 1
+        elif op < 0.2:
+            p = rng.choice(resident)
+            bm.fork(p, nxt)
+            ids[nxt], window[nxt] = list(ids[p]), window[p]
+            live.append(nxt)
+            nxt += 1
+        elif op < 0.75:
+            s = rng.choice(resident)
+            try:
+                slot, src, dst = bm.append_token(s, 0)
+            except B.OutOfBlocks:
+                continue
+            if src >= 0:
+                copy_block(src, dst)
+            ids[s].append(fresh_id())
+            content[slot] = ids[s][-1]
+        elif op < 0.8:
+            s = rng.choice(resident)
+            bm.trim(s, rng.randrange(window[s], 3 * bs + window[s]))
+        elif op < 0.86:
+            s = rng.choice(resident)
+            out = bm.swap_out(s)
+            images[s] = [[content.get(b * bs + o) for o in range(bs)] for b in out]
+            swapped.add(s)
+        elif op < 0.93 and swapped:
+            s = rng.choice(sorted(swapped))
+            try:
+                new = bm.swap_in(s)
+            except B.OutOfBlocks:
+                continue
+            for b, img in zip(new, images.pop(s)):
+                for o, v in enumerate(img):
+                    if v is not None:
+                        content[b * bs + o] = v
+            swapped.discard(s)
+        else:
+            s = live.pop(rng.randrange(len(live)))
+            swapped.discard(s)
+            images.pop(s, None)
+            bm.free_sequence(s)
+        check_invariants_with_trims(bm, num_blocks)
+        for s in live:
+            if s in swapped:
+                continue
+            L = len(ids[s])
+            lo = max(0, L - window[s])
+            for p, slot in zip(range(lo, L), bm.slots(s, lo, L - lo)):
+                assert slot >= 0 and content[slot] == ids[s][p], (step, s, p)
+    return bm
+
+
+@pytest.mark.parametrize("seed,num_blocks,bs", [(0, 40, 4), (1, 25, 3), (2, 64, 16), (3, 12, 2)])
+def test_random_ring_operations_keep_every_window_readable(seed, num_blocks, bs):
+    ring_ops_with_contents(seed, num_blocks, bs, 1200)

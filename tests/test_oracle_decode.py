@@ -361,3 +361,52 @@ def test_a_lost_or_doubled_piece_leaves_the_parity_envelope():
             moved.append(np.abs(bad - whole).max())
     assert min(moved) > 10 * BF16_ENVELOPE
     assert min(moved) < BF16_TOL[0]          # the contract bound alone would not have caught some
+
+
+@pytest.mark.parametrize("W,BS", [(1, 16), (16, 16), (33, 16), (64, 32), (100, 48)])
+def test_ring_decode_through_the_manager_is_dense_attention_over_the_window(W, BS):
+    """Local-layer sequences in ring tables kept by the manager model: each
+    token's K/V goes to the slot the manager hands out, and after every step
+    the ring decode (logical block b at entry b % entries) equals dense
+    attention over the raw rows of the last W positions, which never pass
+    through the cache.  The sequences go round their rings several times,
+    one of them from a prompt that starts part-way round."""
+    from oracle import blocks as B
+    rng = np.random.default_rng(900 + W + BS)
+    Hq, Hkv, D = 4, 2, 32
+    nblk = 40
+    g = paged.Geom(nblk, BS, Hkv, D)
+    kc = np.full(g.cache_elems, 0x7FC0, dtype=np.uint16)       # NaN everywhere not written
+    vc = kc.copy()
+    bm = B.BlockManager(nblk, BS)
+    prompts = [0, 5, 3 * W + 7]
+    raw = []
+    for s, n in enumerate(prompts):
+        E = bm.add_ring_sequence(s, n, W)
+        kb = bf16_bits(rng.standard_normal((n, Hkv, D)))
+        vb = bf16_bits(rng.standard_normal((n, Hkv, D)))
+        paged.cache_write_bf16(g, kb, vb, np.array(bm.slots(s, 0, n), dtype=np.int64), kc, vc)
+        raw.append([kb, vb])
+    assert E == -(-W // BS) + 1
+    q = bf16_bits(rng.standard_normal((len(prompts), Hq, D)))
+    qf = paged.bf16_bits_to_f64(q)
+    steps = 2 * E * BS + 3
+    for step in range(steps):
+        for s in range(len(prompts)):
+            slot, src, dst = bm.append_token(s, 0)
+            assert src == -1
+            kb = bf16_bits(rng.standard_normal((1, Hkv, D)))
+            vb = bf16_bits(rng.standard_normal((1, Hkv, D)))
+            paged.cache_write_bf16(g, kb, vb, np.array([slot], dtype=np.int64), kc, vc)
+            raw[s] = [np.concatenate([raw[s][0], kb]), np.concatenate([raw[s][1], vb])]
+        if step % 3 and step != steps - 1:
+            continue
+        bt = np.array([bm.table(s) for s in range(len(prompts))], dtype=np.int32)
+        sl = np.array([bm.length(s) for s in range(len(prompts))], dtype=np.int32)
+        assert bt.shape[1] == E
+        out = paged.decode(g, q, kc, vc, bt, sl, 0.3, window=W, ring=True)
+        for s in range(len(prompts)):
+            K = paged.bf16_bits_to_f64(raw[s][0][-W:])
+            V = paged.bf16_bits_to_f64(raw[s][1][-W:])
+            ref = paged.dense_attention(qf[s], K, V, 0.3)
+            assert np.max(np.abs(out[s] - ref)) < 1e-12, (step, s)
