@@ -33,8 +33,16 @@ Other workloads (--workload), each on the same 70B layer shape:
                        replayed as one HIP graph; `value` is KV GB/s over the
                        whole step, decode tok/s = 128 / step time
   sliding_window_llama70b  the default batch decoded by a local layer with a
-                       1,024-token window (pa_decode_window): `value` counts the
-                       K/V of the last min(L, 1024) tokens of each sequence
+                       1,024-token window from ring tables of 65 entries
+                       (pa_decode_ring; the fused step is pa_decode_ring with
+                       the new tokens): `value` counts the K/V of the last
+                       min(L, 1024) tokens of each sequence; the linear-table
+                       pa_decode_window of the same batch is timed beside it
+  bulk_write_llama70b  pa_cache_write of 64 prompts of 2,000 to 2,800 tokens
+                       (153,600 tokens) into fresh blocks of the 70B layer's
+                       pool, as a prefill writes them: `value` is the bytes
+                       read (new K/V rows, slots) plus written (cache tiles)
+                       per call / time; the fp8 write is timed beside it
   copy_blocks_llama70b pa_copy_blocks of 4,096 independent block pairs on the
                        70B layer's bf16 pool (block 16): `value` is bytes read
                        plus written per call / time; also the host block
@@ -95,7 +103,7 @@ SCRUB_BYTES = 512 << 20
 WORKLOADS = {"llama70b_layer_bs64": 2, "prefix_shared_bs256": 3, "long_context_128k": 4,
              "fp8_80layer_bs128": 5, "copy_blocks_llama70b": 2, "sliding_window_llama70b": 2,
              "swap_blocks_llama70b": 2, "quest_long_context_128k": 4, "quest_llama70b_bs64": 2,
-             "cascade_prefix_shared_bs256": 3}
+             "cascade_prefix_shared_bs256": 3, "bulk_write_llama70b": 2}
 CASCADE_CHUNK_TOKENS = 1024
 QUEST_BUDGET = {"quest_long_context_128k": 256, "quest_llama70b_bs64": 64}   # pages per (seq, KV head)
 HOST_LINK_GBS = 64.0  # PCIe 5.0 x16, per direction: 32 GT/s x 16 lanes / 8 bits
@@ -126,15 +134,18 @@ def algorithmic_bytes(w, physical=False, window=0):
 
 KERNEL_SOURCES = ("paged_kv_cache_32_amd/csrc/decode.hip", "paged_kv_cache_32_amd/csrc/pa_internal.h",
                   "paged_kv_cache_32_amd/csrc/api.hip")
+CACHE_WRITE_SOURCES = ("paged_kv_cache_32_amd/csrc/cache_write.hip", "paged_kv_cache_32_amd/csrc/pa_internal.h",
+                       "paged_kv_cache_32_amd/csrc/api.hip")
 TRAFFIC_PROFILES = {"llama70b_layer_bs64": "profiles/decode_kernel_llama70b_bs64_traffic.md",
                     "prefix_shared_bs256": "profiles/decode_kernel_prefix_shared_bs256_traffic.md",
                     "long_context_128k": "profiles/decode_kernel_long_context_128k_traffic.md",
-                    "fp8_80layer_bs128": "profiles/decode_kernel_fp8_80layer_bs128_traffic.md"}
+                    "fp8_80layer_bs128": "profiles/decode_kernel_fp8_80layer_bs128_traffic.md",
+                    "bulk_write_llama70b": "profiles/cache_write_tiles_kernel_bulk_write_llama70b_traffic.md"}
 
 
-def kernel_source_hash():
+def kernel_source_hash(sources=KERNEL_SOURCES):
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in sources:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -153,9 +164,19 @@ def measured_traffic(workload="llama70b_layer_bs64"):
     if not m:
         return None
     rec = json.loads(m.group(1))
-    if rec.get("kernel_source_sha256") != kernel_source_hash():
+    sources = CACHE_WRITE_SOURCES if workload == "bulk_write_llama70b" else KERNEL_SOURCES
+    if rec.get("kernel_source_sha256") != kernel_source_hash(sources):
         return None
     return rec.get("traffic_bytes_per_launch")
+
+
+def host_cores():
+    """Host cores this process may run on, with the BLAS pool set to that
+    many threads for the oracle's matrix products."""
+    from threadpoolctl import threadpool_limits
+    n = len(os.sched_getaffinity(0))
+    threadpool_limits(limits=n, user_api="blas")
+    return n
 
 
 def cpu_baseline(w, t, out_gpu, layer=0, min_seconds=10.0, max_seconds=30.0, window=0):
@@ -164,8 +185,6 @@ def cpu_baseline(w, t, out_gpu, layer=0, min_seconds=10.0, max_seconds=30.0, win
     about 10 s have elapsed (a whole pass when the batch fits in that time).
     Reports logical KV GB/s of the oracle and its agreement with the GPU on
     the sequences it computed."""
-    from threadpoolctl import threadpool_info
-
     from oracle import paged
     g = paged.Geom(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.kv_dtype)
 
@@ -184,7 +203,7 @@ def cpu_baseline(w, t, out_gpu, layer=0, min_seconds=10.0, max_seconds=30.0, win
     else:
         ks, vs = float(t["k_scale"][layer]), float(t["v_scale"][layer])
         paged.cache_write_fp8(g, kn, vn, w.slot_mapping, kc, vc, np.float32(ks), np.float32(vs))
-    threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    threads = host_cores()
     per_token = 2 * w.num_kv_heads * w.head_dim * w.elem_bytes
     read = (lambda L: min(L, window)) if window else (lambda L: L)
     ref = np.full((w.num_seqs, w.num_q_heads, w.head_dim), np.nan)
@@ -312,11 +331,22 @@ def bench_layer(args, dev):
     def write():
         pa.pa_cache_write(kn, vn, sm, kc, vc, block_size=w.block_size)
 
+    ring = None
+    if window:
+        # A local layer's ring rows: logical block b of the window's span
+        # at entry b % (ceil(window / block_size) + 1).
+        E = -(-window // w.block_size) + 1
+        rt = np.full((w.num_seqs, E), -1, dtype=np.int32)
+        for s, L in enumerate(w.seq_lens):
+            for b in range(max(0, int(L) - window) // w.block_size, -(-int(L) // w.block_size)):
+                rt[s, b % E] = w.block_tables[s, b]
+        ring = torch.from_numpy(rt).to(dev)
+
     def decode():
         if window:
-            pa.pa_decode_window(q, kc, vc, bt, sl, window, w.scale, out, num_kv_heads=w.num_kv_heads,
-                                block_size=w.block_size, partition_tokens=args.partition_tokens,
-                                workspace=ws)
+            pa.pa_decode_ring(q, kc, vc, ring, sl, window, w.scale, out, num_kv_heads=w.num_kv_heads,
+                              block_size=w.block_size, partition_tokens=args.partition_tokens,
+                              workspace=ws)
         else:
             pa.pa_decode(q, kc, vc, bt, sl, w.scale, out, num_kv_heads=w.num_kv_heads,
                          block_size=w.block_size, partition_tokens=args.partition_tokens, workspace=ws)
@@ -354,14 +384,34 @@ def bench_layer(args, dev):
     torch.cuda.synchronize()
     hot_ms = hot[0].elapsed_time(hot[1]) / K
 
-    # The same step as one fused launch (pa_decode_append: the write of the
-    # new tokens folded into the decode), timed the same way.
+    # The local layer's decode from its linear table, timed the same way.
+    linear = None
+    if window:
+        lev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+        for i in range(K):
+            if not args.no_scrub:
+                torch.sum(scrub, dim=0, out=sink)
+            lev[i][0].record(stream)
+            pa.pa_decode_window(q, kc, vc, bt, sl, window, w.scale, out, num_kv_heads=w.num_kv_heads,
+                                block_size=w.block_size, partition_tokens=args.partition_tokens, workspace=ws)
+            lev[i][1].record(stream)
+        torch.cuda.synchronize()
+        linear = np.array([e[0].elapsed_time(e[1]) for e in lev])
+
+    # The same step as one fused launch (pa_decode_append, or pa_decode_ring
+    # with the new tokens: the write folded into the decode), timed the same
+    # way.
     fused = None
     if new_token_blocks_private(w):
         def fused_step():
-            pa.pa_decode_append(q, kn, vn, kc, vc, bt, sl, w.scale, out, num_kv_heads=w.num_kv_heads,
-                                block_size=w.block_size, window=window,
-                                partition_tokens=args.partition_tokens, workspace=ws)
+            if window:
+                pa.pa_decode_ring(q, kc, vc, ring, sl, window, w.scale, out, num_kv_heads=w.num_kv_heads,
+                                  block_size=w.block_size, k_new=kn, v_new=vn,
+                                  partition_tokens=args.partition_tokens, workspace=ws)
+            else:
+                pa.pa_decode_append(q, kn, vn, kc, vc, bt, sl, w.scale, out, num_kv_heads=w.num_kv_heads,
+                                    block_size=w.block_size, partition_tokens=args.partition_tokens,
+                                    workspace=ws)
         for _ in range(args.warmup):
             if not args.no_scrub:
                 torch.sum(scrub, dim=0, out=sink)
@@ -413,6 +463,11 @@ def bench_layer(args, dev):
                      "kernel": "decode_kernel (pa_decode is one launch)",
                      "bytes_per_launch": alg_bytes},
     })
+    if window:
+        res["config"]["ring_entries"] = int(ring.shape[1])
+        res["config"]["linear_table_entries"] = int(w.max_blocks_per_seq)
+        res["linear_table_window_decode_us"] = {"mean": round(float(linear.mean()) * 1e3, 2),
+                                                "p50": round(float(np.median(linear)) * 1e3, 2)}
     ceilings["decode_frac_of_stream_read"] = round(kv_gbs / ceilings["stream_read_gbs"], 4)
     if "tile_read_us" in ceilings:
         # Both read the same tiles: the ratio of times is the fraction of the
@@ -422,7 +477,7 @@ def bench_layer(args, dev):
     if fused is not None:
         f_ms = float(fused.mean())
         res["fused_append_decode"] = {
-            "entry_point": "pa_decode_append", "us_mean": round(f_ms * 1e3, 2),
+            "entry_point": "pa_decode_ring" if window else "pa_decode_append", "us_mean": round(f_ms * 1e3, 2),
             "us_p50": round(float(np.median(fused)) * 1e3, 2),
             "layer_tok_s": round(w.num_seqs / (f_ms / 1e3), 1),
             "step_saving_us": round((step_ms - f_ms) * 1e3, 2)}
@@ -634,6 +689,133 @@ def bench_copy_blocks(args, dev):
     return res
 
 
+BULK_PROMPTS, BULK_MEAN_TOKENS = 64, 2400
+
+
+def bulk_write_inputs(w, rng):
+    """Slots of 64 prompts of 2,000 to 2,800 tokens (153,600 in all), each
+    written from position 0 into blocks drawn at random from the pool."""
+    d = rng.integers(-400, 401, BULK_PROMPTS // 2)
+    lens = BULK_MEAN_TOKENS + rng.permutation(np.concatenate([d, -d]))
+    perm = rng.permutation(w.num_blocks)
+    slots, used = [], 0
+    for L in lens:
+        nb = -(-int(L) // w.block_size)
+        blocks = perm[used:used + nb].astype(np.int64)
+        used += nb
+        pos = np.arange(int(L))
+        slots.append(blocks[pos // w.block_size] * w.block_size + pos % w.block_size)
+    assert used <= w.num_blocks
+    return lens, np.concatenate(slots)
+
+
+def bench_bulk_write(args, dev):
+    """pa_cache_write of a prefill-sized batch of prompt rows."""
+    w = W.config(2)
+    Hkv, D, BS = w.num_kv_heads, w.head_dim, w.block_size
+    rng = np.random.default_rng(8)
+    lens, slots = bulk_write_inputs(w, rng)
+    T = int(slots.size)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(8)
+    k = torch.randn((T, Hkv, D), generator=gen, device=dev).to(torch.bfloat16)
+    v = torch.randn((T, Hkv, D), generator=gen, device=dev).to(torch.bfloat16)
+    sm = torch.from_numpy(slots).to(dev)
+    elems = w.num_blocks * Hkv * BS * D
+    kc = torch.zeros(elems, dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros(elems, dtype=torch.bfloat16, device=dev)
+    kc8 = torch.zeros(elems, dtype=torch.uint8, device=dev)
+    vc8 = torch.zeros(elems, dtype=torch.uint8, device=dev)
+    scrub = torch.ones(SCRUB_BYTES // 4, dtype=torch.float32, device=dev)
+    sink = torch.zeros((), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    ks, vs = 0.02, 0.02
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            if not args.no_scrub:
+                torch.sum(scrub, dim=0, out=sink)
+            ev[i][0].record(stream)
+            fn()
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        return np.array([e[0].elapsed_time(e[1]) for e in ev])
+
+    t0 = time.perf_counter()
+    ms = timed(lambda: pa.pa_cache_write(k, v, sm, kc, vc, block_size=BS))
+    wall = time.perf_counter() - t0
+    ms8 = timed(lambda: pa.pa_cache_write_fp8(k, v, sm, kc8, vc8, ks, vs, block_size=BS))
+    row = Hkv * D
+    read = T * row * 2 * 2 + T * 8                  # new K and V rows (bf16), slots
+    wrote, wrote8 = T * row * 2 * 2, T * row * 2    # K and V tiles
+    gbs = (read + wrote) / (ms.mean() / 1e3) / 1e9
+    gbs8 = (read + wrote8) / (ms8.mean() / 1e3) / 1e9
+    whole = sum(int(L) // 16 for L in lens)
+    res = base_record(args, w, args.steps)
+    res["metric"] = "pa_cache_write GB/s (bytes read + written) of a prefill-sized batch, 70B layer"
+    res.update({"value": round(gbs, 1), "ms_per_step": round(float(ms.mean()), 4),
+                "data": "synthetic (seeded N(0,1) bf16 K/V rows, prompt lengths uniform in [2000, 2800], "
+                        "shuffled block pool)"})
+    res["config"].update({"workload": args.workload, "num_seqs": BULK_PROMPTS, "tokens": T,
+                          "prompt_tokens_min_max": [int(lens.min()), int(lens.max())],
+                          "whole_16_token_sub_blocks": whole, "bytes_read_per_call": read,
+                          "bytes_written_per_call": wrote})
+    res.update({
+        "write_us": {"mean": round(float(ms.mean()) * 1e3, 2), "p10": round(float(np.percentile(ms, 10)) * 1e3, 2),
+                     "p90": round(float(np.percentile(ms, 90)) * 1e3, 2)},
+        "tokens_per_s": round(T / (ms.mean() / 1e3), 1),
+        "wall_s_timed_region": round(wall, 4),
+        "fp8_write": {"us_mean": round(float(ms8.mean()) * 1e3, 2), "gbs": round(gbs8, 1),
+                      "bytes_written_per_call": wrote8, "hbm_peak_frac": round(gbs8 / HBM_PEAK_GBS, 4)},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.workload),
+                     "kernel": "cache_write_tiles_kernel (pa_cache_write is one launch)",
+                     "bytes_per_launch": read + wrote},
+    })
+    if not args.skip_cpu:
+        res["cpu_baseline"] = bulk_write_cpu_baseline(w, lens, slots, k, v, kc)
+    return res
+
+
+def bulk_write_cpu_baseline(w, lens, slots, k, v, kc_gpu, min_seconds=10.0):
+    """The oracle's scatter (numpy) on whole prompts of the same batch, in
+    order until about 10 s have elapsed; the written slots are compared with
+    the GPU's cache."""
+    from oracle import paged
+    g = paged.Geom(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, "bf16")
+    cores = host_cores()
+
+    def bits(x):
+        return x.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+
+    kb, vb = bits(k), bits(v)
+    kc = np.zeros(g.cache_elems, dtype=np.uint16)
+    vc = kc.copy()
+    starts = np.concatenate([[0], np.cumsum(lens)])
+    elapsed, done = 0.0, 0
+    while elapsed < min_seconds and done < len(lens):
+        a, b = int(starts[done]), int(starts[done + 1])
+        t0 = time.perf_counter()
+        paged.cache_write_bf16(g, kb[a:b], vb[a:b], slots[a:b], kc, vc)
+        elapsed += time.perf_counter() - t0
+        done += 1
+    n = int(starts[done])
+    got = bits(kc_gpu)
+    hh, dd = np.meshgrid(np.arange(w.num_kv_heads), np.arange(w.head_dim), indexing="ij")
+    blk, off = np.divmod(slots[:n:97], w.block_size)
+    idx = np.stack([paged.k_offset(g, b, hh, o, dd) for b, o in zip(blk, off)]).ravel()
+    row = w.num_kv_heads * w.head_dim
+    moved = n * row * 2 * 4 + n * 8
+    return {"value": moved / elapsed / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": (f"{done} of the {len(lens)} prompts ({n} tokens) of the same batch, numpy oracle "
+                       f"scatter, {elapsed:.1f} s"),
+            "seconds": elapsed, "gpu_vs_oracle_k_mismatches_sampled": int((got[idx] != kc[idx]).sum())}
+
+
 def quest_bytes(w, budget):
     """Algorithmic bytes of one query-aware step, per call: the update reads
     the new keys and rewrites their blocks' summary words; the selection
@@ -658,8 +840,6 @@ def quest_cpu_baseline(w, t, out_gpu, budget, min_seconds=10.0):
     head) units in order until about 10 s have elapsed; bytes as the GPU's
     algorithmic bytes for those units (summaries of every page, K/V of the
     kept tokens)."""
-    from threadpoolctl import threadpool_info
-
     from oracle import paged, quest
     g = paged.Geom(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.kv_dtype)
 
@@ -672,7 +852,7 @@ def quest_cpu_baseline(w, t, out_gpu, budget, min_seconds=10.0):
     qf = paged.bf16_bits_to_f64(bits(t["q"][0]))
     G, BS, D = w.num_q_heads // w.num_kv_heads, w.block_size, w.head_dim
     got = out_gpu.detach().cpu().double().numpy()
-    threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    threads = host_cores()
     elapsed, nbytes, units, errs = 0.0, 0, 0, []
     u = 0
     while elapsed < min_seconds and units < w.num_seqs * w.num_kv_heads:
@@ -1044,6 +1224,8 @@ def main():
         res = bench_quest(args, dev)
     elif args.workload == "cascade_prefix_shared_bs256":
         res = bench_cascade(args, dev)
+    elif args.workload == "bulk_write_llama70b":
+        res = bench_bulk_write(args, dev)
     else:
         res = bench_layer(args, dev)
     print(json.dumps(res), flush=True)

@@ -95,3 +95,79 @@ def test_zero_tokens_is_a_noop():
     pa.pa_cache_write(e, e, torch.empty(0, dtype=torch.int64, device="cuda"), kc, vc, block_size=16)
     torch.cuda.synchronize()
     assert np.all(H.host_bits(kc) == 0x1234)
+
+
+def _prefill_slots(rng, NB, BS, seqs):
+    """Slots of a batch of prompt continuations: sequence i already holds
+    starts[i] tokens and appends n[i] more, in blocks drawn at random from
+    the pool; the tokens of all sequences are concatenated."""
+    free = list(rng.permutation(NB))
+    out = []
+    for start, n in seqs:
+        blocks = [free.pop() for _ in range(-(-(start + n) // BS))]
+        out += [blocks[p // BS] * BS + p % BS for p in range(start, start + n)]
+    return np.array(out, dtype=np.int64)
+
+
+def _runs(slots):
+    """(anchor indices of whole 16-token sub-block runs, tokens in no run)."""
+    T = len(slots)
+    anchors, covered = [], np.zeros(T, bool)
+    for a in range(T - 15):
+        if slots[a] >= 0 and slots[a] % 16 == 0 and np.array_equal(slots[a:a + 16], slots[a] + np.arange(16)):
+            anchors.append(a)
+            covered[a:a + 16] = True
+    return anchors, int((~covered).sum())
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("block_size,head_dim,Hkv", [(16, 128, 8), (32, 64, 3), (48, 128, 5)])
+def test_bulk_write_whole_sub_blocks_and_ragged_edges(kv_dtype, block_size, head_dim, Hkv):
+    """A prefill-sized call (over 2,000 tokens): prompt continuations that
+    start and end inside sub-blocks, so the call mixes whole 16-token
+    sub-blocks (written as whole tiles), runs that start at token indices
+    not divisible by 16, partial sub-blocks, and skipped or out-of-pool
+    slots that break runs.  Bit-exact against the oracle's scatter, and
+    equal to the same tokens written in calls of 100 tokens (the per-token
+    kernel)."""
+    rng = np.random.default_rng(block_size * 7 + head_dim + Hkv)
+    NB = 400
+    seqs = [(0, 700), (5, 333), (16, 160), (37, 1), (3, 500), (0, 16), (250, 300), (11, 21)]
+    slots = _prefill_slots(rng, NB, block_size, seqs)
+    T = len(slots)
+    slots[rng.choice(T, 6, replace=False)] = -1
+    slots[rng.choice(T, 3, replace=False)] = NB * block_size + 7        # past the pool: skipped
+    anchors, singles = _runs(slots)
+    assert T >= 2000 and len(anchors) > 50 and singles > 50
+    assert any(a % 16 for a in anchors) and any(a % 16 == 0 for a in anchors)
+    g = paged.Geom(NB, block_size, Hkv, head_dim, kv_dtype)
+    kb = (rng.standard_normal((T, Hkv, head_dim)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    vb = (rng.standard_normal((T, Hkv, head_dim)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    fill = 0x7FC0 if kv_dtype == "bf16" else 0x7F
+    k = torch.from_numpy(kb.view(np.int16)).cuda().view(torch.bfloat16)
+    v = torch.from_numpy(vb.view(np.int16)).cuda().view(torch.bfloat16)
+    sl = torch.from_numpy(slots).cuda()
+    ks, vs = 0.021, 0.017
+
+    def write(kc, vc, lo, hi):
+        if kv_dtype == "bf16":
+            pa.pa_cache_write(k[lo:hi], v[lo:hi], sl[lo:hi], kc, vc, block_size=block_size)
+        else:
+            pa.pa_cache_write_fp8(k[lo:hi], v[lo:hi], sl[lo:hi], kc, vc, ks, vs, block_size=block_size)
+
+    kc, vc = _flat_caches(g, fill)
+    write(kc, vc, 0, T)
+    kc2, vc2 = _flat_caches(g, fill)
+    for lo in range(0, T, 100):
+        write(kc2, vc2, lo, min(T, lo + 100))
+    torch.cuda.synchronize()
+    kref = np.full(g.cache_elems, fill, dtype=g.np_dtype)
+    vref = kref.copy()
+    if kv_dtype == "bf16":
+        paged.cache_write_bf16(g, kb, vb, slots, kref, vref)
+    else:
+        paged.cache_write_fp8(g, kb, vb, slots, kref, vref, np.float32(ks), np.float32(vs))
+    assert np.array_equal(H.host_bits(kc), kref), "K cache differs from the oracle's scatter"
+    assert np.array_equal(H.host_bits(vc), vref), "V cache differs from the oracle's scatter"
+    assert torch.equal(kc.view(torch.uint8), kc2.view(torch.uint8))
+    assert torch.equal(vc.view(torch.uint8), vc2.view(torch.uint8))
