@@ -197,12 +197,29 @@ __device__ __forceinline__ int wave_incl_sum(int v, int lane) {
 // (slot, head) with the heads fastest, so the lanes of a page read one run
 // of the block's summary words (all heads' quads of 4 dimensions, 128 bytes
 // at 8 heads) per load instruction.  kScoreAhead dimension quads of every
-// page are in flight while the previous ones are summed.
+// page are in flight while the previous ones are summed.  Every LDS read of
+// a q+ / q- quad serves the lane's kScorePages pages: at four pages the
+// reads cost half what they cost at two (at 8 heads, a read of 8 distinct
+// quads takes the LDS as long as a full 1 KiB read), for 2 quads ahead
+// instead of 8 at the same register count.
+#ifndef PA_SCORE_PAGES
+#define PA_SCORE_PAGES 4
+#endif
+#ifndef PA_SCORE_LDS_FLOATS
+#define PA_SCORE_LDS_FLOATS 16384
+#endif
+#ifndef PA_SCORE_AHEAD
+#define PA_SCORE_AHEAD 2
+#endif
+#ifndef PA_SCORE_GROUPS_PER_CU
+#define PA_SCORE_GROUPS_PER_CU 2
+#endif
 constexpr int kScoreWaves = 4;
 constexpr int kScoreThreads = 64 * kScoreWaves;
-constexpr int kScorePages = 2;
-constexpr int kScoreAhead = 8;
-constexpr int kScoreLdsFloats = 16384;   // q+ and q- of the staged heads: 64 KiB
+constexpr int kScorePages = PA_SCORE_PAGES;
+constexpr int kScoreAhead = PA_SCORE_AHEAD;
+constexpr int kScoreLdsFloats = PA_SCORE_LDS_FLOATS;   // q+ and q- of the staged heads
+constexpr int kScoreGroupsPerCu = PA_SCORE_GROUPS_PER_CU;
 
 // Work item: the item_pages pages c * item_pages .. of sequence s (a
 // sequence of n pages has ceil(n / item_pages) items, numbered in sequence
@@ -800,7 +817,7 @@ hipError_t launch_page_select(const SelectParams& p_in, hipStream_t stream) {
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return hipErrorInvalidDevice;
   const int64_t most = (int64_t)p.num_seqs * ((p.max_blocks + p.item_pages - 1) / p.item_pages);
-  int64_t groups = 2 * (int64_t)cus;
+  int64_t groups = kScoreGroupsPerCu * (int64_t)cus;
   if (groups > most) groups = most;
   if (groups > 0) {
     const dim3 grid((unsigned)groups);
