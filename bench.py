@@ -38,6 +38,10 @@ Other workloads (--workload), each on the same 70B layer shape:
                        the new tokens): `value` counts the K/V of the last
                        min(L, 1024) tokens of each sequence; the linear-table
                        pa_decode_window of the same batch is timed beside it
+  llama70b_tp2_shard_bs64, llama70b_tp8_shard_bs64  one GPU's share of the
+                       default layer split by KV head over 2 or 8 GPUs (4 or 1
+                       KV heads, 32 or 8 query heads; the same sequences), as
+                       the default step
   bulk_write_llama70b  pa_cache_write of 64 prompts of 2,000 to 2,800 tokens
                        (153,600 tokens) into fresh blocks of the 70B layer's
                        pool, as a prefill writes them: `value` is the bytes
@@ -103,7 +107,8 @@ SCRUB_BYTES = 512 << 20
 WORKLOADS = {"llama70b_layer_bs64": 2, "prefix_shared_bs256": 3, "long_context_128k": 4,
              "fp8_80layer_bs128": 5, "copy_blocks_llama70b": 2, "sliding_window_llama70b": 2,
              "swap_blocks_llama70b": 2, "quest_long_context_128k": 4, "quest_llama70b_bs64": 2,
-             "cascade_prefix_shared_bs256": 3, "bulk_write_llama70b": 2}
+             "cascade_prefix_shared_bs256": 3, "bulk_write_llama70b": 2,
+             "llama70b_tp2_shard_bs64": 2, "llama70b_tp8_shard_bs64": 2}
 CASCADE_CHUNK_TOKENS = 1024
 QUEST_BUDGET = {"quest_long_context_128k": 256, "quest_llama70b_bs64": 64}   # pages per (seq, KV head)
 HOST_LINK_GBS = 64.0  # PCIe 5.0 x16, per direction: 32 GT/s x 16 lanes / 8 bits
@@ -308,7 +313,8 @@ def new_token_blocks_private(w):
 
 def bench_layer(args, dev):
     """One-layer workloads: the cache write and the decode of one batch."""
-    w = W.config(WORKLOADS[args.workload])
+    m = re.match(r"llama70b_tp(\d)_shard_bs64$", args.workload)
+    w = W.llama70b_tp_shard(int(m.group(1))) if m else W.config(WORKLOADS[args.workload])
     shared = args.workload == "prefix_shared_bs256"
     window = LOCAL_WINDOW if args.workload == "sliding_window_llama70b" else 0
     log("workload:", json.dumps(w.summary()))

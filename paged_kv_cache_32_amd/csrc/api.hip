@@ -17,7 +17,10 @@ namespace {
 constexpr int kMaxDevices = 64;
 constexpr int kMaxGroup = 16;
 constexpr int kMaxBlockSize = 256;
-constexpr int kChunkMinAuto = 16;  // at least 256 tokens per wavefront when splitting automatically
+#ifndef PA_DECODE_CHUNK_MIN
+#define PA_DECODE_CHUNK_MIN 32
+#endif
+constexpr int kChunkMinAuto = PA_DECODE_CHUNK_MIN;  // fewest chunks per wavefront when splitting automatically
 // Wavefronts launched per resident slot in the automatic split: ranges left
 // over are picked up by whichever slots free up first.
 #ifndef PA_DECODE_OVERSUB

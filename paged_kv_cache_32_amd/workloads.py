@@ -373,19 +373,29 @@ def tiny(seed=1, new_token_at_end=True):
 
 
 def llama70b_layer(seed=2, num_seqs=64, block_size=16, kv_dtype="bf16", num_layers=1,
-                   name="llama70b_layer_bs64"):
+                   name="llama70b_layer_bs64", tp=1):
     """A Llama-70B-shaped layer: 64 query heads, 8 KV heads, head_dim 128;
     lognormal lengths (median 2,400, p95 about 18,000, clipped to
     [16, 32768]); a pool of 1.25x the blocks needed, handed out from a seeded
-    shuffle in sequence order."""
+    shuffle in sequence order.  tp > 1: one GPU's share of the layer split by
+    KV head over tp GPUs (64 / tp query heads, 8 / tp KV heads, the same
+    sequences and tables)."""
+    if tp not in (1, 2, 4, 8):
+        raise ValueError("tp must divide the 8 KV heads")
     rng = np.random.default_rng(seed)
     lens = lognormal_lengths(rng, num_seqs)
     need = int(sum(-(-int(L) // block_size) for L in lens))
     nb = _pool_size(need)
     bt = _tables_from_pool(lens, block_size, rng.permutation(nb))
-    return Workload(name, 64, 8, 128, block_size, nb, lens, bt,
+    return Workload(name, 64 // tp, 8 // tp, 128, block_size, nb, lens, bt,
                     _slots_for_last_token(lens, bt, block_size), 1.0 / math.sqrt(128),
                     kv_dtype=kv_dtype, num_layers=num_layers, seed=seed)
+
+
+def llama70b_tp_shard(tp, seed=2):
+    """One GPU's share of the 70B layer bs=64 under tensor parallelism over
+    tp GPUs: KV heads 8 / tp, query heads 64 / tp, same lengths and tables."""
+    return llama70b_layer(seed=seed, name=f"llama70b_tp{tp}_shard_bs64", tp=tp)
 
 
 def prefix_shared(seed=3, num_seqs=256, block_size=32, system_tokens=900, num_pools=12,

@@ -52,6 +52,19 @@ def test_llama70b_layer_bs64_every_sequence_and_deterministic():
     assert torch.equal(a.view(torch.int32), b.view(torch.int32))
 
 
+@pytest.mark.parametrize("tp", [2, 8])
+def test_llama70b_tensor_parallel_shard_every_sequence(tp):
+    """One GPU's share of the 70B layer bs=64 split by KV head over tp GPUs
+    (8 / tp KV heads, 64 / tp query heads, the same sequences): with one KV
+    head (tp = 8) the 64 units are split over all wavefronts, each into
+    many pieces."""
+    w = W.llama70b_tp_shard(tp)
+    print(f"[configs] {w.name}: {w.num_kv_heads} KV heads", flush=True)
+    t = device_inputs(w)
+    mx, mean = step_and_check(w, t, label=w.name)
+    print(f"[configs] {w.name}: max-abs {mx:.2e} mean-abs {mean:.2e}", flush=True)
+
+
 def test_prefix_shared_bs256_every_sequence():
     w = W.config(3)
     s = w.summary()
