@@ -17,6 +17,16 @@ namespace {
 constexpr int kMaxDevices = 64;
 constexpr int kMaxGroup = 16;
 constexpr int kMaxBlockSize = 256;
+// Chunks each unit counts for beyond its own in the automatic split (its
+// fixed costs: the sequence's length and table entries, the query, a
+// partial record).  They pay on the fp8 cache, where a chunk is half the
+// bytes; on bf16 the split by chunks alone measured best.
+#ifndef PA_DECODE_UNIT_CHARGE
+#define PA_DECODE_UNIT_CHARGE 0
+#endif
+#ifndef PA_DECODE_UNIT_CHARGE_FP8
+#define PA_DECODE_UNIT_CHARGE_FP8 4
+#endif
 #ifndef PA_DECODE_CHUNK_MIN
 #define PA_DECODE_CHUNK_MIN 32
 #endif
@@ -216,6 +226,7 @@ pa_status decode(const pa_cache_desc* cache, const void* q, int32_t num_seqs, in
   p.num_waves = (int32_t)num_waves;
   p.chunk_min = kChunkMinAuto;
   p.chunk_fixed = chunk_fixed;
+  p.unit_charge = chunk_fixed > 0 ? 0 : (fp8 ? PA_DECODE_UNIT_CHARGE_FP8 : PA_DECODE_UNIT_CHARGE);
   p.window = window;
   p.ring = ring ? 1 : 0;
   p.subs = cache->block_size / pa::kSub;

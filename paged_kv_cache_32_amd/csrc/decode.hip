@@ -218,15 +218,18 @@ enum : int {
 
 // A piece: chunks [j0, j1) of unit (s, h), whose first chunk sits at u0 in
 // the linear chunk list; the unit has n chunks and the sequence L tokens.
-// Unit chunk j is the sequence's chunk window_lo(L, W) / 16 + j.
+// Unit chunk j is the sequence's chunk window_lo(L, W) / 16 + j.  uw: the
+// unit's first chunk in the weighted list that the split cuts (each unit
+// preceded by its charge), set for the boundary pieces A and Z only, the
+// only ones that can be part of a unit.
 struct Piece {
-  int s, h, n, L, u0, j0, j1;
+  int s, h, n, L, u0, j0, j1, uw;
 };
 
 // One stage, uniform across the wavefront: chunks [j, j + cnt) of a piece,
 // j counted in the sequence (not in the unit).
 struct Stage {
-  int s, h, n, L, u0, j, cnt, flags;
+  int s, h, n, L, u0, j, cnt, flags, uw;
 };
 
 // Where a wavefront stands in its range [a, b) of the chunk list.  The
@@ -247,7 +250,7 @@ struct Cursor {
 // complete first), then counted (the counter's old value is in flight).
 struct Pending {
   int state;       // 0 empty/done, 1 stored, 2 counted, 3 to be merged here
-  int s, h, u0, n;
+  int s, h, u0, n, uw;
   int prior;       // lane 0: counter value before this piece was counted
 };
 
@@ -348,13 +351,13 @@ __device__ __forceinline__ Stage next_stage(Cursor& c, const DecodeParams& p, in
       int L = sload(p.seq_lens, s);
       int n = chunks_of(L, max_len, p.window);
       next_unit(p, max_len, s, h, n, L);
-      c.cur = Piece{s, h, n, L, c.a_end, 0, n};
+      c.cur = Piece{s, h, n, L, c.a_end, 0, n, 0};
       c.phase = 2;
     } else if (c.phase == 2 && c.cur.u0 + c.cur.n < c.z.u0) {
       int s = c.cur.s, h = c.cur.h, n = c.cur.n, L = c.cur.L;
       const int u0 = c.cur.u0 + n;
       next_unit(p, max_len, s, h, n, L);
-      c.cur = Piece{s, h, n, L, u0, 0, n};
+      c.cur = Piece{s, h, n, L, u0, 0, n, 0};
     } else {
       c.phase = 3;
     }
@@ -362,7 +365,7 @@ __device__ __forceinline__ Stage next_stage(Cursor& c, const DecodeParams& p, in
   }
   Stage st;
   if (c.phase == 3) {
-    st = Stage{0, 0, 0, 0, 0, 0, 0, 0};
+    st = Stage{0, 0, 0, 0, 0, 0, 0, 0, 0};
     return st;
   }
   const Piece& pc = c.cur;
@@ -377,7 +380,7 @@ __device__ __forceinline__ Stage next_stage(Cursor& c, const DecodeParams& p, in
   if (c.j == 0 && lo > c0 * kSub) f |= kHead;
   if (c.phase == 0) f |= kAtA;
   if (pc.j0 == 0 && pc.j1 == pc.n) f |= kWhole;
-  st = Stage{uni(pc.s), uni(pc.h), uni(pc.n), uni(pc.L), uni(pc.u0), uni(c0 + c.j), uni(cnt), uni(f)};
+  st = Stage{uni(pc.s), uni(pc.h), uni(pc.n), uni(pc.L), uni(pc.u0), uni(c0 + c.j), uni(cnt), uni(f), uni(pc.uw)};
   c.j += cnt;
   return st;
 }
@@ -626,8 +629,11 @@ __device__ __forceinline__ f32x4 load_record(__amdgpu_buffer_rsrc_t r, int byte_
 
 // Pieces of wavefront w are stored in slot 2w (the piece that starts at the
 // wavefront's first chunk) or 2w + 1 (the piece that ends at its last).
-__device__ __forceinline__ int piece_slot(int w, int w0, int u0, int C) {
-  return (w == w0 && u0 != w0 * C) ? 2 * w + 1 : 2 * w;
+// Wavefront w covers the weighted positions [w C, (w + 1) C); a unit's piece
+// in its first wavefront w0 is that wavefront's second piece when the chunk
+// before the unit (weight uw - 1 - charge) lies in the same range.
+__device__ __forceinline__ int piece_slot(int w, int w0, bool second) {
+  return (w == w0 && second) ? 2 * w + 1 : 2 * w;
 }
 
 // Merge the partial softmax states of unit (s, h), pieces from wavefronts
@@ -643,7 +649,8 @@ __device__ __forceinline__ void merge_unit(const DecodeParams& p, const Pending&
   const int G = p.group;
   const int groups = G * D / 4;
   const int rec_bytes = G * (D + 4) * 4;
-  const int w0 = pd.u0 / C, w1 = (pd.u0 + pd.n - 1) / C;
+  const int w0 = pd.uw / C, w1 = (pd.uw + pd.n - 1) / C;
+  const bool second = pd.u0 > 0 && pd.uw - 1 - p.unit_charge >= w0 * C;
   f32x4* o = reinterpret_cast<f32x4*>(p.out + ((int64_t)pd.s * p.num_q_heads + (int64_t)pd.h * G) * D);
   for (int e0 = 0; e0 < groups; e0 += 64 * kIt) {
     const int e_first = e0 + lane * kIt;
@@ -658,7 +665,7 @@ __device__ __forceinline__ void merge_unit(const DecodeParams& p, const Pending&
 #pragma unroll
       for (int b = 0; b < kBatch; ++b) {
         const int w = (wb + b <= w1) ? wb + b : w1;
-        const auto r = record_rsrc(p.partials + (int64_t)piece_slot(w, w0, pd.u0, C) * (rec_bytes / 4), rec_bytes);
+        const auto r = record_rsrc(p.partials + (int64_t)piece_slot(w, w0, second) * (rec_bytes / 4), rec_bytes);
         ml[b] = load_record(r, in ? (G * D + g * 4) * 4 : 0);
 #pragma unroll
         for (int it = 0; it < kIt; ++it) acc[b][it] = load_record(r, in ? ((d40 + it) * G + g) * 16 : 0);
@@ -697,7 +704,7 @@ __device__ __forceinline__ void count_piece(const DecodeParams& p, Pending& pd, 
 // the next call; the others are done with the piece.
 __device__ __forceinline__ void resolve_piece(Pending& pd, int C) {
   const int prior = readlane(pd.prior, 0);
-  const int pieces = (pd.u0 + pd.n - 1) / C - pd.u0 / C + 1;
+  const int pieces = (pd.uw + pd.n - 1) / C - pd.uw / C + 1;
   pd.state = (prior == pieces - 1) ? 3 : 0;
 }
 
@@ -775,6 +782,7 @@ __device__ __forceinline__ void finish_stage(const DecodeParams& p, const Stage&
   pd.h = st.h;
   pd.u0 = st.u0;
   pd.n = st.n;
+  pd.uw = st.uw;
 }
 
 // Advance the pieces waiting to be counted in.  Called right after a
@@ -816,9 +824,10 @@ __global__ __launch_bounds__(kDecodeThreads, PA_DECODE_MIN_WAVES) void decode_ke
   // whose chunk count stays inside int range.
   const int max_len = p.ring ? INT32_MAX - kSub : p.max_blocks * p.block_size;
 
-  // Pass 1: total chunks.  Wavefront 0 also writes the rows no other
-  // wavefront will touch: zeros for empty sequences, NaN for invalid ones.
-  int total = 0;
+  // Pass 1: total chunks and sequences with chunks.  Wavefront 0 also
+  // writes the rows no other wavefront will touch: zeros for empty
+  // sequences, NaN for invalid ones.
+  int total = 0, filled = 0;
   for (int base = 0; base < S; base += 64) {
     const int si = base + lane;
     int n = 0;
@@ -839,25 +848,75 @@ __global__ __launch_bounds__(kDecodeThreads, PA_DECODE_MIN_WAVES) void decode_ke
     }
     n = n < 0 ? 0 : n;
     total += uni(wave_reduce_sum(n));
+    filled += uni(wave_reduce_sum(n > 0 ? 1 : 0));
   }
   // The host guarantees num_seqs * Hkv * (chunks per sequence) < 2^30, so
   // every chunk-list index below fits an int.
+  //
+  // The split cuts a weighted list: each unit (sequence, KV head) counts as
+  // its chunks plus `charge` more in front of them, for the fixed costs a
+  // unit brings to the wavefront that starts it (the sequence's length and
+  // table entries, the query, a partial record).  Wavefront w takes the
+  // weighted positions [w C, (w + 1) C), i.e. the chunks whose position (the
+  // chunk's index plus the charges of its unit and the units before it)
+  // falls there.  With no charge (fixed partitions) positions are chunk
+  // indices.
+  const int charge = p.unit_charge;
   const int W = uni(total * Hkv);
+  const int Wt = uni(W + charge * Hkv * filled);
   int C = p.chunk_fixed;
   if (C <= 0) {
-    C = (W + p.num_waves - 1) / p.num_waves;
+    C = (Wt + p.num_waves - 1) / p.num_waves;
     if (C < p.chunk_min) C = p.chunk_min;
   }
   C = uni(C);
-  if ((int64_t)wave * C >= W) return;
-  const int a = uni(wave * C);
-  const int b = (W - a > C) ? a + C : W;
+  if ((int64_t)wave * C >= Wt) return;
+  int a = uni(wave * C);
+  int b = (Wt - a > C) ? a + C : Wt;
+  if (charge > 0) {
+    // The first chunk at or after weighted position a, and the one at or
+    // after b (W when there is none).
+    const int xa = a, xb = b;
+    a = W;
+    b = W;
+    bool fa = false, fb = false;
+    int carry_w = 0, carry_c = 0;
+    for (int base = 0; base < S && !(fa && fb); base += 64) {
+      const int si = base + lane;
+      int n = 0;
+      if (si < S) n = chunks_of(p.seq_lens[si], max_len, p.window);
+      n = n < 0 ? 0 : n;
+      const int span = n > 0 ? Hkv * (n + charge) : 0;
+      const int incl_w = wave_incl_scan(span, lane);
+      const int incl_c = wave_incl_scan(Hkv * n, lane);
+      const int lo_w = carry_w + incl_w - span;
+      const uint64_t hit_a = __ballot(n > 0 && lo_w <= xa && xa < lo_w + span);
+      const uint64_t hit_b = __ballot(n > 0 && lo_w <= xb && xb < lo_w + span);
+      if (hit_a && !fa) {
+        const int l0 = uni(__builtin_ctzll(hit_a));
+        const int nn = readlane(n, l0), rel = xa - readlane(lo_w, l0);
+        const int h = rel / (nn + charge), off = rel - h * (nn + charge);
+        a = uni(carry_c + readlane(incl_c, l0) - Hkv * nn + h * nn + (off < charge ? 0 : off - charge));
+        fa = true;
+      }
+      if (hit_b && !fb) {
+        const int l0 = uni(__builtin_ctzll(hit_b));
+        const int nn = readlane(n, l0), rel = xb - readlane(lo_w, l0);
+        const int h = rel / (nn + charge), off = rel - h * (nn + charge);
+        b = uni(carry_c + readlane(incl_c, l0) - Hkv * nn + h * nn + (off < charge ? 0 : off - charge));
+        fb = true;
+      }
+      carry_w += readlane(incl_w, 63);
+      carry_c += readlane(incl_c, 63);
+    }
+    if (a >= b) return;     // a range inside one unit's charge (C > charge rules it out)
+  }
 
-  // Pass 2: the sequences holding chunks a and b - 1, and the chunks of
-  // the sequences before them.
-  int sa = 0, sz = 0, before_a = 0, before_z = 0;
+  // Pass 2: the sequences holding chunks a and b - 1, the chunks of the
+  // sequences before them, and how many of those have chunks.
+  int sa = 0, sz = 0, before_a = 0, before_z = 0, filled_a = 0, filled_z = 0;
   {
-    int carry = 0;
+    int carry = 0, carry_f = 0;
     bool found_a = false, found_z = false;
     for (int base = 0; base < S && !(found_a && found_z); base += 64) {
       const int si = base + lane;
@@ -865,6 +924,7 @@ __global__ __launch_bounds__(kDecodeThreads, PA_DECODE_MIN_WAVES) void decode_ke
       if (si < S) n = chunks_of(p.seq_lens[si], max_len, p.window);
       n = n < 0 ? 0 : n;
       const int incl = wave_incl_scan(n, lane);
+      const int incl_f = wave_incl_scan(n > 0 ? 1 : 0, lane);
       const int lo = Hkv * (carry + incl - n), hi = Hkv * (carry + incl);
       const uint64_t hit_a = __ballot(n > 0 && lo <= a && a < hi);
       const uint64_t hit_z = __ballot(n > 0 && lo <= b - 1 && b - 1 < hi);
@@ -872,15 +932,18 @@ __global__ __launch_bounds__(kDecodeThreads, PA_DECODE_MIN_WAVES) void decode_ke
         const int l0 = uni(__builtin_ctzll(hit_a));
         sa = uni(base + l0);
         before_a = uni(carry + readlane(incl - n, l0));
+        filled_a = uni(carry_f + readlane(incl_f, l0) - 1);
         found_a = true;
       }
       if (hit_z && !found_z) {
         const int l0 = uni(__builtin_ctzll(hit_z));
         sz = uni(base + l0);
         before_z = uni(carry + readlane(incl - n, l0));
+        filled_z = uni(carry_f + readlane(incl_f, l0) - 1);
         found_z = true;
       }
       carry += readlane(incl, 63);
+      carry_f += readlane(incl_f, 63);
     }
   }
   Cursor cur;
@@ -889,18 +952,21 @@ __global__ __launch_bounds__(kDecodeThreads, PA_DECODE_MIN_WAVES) void decode_ke
     const int ha = uni((a - Hkv * before_a) / na);
     const int u0a = Hkv * before_a + ha * na;
     const int a_end = u0a + na;
-    cur.cur = Piece{sa, ha, na, La, u0a, a - u0a, (b < a_end ? b : a_end) - u0a};
+    // Weighted position of a unit's first chunk: its index plus the charges
+    // of the units up to and including it.
+    const int uwa = u0a + charge * (Hkv * filled_a + ha + 1);
+    cur.cur = Piece{sa, ha, na, La, u0a, a - u0a, (b < a_end ? b : a_end) - u0a, uwa};
     cur.j = cur.cur.j0;
     cur.phase = 0;
     cur.a_end = a_end;
     cur.a_s = sa;
     cur.a_h = ha;
-    cur.z = Piece{0, 0, 0, 0, a_end, 0, 0};  // no piece Z: j1 = 0, middle walk ends at a_end
+    cur.z = Piece{0, 0, 0, 0, a_end, 0, 0, 0};  // no piece Z: j1 = 0, middle walk ends at a_end
     if (b > a_end) {
       const int Lz = sload(p.seq_lens, sz), nz = chunks_of(Lz, max_len, p.window);
       const int hz = uni((b - 1 - Hkv * before_z) / nz);
       const int u0z = Hkv * before_z + hz * nz;
-      cur.z = Piece{sz, hz, nz, Lz, u0z, 0, b - u0z};
+      cur.z = Piece{sz, hz, nz, Lz, u0z, 0, b - u0z, u0z + charge * (Hkv * filled_z + hz + 1)};
     }
   }
   if constexpr (APPEND) append_range<D, FP8>(p, cur, b, max_len, lane);

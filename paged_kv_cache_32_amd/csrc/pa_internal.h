@@ -75,6 +75,8 @@ struct DecodeParams {
   int32_t num_waves;            // wavefronts launched
   int32_t chunk_min;            // auto split: fewest chunks a wavefront takes
   int32_t chunk_fixed;          // > 0: every wavefront takes this many chunks
+  int32_t unit_charge;          // auto split: chunks each unit counts for beyond its own (0 with
+                                // fixed partitions)
   int32_t window;               // > 0: attend to the last `window` tokens only
   int32_t ring;                 // != 0: each table row is a ring of max_blocks entries, logical
                                 // block b at entry b % max_blocks (local layers, window > 0)

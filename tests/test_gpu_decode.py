@@ -171,3 +171,20 @@ def test_long_units_split_into_many_pieces_match_the_oracle(kv):
         t = H.device_inputs(w)
         mx, _ = H.step_and_check(w, t, partition_tokens=part, label=f"long units {kv} part={part}")
         print(f"[decode] long units {kv} part={part}: max-abs {mx:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_automatic_split_over_many_short_and_a_few_long_units(kv):
+    """The automatic split (partition_tokens = 0) over a batch that mixes
+    units of 1 to 4 chunks with units of hundreds: wavefronts then cover from
+    part of one unit to dozens of whole ones.  On the fp8 cache the split
+    charges every unit extra chunks for its fixed costs, so wavefront ranges
+    are cut in a weighted list and the merge finds a unit's pieces through
+    the same weights; every row is checked against the oracle."""
+    rng = np.random.default_rng(81)
+    short = rng.integers(1, 65, 180).tolist()
+    lens = short[:60] + [9000] + short[60:120] + [7001, 4100] + short[120:] + [12000]
+    w = W.random_workload(82, len(lens), 16, 8, 128, 16, 0, kv_dtype=kv, lens=lens)
+    t = H.device_inputs(w)
+    mx, _ = H.step_and_check(w, t, partition_tokens=0, label=f"mixed units {kv}")
+    print(f"[decode] mixed units {kv}: max-abs {mx:.2e}", flush=True)
