@@ -161,20 +161,21 @@ pa_status pa_decode_workspace_init(void* workspace, size_t workspace_bytes, void
  * same kernel launch.
  *   workspace     device buffer of >= pa_decode_workspace_size(...) bytes,
  *                 zero-filled before its first use (pa_decode_workspace_init
- *                 or any zero fill).  Its first max(U, 16384) * 4 bytes,
- *                 U = num_seqs * num_kv_heads, hold one merge counter per
- *                 (sequence, KV head) unit, and every call that runs to
- *                 completion leaves them at zero; the rest holds partial
- *                 results that each call writes before reading.  So one
- *                 workspace serves any number of calls of any sizes that
- *                 fit (any partition_tokens, window, dtype, group or
- *                 head_dim) as long as U <= 16384 in each: their counters
- *                 all lie in the same first 64 KiB, which nothing else uses.
- *                 A call with U > 16384 needs a workspace zero-filled since
- *                 it was last used with a different U, and so does any call
- *                 after one that did not run to completion.  A workspace
- *                 must not be shared by calls that may run at the same time
- *                 (different streams).
+ *                 or any zero fill).  Its first max(U, 16384) * 4 + 65,536
+ *                 bytes, U = num_seqs * num_kv_heads, hold merge counters:
+ *                 one per (sequence, KV head) unit, then 16,384 for the
+ *                 groups of pieces a long unit's merge tree counts; every
+ *                 call that runs to completion leaves them at zero.  The
+ *                 rest holds partial results that each call writes before
+ *                 reading.  So one workspace serves any number of calls of
+ *                 any sizes that fit (any partition_tokens, window, dtype,
+ *                 group or head_dim) as long as U <= 16384 in each: their
+ *                 counters all lie in the same first 128 KiB, which nothing
+ *                 else uses.  A call with U > 16384 needs a workspace
+ *                 zero-filled since it was last used with a different U, and
+ *                 so does any call after one that did not run to
+ *                 completion.  A workspace must not be shared by calls that
+ *                 may run at the same time (different streams).
  * Results differ from exact arithmetic only by float32 rounding.            */
 pa_status pa_decode(const pa_cache_desc* cache, const void* q, int32_t num_seqs,
                     int32_t num_q_heads, const void* k_cache, const void* v_cache,

@@ -104,7 +104,7 @@ typedef struct {
 } pa_cascade_device_plan;
 
 /* DEVICE workspace bytes of pa_decode_cascade(_fp8): the private decode's
- * workspace first (its merge counters in the first max(U, 16384) * 4 bytes,
+ * workspace first (its merge counters in the first max(U, 16384) * 4 + 65,536 bytes,
  * U = num_seqs * num_kv_heads), then the private outputs and the partial
  * records, which each call writes before reading.  Zero-fill it once (as
  * pa_decode's); it then serves any number of calls with any plan and sizes

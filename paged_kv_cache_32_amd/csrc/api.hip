@@ -215,6 +215,10 @@ pa_status decode(const pa_cache_desc* cache, const void* q, int32_t num_seqs, in
   p.lse = lse;
   p.partials = reinterpret_cast<float*>(ws + lay.partials_off);
   p.counters = reinterpret_cast<int32_t*>(ws + lay.counters_off);
+  // The merge tree counts groups of pieces by record slot (2 per wavefront).
+  p.group_counters = 2 * num_waves <= pa::kGroupCounters
+                         ? reinterpret_cast<int32_t*>(ws + lay.group_counters_off)
+                         : nullptr;
   p.num_seqs = num_seqs;
   p.num_q_heads = num_q_heads;
   p.num_kv_heads = cache->num_kv_heads;

@@ -249,7 +249,9 @@ struct Cursor {
 // A partial piece on its way to being counted in: stored (its stores must
 // complete first), then counted (the counter's old value is in flight).
 struct Pending {
-  int state;       // 0 empty/done, 1 stored, 2 counted, 3 to be merged here
+  int state;       // 0 empty/done, 1 stored, 2 counted, 3 unit to be merged here, 4 group to be
+                   // merged here
+  int lvl;         // counted on: 1 its group's counter, 0 the unit's
   int s, h, u0, n, uw;
   int prior;       // lane 0: counter value before this piece was counted
 };
@@ -636,21 +638,46 @@ __device__ __forceinline__ int piece_slot(int w, int w0, bool second) {
   return (w == w0 && second) ? 2 * w + 1 : 2 * w;
 }
 
-// Merge the partial softmax states of unit (s, h), pieces from wavefronts
-// w0..w1, into out (run by the wavefront that counted in the last piece):
-// out = sum_p e^(m_p - M) acc_p / sum_p e^(m_p - M) l_p, M = max_p m_p, taken
-// one piece at a time with a running maximum.  Lane l handles kIt adjacent
-// 4-float groups of one query head's output row per pass, so one load of a
-// piece's (m, l) serves all of them; the loads of kBatch pieces are issued
-// together (one memory round trip per kBatch pieces: this merge is the tail
-// of the launch when a unit is split over many wavefronts).
+// Where a split unit's pieces are: wavefronts w0..w1, one piece each.  A
+// unit of more than kMergeGroup pieces is merged as a tree when the
+// workspace has group counters: the last piece counted in of each group of
+// kMergeGroup consecutive pieces merges its group into the record slot of
+// the group's first piece, and the last group counted in merges the group
+// records.  Each level is then at most a few memory round trips instead of
+// one per kMergeGroup pieces of the unit (a unit of a long sequence split
+// over a hundred wavefronts otherwise ends the launch with a long serial
+// merge).
+constexpr int kMergeGroup = PA_DECODE_MERGE_BATCH;
+struct UnitShape {
+  int w0, w1;
+  bool second;     // the piece in wavefront w0 is that wavefront's second piece
+  bool tree;
+};
+__device__ __forceinline__ UnitShape unit_shape(const DecodeParams& p, const Pending& pd, int C) {
+  UnitShape u;
+  u.w0 = pd.uw / C;
+  u.w1 = (pd.uw + pd.n - 1) / C;
+  u.second = pd.u0 > 0 && pd.uw - 1 - p.unit_charge >= u.w0 * C;
+  u.tree = p.group_counters != nullptr && u.w1 - u.w0 + 1 > kMergeGroup;
+  return u;
+}
+
+// Merge the partial softmax states held in the record slots of wavefronts
+// wf, wf + step, .. <= wl (pieces, or with step kMergeGroup the group
+// records) of unit (s, h): out = sum_p e^(m_p - M) acc_p / sum_p e^(m_p - M)
+// l_p, M = max_p m_p, taken one record at a time with a running maximum.
+// The result goes to out (and lse) when dst_slot < 0, else into record slot
+// dst_slot as a record of its own (acc = the weighted sum, m = M, l = the
+// weight), with the same device-coherent stores as the pieces.  Lane l
+// handles kIt adjacent 4-float groups of one query head's row per pass, so
+// one load of a record's (m, l) serves all of them; the loads of kBatch
+// records are issued together (one memory round trip per kBatch records).
 template <int D, int kIt, int kBatch>
-__device__ __forceinline__ void merge_unit(const DecodeParams& p, const Pending& pd, int C, int lane) {
+__device__ __forceinline__ void merge_records(const DecodeParams& p, const Pending& pd, const UnitShape& u,
+                                              int wf, int wl, int step, int dst_slot, int lane) {
   const int G = p.group;
   const int groups = G * D / 4;
   const int rec_bytes = G * (D + 4) * 4;
-  const int w0 = pd.uw / C, w1 = (pd.uw + pd.n - 1) / C;
-  const bool second = pd.u0 > 0 && pd.uw - 1 - p.unit_charge >= w0 * C;
   f32x4* o = reinterpret_cast<f32x4*>(p.out + ((int64_t)pd.s * p.num_q_heads + (int64_t)pd.h * G) * D);
   for (int e0 = 0; e0 < groups; e0 += 64 * kIt) {
     const int e_first = e0 + lane * kIt;
@@ -660,19 +687,19 @@ __device__ __forceinline__ void merge_unit(const DecodeParams& p, const Pending&
     f32x4 num[kIt];
 #pragma unroll
     for (int it = 0; it < kIt; ++it) num[it] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int wb = w0; wb <= w1; wb += kBatch) {
+    for (int wb = wf; wb <= wl; wb += kBatch * step) {
       f32x4 ml[kBatch], acc[kBatch][kIt];
 #pragma unroll
       for (int b = 0; b < kBatch; ++b) {
-        const int w = (wb + b <= w1) ? wb + b : w1;
-        const auto r = record_rsrc(p.partials + (int64_t)piece_slot(w, w0, second) * (rec_bytes / 4), rec_bytes);
+        const int w = (wb + b * step <= wl) ? wb + b * step : wb;
+        const auto r = record_rsrc(p.partials + (int64_t)piece_slot(w, u.w0, u.second) * (rec_bytes / 4), rec_bytes);
         ml[b] = load_record(r, in ? (G * D + g * 4) * 4 : 0);
 #pragma unroll
         for (int it = 0; it < kIt; ++it) acc[b][it] = load_record(r, in ? ((d40 + it) * G + g) * 16 : 0);
       }
 #pragma unroll
       for (int b = 0; b < kBatch; ++b) {
-        if (wb + b <= w1) {
+        if (wb + b * step <= wl) {
           const float m_new = __builtin_fmaxf(M, ml[b][0]);
           const float a = (M == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(M - m_new);
           const float f = (ml[b][0] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(ml[b][0] - m_new);
@@ -683,38 +710,90 @@ __device__ __forceinline__ void merge_unit(const DecodeParams& p, const Pending&
         }
       }
     }
+    if (dst_slot < 0) {
 #pragma unroll
-    for (int it = 0; it < kIt; ++it)
-      if (in) o[e_first + it] = num[it] * (p.out_scale / den);
-    if (p.lse && in && d40 == 0)
-      p.lse[(int64_t)pd.s * p.num_q_heads + (int64_t)pd.h * G + g] = M + __builtin_amdgcn_logf(den);
+      for (int it = 0; it < kIt; ++it)
+        if (in) o[e_first + it] = num[it] * (p.out_scale / den);
+      if (p.lse && in && d40 == 0)
+        p.lse[(int64_t)pd.s * p.num_q_heads + (int64_t)pd.h * G + g] = M + __builtin_amdgcn_logf(den);
+    } else {
+      const auto r = record_rsrc(p.partials + (int64_t)dst_slot * (rec_bytes / 4), rec_bytes);
+#pragma unroll
+      for (int it = 0; it < kIt; ++it)
+        if (in) store_record(r, ((d40 + it) * G + g) * 16, num[it]);
+      if (in && d40 == 0) store_record(r, (G * D + g * 4) * 4, f32x4{M, den, 0.f, 0.f});
+    }
   }
 }
 
-// Count a stored piece in (its stores have completed).
-__device__ __forceinline__ void count_piece(const DecodeParams& p, Pending& pd, int lane) {
+// Count a stored piece in (its stores have completed): on its group's
+// counter when the unit is merged as a tree, else on the unit's.
+__device__ __forceinline__ void count_piece(const DecodeParams& p, Pending& pd, int C, int wave, int lane) {
+  const UnitShape u = unit_shape(p, pd, C);
   int32_t* counter = p.counters + (int64_t)pd.s * p.num_kv_heads + pd.h;
+  pd.lvl = 0;
+  if (u.tree) {
+    const int g = (wave - u.w0) / kMergeGroup;
+    counter = p.group_counters + piece_slot(u.w0 + g * kMergeGroup, u.w0, u.second);
+    pd.lvl = 1;
+  }
   pd.prior = 0;
   if (lane == 0) pd.prior = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   pd.state = 2;
 }
 
-// Read the counter's old value: the wavefront that counted in the unit's
-// last piece merges all of them (state 3) and then re-arms the counter for
-// the next call; the others are done with the piece.
-__device__ __forceinline__ void resolve_piece(Pending& pd, int C) {
+// Read the counter's old value.  The wavefront that counted in the last
+// piece of a group merges the group (state 4); the one that counted in the
+// unit's last piece, or last group, merges the unit (state 3) and then
+// re-arms the counter for the next call; the others are done.
+__device__ __forceinline__ void resolve_piece(const DecodeParams& p, Pending& pd, int C, int wave) {
   const int prior = readlane(pd.prior, 0);
-  const int pieces = (pd.uw + pd.n - 1) / C - pd.uw / C + 1;
-  pd.state = (prior == pieces - 1) ? 3 : 0;
+  const UnitShape u = unit_shape(p, pd, C);
+  const int pieces = u.w1 - u.w0 + 1;
+  if (pd.lvl == 1) {
+    const int g = (wave - u.w0) / kMergeGroup;
+    const int size = pieces - g * kMergeGroup < kMergeGroup ? pieces - g * kMergeGroup : kMergeGroup;
+    pd.state = (prior == size - 1) ? 4 : 0;
+  } else {
+    const int items = u.tree ? (pieces + kMergeGroup - 1) / kMergeGroup : pieces;
+    pd.state = (prior == items - 1) ? 3 : 0;
+  }
 }
 
+// The merges this wavefront owes, at the end of its range: a group (state
+// 4) is merged into its first piece's slot, its counter re-armed, and the
+// group counted in on the unit's counter once the group record's stores
+// have completed, which may leave the unit's merge to this wavefront too
+// (state 3).  One call site of the merge keeps a single copy of its code.
 template <int D>
-__device__ __forceinline__ void merge_and_rearm(const DecodeParams& p, Pending& pd, int C, int lane) {
-  merge_unit<D, D / 32, PA_DECODE_MERGE_BATCH>(p, pd, C, lane);
-  if (lane == 0)
-    __hip_atomic_store(p.counters + (int64_t)pd.s * p.num_kv_heads + pd.h, 0, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-  pd.state = 0;
+__device__ __forceinline__ void merge_owed(const DecodeParams& p, Pending& pd, int C, int wave, int lane) {
+  const UnitShape u = unit_shape(p, pd, C);
+  while (pd.state >= 3) {
+    const bool group = pd.state == 4;
+    int wf = u.w0, wl = u.w1, step = u.tree ? kMergeGroup : 1, dst = -1;
+    if (group) {
+      wf = u.w0 + (wave - u.w0) / kMergeGroup * kMergeGroup;
+      wl = wf + kMergeGroup - 1 < u.w1 ? wf + kMergeGroup - 1 : u.w1;
+      step = 1;
+      dst = piece_slot(wf, u.w0, u.second);
+    }
+    merge_records<D, D / 32, kMergeGroup>(p, pd, u, wf, wl, step, dst, lane);
+    if (group) {
+      wait_vmcnt<0>();
+      if (lane == 0) {
+        __hip_atomic_store(p.group_counters + dst, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        pd.prior = __hip_atomic_fetch_add(p.counters + (int64_t)pd.s * p.num_kv_heads + pd.h, 1, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+      }
+      pd.lvl = 0;
+      resolve_piece(p, pd, C, wave);
+    } else {
+      if (lane == 0)
+        __hip_atomic_store(p.counters + (int64_t)pd.s * p.num_kv_heads + pd.h, 0, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      pd.state = 0;
+    }
+  }
 }
 
 // Per-wavefront state carried across stages.
@@ -792,15 +871,15 @@ __device__ __forceinline__ void finish_stage(const DecodeParams& p, const Stage&
 // owes is left for the end of its range, where the registers that hold the
 // pipeline's loads are free for the merge's own.
 template <int D, bool FP8, int LOADS>
-__device__ __forceinline__ void settle(const DecodeParams& p, WaveState<D, FP8>& ws, int C, int lane) {
+__device__ __forceinline__ void settle(const DecodeParams& p, WaveState<D, FP8>& ws, int C, int wave, int lane) {
 #pragma unroll
   for (int i = 0; i < 2; ++i)
-    if (ws.pend[i].state == 2) resolve_piece(ws.pend[i], C);
+    if (ws.pend[i].state == 2) resolve_piece(p, ws.pend[i], C, wave);
   if (ws.pend[0].state == 1 || ws.pend[1].state == 1) {
     wait_vmcnt<LOADS>();
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-      if (ws.pend[i].state == 1) count_piece(p, ws.pend[i], lane);
+      if (ws.pend[i].state == 1) count_piece(p, ws.pend[i], C, wave, lane);
   }
 }
 
@@ -990,12 +1069,12 @@ __global__ __launch_bounds__(kDecodeThreads, PA_DECODE_MIN_WAVES) void decode_ke
   for (;;) {
     const Stage stb = next_stage<NSUB>(cur, p, max_len);
     const bool bad_b = issue_stage<D, FP8, NSUB>(p, stb, B, q_off, k_off, v_off);
-    settle<D, FP8, Buf::kLoads>(p, ws, C, lane);
+    settle<D, FP8, Buf::kLoads>(p, ws, C, wave, lane);
     finish_stage<D, FP8, NSUB>(p, sta, bad_a, A, ws, wave, lane);
     if (!(stb.flags & kValid)) break;
     sta = next_stage<NSUB>(cur, p, max_len);
     bad_a = issue_stage<D, FP8, NSUB>(p, sta, A, q_off, k_off, v_off);
-    settle<D, FP8, Buf::kLoads>(p, ws, C, lane);
+    settle<D, FP8, Buf::kLoads>(p, ws, C, wave, lane);
     finish_stage<D, FP8, NSUB>(p, stb, bad_b, B, ws, wave, lane);
     if (!(sta.flags & kValid)) break;
   }
@@ -1003,9 +1082,9 @@ __global__ __launch_bounds__(kDecodeThreads, PA_DECODE_MIN_WAVES) void decode_ke
   wait_vmcnt<0>();
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    if (ws.pend[i].state == 1) count_piece(p, ws.pend[i], lane);
-    if (ws.pend[i].state == 2) resolve_piece(ws.pend[i], C);
-    if (ws.pend[i].state == 3) merge_and_rearm<D>(p, ws.pend[i], C, lane);
+    if (ws.pend[i].state == 1) count_piece(p, ws.pend[i], C, wave, lane);
+    if (ws.pend[i].state == 2) resolve_piece(p, ws.pend[i], C, wave);
+    if (ws.pend[i].state >= 3) merge_owed<D>(p, ws.pend[i], C, wave, lane);
   }
 }
 

@@ -70,7 +70,10 @@ struct DecodeParams {
   float* lse;                   // null, or [S][Hq]: log2 of each row's softmax sum in logit
                                 // units of qk_scale (m + log2 l); -inf for empty rows
   float* partials;              // [2 * num_waves][G * (D + 4)]
-  int32_t* counters;            // [S * Hkv] pieces stored per unit; zero between calls
+  int32_t* counters;            // [S * Hkv] pieces (or groups) counted in per unit; zero between calls
+  int32_t* group_counters;      // null, or [kGroupCounters] pieces counted in per merge-tree group,
+                                // indexed by the record slot of the group's first piece; zero
+                                // between calls
   int32_t num_seqs, num_q_heads, num_kv_heads, group, head_dim, block_size, num_blocks, max_blocks;
   int32_t num_waves;            // wavefronts launched
   int32_t chunk_min;            // auto split: fewest chunks a wavefront takes
@@ -199,16 +202,19 @@ int decode_resident_waves(int head_dim, bool fp8);
 
 // Workspace carve-up shared by the size query and the launchers.  The
 // per-unit counters come first, in a region of at least kMinCounterUnits
-// entries: for every call with num_seqs * num_kv_heads <= kMinCounterUnits
-// the counters then occupy the same first 64 KiB, which nothing else in the
-// workspace is ever used for, whatever the other sizes (wave count, group,
-// head_dim, partition) of the calls sharing it.  Each call leaves its
-// counters at zero, so such calls can share one workspace that was zero-
-// filled once.  The partial records follow; they are always written before
-// they are read, so their contents between calls do not matter.
+// entries, then kGroupCounters counters of the merge tree's groups (indexed
+// by record slot): for every call with num_seqs * num_kv_heads <=
+// kMinCounterUnits the counters then occupy the same first 128 KiB, which
+// nothing else in the workspace is ever used for, whatever the other sizes
+// (wave count, group, head_dim, partition) of the calls sharing it.  Each
+// call leaves its counters at zero, so such calls can share one workspace
+// that was zero-filled once.  The partial records follow; they are always
+// written before they are read, so their contents between calls do not
+// matter.
 constexpr int64_t kMinCounterUnits = 16384;
+constexpr int64_t kGroupCounters = 16384;   // record slots (2 per wavefront) the tree can count
 struct WorkspaceLayout {
-  size_t counters_off, partials_off, total;
+  size_t counters_off, group_counters_off, partials_off, total;
 };
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline size_t counter_region_bytes(int64_t units) {
@@ -218,7 +224,8 @@ inline WorkspaceLayout workspace_layout(int64_t num_waves, int group, int head_d
                                         int num_seqs, int num_kv_heads) {
   WorkspaceLayout w;
   w.counters_off = 0;
-  w.partials_off = counter_region_bytes((int64_t)num_seqs * num_kv_heads);
+  w.group_counters_off = counter_region_bytes((int64_t)num_seqs * num_kv_heads);
+  w.partials_off = w.group_counters_off + (size_t)kGroupCounters * sizeof(int32_t);
   const size_t part = (size_t)(2 * num_waves) * (size_t)group * (size_t)(head_dim + 4) * sizeof(float);
   w.total = align_up(w.partials_off + part, 256);
   return w;
