@@ -639,15 +639,19 @@ __device__ __forceinline__ int piece_slot(int w, int w0, bool second) {
 }
 
 // Where a split unit's pieces are: wavefronts w0..w1, one piece each.  A
-// unit of more than kMergeGroup pieces is merged as a tree when the
+// unit of more than kTreeMinPieces pieces is merged as a tree when the
 // workspace has group counters: the last piece counted in of each group of
 // kMergeGroup consecutive pieces merges its group into the record slot of
 // the group's first piece, and the last group counted in merges the group
-// records.  Each level is then at most a few memory round trips instead of
-// one per kMergeGroup pieces of the unit (a unit of a long sequence split
-// over a hundred wavefronts otherwise ends the launch with a long serial
-// merge).
+// records.  The group merges run on many wavefronts at once, as their
+// groups complete, so the unit's last merge reads a handful of group
+// records instead of every piece (a unit of a long sequence split over a
+// hundred wavefronts otherwise ends the launch with a long serial merge).
+// Measured, the tree pays from 9 pieces on: with it only above 32 pieces
+// the long-context batch (32 pieces per unit) took 342-345 us against
+// 334-341 us.
 constexpr int kMergeGroup = PA_DECODE_MERGE_BATCH;
+constexpr int kTreeMinPieces = kMergeGroup;
 struct UnitShape {
   int w0, w1;
   bool second;     // the piece in wavefront w0 is that wavefront's second piece
@@ -658,7 +662,7 @@ __device__ __forceinline__ UnitShape unit_shape(const DecodeParams& p, const Pen
   u.w0 = pd.uw / C;
   u.w1 = (pd.uw + pd.n - 1) / C;
   u.second = pd.u0 > 0 && pd.uw - 1 - p.unit_charge >= u.w0 * C;
-  u.tree = p.group_counters != nullptr && u.w1 - u.w0 + 1 > kMergeGroup;
+  u.tree = p.group_counters != nullptr && u.w1 - u.w0 + 1 > kTreeMinPieces;
   return u;
 }
 
