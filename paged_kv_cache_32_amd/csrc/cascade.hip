@@ -321,6 +321,12 @@ __global__ __launch_bounds__(kSegThreads) void segment_kernel(const SegmentParam
 }
 
 // One thread per (sequence, query head, 4 dims).
+// One thread per (sequence, query head, 4 dims).  The parts are merged with
+// a running maximum, kCombineBatch at a time: the slots of a batch are
+// loaded together, then all of their records' (m, l) and acc pieces, so a
+// sequence with up to kCombineBatch shared parts costs three dependent
+// memory round trips (its part range, the slots, the records).
+constexpr int kCombineBatch = 4;
 __global__ __launch_bounds__(256) void combine_kernel(const CombineParams p) {
   const int q4 = p.head_dim / 4;
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -330,34 +336,51 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineParams p) {
   const int s = (int)(row / p.num_q_heads), i = (int)(row - (int64_t)s * p.num_q_heads);
   const int D = p.head_dim;
   const int k0 = p.parts_off[s], k1 = p.parts_off[s + 1];
-  float lse_p = p.part_lse[row];
-  float M = lse_p;
-  for (int k = k0; k < k1; ++k) {
-    if ((unsigned)p.parts[k] >= (unsigned)p.num_slots) {
-      lse_p = __builtin_nanf("");
-      break;
-    }
-    const float* rec = p.partials + ((int64_t)p.parts[k] * p.num_q_heads + i) * (D + 4);
-    M = __builtin_fmaxf(M, rec[D] + __builtin_amdgcn_logf(rec[D + 1]));
-  }
+  const float lse_p = p.part_lse[row];
+  const f32x4 out_p = reinterpret_cast<const f32x4*>(p.part_out + row * D)[d4];
+  // The private part: normalized output out_p, weight 2^lse_p.
+  float M = lse_p, den = 0.f;
   f32x4 num = {0.f, 0.f, 0.f, 0.f};
-  float den = 0.f;
   if (lse_p != kNegInf) {
-    const float w = __builtin_amdgcn_exp2f(lse_p - M);
-    num = reinterpret_cast<const f32x4*>(p.part_out + row * D)[d4] * w;
-    den = w;
+    num = out_p;
+    den = 1.f;
   }
-  for (int k = k0; k < k1 && lse_p == lse_p; ++k) {
-    const float* rec = p.partials + ((int64_t)p.parts[k] * p.num_q_heads + i) * (D + 4);
-    const float lk = rec[D + 1];
-    const float w = __builtin_amdgcn_exp2f(rec[D] + __builtin_amdgcn_logf(lk) - M);
-    num += reinterpret_cast<const f32x4*>(rec)[d4] * (w * p.out_scale / lk);
-    den += w;
+  bool bad = lse_p != lse_p;
+  for (int kb = k0; kb < k1 && !bad; kb += kCombineBatch) {
+    int slot[kCombineBatch];
+#pragma unroll
+    for (int b = 0; b < kCombineBatch; ++b) slot[b] = p.parts[kb + b < k1 ? kb + b : kb];
+    f32x4 acc[kCombineBatch];
+    float m[kCombineBatch], l[kCombineBatch];
+#pragma unroll
+    for (int b = 0; b < kCombineBatch; ++b) {
+      const bool ok = (unsigned)slot[b] < (unsigned)p.num_slots;
+      if (kb + b < k1 && !ok) bad = true;
+      const float* rec = p.partials + ((int64_t)(ok ? slot[b] : 0) * p.num_q_heads + i) * (D + 4);
+      m[b] = rec[D];
+      l[b] = rec[D + 1];
+      acc[b] = reinterpret_cast<const f32x4*>(rec)[d4];
+    }
+#pragma unroll
+    for (int b = 0; b < kCombineBatch; ++b) {
+      if (kb + b < k1) {
+        const float lse_k = m[b] + __builtin_amdgcn_logf(l[b]);
+        const float m_new = __builtin_fmaxf(M, lse_k);
+        const float a = (M == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(M - m_new);
+        const float w = (lse_k == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(lse_k - m_new);
+        num = num * a + acc[b] * (w * p.out_scale / l[b]);
+        den = den * a + w;
+        M = m_new;
+      }
+    }
   }
   f32x4 o;
   if (M == kNegInf) o = f32x4{0.f, 0.f, 0.f, 0.f};   // nothing to attend to
   else o = num * (1.f / den);
-  if (lse_p != lse_p) o = f32x4{lse_p, lse_p, lse_p, lse_p};   // invalid length or slot: NaN rows
+  if (bad) {
+    const float nan = __builtin_nanf("");
+    o = f32x4{nan, nan, nan, nan};                   // invalid length or slot: NaN rows
+  }
   reinterpret_cast<f32x4*>(p.out + row * D)[d4] = o;
 }
 
