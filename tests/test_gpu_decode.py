@@ -188,3 +188,26 @@ def test_automatic_split_over_many_short_and_a_few_long_units(kv):
     t = H.device_inputs(w)
     mx, _ = H.step_and_check(w, t, partition_tokens=0, label=f"mixed units {kv}")
     print(f"[decode] mixed units {kv}: max-abs {mx:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_merge_tree_group_boundaries(kv):
+    """With 16-token partitions a unit of n chunks is split into n pieces,
+    one per wavefront.  Units of 8, 9, 16, 17, 64 and 65 pieces sit on
+    either side of the merge tree's group size (8 pieces) and of its first
+    and eighth group boundaries; 1 and 7 pieces merge flat."""
+    lens = [128, 129, 256, 257, 1024, 1040, 16, 112, 2000]
+    w = W.random_workload(83, len(lens), 16, 2, 128, 16, 0, kv_dtype=kv, lens=lens)
+    t = H.device_inputs(w)
+    H.step_and_check(w, t, partition_tokens=16, label=f"tree boundaries {kv}")
+
+
+def test_many_pieces_without_group_counters():
+    """Fixed partitions that launch more than 8,192 wavefronts leave the
+    merge tree's group counters unused (2 per wavefront do not fit): every
+    unit, up to 128 pieces, then merges in one level."""
+    lens = [2000, 1999, 1500, 16, 1, 700, 2048, 1234, 999, 1888, 32, 2047, 1024, 512, 64, 1600]
+    w = W.random_workload(84, len(lens), 64, 8, 128, 16, 0, kv_dtype="bf16", lens=lens)
+    assert len(lens) * 8 * w.max_blocks_per_seq > 8192   # wavefronts at one chunk each
+    t = H.device_inputs(w)
+    H.step_and_check(w, t, partition_tokens=16, label="one-level merges")
