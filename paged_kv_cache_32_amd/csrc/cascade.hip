@@ -39,6 +39,7 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kSlack = 8.0f;   // the running maximum is raised only when it grows by more
+constexpr float kSlackWeight = 256.0f;   // 2^kSlack
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ __forceinline__ i16x4 as_i16x4(u32x2 v) { return __builtin_bit_cast(i16x4, v); }
@@ -218,20 +219,34 @@ __global__ __launch_bounds__(kSegThreads) void segment_kernel(const SegmentParam
   // softmax in base 2 over the lane's 8 logits (tokens 4 qd + i of either
   // tile, column col), then O^T += V^T P^T with k slots 8 qd .. 8 qd + 7
   // pairing the A operand's 8 tokens with P split into bf16 hi and lo.
-  // qk_scale >= 0, so the maximum of the scaled logits is the scaled
-  // maximum of the raw ones.
+  // The weights are first taken against the running maximum m; one above
+  // 2^kSlack (or infinite, while m is -inf) means some logit exceeds m by
+  // more than kSlack, which a ballot decides: then the column's maximum of
+  // the raw logits is taken (qk_scale >= 0, so it scales to the maximum of
+  // the scaled ones), acc and l are rescaled and the weights taken again.
+  // A missing second tile gets the exponent offset +inf, so weight 0.
   auto pair = [&](const uint8_t* buf, int pp, bool two) {
     const f32x4 s0 = logits(buf + 2 * pp * T::BYTES);
-    f32x4 s1 = logits(buf + (2 * pp + 1) * T::BYTES);
-    if (!two) s1 = f32x4{kNegInf, kNegInf, kNegInf, kNegInf};
-    const float smx = __builtin_fmaxf(
-        __builtin_fmaxf(__builtin_fmaxf(s0[0], s0[1]), __builtin_fmaxf(s0[2], s0[3])),
-        __builtin_fmaxf(__builtin_fmaxf(s1[0], s1[1]), __builtin_fmaxf(s1[2], s1[3])));
-    const float lmx = smx * p.qk_scale;
-    // The column's running maximum m is raised only when a logit exceeds
-    // it by more than kSlack, which a lane-local test and a ballot decide;
-    // then the whole column's maximum is taken.
-    if (__builtin_amdgcn_ballot_w64(lmx > m + kSlack) != 0) {
+    const f32x4 s1 = logits(buf + (2 * pp + 1) * T::BYTES);
+    float pz[8];
+    auto weights = [&]() {
+      const float m1 = two ? m : __builtin_inff();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pz[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[i], p.qk_scale, -m));
+        pz[4 + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], p.qk_scale, -m1));
+      }
+    };
+    weights();
+    const float pmx = __builtin_fmaxf(
+        __builtin_fmaxf(__builtin_fmaxf(pz[0], pz[1]), __builtin_fmaxf(pz[2], pz[3])),
+        __builtin_fmaxf(__builtin_fmaxf(pz[4], pz[5]), __builtin_fmaxf(pz[6], pz[7])));
+    if (__builtin_amdgcn_ballot_w64(pmx > kSlackWeight) != 0) {
+      const float t1 = two ? __builtin_fmaxf(__builtin_fmaxf(s1[0], s1[1]), __builtin_fmaxf(s1[2], s1[3]))
+                           : kNegInf;
+      const float smx = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(s0[0], s0[1]),
+                                                         __builtin_fmaxf(s0[2], s0[3])), t1);
+      const float lmx = smx * p.qk_scale;
       float mx = __builtin_fmaxf(lmx, __shfl_xor(lmx, 16, 64));
       mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32, 64));
       const float m_new = __builtin_fmaxf(m, mx);
@@ -240,14 +255,8 @@ __global__ __launch_bounds__(kSegThreads) void segment_kernel(const SegmentParam
       l *= alpha;
 #pragma unroll
       for (int dc = 0; dc < T::DC; ++dc) acc[dc] *= alpha;
+      weights();
     }
-    float pz[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pz[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[i], p.qk_scale, -m));
-      pz[4 + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], p.qk_scale, -m));
-    }
-    if (!two) pz[4] = pz[5] = pz[6] = pz[7] = 0.f;   // also when qk_scale is 0
     l += ((pz[0] + pz[1]) + (pz[2] + pz[3])) + ((pz[4] + pz[5]) + (pz[6] + pz[7]));
     u32x2 h0, l0, h1, l1;
     split_p(pz, h0, l0);
@@ -276,6 +285,10 @@ __global__ __launch_bounds__(kSegThreads) void segment_kernel(const SegmentParam
     __builtin_amdgcn_s_setprio(0);
   };
 
+  // A wavefront none of whose columns holds a member only brings its share
+  // of each stage and meets the barriers.
+  const bool busy = __builtin_amdgcn_readfirstlane(wave * MPW) < nmem;
+
   if (nst > 0) {
     // Stages 0 .. kPrefetch - 1 in flight; stage s lives in register slot
     // s % kPrefetch until it is stored to LDS buffer s & 1.  The loads,
@@ -293,10 +306,12 @@ __global__ __launch_bounds__(kSegThreads) void segment_kernel(const SegmentParam
       for (int j = 0; j < kPrefetch; ++j) {
         const int i = i0 + j;
         const uint8_t* buf = lds[i & 1];
+        if (busy) {
 #pragma unroll
-        for (int pp = 0; pp < T::TS / 2; ++pp) {
-          const int t0 = i * T::TS + 2 * pp;
-          if (t0 < ntiles) pair(buf, pp, t0 + 1 < ntiles);
+          for (int pp = 0; pp < T::TS / 2; ++pp) {
+            const int t0 = i * T::TS + 2 * pp;
+            if (t0 < ntiles) pair(buf, pp, t0 + 1 < ntiles);
+          }
         }
         // Stage i + 1 to the other buffer (every wavefront is past stage
         // i - 1, which used it), then stage i + 1 + kPrefetch in flight.
