@@ -138,6 +138,19 @@ size_t pa_decode_workspace_size(const pa_cache_desc* cache, int32_t num_seqs,
  * no-op.                                                                    */
 pa_status pa_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 
+/* Counts, on `stream`, the non-zero merge counters of a decode workspace
+ * (the first max(U, 16384) * 4 + 65,536 bytes, U = num_seqs * num_kv_heads,
+ * as pa_decode describes) and stores the count in *nonzero (DEVICE int32,
+ * written when the stream reaches the call).  Every call that ran to
+ * completion leaves them at zero, so a non-zero count means the workspace
+ * was not zero-filled or a call on it did not complete: zero-fill it again
+ * (pa_decode_workspace_init) before the next decode.  For a workspace used
+ * with several sizes, pass the largest U.  PA_ERR_NULL for NULL pointers,
+ * PA_ERR_SHAPE for num_seqs < 0 or num_kv_heads <= 0, PA_ERR_WORKSPACE when
+ * workspace_bytes is smaller than the counter region.                       */
+pa_status pa_decode_workspace_check(const void* workspace, size_t workspace_bytes, int32_t num_seqs,
+                                    int32_t num_kv_heads, int32_t* nonzero, void* stream);
+
 /* Paged-attention decode, bf16 cache.
  * For every sequence s < num_seqs and query head i < num_q_heads, with
  * h = i / (num_q_heads / num_kv_heads) and L = seq_lens[s]:

@@ -81,6 +81,7 @@ def _load():
         "pa_cache_write_fp8": ([dp, vp, vp, vp, i32, vp, vp, f32, f32, vp], i32),
         "pa_decode_workspace_size": ([dp, i32, i32, i32, i32], sz),
         "pa_decode_workspace_init": ([vp, sz, vp], i32),
+        "pa_decode_workspace_check": ([vp, sz, i32, i32, vp, vp], i32),
         "pa_decode": ([dp, vp, i32, i32, vp, vp, vp, i32, vp, f32, vp, i32, vp, sz, vp], i32),
         "pa_decode_fp8": ([dp, vp, i32, i32, vp, vp, vp, i32, vp, f32, f32, f32, vp, i32, vp, sz,
                            vp], i32),
@@ -243,6 +244,22 @@ def pa_decode_workspace_init(workspace):
     with torch.cuda.device(workspace.device):
         st = _load().pa_decode_workspace_init(_ptr(workspace), workspace.numel(), _stream(workspace))
     _check("pa_decode_workspace_init", st)
+
+
+def pa_decode_workspace_check(workspace, num_seqs, num_kv_heads, nonzero=None):
+    """Number of non-zero merge counters in a decode workspace (0 after every
+    completed call).  The count is written on the current stream into
+    ``nonzero`` (int32 device tensor of one element, allocated if None),
+    which is returned; ``int(...)`` of it synchronizes."""
+    _need(workspace, "workspace", torch.uint8, workspace.device)
+    if nonzero is None:
+        nonzero = torch.empty((1,), dtype=torch.int32, device=workspace.device)
+    _need(nonzero, "nonzero", torch.int32, workspace.device, shape=(1,))
+    with torch.cuda.device(workspace.device):
+        st = _load().pa_decode_workspace_check(_ptr(workspace), workspace.numel(), num_seqs, num_kv_heads,
+                                               _ptr(nonzero), _stream(workspace))
+    _check("pa_decode_workspace_check", st)
+    return nonzero
 
 
 def alloc_workspace(num_blocks, block_size, num_kv_heads, head_dim, num_seqs, num_q_heads,

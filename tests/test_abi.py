@@ -175,6 +175,18 @@ def test_workspace_init_validation():
     assert lib.pa_decode_workspace_init(None, 64, None) == NULL
 
 
+def test_workspace_check_validation():
+    lib = pa.lib()
+    region = 16384 * 4 + 65536                    # the counters of up to 16,384 units
+    assert lib.pa_decode_workspace_check(None, region, 4, 8, FAKE, None) == NULL
+    assert lib.pa_decode_workspace_check(FAKE, region, 4, 8, None, None) == NULL
+    assert lib.pa_decode_workspace_check(FAKE, region, -1, 8, FAKE, None) == SHAPE
+    assert lib.pa_decode_workspace_check(FAKE, region, 4, 0, FAKE, None) == SHAPE
+    assert lib.pa_decode_workspace_check(FAKE, region - 1, 4, 8, FAKE, None) == WS
+    # More than 16,384 units: the unit counters grow with U.
+    assert lib.pa_decode_workspace_check(FAKE, region, 4096, 8, FAKE, None) == WS
+
+
 def test_copy_blocks_validation():
     lib = pa.lib()
     d = desc()

@@ -211,3 +211,31 @@ def test_many_pieces_without_group_counters():
     assert len(lens) * 8 * w.max_blocks_per_seq > 8192   # wavefronts at one chunk each
     t = H.device_inputs(w)
     H.step_and_check(w, t, partition_tokens=16, label="one-level merges")
+
+
+def test_workspace_check_counts_only_stale_counters():
+    # Calls that complete leave every merge counter at zero, with and without
+    # the merge tree's group counters in use; planted words are counted, and
+    # a zero fill clears them.
+    w = W.random_workload(4242, 16, 64, 8, 128, 16, 3000, min_len=1)
+    t = H.device_inputs(w)
+    H.gpu_write(w, t)                             # the step's tokens (their slots start poisoned)
+    parts = (16, 32, 0)
+    size = max(pa.pa_decode_workspace_size(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.num_seqs,
+                                           w.num_q_heads, w.max_blocks_per_seq, part) for part in parts)
+    ws = torch.zeros(size, dtype=torch.uint8, device="cuda")
+
+    def stale():
+        return int(pa.pa_decode_workspace_check(ws, w.num_seqs, w.num_kv_heads)[0])
+
+    assert stale() == 0
+    for part in parts:
+        out = H.gpu_decode(w, t, partition_tokens=part, workspace=ws)
+        assert bool(torch.isfinite(out).all()), f"part={part}"
+        assert stale() == 0, f"part={part}: counters left non-zero"
+    words = ws.view(torch.int32)
+    words[7] = 5                                  # a unit counter
+    words[65536 // 4 + 10] = 1                    # a merge-tree group counter
+    assert stale() == 2
+    pa.pa_decode_workspace_init(ws)
+    assert stale() == 0
