@@ -447,42 +447,41 @@ __device__ __forceinline__ int block_sum(int v, int* red) {
   return t;
 }
 
-// Sum over the NW wavefronts' threads of small counts v in [0, 64): each bit of v is
-// counted across the wavefront with a ballot and a scalar popcount, so the
-// wavefront's sum needs no cross-lane data movement.
+// Exclusive prefix sums in thread order of two small counts a, e in [0, 64)
+// and the block's total of a, with one exchange through `scratch` (2 * NW
+// words, not read again by the caller before a barrier).  Within a
+// wavefront each bit of a count is counted over the lower lanes with a
+// ballot and mbcnt (set bits below the lane) and over the wavefront with a
+// scalar popcount, so the wavefront needs no cross-lane data movement.
 template <int NW>
-__device__ __forceinline__ int block_sum_small(int v, int* red) {
-  int t = 0;
-#pragma unroll
-  for (int b = 0; b < 6; ++b) t += __popcll(__ballot((v >> b) & 1)) << b;
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = t;
-  __syncthreads();
-  t = 0;
-#pragma unroll
-  for (int i = 0; i < NW; ++i) t += red[i];
-  __syncthreads();
-  return t;
-}
-
-// Exclusive prefix sum in thread order of small counts v in [0, 64): within
-// a wavefront, each bit of v is counted over the lower lanes with a ballot
-// and mbcnt (set bits below the lane), then the wavefronts' totals are
-// combined through LDS.
-__device__ __forceinline__ int block_excl_sum_small(int v, int* red) {
-  int below = 0, total = 0;
+__device__ __forceinline__ void block_excl_sum2_small(int a, int e, int* scratch, int& a_before, int& e_before,
+                                                      int& a_total) {
+  int ba = 0, be = 0, ta = 0, te = 0;
 #pragma unroll
   for (int b = 0; b < 6; ++b) {
-    const uint64_t m = __ballot((v >> b) & 1);
-    below += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u)) << b;
-    total += __popcll(m) << b;
+    const uint64_t ma = __ballot((a >> b) & 1), me = __ballot((e >> b) & 1);
+    ba += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(ma >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ma, 0u)) << b;
+    be += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(me >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)me, 0u)) << b;
+    ta += __popcll(ma) << b;
+    te += __popcll(me) << b;
   }
   const int wv = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) red[wv] = total;
+  if ((threadIdx.x & 63) == 0) {
+    scratch[wv] = ta;
+    scratch[NW + wv] = te;
+  }
   __syncthreads();
-  int before = 0;
-  for (int i = 0; i < wv; ++i) before += red[i];
-  __syncthreads();
-  return before + below;
+  int pa = 0, pe = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const int x = scratch[i], y = scratch[NW + i];
+    pa += i < wv ? x : 0;
+    pe += i < wv ? y : 0;
+    tot += x;
+  }
+  a_before = pa + ba;
+  e_before = pe + be;
+  a_total = tot;
 }
 
 // Exclusive prefix sum of v over the 256 threads in thread order.
@@ -545,34 +544,73 @@ __device__ __forceinline__ void select_small(const SelectParams& p, int unit, in
   for (int k = 0; k < REGS; ++k)
     if (tid + NT * k < np) lk[lds_index(tid + NT * k)] = kr[k];
   // T = the budget-th largest key.  Units of at most 16 key slots per
-  // thread find it 8 bits per round from the top: the keys that agree with T
-  // above the round's digit are counted per digit value (LDS histogram); T
-  // takes the largest digit with at least `want` of them at or above it,
-  // and `want` drops by those strictly above.  Fuller units, whose keys
-  // crowd the histogram's first-round bins (sign and top exponent bits),
-  // find it bit by bit: T keeps a bit when at least `budget` keys are >= T
-  // with it, counted with one ballot per key slot and scalar popcounts.
+  // thread find it 8 bits per round from the top of the keys' range: with
+  // x = key - (the unit's smallest key), which orders the keys as they are,
+  // the keys whose x agrees with T's above the round's digit are counted per
+  // digit value (LDS histogram); T takes the largest digit with at least
+  // `want` of them at or above it, and `want` drops by those strictly above.
+  // Taking the digits from the range rather than from bit 31 matters: one
+  // unit's keys share their top bits (the sign and exponent range of its
+  // scores), which would crowd the first round into a few bins, and the LDS
+  // atomics on one bin serialize.  Fuller units find T bit by bit: T keeps
+  // a bit when at least `budget` keys are >= T with it, counted with one
+  // ballot per key slot and scalar popcounts.
   const int slots = (np + NT - 1) / NT;     // key slots that hold any page
   uint32_t T = 0u;
   if (slots <= 16) {
+    uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
+#pragma unroll
+    for (int k = 0; k < REGS; ++k) {
+      if (k < slots && tid + NT * k < np) {
+        kmn = kr[k] < kmn ? kr[k] : kmn;
+        kmx = kr[k] > kmx ? kr[k] : kmx;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const uint32_t a = (uint32_t)__shfl_xor((int)kmn, o, 64), b = (uint32_t)__shfl_xor((int)kmx, o, 64);
+      kmn = a < kmn ? a : kmn;
+      kmx = b > kmx ? b : kmx;
+    }
+    // Two histogram buffers alternate between rounds: while wavefront 0
+    // scans one, the other threads clear the next, so a round needs two
+    // barriers.  The block's minimum and maximum pass through the second.
+    if (tid < 256) hist[tid] = 0u;
+    if ((tid & 63) == 0) {
+      hist[256 + (tid >> 6)] = kmn;
+      hist[256 + 64 + (tid >> 6)] = kmx;
+    }
+    __syncthreads();                            // also publishes the LDS keys
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) {
+      kmn = hist[256 + i] < kmn ? hist[256 + i] : kmn;
+      kmx = hist[256 + 64 + i] > kmx ? hist[256 + 64 + i] : kmx;
+    }
+    const int nbits = kmx > kmn ? 32 - __builtin_clz(kmx - kmn) : 0;
+    uint32_t X = 0u;                            // T - kmn
     int want = B;
-    for (int r = 0; r < 4; ++r) {
-      const int shift = 24 - 8 * r;
-      if (tid < 256) hist[tid] = 0u;
-      __syncthreads();                          // also publishes the LDS keys (first round)
+    int r = 0;
+    for (int hi = nbits; hi > 0; hi -= 8, ++r) {
+      const int lo = hi > 8 ? hi - 8 : 0;
+      const uint32_t dmask = (1u << (hi - lo)) - 1u;
+      uint32_t* cur = hist + 256 * (r & 1);
+      uint32_t* nxt = hist + 256 * ((r + 1) & 1);
+      int* rr = red + 2 * (r & 1);
 #pragma unroll
       for (int k = 0; k < REGS; ++k) {
         if (k < slots && tid + NT * k < np) {
-          const bool match = r == 0 || ((kr[k] ^ T) >> (shift + 8)) == 0u;
-          if (match) atomicAdd(&hist[(kr[k] >> shift) & 255u], 1u);
+          const uint32_t x = kr[k] - kmn;
+          const bool match = hi == nbits || ((x ^ X) >> hi) == 0u;
+          if (match) atomicAdd(&cur[(x >> lo) & dmask], 1u);
         }
       }
       __syncthreads();
+      for (int i = tid - 64; i >= 0 && i < 256; i += NT - 64) nxt[i] = 0u;
       if (tid < 64) {
         // Lane l holds digits 4l .. 4l + 3; suffix sums from the top digit.
         uint32_t h[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) h[i] = hist[4 * tid + i];
+        for (int i = 0; i < 4; ++i) h[i] = cur[4 * tid + i];
         const int own = (int)(h[0] + h[1] + h[2] + h[3]);
         int suf = own;                          // sum over lanes >= tid
 #pragma unroll
@@ -595,15 +633,17 @@ __device__ __forceinline__ void select_small(const SelectParams& p, int unit, in
         const uint64_t hit = __ballot(dbest >= 0);
         const int l = 63 - __builtin_clzll(hit);  // the highest lane with a qualifying digit
         if (tid == l) {
-          red[0] = dbest;
-          red[1] = want - above_best;
+          rr[0] = dbest;
+          rr[1] = want - above_best;
         }
       }
+      // Every thread has read the previous round's results (before this
+      // round's first barrier), so those slots are free again next round.
       __syncthreads();
-      T |= (uint32_t)red[0] << shift;
-      want = red[1];
-      __syncthreads();
+      X |= (uint32_t)rr[0] << lo;
+      want = rr[1];
     }
+    T = X + kmn;
   } else {
     for (int bit = 31; bit >= 0; --bit) {
       const uint32_t cand = T | (1u << bit);   // >= 1: the padding keys 0 never count
@@ -627,20 +667,18 @@ __device__ __forceinline__ void select_small(const SelectParams& p, int unit, in
     above += (k < cnt && mine[k] > T) ? 1 : 0;
     equal += (k < cnt && mine[k] == T) ? 1 : 0;
   }
-  const int need = B - block_sum_small<NT / 64>(above, red);
-  const int eq_rank0 = block_excl_sum_small(equal, red);
-  int taken = 0;
-  {
-    int er = eq_rank0;
-#pragma unroll
-    for (int k = 0; k < REGS; ++k) {
-      const bool eq = k < cnt && mine[k] == T;
-      taken += (k < cnt && (mine[k] > T || (eq && er < need))) ? 1 : 0;
-      er += eq ? 1 : 0;
-    }
-  }
-  int pos = block_excl_sum_small(taken, red);
-  int er = eq_rank0;
+  // One scan gives the keys above T and equal to it in the ranges before
+  // this thread's, and the block's keys above T.  The keys equal to T are
+  // taken in page order until `need` of them are, so the thread's first
+  // output position is (above before) + min(equal before, need).  The
+  // scratch words are the histogram's, which nothing reads any more (the
+  // last round, or the bit rounds, ended with a barrier).
+  int above_before, eq_before, above_total;
+  block_excl_sum2_small<NT / 64>(above, equal, reinterpret_cast<int*>(hist), above_before, eq_before,
+                                 above_total);
+  const int need = B - above_total;
+  int pos = above_before + (eq_before < need ? eq_before : need);
+  int er = eq_before;
   const int last_valid = p.seq_lens[s] - (np - 1) * p.block_size;
 #pragma unroll
   for (int k = 0; k < REGS; ++k) {
@@ -719,7 +757,7 @@ __global__ __launch_bounds__(NT) void page_select_kernel(const SelectParams p) {
   constexpr int REGS = NT == 1024 ? 12 : kSelectRegs;   // NT * REGS <= kSelectLds keys held in LDS
   __shared__ uint32_t lk[kSelectLds + kSelectLds / 32];
   __shared__ int red[NT / 64];
-  __shared__ uint32_t hist[256];
+  __shared__ uint32_t hist[512];
   const int unit = blockIdx.x;
   const int s = unit / p.num_kv_heads;
   const int tid = threadIdx.x;
