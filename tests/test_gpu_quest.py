@@ -341,6 +341,25 @@ def test_equal_scores_go_to_the_lower_page():
         run_select_and_decode(w2, t, budget, label=f"ties budget={budget}")
 
 
+def test_scores_of_both_signs():
+    """Pages scoring on both sides of zero: with q >= 0, a block whose K is
+    the constant +0.5 scores 0.5 * sum(q) and one at -0.25 scores
+    -0.25 * sum(q).  The choice's key range then spans the sign bit (the
+    search takes all 32 bits), and the equal scores on either side go to the
+    lower pages."""
+    w = W.random_workload(21, 3, 16, 2, 128, 16, 640, min_len=500)
+    per_block = w.num_kv_heads * w.block_size * w.head_dim
+    for budget in (1, 5, 20):
+        t = device_inputs(w, poison=False)
+        t["q"][0] = t["q"][0].abs()
+        kc = t["k_cache"][0]
+        for s_, L in enumerate(w.seq_lens):
+            for p in range(-(-int(L) // w.block_size)):
+                b = int(w.block_tables[s_, p])
+                kc[b * per_block:(b + 1) * per_block] = 0.5 if p % 3 == 0 else -0.25
+        run_select_and_decode(w, t, budget, label=f"signs budget={budget}")
+
+
 @pytest.mark.parametrize("budget", [3, 100, 5000])
 def test_wide_tables(budget):
     """Tables wider than 2,048 pages take the 1,024-thread choice kernel.
