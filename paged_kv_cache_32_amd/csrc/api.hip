@@ -27,6 +27,13 @@ constexpr int kMaxBlockSize = 256;
 #ifndef PA_DECODE_UNIT_CHARGE_FP8
 #define PA_DECODE_UNIT_CHARGE_FP8 4
 #endif
+// The shared-prefix decode's private parts on a bf16 cache: thousands of
+// short units (each sequence's blocks after its shared prefix, for every KV
+// head), where the per-unit charge pays (measured 600 against 618-625 us
+// per call on the 256-sequence prefix-shared batch, on two machines).
+#ifndef PA_CASCADE_UNIT_CHARGE
+#define PA_CASCADE_UNIT_CHARGE 2
+#endif
 #ifndef PA_DECODE_CHUNK_MIN
 #define PA_DECODE_CHUNK_MIN 32
 #endif
@@ -174,7 +181,7 @@ pa_status decode(const pa_cache_desc* cache, const void* q, int32_t num_seqs, in
                  float k_scale, float v_scale, bool fp8, float* out, int32_t partition_tokens,
                  void* workspace, size_t workspace_bytes, void* stream, int32_t seq_heads = 0,
                  float* lse = nullptr, bool append = false, const void* k_new = nullptr,
-                 const void* v_new = nullptr, bool ring = false) {
+                 const void* v_new = nullptr, bool ring = false, int32_t unit_charge = -1) {
   if (!cache) return PA_ERR_NULL;
   if (!isfinite(scale) || window < 0) return PA_ERR_SHAPE;
   // Ring rows must hold every block a window can span: ceil(W / BS) + 1.
@@ -230,7 +237,11 @@ pa_status decode(const pa_cache_desc* cache, const void* q, int32_t num_seqs, in
   p.num_waves = (int32_t)num_waves;
   p.chunk_min = kChunkMinAuto;
   p.chunk_fixed = chunk_fixed;
-  p.unit_charge = chunk_fixed > 0 ? 0 : (fp8 ? PA_DECODE_UNIT_CHARGE_FP8 : PA_DECODE_UNIT_CHARGE);
+  // unit_charge < 0: the dtype's default.
+  p.unit_charge = chunk_fixed > 0         ? 0
+                  : unit_charge >= 0      ? unit_charge
+                  : fp8                   ? PA_DECODE_UNIT_CHARGE_FP8
+                                          : PA_DECODE_UNIT_CHARGE;
   p.window = window;
   p.ring = ring ? 1 : 0;
   p.subs = cache->block_size / pa::kSub;
@@ -821,7 +832,8 @@ pa_status decode_cascade(const pa_cache_desc* cache, const void* q, int32_t S, i
   hipStream_t s = static_cast<hipStream_t>(stream);
   // Private parts (and the device checks) through the paged decode.
   st = decode(cache, q, S, Hq, k_cache, v_cache, plan->private_tables, maxb, plan->private_lens, 0, scale,
-              k_scale, v_scale, fp8, part_out, partition_tokens, ws, lay.dec_bytes, stream, 0, part_lse);
+              k_scale, v_scale, fp8, part_out, partition_tokens, ws, lay.dec_bytes, stream, 0, part_lse, false,
+              nullptr, nullptr, false, fp8 ? -1 : PA_CASCADE_UNIT_CHARGE);
   if (st != PA_OK) return st;
   pa::SegmentParams sp{};
   sp.q = static_cast<const uint16_t*>(q);
