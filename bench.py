@@ -145,7 +145,14 @@ TRAFFIC_PROFILES = {"llama70b_layer_bs64": "profiles/decode_kernel_llama70b_bs64
                     "prefix_shared_bs256": "profiles/decode_kernel_prefix_shared_bs256_traffic.md",
                     "long_context_128k": "profiles/decode_kernel_long_context_128k_traffic.md",
                     "fp8_80layer_bs128": "profiles/decode_kernel_fp8_80layer_bs128_traffic.md",
-                    "bulk_write_llama70b": "profiles/cache_write_tiles_kernel_bulk_write_llama70b_traffic.md"}
+                    "bulk_write_llama70b": "profiles/cache_write_tiles_kernel_bulk_write_llama70b_traffic.md",
+                    "sliding_window_llama70b": "profiles/decode_kernel_sliding_window_llama70b_traffic.md",
+                    "llama70b_tp2_shard_bs64": "profiles/decode_kernel_llama70b_tp2_shard_bs64_traffic.md",
+                    "llama70b_tp8_shard_bs64": "profiles/decode_kernel_llama70b_tp8_shard_bs64_traffic.md",
+                    "quest_llama70b_bs64": "profiles/quest_llama70b_bs64_traffic.md",
+                    "quest_long_context_128k": "profiles/quest_long_context_128k_traffic.md",
+                    "cascade_prefix_shared_bs256": "profiles/cascade_prefix_shared_bs256_traffic.md",
+                    "copy_blocks_llama70b": "profiles/move_blocks_kernel_copy_llama70b_pool_traffic.md"}
 
 
 def kernel_source_hash(sources=KERNEL_SOURCES):
@@ -156,10 +163,11 @@ def kernel_source_hash(sources=KERNEL_SOURCES):
     return h.hexdigest()
 
 
-def measured_traffic(workload="llama70b_layer_bs64"):
-    """HBM bytes per decode launch from the committed rocprofv3 counter
-    summary of this workload, or None when there is none or the kernel
-    sources changed since it was taken."""
+def measured_traffic(workload="llama70b_layer_bs64", part=None):
+    """HBM bytes per launch of the workload's dominant kernel (or, with
+    ``part``, of that named part of the step) from the committed rocprofv3
+    counter summary, or None when there is none or the sources it names
+    changed since it was taken."""
     if workload not in TRAFFIC_PROFILES:
         return None
     path = os.path.join(ROOT, TRAFFIC_PROFILES[workload])
@@ -169,9 +177,12 @@ def measured_traffic(workload="llama70b_layer_bs64"):
     if not m:
         return None
     rec = json.loads(m.group(1))
-    sources = CACHE_WRITE_SOURCES if workload == "bulk_write_llama70b" else KERNEL_SOURCES
+    sources = rec.get("kernel_sources") or (CACHE_WRITE_SOURCES if workload == "bulk_write_llama70b"
+                                            else KERNEL_SOURCES)
     if rec.get("kernel_source_sha256") != kernel_source_hash(sources):
         return None
+    if part is not None:
+        return rec.get("parts", {}).get(part, {}).get("traffic_bytes_per_launch")
     return rec.get("traffic_bytes_per_launch")
 
 
@@ -686,8 +697,8 @@ def bench_copy_blocks(args, dev):
         "copy_us": {"mean": round(float(ms.mean()) * 1e3, 2), "p10": round(float(np.percentile(ms, 10)) * 1e3, 2),
                     "p90": round(float(np.percentile(ms, 90)) * 1e3, 2)},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "copy_blocks_kernel (pa_copy_blocks is one launch)", "bytes_per_launch": moved},
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.workload),
+                     "kernel": "move_blocks_kernel (pa_copy_blocks is one launch)", "bytes_per_launch": moved},
         "block_manager": {"add_sequence_tokens_per_s": round(float(w.seq_lens.sum()) / t_add, 1),
                           "append_token_per_s": round(n_app / t_app, 1),
                           "prefix_hits": hits, "blocks_taken": misses},
@@ -988,7 +999,7 @@ def bench_quest(args, dev):
         "layer_tok_s": round(S / (step_ms / 1e3), 1),
         "wall_s_timed_region": round(wall, 4),
         "roofline": {"bound": "hbm", "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.workload, dom),
                      "kernel": {"quest_select": "page_score_kernel + page_select_kernel (pa_quest_select)",
                                 "decode_quest": "decode_kernel (pa_decode_quest is one launch)"}[dom],
                      "bytes_per_launch": dom_bytes},
@@ -1084,7 +1095,7 @@ def bench_cascade(args, dev):
         "plan_build_host_ms": round(plan_ms, 2),
         "layer_tok_s": round(S / (step_ms / 1e3), 1),
         "roofline": {"bound": "hbm", "achieved": round(alg_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(alg_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(alg_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.workload),
                      "kernel": "segment_kernel + decode_kernel + combine_kernel (pa_decode_cascade)",
                      "bytes_per_launch": alg_phys},
     })
