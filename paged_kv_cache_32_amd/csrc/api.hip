@@ -34,8 +34,11 @@ constexpr int kMaxBlockSize = 256;
 #ifndef PA_CASCADE_UNIT_CHARGE
 #define PA_CASCADE_UNIT_CHARGE 2
 #endif
+// Fewest chunks a wavefront takes in the automatic split.  It only binds on
+// short reads (fewer chunks than 8 per resident wavefront); there more,
+// shorter pieces win now that a long unit's pieces merge as a tree.
 #ifndef PA_DECODE_CHUNK_MIN
-#define PA_DECODE_CHUNK_MIN 32
+#define PA_DECODE_CHUNK_MIN 8
 #endif
 constexpr int kChunkMinAuto = PA_DECODE_CHUNK_MIN;  // fewest chunks per wavefront when splitting automatically
 // Wavefronts launched per resident slot in the automatic split: ranges left
