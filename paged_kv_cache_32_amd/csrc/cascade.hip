@@ -12,13 +12,13 @@
 //
 // segment_kernel: workgroup = (segment chunk, KV head h, up to
 // PA_CASCADE_WAVES * MPW member sequences).  Each 16-token K/V tile of the
-// chunk is loaded once into LDS (double-buffered) and used by all the
-// workgroup's wavefronts; a wavefront
-// holds MPW = 16 / G members' query groups as the 16 columns of its MFMA
-// tiles (S^T = K Q^T with 16x16x32 bf16, O^T = V^T P^T with 16x16x16 bf16,
-// P split into bf16 hi + lo), the same operand layouts as the paged decode
-// kernel reads from registers, here read from LDS.  Each (member, chunk)
-// gets a partial record {acc[D], m, l} per query head of h.
+// chunk is loaded once into LDS, straight from global memory into one of
+// three stage buffers, and used by all the workgroup's wavefronts; a
+// wavefront holds MPW = 16 / G members' query groups as the 16 columns of
+// its MFMA tiles (S^T = K Q^T and O^T = V^T P^T, both 16x16x32 bf16, P split
+// into bf16 hi + lo), with the K operands in the paged decode's layout.
+// Each (member, chunk) gets a partial record {acc[D], m, l} per query head
+// of h.
 //
 // combine_kernel: per (sequence, query head, 4 dims), the private part's
 // normalized output and log2-sum-exp from the decode kernel and the
@@ -76,6 +76,7 @@ struct SegTile {
   static constexpr int QK = D / 32;                  // 16x16x32 MFMAs per tile (K Q^T)
   static constexpr int DC = D / 16;                  // 16-row blocks of O^T
   static constexpr int R = FP8 ? 4 : 2;              // dim blocks per 16-byte V piece of the cache
+  static constexpr int H = 16 / R;                   // O^T rows of one block that share a piece
   static constexpr int VLD = DC / R;                 // 1 KB blocks of a V tile
   static constexpr int PIECES = BYTES / 16;          // 16-byte pieces per tile
   static constexpr int TS = 8192 / BYTES;            // tiles per stage: 2, 4 or 8
@@ -85,19 +86,34 @@ struct SegTile {
 
 constexpr int kSegThreads = 64 * PA_CASCADE_WAVES;
 constexpr int kHalfStage = 8192;    // a stage: K tiles (8 KB) then V tiles (8 KB)
-constexpr int kPrefetch = 3;        // stages in flight per thread, in registers
+constexpr int kStages = 3;          // stage buffers in LDS: the one worked on and two loading
 static_assert(kSegThreads * 16 == kHalfStage, "one K piece and one V piece per thread and stage");
 
-// LDS image of a stage.  K tiles keep the cache layout.  V tiles are stored
-// by pairs (2p, 2p + 1): unit (p, dim block dc, lane L) holds, for dim
-// 16 dc + L % 16 and tokens 4 (L / 16) .. 4 (L / 16) + 3, the U bytes of
-// tile 2p then those of tile 2p + 1.  A lane's 2U-byte read is then the
-// MFMA A operand for 8 tokens of two tiles, and the reads of a wavefront
-// are contiguous (no bank conflicts).
+// s_waitcnt immediate that waits until at most n vector memory operations
+// of this wavefront are outstanding (expcnt and lgkmcnt left alone).
+constexpr unsigned vmcnt_imm(unsigned n) { return (n & 15u) | (7u << 4) | (15u << 8) | ((n >> 4) << 14); }
+
+// LDS image of a stage, filled by direct global-to-LDS loads of whole
+// 16-byte pieces (each wavefront instruction writes 1 KB, lane L at 16 L).
+// K tiles keep the cache layout: lane (token t, group g) reads the 8 (bf16)
+// or 16 (fp8) consecutive dims of K operand c.  A V tile keeps its 1 KB
+// blocks of R dim blocks, but each block's 64 pieces are reordered: the
+// piece of dims 16 (R e + r) + dd (r = 0 .. R - 1), tokens 4 g .. 4 g + 3,
+// goes to slot (dd / H) 4H + g H + dd % H.  O^T block j = R e + s takes on
+// row m the dim 16 (R e + r) + dd with r = (m / H) ^ s, dd = m % H + H s,
+// so its A operand for lane (m, g) is the 16 / R bytes of piece slot
+// s 4H + g H + m % H at part r, from tile 2p then tile 2p + 1 (8 tokens of
+// one dim), and the 16 lanes of a token group read 256 / R contiguous bytes.
 template <int D, bool FP8>
 __global__ __launch_bounds__(kSegThreads) void segment_kernel(const SegmentParams p) {
   using T = SegTile<D, FP8>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][2 * kHalfStage];
+  // Three separate arrays, so that the compiler sees that the loads into
+  // one buffer do not touch the others and adds no waits for them.
+  __shared__ __attribute__((aligned(16))) uint8_t lds0[2 * kHalfStage];
+  __shared__ __attribute__((aligned(16))) uint8_t lds1[2 * kHalfStage];
+  __shared__ __attribute__((aligned(16))) uint8_t lds2[2 * kHalfStage];
+  static_assert(kStages == 3, "one array per stage buffer");
+  auto stage_buf = [&](int j) -> uint8_t* { return j == 0 ? lds0 : j == 1 ? lds1 : lds2; };
   __shared__ int32_t ids[PA_CASCADE_MAX_CHUNK_BLOCKS];
   const int32_t* it = p.items + (int64_t)blockIdx.x * 8;
   const int blk_off = it[0], mem_off = it[2], nmem = it[3], h = it[4], slot0 = it[5];
@@ -137,20 +153,23 @@ __global__ __launch_bounds__(kSegThreads) void segment_kernel(const SegmentParam
     ids[b] = ok ? blk : 0;
   }
   bad = __syncthreads_or(bad);
+  // The query loads are complete before the stage loads start, so that no
+  // later wait for them has to cover the stage loads as well.
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
-  // Per stage, thread tid brings K piece tid (tile tid / PIECES) and one
-  // 16-byte V piece: wavefront w takes 1 KB block w % VLD of tile w / VLD,
-  // lane L the piece of dims 16 (R e + r) + L % 16, tokens 4 (L / 16) ...
-  // Both tiles are the same for a whole wavefront, so their addresses are
-  // scalar.
+  // Per stage, thread tid brings K piece tid (tile tid / PIECES) to slot
+  // tid, and wavefront w fills V block w % VLD of tile w / VLD, lane L
+  // taking the piece its slot holds (see above).  Both tiles are the same
+  // for a whole wavefront, so their addresses are scalar.
   const int kt = __builtin_amdgcn_readfirstlane(tid / T::PIECES);
   const uint32_t kpc = (tid % T::PIECES) * 16;
   const int vt = __builtin_amdgcn_readfirstlane(wave / T::VLD), ve = wave % T::VLD;
-  const uint32_t vpc = (ve * 64 + col * 4 + qd) * 16;
+  uint32_t vpc;
+  {
+    const int s_ = lane / (4 * T::H), g_ = (lane / T::H) % 4, dd = lane % T::H + T::H * s_;
+    vpc = (uint32_t)(((ve * 16 + dd) * 4 + g_) * 16);
+  }
   const uint32_t magic = subs > 1 ? 0xFFFFFFFFu / (uint32_t)subs + 1u : 0u;   // t / subs for t < 2^16
-  struct Pieces {
-    u32x4 k, v;
-  };
   // Block ids of the two tiles of stage `stage` this wavefront brings.
   auto stage_ids = [&](int stage, int& tk, int& tv, int& bk, int& bv) {
     tk = stage * T::TS + kt;
@@ -164,25 +183,19 @@ __global__ __launch_bounds__(kSegThreads) void segment_kernel(const SegmentParam
     tk -= b0 * subs;
     tv -= b1 * subs;
   };
-  auto gload = [&](int stage) -> Pieces {
+  // Both pieces of stage `stage` straight into LDS buffer `buf`.
+  auto issue = [&](int stage, int buf) {
     int sk, sv, bk, bv;
     stage_ids(stage, sk, sv, bk, bv);
     const uint8_t* kb = p.k_cache + (int64_t)bk * p.blk_stride + (int64_t)(h * subs + sk) * T::BYTES;
     const uint8_t* vb = p.v_cache + (int64_t)bv * p.blk_stride + (int64_t)(h * subs + sv) * T::BYTES;
-    Pieces r;
-    r.k = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + kpc));
-    r.v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb + vpc));
-    return r;
-  };
-  auto lstore = [&](int buf, const Pieces& pc) {
-    *reinterpret_cast<u32x4*>(lds[buf] + tid * 16) = pc.k;
-    uint8_t* vb = lds[buf] + kHalfStage + (vt >> 1) * (T::DC * 64 * 2 * T::U) + (vt & 1) * T::U;
-#pragma unroll
-    for (int r = 0; r < T::R; ++r) {
-      uint8_t* dst = vb + ((ve * T::R + r) * 64 + lane) * (2 * T::U);
-      if constexpr (FP8) *reinterpret_cast<uint32_t*>(dst) = pc.v[r];
-      else *reinterpret_cast<u32x2*>(dst) = u32x2{pc.v[2 * r], pc.v[2 * r + 1]};
-    }
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kb + kpc),
+                                     (__attribute__((address_space(3))) void*)(stage_buf(buf) + wave * 1024), 16, 0,
+                                     0);
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vb + vpc),
+                                     (__attribute__((address_space(3))) void*)(stage_buf(buf) + kHalfStage +
+                                                                                wave * 1024),
+                                     16, 0, 0);
   };
 
   float m = kNegInf, l = 0.f;
@@ -215,6 +228,13 @@ __global__ __launch_bounds__(kSegThreads) void segment_kernel(const SegmentParam
     return sc;
   };
 
+  // Lane part of the V operand reads: slot g H + m % H of block part s,
+  // at byte (r = (m / H) ^ s) * U; one address per s.
+  uint32_t voff[T::R];
+#pragma unroll
+  for (int s_ = 0; s_ < T::R; ++s_)
+    voff[s_] = (uint32_t)((s_ * 4 * T::H + qd * T::H + col % T::H) * 16 + (((col / T::H) ^ s_) * T::U));
+
   // Tiles 2p and 2p + 1 of a stage (the second only when `two`): online
   // softmax in base 2 over the lane's 8 logits (tokens 4 qd + i of either
   // tile, column col), then O^T += V^T P^T with k slots 8 qd .. 8 qd + 7
@@ -228,6 +248,7 @@ __global__ __launch_bounds__(kSegThreads) void segment_kernel(const SegmentParam
   auto pair = [&](const uint8_t* buf, int pp, bool two) {
     const f32x4 s0 = logits(buf + 2 * pp * T::BYTES);
     const f32x4 s1 = logits(buf + (2 * pp + 1) * T::BYTES);
+    const uint8_t* v0 = buf + kHalfStage + 2 * pp * T::BYTES;
     float pz[8];
     auto weights = [&]() {
       const float m1 = two ? m : __builtin_inff();
@@ -265,22 +286,25 @@ __global__ __launch_bounds__(kSegThreads) void segment_kernel(const SegmentParam
     // The products with V run at raised wave priority: a wavefront that
     // has reached them issues its MFMAs ahead of the others' softmax
     // arithmetic, which keeps the matrix unit fed.
-    const uint8_t* vb = buf + kHalfStage + pp * (T::DC * 64 * 2 * T::U) + lane * (2 * T::U);
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int dc = 0; dc < T::DC; ++dc) {
+    for (int j = 0; j < T::DC; ++j) {
+      const int off = (j / T::R) * 1024;
       u32x4 a;
       if constexpr (FP8) {
-        const u32x2 w = *reinterpret_cast<const u32x2*>(vb + dc * 64 * 2 * T::U);
-        a[0] = fp8x2_to_bf16x2<false>(w[0]);
-        a[1] = fp8x2_to_bf16x2<true>(w[0]);
-        a[2] = fp8x2_to_bf16x2<false>(w[1]);
-        a[3] = fp8x2_to_bf16x2<true>(w[1]);
+        const uint32_t w0 = *reinterpret_cast<const uint32_t*>(v0 + voff[j % T::R] + off);
+        const uint32_t w1 = *reinterpret_cast<const uint32_t*>(v0 + T::BYTES + voff[j % T::R] + off);
+        a[0] = fp8x2_to_bf16x2<false>(w0);
+        a[1] = fp8x2_to_bf16x2<true>(w0);
+        a[2] = fp8x2_to_bf16x2<false>(w1);
+        a[3] = fp8x2_to_bf16x2<true>(w1);
       } else {
-        a = *reinterpret_cast<const u32x4*>(vb + dc * 64 * 2 * T::U);
+        const u32x2 a0 = *reinterpret_cast<const u32x2*>(v0 + voff[j % T::R] + off);
+        const u32x2 a1 = *reinterpret_cast<const u32x2*>(v0 + T::BYTES + voff[j % T::R] + off);
+        a = u32x4{a0[0], a0[1], a1[0], a1[1]};
       }
-      acc[dc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(bh), acc[dc], 0, 0, 0);
-      acc[dc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(bl), acc[dc], 0, 0, 0);
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(bh), acc[j], 0, 0, 0);
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(bl), acc[j], 0, 0, 0);
     }
     __builtin_amdgcn_s_setprio(0);
   };
@@ -290,47 +314,54 @@ __global__ __launch_bounds__(kSegThreads) void segment_kernel(const SegmentParam
   const bool busy = __builtin_amdgcn_readfirstlane(wave * MPW) < nmem;
 
   if (nst > 0) {
-    // Stages 0 .. kPrefetch - 1 in flight; stage s lives in register slot
-    // s % kPrefetch until it is stored to LDS buffer s & 1.  The loads,
-    // stores and barriers run for whole groups of kPrefetch stages (past
-    // the last stage they move a valid tile nobody reads), so that every
-    // path keeps the same loads in flight.
-    Pieces stg[kPrefetch];
+    // Stages 0 .. kStages - 2 in flight; stage s lands in buffer s %
+    // kStages.  At the top of stage i this wavefront waits for its own two
+    // loads of stage i, and the barrier then stands for everyone's; every
+    // wavefront is also past stage i - 1, so its buffer takes stage
+    // i + kStages - 1.  The loads and barriers run for whole groups of
+    // kStages stages (past the last stage they move a valid tile nobody
+    // reads), so that every path keeps the same loads in flight.
 #pragma unroll
-    for (int j = 0; j < kPrefetch; ++j) stg[j] = gload(j < nst ? j : nst - 1);
-    lstore(0, stg[0]);
-    stg[0] = gload(kPrefetch < nst ? kPrefetch : nst - 1);
-    __syncthreads();
-    for (int i0 = 0; i0 < nst; i0 += kPrefetch) {
+    for (int j = 0; j < kStages - 1; ++j) issue(j < nst ? j : nst - 1, j);
+    for (int i0 = 0; i0 < nst; i0 += kStages) {
 #pragma unroll
-      for (int j = 0; j < kPrefetch; ++j) {
+      for (int j = 0; j < kStages; ++j) {
         const int i = i0 + j;
-        const uint8_t* buf = lds[i & 1];
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * (kStages - 2)));
+        // A barrier without a memory fence: a fence would wait for every
+        // load in flight, the later stages' included.  The memory clobber
+        // keeps the compiler from moving LDS reads across it, and this
+        // stage's data is covered by the wait above.
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        const int nx = i + kStages - 1;
+        issue(nx < nst ? nx : nst - 1, (j + kStages - 1) % kStages);
         if (busy) {
+          const uint8_t* buf = stage_buf(j);
 #pragma unroll
           for (int pp = 0; pp < T::TS / 2; ++pp) {
             const int t0 = i * T::TS + 2 * pp;
             if (t0 < ntiles) pair(buf, pp, t0 + 1 < ntiles);
           }
         }
-        // Stage i + 1 to the other buffer (every wavefront is past stage
-        // i - 1, which used it), then stage i + 1 + kPrefetch in flight.
-        const int jn = (j + 1) % kPrefetch;   // a constant once unrolled
-        lstore((i + 1) & 1, stg[jn]);
-        const int nx = i + 1 + kPrefetch;
-        stg[jn] = gload(nx < nst ? nx : nst - 1);
-        __syncthreads();
       }
     }
+    // No load may still be writing LDS when the workgroup ends.
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   }
 
   float ltot = l + __shfl_xor(l, 16, 64);
   ltot += __shfl_xor(ltot, 32, 64);
   if (bad) ltot = __builtin_nanf("");
   if (col_ok) {
+    // O^T block j = R e + s holds on row 4 qd + i the dim
+    // 16 (R e + ((4 qd / H) ^ s)) + H s + 4 qd % H + i.
     float* rec = p.partials + ((int64_t)(slot0 + mk) * p.num_q_heads + qh) * (D + 4);
 #pragma unroll
-    for (int dc = 0; dc < T::DC; ++dc) *reinterpret_cast<f32x4*>(rec + 16 * dc + 4 * qd) = acc[dc];
+    for (int j = 0; j < T::DC; ++j) {
+      const int e = j / T::R, s_ = j % T::R;
+      const int d0 = 16 * (T::R * e + (((4 * qd) / T::H) ^ s_)) + T::H * s_ + (4 * qd) % T::H;
+      *reinterpret_cast<f32x4*>(rec + d0) = acc[j];
+    }
     if (qd == 0) *reinterpret_cast<f32x4*>(rec + D) = f32x4{m, ltot, 0.f, 0.f};
   }
 }
