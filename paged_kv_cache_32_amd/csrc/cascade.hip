@@ -205,24 +205,25 @@ __global__ __launch_bounds__(kSegThreads) void segment_kernel(const SegmentParam
 
   // S^T = K Q^T of one tile from LDS.
   auto logits = [&](const uint8_t* kt_) -> f32x4 {
-    u32x4 kw[T::KLD];
-#pragma unroll
-    for (int c = 0; c < T::KLD; ++c) kw[c] = *reinterpret_cast<const u32x4*>(kt_ + c * 1024 + lane * 16);
+    // Each K operand is read one MFMA ahead of its use.
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+    u32x4 kn = *reinterpret_cast<const u32x4*>(kt_ + lane * 16);
 #pragma unroll
     for (int c = 0; c < T::KLD; ++c) {
+      const u32x4 kw = kn;
+      if (c + 1 < T::KLD) kn = *reinterpret_cast<const u32x4*>(kt_ + (c + 1) * 1024 + lane * 16);
       if constexpr (FP8) {
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
           u32x4 w;
-          w[0] = fp8x2_to_bf16x2<false>(kw[c][2 * hf]);
-          w[1] = fp8x2_to_bf16x2<true>(kw[c][2 * hf]);
-          w[2] = fp8x2_to_bf16x2<false>(kw[c][2 * hf + 1]);
-          w[3] = fp8x2_to_bf16x2<true>(kw[c][2 * hf + 1]);
+          w[0] = fp8x2_to_bf16x2<false>(kw[2 * hf]);
+          w[1] = fp8x2_to_bf16x2<true>(kw[2 * hf]);
+          w[2] = fp8x2_to_bf16x2<false>(kw[2 * hf + 1]);
+          w[3] = fp8x2_to_bf16x2<true>(kw[2 * hf + 1]);
           sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w), qop[2 * c + hf], sc, 0, 0, 0);
         }
       } else {
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kw[c]), qop[c], sc, 0, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kw), qop[c], sc, 0, 0, 0);
       }
     }
     return sc;
@@ -283,12 +284,9 @@ __global__ __launch_bounds__(kSegThreads) void segment_kernel(const SegmentParam
     split_p(pz, h0, l0);
     split_p(pz + 4, h1, l1);
     const u32x4 bh = {h0[0], h0[1], h1[0], h1[1]}, bl = {l0[0], l0[1], l1[0], l1[1]};
-    // The products with V run at raised wave priority: a wavefront that
-    // has reached them issues its MFMAs ahead of the others' softmax
-    // arithmetic, which keeps the matrix unit fed.
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int j = 0; j < T::DC; ++j) {
+    // V operand j, as the A operand of a 16x16x32 MFMA: 8 tokens (4 of tile
+    // 2p, then 4 of tile 2p + 1) of one dim, widened to bf16 for fp8.
+    auto v_op = [&](int j) -> u32x4 {
       const int off = (j / T::R) * 1024;
       u32x4 a;
       if constexpr (FP8) {
@@ -303,8 +301,23 @@ __global__ __launch_bounds__(kSegThreads) void segment_kernel(const SegmentParam
         const u32x2 a1 = *reinterpret_cast<const u32x2*>(v0 + T::BYTES + voff[j % T::R] + off);
         a = u32x4{a0[0], a0[1], a1[0], a1[1]};
       }
+      return a;
+    };
+    // The products with V run at raised wave priority: a wavefront that
+    // has reached them issues its MFMAs ahead of the others' softmax
+    // arithmetic, which keeps the matrix unit fed.
+    // Operand j + 1 is read while the products of operand j run; the
+    // scheduling barrier keeps the compiler from hoisting all the reads
+    // ahead of the products, which measured 8-10 % slower on the kernel.
+    __builtin_amdgcn_s_setprio(1);
+    u32x4 a = v_op(0);
+#pragma unroll
+    for (int j = 0; j < T::DC; ++j) {
+      const u32x4 an = j + 1 < T::DC ? v_op(j + 1) : a;
       acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(bh), acc[j], 0, 0, 0);
       acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(bl), acc[j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      a = an;
     }
     __builtin_amdgcn_s_setprio(0);
   };
