@@ -198,12 +198,13 @@ __device__ __forceinline__ int wave_incl_sum(int v, int lane) {
 // of the block's summary words (all heads' quads of 4 dimensions, 128 bytes
 // at 8 heads) per load instruction.  kScoreAhead dimension quads of every
 // page are in flight while the previous ones are summed.  Every LDS read of
-// a q+ / q- quad serves the lane's kScorePages pages: at four pages the
-// reads cost half what they cost at two (at 8 heads, a read of 8 distinct
-// quads takes the LDS as long as a full 1 KiB read), for 2 quads ahead
-// instead of 8 at the same register count.
+// a q+ / q- quad serves the lane's kScorePages pages (at 8 heads, a read of
+// 8 distinct quads takes the LDS as long as a full 1 KiB read).  Two pages
+// per lane keep a workgroup's item at 64 pages: four halved those reads but
+// left a batch of 64 sequences, or of 4 sequences of 8,192 pages, with
+// fewer items than the two workgroups per CU can hold.
 #ifndef PA_SCORE_PAGES
-#define PA_SCORE_PAGES 4
+#define PA_SCORE_PAGES 2
 #endif
 #ifndef PA_SCORE_LDS_FLOATS
 #define PA_SCORE_LDS_FLOATS 16384
