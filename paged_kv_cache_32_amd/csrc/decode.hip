@@ -56,7 +56,7 @@
 // Sub-blocks loaded per online-softmax step, and the fewest wavefronts per
 // SIMD the register allocation must leave room for.
 #ifndef PA_DECODE_STAGE
-#define PA_DECODE_STAGE 2
+#define PA_DECODE_STAGE 1
 #endif
 #ifndef PA_DECODE_STAGE_FP8
 #define PA_DECODE_STAGE_FP8 4
@@ -1092,9 +1092,10 @@ __global__ __launch_bounds__(kDecodeThreads, PA_DECODE_MIN_WAVES) void decode_ke
   }
 }
 
-// fp8 tiles are half the bytes of bf16 ones: twice the sub-blocks per stage
-// keep the same bytes in flight per wavefront (16 KiB per stage, two stages
-// in flight).
+// Sub-blocks per stage: one for bf16 (8 KiB of K and V per stage, two
+// stages in flight), four for fp8 (16 KiB).  Measured on MI355X, one bf16
+// sub-block per stage beat two by 1-2 % on long reads, and fp8 stages of
+// two sub-blocks lost 7 % to four.
 template <bool FP8>
 constexpr int kStage = FP8 ? PA_DECODE_STAGE_FP8 : PA_DECODE_STAGE;
 
