@@ -8,6 +8,8 @@ budgets below and above the page counts, and prefix-shared batches of
 random pool structure and chunk size.  Every case prints its parameters
 before it runs, so a failure names what to rerun."""
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -65,10 +67,13 @@ def _cascade_case(rng):
     return c
 
 
-DECODE = _draw(101, 24, _decode_case)
-WINDOW = _draw(102, 16, _window_case)
-QUEST = _draw(103, 10, _quest_case)
-CASCADE = _draw(104, 10, _cascade_case)
+# PA_RANDOM_SCALE=k draws k times as many cases from the same generators
+# (the first ones are always the default run's), for longer sweeps.
+SCALE = max(1, int(os.environ.get("PA_RANDOM_SCALE", "1")))
+DECODE = _draw(101, 24 * SCALE, _decode_case)
+WINDOW = _draw(102, 16 * SCALE, _window_case)
+QUEST = _draw(103, 10 * SCALE, _quest_case)
+CASCADE = _draw(104, 10 * SCALE, _cascade_case)
 
 
 def _label(kind, i, c):
