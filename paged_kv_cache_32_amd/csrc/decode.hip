@@ -93,22 +93,27 @@ constexpr float kNegInf = -__builtin_huge_valf();
 // first stage of a piece is rare.
 constexpr float kRescaleSlack = 8.0f;
 
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int t = __shfl_up(v, d, 64);
-    if (lane >= d) v += t;
-  }
+// Inclusive prefix sum over the wavefront's 64 lanes with DPP row shifts and
+// row broadcasts (seven dependent VALU adds, no LDS permutes): each lane first
+// sums itself and the three lanes before it in its row of 16, then the row
+// sums double across banks (shift 4, then 8), and rows take the last lane of
+// the row before them (broadcasts of lanes 15 and 31).
+__device__ __forceinline__ int wave_incl_scan(int v, int /*lane*/) {
+  const int o = v;
+  v += __builtin_amdgcn_update_dpp(0, o, 0x111, 0xf, 0xf, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, o, 0x112, 0xf, 0xf, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, o, 0x113, 0xf, 0xf, true);   // row_shr:3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xe, true);   // row_shr:4, banks 1-3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xc, true);   // row_shr:8, banks 2-3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15, rows 1 and 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31, rows 2 and 3
   return v;
 }
 
 __device__ __forceinline__ int readlane(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
 
-__device__ __forceinline__ int wave_reduce_sum(int v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
-  return v;
-}
+// Sum over the wavefront, the same in every lane.
+__device__ __forceinline__ int wave_reduce_sum(int v) { return readlane(wave_incl_scan(v, 0), 63); }
 
 // First token a sequence of L tokens attends to: L - W with a window of W
 // tokens ("KV Cache Engineering for LLM Serving", section 3, sliding
