@@ -301,13 +301,16 @@ __global__ __launch_bounds__(kScoreThreads) void page_score_kernel(const SelectP
 #pragma unroll
       for (int k = 0; k < PP; ++k)
         row[k] = reinterpret_cast<const u32x4*>(p.words + summary_word(blk[k], h, 0, Hkv, D));
-      // Quad j of a page's head h sits Hkv quads after quad j - 1.
+      // Quad j of a page's head h sits Hkv quads after quad j - 1.  The
+      // loads are non-temporal: a call reads each summary line once, and
+      // from HBM (a step's other reads evict the summaries between calls)
+      // they measured faster than cached loads.
       auto load = [&](u32x4 (&v)[PF][PP], int j0) {
 #pragma unroll
         for (int jj = 0; jj < PF; ++jj) {
           const int j = j0 + jj < Q4 ? j0 + jj : Q4 - 1;   // past the end: a repeat, never summed
 #pragma unroll
-          for (int k = 0; k < PP; ++k) v[jj][k] = row[k][(int64_t)j * Hkv];
+          for (int k = 0; k < PP; ++k) v[jj][k] = __builtin_nontemporal_load(&row[k][(int64_t)j * Hkv]);
         }
       };
       float acc[PP][GP];
